@@ -1,0 +1,164 @@
+"""Exact-arithmetic versions of the row ops, for tiny rows.
+
+TEST INFRASTRUCTURE (see the package docstring).  Independent of
+:mod:`oracle.rows` and :mod:`oracle.bf16`: inputs become exact rationals
+(``fractions.Fraction``), sums of squares are exact, square roots and
+quotients are carried in 60-digit ``decimal`` arithmetic, and rounding to
+bf16 / fp32 is done on the exact rational by integer arithmetic.  Each result
+comes with a flag that marks values lying so close to a rounding midpoint that
+60 digits, or float64's rounding in the fast oracle, could decide either way.
+
+Definitions followed: TensorFold PR #1260 (the l2 and slerp row kernels; the
+lerp in fp32 steps) and the DragonScale README's W_eff formula ("What
+DragonScale changes").
+"""
+from __future__ import annotations
+
+import struct
+from decimal import Decimal, localcontext
+from fractions import Fraction
+from typing import List, Optional, Sequence, Tuple
+
+__all__ = ["bits_to_fraction", "round_fraction", "bf16_of", "fp32_of",
+           "l2_row", "slerp_row", "rownorm_row", "NEAR_TIE_REL"]
+
+PREC = 60
+NEAR_TIE_REL = Fraction(1, 10 ** 12)     # flag values this close to a midpoint
+
+
+def bits_to_fraction(bits: int, width: int = 16) -> Optional[Fraction]:
+    """Exact value of a bf16 (width 16) or fp32 (width 32) bit pattern."""
+    if width == 16:
+        bits = bits << 16
+    sign = -1 if bits >> 31 else 1
+    exp = (bits >> 23) & 0xFF
+    man = bits & 0x7FFFFF
+    if exp == 0xFF:
+        return None                                  # inf / nan: not used here
+    if exp == 0:
+        return sign * Fraction(man, 1 << 149)
+    return sign * Fraction((1 << 23) | man, 1) * Fraction(2) ** (exp - 150)
+
+
+def f32_to_fraction(x: float) -> Fraction:
+    (b,) = struct.unpack("<I", struct.pack("<f", x))
+    return bits_to_fraction(b, 32)
+
+
+def _binade(a: Fraction) -> int:
+    """floor(log2(a)) for a > 0, by integer arithmetic."""
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if a < Fraction(2) ** e:
+        e -= 1
+    return e
+
+
+def round_fraction(v: Fraction, sig_bits: int, emin: int, emax: int
+                   ) -> Tuple[Fraction, bool]:
+    """Round exact v to a binary format (nearest, ties to even).
+
+    sig_bits counts the leading bit; emin is the smallest normal exponent.
+    Returns (rounded value or +-inf as None-free Fraction sentinel, near_tie),
+    where near_tie says v is within NEAR_TIE_REL (relative) of a midpoint.
+    Overflow returns Fraction(+-2**(emax+1)) so callers can test for it.
+    """
+    if v == 0:
+        return Fraction(0), False
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = max(_binade(a), emin)
+    q = Fraction(2) ** (e - sig_bits + 1)
+    m = a / q
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    near = abs(rem - Fraction(1, 2)) * q <= NEAR_TIE_REL * a
+    r = fl * q
+    if r >= Fraction(2) ** (emax + 1):
+        r = Fraction(2) ** (emax + 1)               # overflow marker
+    return sign * r, near
+
+
+def bf16_of(v: Fraction) -> Tuple[Fraction, bool]:
+    return round_fraction(v, 8, -126, 127)
+
+
+def fp32_of(v: Fraction) -> Tuple[Fraction, bool]:
+    return round_fraction(v, 24, -126, 127)
+
+
+def _dec(f: Fraction) -> Decimal:
+    return Decimal(f.numerator) / Decimal(f.denominator)
+
+
+def _l2_exact(s: Sequence[Fraction], eps: Fraction) -> Tuple[List[Fraction], List[bool]]:
+    """bf16(s_j / sqrt(sum s^2 + eps)) for every j, with near-tie flags."""
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        total = sum((x * x for x in s), Fraction(0)) + eps
+        root = _dec(total).sqrt()
+        out, near = [], []
+        for x in s:
+            q = Fraction(_dec(x) / root)
+            r, n = bf16_of(q)
+            out.append(r)
+            near.append(n)
+    return out, near
+
+
+def l2_row(x_bits: Sequence[int], r_bits: Optional[Sequence[int]], eps32: float
+           ) -> Tuple[List[Fraction], List[bool]]:
+    """One row of l2_rows, exactly: s = x or bf16(x + r), then the normalised row."""
+    x = [bits_to_fraction(int(b)) for b in x_bits]
+    if r_bits is not None:
+        # x + r is exact here, so its rounding is exact too (a tie is a tie)
+        s = [bf16_of(xj + bits_to_fraction(int(rb)))[0] for xj, rb in zip(x, r_bits)]
+    else:
+        s = x
+    return _l2_exact(s, f32_to_fraction(eps32))
+
+
+def slerp_row(res_bits: Sequence[int], out_bits: Sequence[int],
+              alpha: Sequence[float], eps32: float) -> Tuple[List[Fraction], bool]:
+    """One row of slerp_rows, exactly; the flag covers the whole row.
+
+    a, b are exact bf16 roundings of the exact l2 rows; the lerp is three
+    binary32 roundings (b - a, |alpha| * that, a + that); h is the exact bf16
+    rounding of the exact l2 of u.  The lerp's operands are exact, so its
+    roundings are exact; a near-tie in a, b or h (values carried through a
+    60-digit square root) flags the row.
+    """
+    eps = f32_to_fraction(eps32)
+    res = [bits_to_fraction(int(b)) for b in res_bits]
+    out = [bits_to_fraction(int(b)) for b in out_bits]
+    a, na = _l2_exact(res, eps)
+    b, nb = _l2_exact(out, eps)
+    u = []
+    near = any(na) or any(nb)
+    for aj, bj, al in zip(a, b, alpha):
+        d = fp32_of(bj - aj)[0]
+        t = fp32_of(abs(f32_to_fraction(float(al))) * d)[0]
+        u.append(fp32_of(aj + t)[0])
+    h, nh = _l2_exact(u, eps)
+    return h, near or any(nh)
+
+
+def rownorm_row(w: Sequence[float], g: float, rho: float
+                ) -> Tuple[Fraction, List[Fraction], bool]:
+    """One weight row exactly: fp32(||w||) and bf16(g rho w / ||w||), with a flag."""
+    wf = [f32_to_fraction(x) for x in w]
+    gf = f32_to_fraction(g) * f32_to_fraction(rho)
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        total = sum((x * x for x in wf), Fraction(0))
+        if total == 0:
+            return Fraction(0), [Fraction(0)] * len(wf), False
+        root = _dec(total).sqrt()
+        n32, near = fp32_of(Fraction(root))
+        out = []
+        for x in wf:
+            r, n = bf16_of(Fraction(_dec(gf * x) / root))
+            out.append(r)
+            near = near or n
+    return n32, out, near

@@ -1,0 +1,346 @@
+"""Tolerance checks of a result against the oracle.
+
+TEST INFRASTRUCTURE (see the package docstring).
+
+Two checks:
+
+1. **Contract**: every bf16 output within one bf16 ulp (the spacing at the
+   oracle value's binade) of the oracle's value, with NaN where the oracle has
+   NaN, the same infinities, and the same sign on zeros; every fp32 row length
+   within 2e-6 relative of the float64 length.
+
+2. **Admissible set** (the method of TensorFold PR #1260's kernel-contract
+   check: each output compared with float64's value at the bf16 rounding
+   points "as a range over the fp32 run's spread").  For every element the
+   float64 value of what an fp32 run may compute is bounded above and below,
+   and the admissible outputs are the bf16 values from bf16(lo) to bf16(hi):
+   one value, or two at a near-tie.  The fp32 run modelled here:
+
+   * a sum of squares of exactly representable terms accumulated by any tree
+     whose deepest path has at most ``depth`` additions, each rounded once
+     (relative error at most (1 + u)**depth - 1 for nonnegative terms,
+     u = 2**-24), with the sum kept free of overflow and of underflow loss by
+     power-of-two scaling;
+   * one rounding each for adding eps, the square root and the reciprocal;
+   * one rounding for each product, plus 2**-149 absolute for results in the
+     subnormal range;
+   * for slerp, the lerp's three fp32 steps exactly as the oracle does them,
+     over every admissible choice of a and b.
+
+   An interval that spans more than two bf16 values means the bound is too
+   loose for the check to be sharp; it is reported, not hidden.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+from .bf16 import bf16_rne, bf16_ulp, bf16_value
+from .rows import eps_as_passed, sum_sq
+
+U = 2.0 ** -24
+ETA = 2.0 ** -149          # least fp32 subnormal step
+F64_WIDEN = 2.0 ** -46     # covers float64 rounding inside the bound arithmetic
+
+__all__ = ["contract_bf16", "contract_rel", "Report", "admissible_l2_rows",
+           "admissible_slerp_rows", "admissible_rownorm", "default_depth",
+           "ordered"]
+
+
+def default_depth(cols: int) -> int:
+    """A bound on the additions along any path of a row's fp32 sum tree."""
+    return cols // 64 + 32
+
+
+# ----------------------------------------------------------------- contract
+
+def contract_bf16(got_bits, want_bits, zero_sign: bool = True) -> np.ndarray:
+    """Boolean mask of elements that MEET the 1-ulp contract."""
+    g = bf16_value(got_bits)
+    w = bf16_value(want_bits)
+    gn, wn = np.isnan(g), np.isnan(w)
+    with np.errstate(all="ignore"):
+        near = np.abs(g - w) <= bf16_ulp(w)
+    inf = np.isinf(g) | np.isinf(w)
+    ok = np.where(inf, g == w, near)
+    ok = np.where(gn | wn, gn & wn, ok)
+    if zero_sign:
+        both0 = (g == 0) & (w == 0)
+        ok &= ~both0 | (np.signbit(g) == np.signbit(w))
+    return ok
+
+
+def contract_rel(got, want, rel: float = 2e-6) -> np.ndarray:
+    """Boolean mask of fp32 values within ``rel`` of the float64/fp32 reference."""
+    g = np.asarray(got, dtype=np.float64)
+    w = np.asarray(want, dtype=np.float64)
+    gn, wn = np.isnan(g), np.isnan(w)
+    with np.errstate(all="ignore"):
+        ok = np.abs(g - w) <= rel * np.abs(w)
+        ok |= (g == w)
+    return np.where(gn | wn, gn & wn, ok)
+
+
+# ------------------------------------------------------------ admissible set
+
+def ordered(bits) -> np.ndarray:
+    """bf16 bits -> integers in value order (+0 and -0 both map to 0)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+@dataclass
+class Report:
+    """Outcome of an admissible-set check over many elements."""
+    n: int = 0
+    outside: int = 0          # result not in its admissible set
+    two: int = 0              # elements whose set has two values (near-ties)
+    loose: int = 0            # sets wider than two values (bound too loose)
+    first_bad: list = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return self.outside == 0 and self.loose == 0
+
+    def merge(self, other: "Report") -> "Report":
+        self.n += other.n
+        self.outside += other.outside
+        self.two += other.two
+        self.loose += other.loose
+        self.first_bad = (self.first_bad + other.first_bad)[:20]
+        return self
+
+    def __str__(self) -> str:
+        return (f"n={self.n} outside={self.outside} two={self.two} "
+                f"loose={self.loose} first_bad={self.first_bad[:5]}")
+
+
+def _sum_bounds(sq_lo: np.ndarray, sq_hi: np.ndarray, depth: int):
+    """Bounds of an fp32 sum of nonnegative terms lying in [sq_lo, sq_hi]."""
+    lo = math.fsum(sq_lo)
+    hi = math.fsum(sq_hi)
+    k = depth + 1
+    return lo * (1 - U) ** k * (1 - F64_WIDEN), hi * (1 + U) ** k * (1 + F64_WIDEN)
+
+
+def _inv_bounds(s_lo: float, s_hi: float, eps64: float):
+    """Bounds of fl(1 / fl(sqrt(fl(S + eps)))) for S in [s_lo, s_hi]."""
+    t_lo = (s_lo + eps64) * (1 - 2 * U)
+    t_hi = (s_hi + eps64) * (1 + 2 * U)
+    r_lo = math.sqrt(t_lo) * (1 - U)
+    r_hi = math.sqrt(t_hi) * (1 + U)
+    with np.errstate(all="ignore"):
+        inv_lo = (1.0 / r_hi) * (1 - U) * (1 - F64_WIDEN) if r_hi > 0 else math.inf
+        inv_hi = (1.0 / r_lo) * (1 + U) * (1 + F64_WIDEN) if r_lo > 0 else math.inf
+    return inv_lo, inv_hi
+
+
+def _product_bounds(v_lo, v_hi, c_lo, c_hi):
+    """Bounds of fl(v * c) for v in [v_lo, v_hi] (arrays), c in [c_lo, c_hi] > 0."""
+    with np.errstate(all="ignore"):
+        cands = np.stack([v_lo * c_lo, v_lo * c_hi, v_hi * c_lo, v_hi * c_hi])
+    lo = cands.min(axis=0)
+    hi = cands.max(axis=0)
+    lo = np.where(lo >= 0, lo * (1 - U), lo * (1 + U)) * (1 + np.sign(-lo) * F64_WIDEN) - 2 * ETA
+    hi = np.where(hi >= 0, hi * (1 + U), hi * (1 - U)) * (1 + np.sign(hi) * F64_WIDEN) + 2 * ETA
+    return lo, hi
+
+
+def _judge(got_bits, lo, hi, exact_bits, exact_mask, zero_any_sign,
+           base_index, report: Report):
+    """Compare one row: interval elements and exactly-determined elements."""
+    lo_b = bf16_rne(lo)
+    hi_b = bf16_rne(hi)
+    g = ordered(got_bits)
+    ol, oh = ordered(lo_b), ordered(hi_b)
+    width = oh - ol + 1
+    inside = (g >= ol) & (g <= oh)
+    # Exactly-determined elements: zeros from zero inputs, non-finite rows.
+    if exact_mask is not None and exact_mask.any():
+        gv = bf16_value(got_bits[exact_mask])
+        ev = bf16_value(exact_bits[exact_mask])
+        same = (np.isnan(gv) & np.isnan(ev)) | (gv == ev)
+        if not zero_any_sign:
+            z = (gv == 0) & (ev == 0)
+            same &= ~z | (np.signbit(gv) == np.signbit(ev))
+        inside[exact_mask] = same
+        width[exact_mask] = 1
+    n = got_bits.size
+    bad = np.nonzero(~inside)[0]
+    report.n += n
+    report.outside += bad.size
+    report.two += int((width == 2).sum())
+    report.loose += int((width > 2).sum())
+    for j in bad[: max(0, 20 - len(report.first_bad))]:
+        report.first_bad.append(int(base_index + j))
+
+
+def _row_inv(s_row: np.ndarray, eps64: float, depth: int):
+    sq = s_row.astype(np.float64) ** 2
+    s_lo, s_hi = _sum_bounds(sq, sq, depth)
+    return _inv_bounds(s_lo, s_hi, eps64)
+
+
+def _l2_value_bounds(s_row: np.ndarray, eps64: float, depth: int):
+    inv_lo, inv_hi = _row_inv(s_row, eps64, depth)
+    return _product_bounds(s_row, s_row, inv_lo, inv_hi)
+
+
+def admissible_l2_rows(got_bits, x_bits, r_bits=None, eps: float = 1e-6,
+                       depth: Optional[int] = None, row_ids=None) -> Report:
+    """Strict check of l2_rows outputs ``got_bits`` for the given input rows."""
+    from .rows import l2_rows as l2_ref
+    x = bf16_value(np.atleast_2d(x_bits))
+    if r_bits is not None:
+        with np.errstate(all="ignore"):
+            s = bf16_value(bf16_rne(x + bf16_value(np.atleast_2d(r_bits))))
+    else:
+        s = x
+    got = np.atleast_2d(got_bits)
+    cols = s.shape[1]
+    depth = default_depth(cols) if depth is None else depth
+    eps64 = eps_as_passed(eps)
+    rep = Report()
+    for i in range(s.shape[0]):
+        row = s[i]
+        base = (row_ids[i] if row_ids is not None else i) * cols
+        if not np.isfinite(row).all() or (eps64 == 0 and not row.any()):
+            exact = l2_ref(x_bits[i:i + 1] if x_bits.ndim == 2 else x_bits,
+                           None if r_bits is None else r_bits[i:i + 1], eps)[0]
+            _judge(got[i], row, row, exact, np.ones(cols, bool), False, base, rep)
+            continue
+        lo, hi = _l2_value_bounds(row, eps64, depth)
+        zero = row == 0
+        exact = np.where(np.signbit(row), np.uint16(0x8000), np.uint16(0)).astype(np.uint16)
+        _judge(got[i], lo, hi, exact, zero, False, base, rep)
+    return rep
+
+
+def _f32_lerp(a32, b32, abs_alpha):
+    with np.errstate(all="ignore"):
+        d = b32 - a32
+        t = abs_alpha * d
+        return a32 + t
+
+
+def admissible_slerp_rows(got_bits, res_bits, out_bits, alpha, eps: float = 1e-6,
+                          depth: Optional[int] = None, row_ids=None) -> Report:
+    """Strict check of slerp_rows outputs over every admissible a and b."""
+    from .rows import slerp_rows as slerp_ref
+    res = bf16_value(np.atleast_2d(res_bits))
+    out = bf16_value(np.atleast_2d(out_bits))
+    got = np.atleast_2d(got_bits)
+    cols = res.shape[1]
+    depth = default_depth(cols) if depth is None else depth
+    eps64 = eps_as_passed(eps)
+    abs_alpha = np.abs(np.asarray(alpha, dtype=np.float32))
+    rep = Report()
+    for i in range(res.shape[0]):
+        base = (row_ids[i] if row_ids is not None else i) * cols
+        if not (np.isfinite(res[i]).all() and np.isfinite(out[i]).all()
+                and np.isfinite(abs_alpha).all()):
+            exact = slerp_ref(np.atleast_2d(res_bits)[i:i + 1],
+                              np.atleast_2d(out_bits)[i:i + 1], alpha, eps)[0]
+            _judge(got[i], res[i], res[i], exact, np.ones(cols, bool), False, base, rep)
+            continue
+        cand = []
+        for v in (res[i], out[i]):
+            lo, hi = _l2_value_bounds(v, eps64, depth)
+            lo_b, hi_b = bf16_rne(lo), bf16_rne(hi)
+            if (ordered(hi_b) - ordered(lo_b) > 1).any():
+                rep.loose += int((ordered(hi_b) - ordered(lo_b) > 1).sum())
+            cand.append((bf16_value(lo_b).astype(np.float32),
+                         bf16_value(hi_b).astype(np.float32)))
+        (a_lo, a_hi), (b_lo, b_hi) = cand
+        us = np.stack([_f32_lerp(a, b, abs_alpha)
+                       for a in (a_lo, a_hi) for b in (b_lo, b_hi)]).astype(np.float64)
+        sq = us ** 2
+        s_lo, s_hi = _sum_bounds(sq.min(axis=0), sq.max(axis=0), depth)
+        inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, eps64)
+        # admissible: the union over the choices of (a, b) of each choice's set
+        g = ordered(got[i])
+        inside = np.zeros(cols, bool)
+        width = np.zeros(cols, np.int64)
+        for u in us:
+            lo, hi = _product_bounds(u, u, inv_lo, inv_hi)
+            ol, oh = ordered(bf16_rne(lo)), ordered(bf16_rne(hi))
+            zero = u == 0
+            # a zero u gives a zero h of the same sign
+            zs = np.where(np.signbit(u), -1, 1)
+            ok = np.where(zero, (g == 0) & (np.where(np.signbit(bf16_value(got[i])), -1, 1) == zs),
+                          (g >= ol) & (g <= oh))
+            inside |= ok
+            width = np.maximum(width, np.where(zero, 1, oh - ol + 1))
+        bad = np.nonzero(~inside)[0]
+        rep.n += cols
+        rep.outside += bad.size
+        rep.two += int((width == 2).sum())
+        rep.loose += int((width > 2).sum())
+        for j in bad[: max(0, 20 - len(rep.first_bad))]:
+            rep.first_bad.append(int(base + j))
+    return rep
+
+
+def admissible_rownorm(got_norm, got_weff_bits, w, g, rho: float = 1.0,
+                       depth: Optional[int] = None, row_offset: int = 0):
+    """Strict check of one matrix: (norm Report, W_eff Report).
+
+    The row length must lie in [fl(sqrt(S_lo)), fl(sqrt(S_hi))]; W_eff in the
+    admissible set of fl(w * fl(fl(g * rho) / norm)).
+    """
+    w64 = np.asarray(w, dtype=np.float64)
+    g64 = np.asarray(g, dtype=np.float64)
+    rho64 = float(np.float32(rho))
+    rows, cols = w64.shape
+    depth = default_depth(cols) if depth is None else depth
+    got_w = np.atleast_2d(got_weff_bits)
+    got_n = np.asarray(got_norm, dtype=np.float64)
+    rn, rw = Report(), Report()
+    for i in range(rows):
+        base = (row_offset + i) * cols
+        row = w64[i]
+        if not np.isfinite(row).all() or not np.isfinite(g64[i]):
+            from .rows import weight_rownorm_gain as ref
+            n_ref, w_ref = ref([w[i:i + 1]], [g[i:i + 1]], [rho])
+            rn.n += 1
+            same = (np.isnan(got_n[i]) and np.isnan(n_ref[0][0])) or got_n[i] == n_ref[0][0]
+            rn.outside += 0 if same else 1
+            _judge(got_w[i], row, row, w_ref[0][0], np.ones(cols, bool), True, base, rw)
+            continue
+        s_lo, s_hi = _sum_bounds(row ** 2, row ** 2, depth)
+        n_lo = math.sqrt(s_lo) * (1 - U) * (1 - F64_WIDEN) - ETA
+        n_hi = math.sqrt(s_hi) * (1 + U) * (1 + F64_WIDEN) + ETA
+        rn.n += 1
+        if not (n_lo <= got_n[i] <= n_hi):
+            rn.outside += 1
+            if len(rn.first_bad) < 20:
+                rn.first_bad.append(row_offset + i)
+        if s_hi == 0:
+            exact = np.zeros(cols, np.uint16)
+            _judge(got_w[i], row, row, exact, np.ones(cols, bool), True, base, rw)
+            continue
+        gr = g64[i] * rho64
+        gr_lo, gr_hi = sorted((gr * (1 - U), gr * (1 + U)))
+        if rho64 == 1.0:
+            gr_lo = gr_hi = gr
+        r_lo = max(math.sqrt(s_lo) * (1 - U), 0.0)
+        r_hi = math.sqrt(s_hi) * (1 + U)
+        with np.errstate(all="ignore"):
+            cs = [gr_lo / r_lo, gr_lo / r_hi, gr_hi / r_lo, gr_hi / r_hi]
+        c_lo = min(cs)
+        c_hi = max(cs)
+        c_lo = c_lo * (1 - U) if c_lo >= 0 else c_lo * (1 + U)
+        c_hi = c_hi * (1 + U) if c_hi >= 0 else c_hi * (1 - U)
+        with np.errstate(all="ignore"):
+            cands = np.stack([row * c_lo, row * c_hi])
+        lo = cands.min(axis=0)
+        hi = cands.max(axis=0)
+        lo = np.where(lo >= 0, lo * (1 - U), lo * (1 + U)) * (1 - np.sign(lo) * F64_WIDEN) - 2 * ETA
+        hi = np.where(hi >= 0, hi * (1 + U), hi * (1 - U)) * (1 + np.sign(hi) * F64_WIDEN) + 2 * ETA
+        zero = row == 0
+        _judge(got_w[i], lo, hi, np.zeros(cols, np.uint16), zero, True, base, rw)
+    return rn, rw

@@ -1,0 +1,148 @@
+"""The row ops written out from their definitions, in float64.
+
+TEST INFRASTRUCTURE (see the package docstring).  Plain and slow: one row at a
+time, ``math.fsum`` for every sum of squares, float64 everywhere except at the
+rounding points the pages fix.
+
+Sources (cited by page and section):
+
+* TensorFold PR #1260, the commit adding the unit-sphere row kernels for the
+  looped nGPT model: ``l2_rows`` computes y = bf16(s / sqrt(sum(s^2) + eps))
+  with s = x, or s = bf16(x + r) when a residual is given; ``slerp_rows``
+  computes h = bf16(l2(a + |alpha| (b - a))) with a = bf16(l2(res)),
+  b = bf16(l2(out)) and the lerp done in fp32 steps.  Its rounding points are
+  the sum before the norm, the slerp's a and b, and each output.  eps is added
+  to the sum of squares (same PR, the q/k row kernel's "eps on the sum").
+* DragonScale README, "What DragonScale changes": W_eff = diag(g) r W / ||W||_row,
+  one gain per row, r the row radius (1 for linears and convs, sqrt(dim) for
+  embeddings).  The formula has no eps.
+
+Readings where the pages leave a step open:
+
+* bf16 rounding is to nearest, ties to even.
+* eps arrives as an fp32 value, so the oracle uses float64(float32(eps)).
+* The lerp's "fp32 steps" are three separately rounded binary32 operations in
+  the written order: d = b - a, t = |alpha| * d, u = a + t (no fused
+  multiply-add).  u itself is not rounded to bf16.  numpy's float32 arithmetic
+  is IEEE binary32 with round-to-nearest-even, which is what these steps are.
+* A weight row of length zero scales by 0 (W_eff = bf16(w * 0)).
+* Non-finite inputs follow IEEE float64 semantics.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from .bf16 import bf16_rne, bf16_value
+
+__all__ = ["eps_as_passed", "l2_rows", "slerp_rows", "slerp_rows_detail",
+           "weight_rownorm_gain", "sum_sq"]
+
+
+def eps_as_passed(eps: float) -> float:
+    """eps as the kernels receive it: rounded to fp32, held in float64."""
+    return float(np.float32(eps))
+
+
+def sum_sq(row: np.ndarray) -> float:
+    """Correctly rounded float64 sum of squares of one row.
+
+    Squares of bf16 and fp32 values are exact in float64 (at most 48
+    significant bits), so ``math.fsum`` returns the exact sum, rounded once.
+    """
+    with np.errstate(all="ignore"):
+        sq = np.asarray(row, dtype=np.float64) ** 2
+    if np.isnan(sq).any():
+        return math.nan
+    if np.isinf(sq).any():
+        return math.inf
+    return math.fsum(sq)
+
+
+def _l2_of_values(s: np.ndarray, eps64: float) -> np.ndarray:
+    """Row-wise s / sqrt(sum(s^2) + eps) in float64 (not yet rounded)."""
+    out = np.empty_like(s)
+    with np.errstate(all="ignore"):
+        for i in range(s.shape[0]):
+            d = math.sqrt(sum_sq(s[i]) + eps64)
+            out[i] = s[i] / d
+    return out
+
+
+def l2_rows(x_bits: np.ndarray, r_bits: Optional[np.ndarray] = None,
+            eps: float = 1e-6) -> np.ndarray:
+    """y = bf16(s / sqrt(sum(s^2) + eps)), s = x or bf16(x + r); bf16 bits in/out.
+
+    TensorFold PR #1260, the l2 row kernel.  The sum x + r of two bf16 values
+    is formed in float64 and rounded once to bf16 (the first rounding point).
+    """
+    x = bf16_value(np.atleast_2d(x_bits))
+    if r_bits is not None:
+        with np.errstate(all="ignore"):
+            s = bf16_value(bf16_rne(x + bf16_value(np.atleast_2d(r_bits))))
+    else:
+        s = x
+    y = _l2_of_values(s, eps_as_passed(eps))
+    return bf16_rne(y).reshape(np.shape(x_bits))
+
+
+def slerp_rows_detail(res_bits: np.ndarray, out_bits: np.ndarray,
+                      alpha: np.ndarray, eps: float = 1e-6
+                      ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """slerp_rows with its intermediates: returns (a_bits, b_bits, u_f32, h_bits).
+
+    TensorFold PR #1260, the slerp row kernel (the nGPT residual update):
+    a = bf16(l2(res)), b = bf16(l2(out)), u = a + |alpha| (b - a) in fp32
+    steps, h = bf16(l2(u)).  alpha is one fp32 value per column.
+    """
+    eps64 = eps_as_passed(eps)
+    res = bf16_value(np.atleast_2d(res_bits))
+    out = bf16_value(np.atleast_2d(out_bits))
+    a_bits = bf16_rne(_l2_of_values(res, eps64))
+    b_bits = bf16_rne(_l2_of_values(out, eps64))
+    a32 = bf16_value(a_bits).astype(np.float32)
+    b32 = bf16_value(b_bits).astype(np.float32)
+    abs_alpha = np.abs(np.asarray(alpha, dtype=np.float32))
+    with np.errstate(all="ignore"):
+        d = b32 - a32                 # fp32 step 1
+        t = abs_alpha * d             # fp32 step 2
+        u = a32 + t                   # fp32 step 3
+    h = _l2_of_values(u.astype(np.float64), eps64)
+    return a_bits, b_bits, u, bf16_rne(h)
+
+
+def slerp_rows(res_bits: np.ndarray, out_bits: np.ndarray, alpha: np.ndarray,
+               eps: float = 1e-6) -> np.ndarray:
+    """h bits of :func:`slerp_rows_detail`."""
+    return slerp_rows_detail(res_bits, out_bits, alpha, eps)[3].reshape(np.shape(res_bits))
+
+
+def weight_rownorm_gain(w: Sequence[np.ndarray], gain: Sequence[np.ndarray],
+                        radius: Sequence[float]
+                        ) -> Tuple[list, list]:
+    """Per matrix m and row i: n_i = ||W_i||, W_eff_i = bf16(g_i rho W_i / n_i).
+
+    DragonScale README, "What DragonScale changes".  Returns, per matrix, the
+    fp32 row lengths (the float64 length rounded to fp32) and the bf16 bits of
+    W_eff.  A zero-length row scales by 0.
+    """
+    norms, weffs = [], []
+    for wm, gm, rho in zip(w, gain, radius):
+        w64 = np.asarray(wm, dtype=np.float64)
+        g64 = np.asarray(gm, dtype=np.float64)
+        rho64 = float(np.float32(rho))
+        n = np.empty(w64.shape[0])
+        weff = np.empty_like(w64)
+        with np.errstate(all="ignore"):
+            for i in range(w64.shape[0]):
+                ss = sum_sq(w64[i])
+                n[i] = math.sqrt(ss)
+                if n[i] == 0.0:
+                    weff[i] = w64[i] * 0.0
+                else:
+                    weff[i] = (g64[i] * rho64 * w64[i]) / n[i]
+        norms.append(n.astype(np.float32))
+        weffs.append(bf16_rne(weff))
+    return norms, weffs

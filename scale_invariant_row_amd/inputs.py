@@ -1,0 +1,217 @@
+"""Seeded synthetic workloads for the row ops.
+
+This module draws random numbers and lays out the workloads; it holds none of
+the row ops' arithmetic.  Every value is fixed here once, as bit patterns
+(bf16 activations as ``uint16``, fp32 weights/gains/scales as ``float32``), and
+the same arrays feed the CPU oracle and the GPU library.
+
+Recipe (shared by every workload):
+
+* ``numpy.random.Generator(PCG64(SeedSequence(seed)))``; one child stream per
+  tensor, spawned in a fixed order (``SeedSequence.spawn``).
+* Activations: float64 samples, cast to float32 by numpy, then to bf16 by
+  torch's own round-to-nearest-even conversion.  The cast only decides what the
+  input values are.
+* Weights and gains: float64 samples cast to float32 by numpy (round to
+  nearest even).
+
+Workloads (widths follow the pages: activation rows 1,024-8,192 wide and the
+7,168-wide MLP row of the looped nGPT model in the TensorFold Dory PR; weights
+are the linears of a 12-layer pre-norm transformer, d=768, d_ff=3072, as in the
+DragonScale README's unit-row op):
+
+========================  =======================================================
+name                      contents
+========================  =======================================================
+l2_rows_64x1024           x ~ N(0,1), no residual, eps 1e-6
+l2_rows_res_8192x4096     x, r ~ N(0,1) independent, eps 1e-6
+slerp_rows_8192x7168      res ~ N(0,1), out ~ N(0, sd 2), alpha ~ U(-0.2, 0.2)
+rownorm_gain_12x4_d768    12 x {qkv 2304x768, o 768x768, up 3072x768,
+                          down 768x3072}; W ~ N(0, sd 0.02); g ~ U(0.5, 2); rho 1
+l2_rows_res_stress        32768x8192: x ~ N(0,1), 1% of entries x1000; 327 rows
+                          all-zero in x and r; 327 rows of integers in [-64, 64]
+                          with r = 0; r ~ N(0,1) elsewhere
+slerp_rows_8192x4096      as slerp_rows_8192x7168 at width 4096
+========================  =======================================================
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+__all__ = [
+    "L2Case", "SlerpCase", "RownormCase",
+    "to_bf16_bits", "l2_case", "slerp_case", "rownorm_case",
+    "transformer_linears", "stress_l2_case", "WORKLOADS", "make",
+]
+
+
+@dataclass
+class L2Case:
+    """Inputs of ``l2_rows``: ``x`` and optional residual ``r`` as bf16 bits."""
+    name: str
+    x: np.ndarray                     # uint16 [rows, cols]
+    r: Optional[np.ndarray]           # uint16 [rows, cols] or None
+    eps: float = 1e-6
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.x.shape[1]
+
+
+@dataclass
+class SlerpCase:
+    """Inputs of ``slerp_rows``: ``res``, ``out`` (bf16 bits), ``alpha`` (fp32)."""
+    name: str
+    res: np.ndarray                   # uint16 [rows, cols]
+    out: np.ndarray                   # uint16 [rows, cols]
+    alpha: np.ndarray                 # float32 [cols]
+    eps: float = 1e-6
+
+    @property
+    def rows(self) -> int:
+        return self.res.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.res.shape[1]
+
+
+@dataclass
+class RownormCase:
+    """Inputs of ``weight_rownorm_gain``: a ragged list of fp32 matrices."""
+    name: str
+    w: List[np.ndarray]               # float32 [rows_m, cols_m] each
+    gain: List[np.ndarray]            # float32 [rows_m] each
+    radius: List[float]
+
+    @property
+    def total_rows(self) -> int:
+        return sum(m.shape[0] for m in self.w)
+
+    @property
+    def total_elems(self) -> int:
+        return sum(m.size for m in self.w)
+
+
+def _streams(seed: int, n: int) -> List[np.random.Generator]:
+    children = np.random.SeedSequence(seed).spawn(n)
+    return [np.random.Generator(np.random.PCG64(c)) for c in children]
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float64/float32 samples -> bf16 bit patterns (uint16), via torch's cast."""
+    import torch
+    f32 = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    t = torch.from_numpy(f32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def l2_case(rows: int, cols: int, seed: int, residual: bool = True,
+            eps: float = 1e-6, name: Optional[str] = None) -> L2Case:
+    gx, gr = _streams(seed, 2)
+    x = to_bf16_bits(gx.standard_normal((rows, cols)))
+    r = to_bf16_bits(gr.standard_normal((rows, cols))) if residual else None
+    return L2Case(name or f"l2_rows{'_res' if residual else ''}_{rows}x{cols}", x, r, eps)
+
+
+def slerp_case(rows: int, cols: int, seed: int, eps: float = 1e-6,
+               out_sd: float = 2.0, alpha_lim: float = 0.2,
+               name: Optional[str] = None) -> SlerpCase:
+    gres, gout, galpha = _streams(seed, 3)
+    res = to_bf16_bits(gres.standard_normal((rows, cols)))
+    out = to_bf16_bits(out_sd * gout.standard_normal((rows, cols)))
+    alpha = galpha.uniform(-alpha_lim, alpha_lim, cols).astype(np.float32)
+    return SlerpCase(name or f"slerp_rows_{rows}x{cols}", res, out, alpha, eps)
+
+
+def transformer_linears(layers: int = 12, d: int = 768, d_ff: int = 3072):
+    """(rows, cols) of each linear, layer-major: qkv, o, up, down."""
+    shapes = []
+    for _ in range(layers):
+        shapes += [(3 * d, d), (d, d), (d_ff, d), (d, d_ff)]
+    return shapes
+
+
+def rownorm_case(shapes, seed: int, w_sd: float = 0.02, g_lo: float = 0.5,
+                 g_hi: float = 2.0, radius: float = 1.0,
+                 name: Optional[str] = None) -> RownormCase:
+    gens = _streams(seed, 2 * len(shapes))
+    ws, gs = [], []
+    for i, (rows, cols) in enumerate(shapes):
+        gw, gg = gens[2 * i], gens[2 * i + 1]
+        ws.append((w_sd * gw.standard_normal((rows, cols))).astype(np.float32))
+        gs.append(gg.uniform(g_lo, g_hi, rows).astype(np.float32))
+    return RownormCase(name or f"rownorm_gain_{len(shapes)}", ws, gs,
+                       [float(radius)] * len(shapes))
+
+
+def stress_l2_case(rows: int = 32768, cols: int = 8192, seed: int = 1005,
+                   residual: bool = True, eps: float = 1e-6,
+                   outlier_p: float = 0.01, outlier_scale: float = 1000.0,
+                   int_lim: int = 64, name: Optional[str] = None) -> L2Case:
+    """Outlier entries, all-zero rows and small-integer rows (see module doc).
+
+    The integer rows keep r = 0 so that s stays an integer row, and their
+    sums of squares stay below 2**24 so that every fp32 partial sum is an
+    exact integer.
+    """
+    gx, gr, gmask, gperm, gint = _streams(seed, 5)
+    x = gx.standard_normal((rows, cols))
+    mask = gmask.random((rows, cols)) < outlier_p
+    x[mask] *= outlier_scale
+    r = gr.standard_normal((rows, cols))
+    n_special = int(rows * 0.01)
+    perm = gperm.permutation(rows)
+    zero_rows = np.sort(perm[:n_special])
+    int_rows = np.sort(perm[n_special:2 * n_special])
+    x[zero_rows] = 0.0
+    r[zero_rows] = 0.0
+    ints = gint.integers(-int_lim, int_lim + 1, (len(int_rows), cols))
+    assert (ints.astype(np.int64) ** 2).sum(axis=1).max() < 2 ** 24
+    x[int_rows] = ints
+    r[int_rows] = 0.0
+    xb = to_bf16_bits(x)
+    rb = to_bf16_bits(r) if residual else None
+    meta = {"zero_rows": zero_rows, "int_rows": int_rows}
+    return L2Case(name or f"l2_rows{'_res' if residual else ''}_stress_{rows}x{cols}",
+                  xb, rb, eps, meta)
+
+
+# name -> (description, builder, seed).  Seeds are 1000 + a fixed number.
+WORKLOADS = {
+    "l2_rows_64x1024": (
+        "l2_rows, no residual, 64 x 1024 bf16, x ~ N(0,1), eps 1e-6",
+        lambda: l2_case(64, 1024, 1001, residual=False, name="l2_rows_64x1024")),
+    "l2_rows_res_8192x4096": (
+        "l2_rows with fused residual, 8192 x 4096 bf16, x, r ~ N(0,1), eps 1e-6",
+        lambda: l2_case(8192, 4096, 1002, residual=True, name="l2_rows_res_8192x4096")),
+    "slerp_rows_8192x7168": (
+        "slerp_rows, 8192 x 7168 bf16, res ~ N(0,1), out ~ N(0, sd 2), "
+        "alpha ~ U(-0.2, 0.2) fp32, eps 1e-6",
+        lambda: slerp_case(8192, 7168, 1003, name="slerp_rows_8192x7168")),
+    "rownorm_gain_12x4_d768": (
+        "weight rownorm + gain over 12 pre-norm layers' linears (d 768, d_ff 3072), "
+        "W ~ N(0, sd 0.02) fp32, g ~ U(0.5, 2) fp32, rho 1",
+        lambda: rownorm_case(transformer_linears(), 1004, name="rownorm_gain_12x4_d768")),
+    "l2_rows_res_stress_32768x8192": (
+        "l2_rows with residual, 32768 x 8192 bf16: 1% outliers x1000, 1% zero rows, "
+        "1% integer rows in [-64, 64], eps 1e-6",
+        lambda: stress_l2_case(name="l2_rows_res_stress_32768x8192")),
+    "slerp_rows_8192x4096": (
+        "slerp_rows, 8192 x 4096 bf16, res ~ N(0,1), out ~ N(0, sd 2), "
+        "alpha ~ U(-0.2, 0.2) fp32, eps 1e-6",
+        lambda: slerp_case(8192, 4096, 1006, name="slerp_rows_8192x4096")),
+}
+
+
+def make(name: str):
+    """Build a named workload (deterministic)."""
+    return WORKLOADS[name][1]()

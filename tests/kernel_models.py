@@ -1,0 +1,81 @@
+"""numpy float32 models of an fp32 row kernel, for testing the strict checker.
+
+These emulate what an fp32 GPU run computes (fp32 sums of squares in a
+64-lane layout, fp32 square root and reciprocal, bf16 rounding at the named
+points).  The faithful model must pass the admissible-set check; each control
+drops one rounding point or narrows the accumulator and must fail it --
+TensorFold PR #1260's mutation controls (the sum before the norm, the slerp's
+a, its b) and its fp16-sum control on integer rows.  Test code only.
+"""
+import numpy as np
+
+from oracle.bf16 import bf16_rne, bf16_value
+
+
+def bf16_of_f32(v32):
+    return bf16_value(bf16_rne(np.asarray(v32, np.float32).astype(np.float64))).astype(np.float32)
+
+
+def lane_sum_sq(s32, acc="f32"):
+    """Row sums of squares: 64 lane accumulators, then a pairwise tree."""
+    rows, cols = s32.shape
+    pad = (-cols) % 64
+    s = np.concatenate([s32, np.zeros((rows, pad), np.float32)], axis=1)
+    sq = (s * s).astype(np.float32)
+    if acc == "f16":
+        a = np.zeros((rows, 64), np.float16)
+        with np.errstate(over="ignore"):
+            for c in range(0, s.shape[1], 64):
+                a = (a + sq[:, c:c + 64].astype(np.float16)).astype(np.float16)
+            while a.shape[1] > 1:
+                a = (a[:, 0::2] + a[:, 1::2]).astype(np.float16)
+        return a[:, 0].astype(np.float32)
+    a = np.zeros((rows, 64), np.float32)
+    for c in range(0, s.shape[1], 64):
+        a = a + sq[:, c:c + 64]
+        if acc == "bf16":
+            a = bf16_of_f32(a)
+    while a.shape[1] > 1:
+        a = a[:, 0::2] + a[:, 1::2]
+        if acc == "bf16":
+            a = bf16_of_f32(a)
+    return a[:, 0]
+
+
+def inv_norm(S32, eps):
+    with np.errstate(all="ignore"):
+        return np.float32(1.0) / np.sqrt((S32 + np.float32(eps)).astype(np.float32))
+
+
+def l2_model(x_bits, r_bits=None, eps=1e-6, round_s=True, acc="f32"):
+    x = bf16_value(x_bits).astype(np.float32)
+    s = x if r_bits is None else x + bf16_value(r_bits).astype(np.float32)
+    if r_bits is not None and round_s:
+        s = bf16_of_f32(s)
+    inv = inv_norm(lane_sum_sq(s, acc), eps)
+    return bf16_rne((s * inv[:, None]).astype(np.float64))
+
+
+def slerp_model(res_bits, out_bits, alpha, eps=1e-6, round_a=True, round_b=True):
+    res = bf16_value(res_bits).astype(np.float32)
+    out = bf16_value(out_bits).astype(np.float32)
+    a = res * inv_norm(lane_sum_sq(res), eps)[:, None]
+    b = out * inv_norm(lane_sum_sq(out), eps)[:, None]
+    if round_a:
+        a = bf16_of_f32(a)
+    if round_b:
+        b = bf16_of_f32(b)
+    d = b - a
+    t = np.abs(alpha.astype(np.float32)) * d
+    u = a + t
+    inv = inv_norm(lane_sum_sq(u), eps)
+    return bf16_rne((u * inv[:, None]).astype(np.float64))
+
+
+def rownorm_model(w, g, rho=1.0):
+    w32 = np.asarray(w, np.float32)
+    S = lane_sum_sq(w32)
+    n = np.sqrt(S).astype(np.float32)
+    with np.errstate(all="ignore"):
+        c = np.where(n > 0, (np.asarray(g, np.float32) * np.float32(rho)) / n, np.float32(0))
+    return n, bf16_rne((w32 * c[:, None].astype(np.float32)).astype(np.float64))
