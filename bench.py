@@ -1,0 +1,259 @@
+"""Throughput of the row-L2 hot path on one MI355X.
+
+A step is one pass of the path over one batch at the workload the headline
+metric is quoted on: ds_l2_rows with the fused residual on 8192 x 4096 bf16
+rows, then ds_slerp_rows on 8192 x 4096 bf16 rows (synthetic, seeded inputs).
+Inputs are resident in HBM before timing starts; the steps rotate over
+several buffer sets whose total is well above the 256 MB last-level cache, so
+every launch streams from HBM.  The weight op (ds_weight_rownorm_gain over a
+12-layer transformer's 48 linears) is timed after the headline steps and
+reported beside them.
+
+Prints one JSON line.  ``value`` is the step's algorithmic bytes (each input
+read once, each output written once) over its time, in GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+ROWS, COLS = 8192, 4096
+EPS = 1e-6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
+                  "inst_rownorm.hip", "ds_rows.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "scale_invariant_row_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, per_launch_algo: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when they are missing or were taken from different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or kernel not in t.get("kernels", {}):
+        return None
+    return t["kernels"][kernel]["bytes_per_dispatch"]
+
+
+def cpu_baseline(l2c, slc, rows: int):
+    """The CPU oracle as it stands, timed on the first `rows` rows of each op."""
+    from oracle.rows import l2_rows, slerp_rows
+    t0 = time.perf_counter()
+    l2_rows(l2c.x[:rows], l2c.r[:rows], EPS)
+    t1 = time.perf_counter()
+    slerp_rows(slc.res[:rows], slc.out[:rows], slc.alpha, EPS)
+    t2 = time.perf_counter()
+    nbytes = rows * COLS * 6 * 2 + COLS * 4
+    return {
+        "value": round(nbytes / (t2 - t0) / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {rows} of {ROWS} rows of each op (l2_rows {t1 - t0:.1f} s, "
+                   f"slerp_rows {t2 - t1:.1f} s), float64 numpy/math.fsum, one thread; "
+                   f"host reports {os.cpu_count()} cpus"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the row ops shard by rows with no exchange, "
+              "and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from scale_invariant_row_amd import binding as B
+    from scale_invariant_row_amd import inputs
+
+    L = B.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating inputs {ROWS}x{COLS}", file=sys.stderr, flush=True)
+    l2c = inputs.make("l2_rows_res_8192x4096")
+    slc = inputs.make("slerp_rows_8192x4096")
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    x0, r0, res0, out0 = to_dev(l2c.x), to_dev(l2c.r), to_dev(slc.res), to_dev(slc.out)
+    alpha = torch.from_numpy(slc.alpha).to(dev)
+    sets = []
+    for _ in range(args.sets):
+        sets.append(dict(x=x0.clone(), r=r0.clone(), y=torch.empty_like(x0),
+                         res=res0.clone(), out=out0.clone(), h=torch.empty_like(res0)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    eps = ctypes.c_float(EPS)
+
+    def l2(s):
+        return L.ds_l2_rows(s["x"].data_ptr(), s["r"].data_ptr(), s["y"].data_ptr(), ROWS, COLS, eps, sp)
+
+    def slerp(s):
+        return L.ds_slerp_rows(s["res"].data_ptr(), s["out"].data_ptr(), alpha.data_ptr(),
+                               s["h"].data_ptr(), ROWS, COLS, eps, sp)
+
+    for i in range(args.warmup):
+        s = sets[i % len(sets)]
+        assert l2(s) == 0 and slerp(s) == 0
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        s = sets[i % len(sets)]
+        e = ev[i]
+        e[0].record(stream)
+        st1 = l2(s)
+        e[1].record(stream)
+        e[2].record(stream)
+        st2 = slerp(s)
+        e[3].record(stream)
+        if st1 or st2:
+            raise RuntimeError(f"launch failed: {B.ds_status_string(st1 or st2)}")
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    l2_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    sl_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    ms_per_step = total_ms / K
+
+    l2_bytes = ROWS * COLS * 2 * 3                      # x, r read; y written
+    sl_bytes = ROWS * COLS * 2 * 3 + COLS * 4           # res, out read; h written; alpha once
+    step_bytes = l2_bytes + sl_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    l2_us = 1e3 * float(np.mean(l2_ms))
+    sl_us = 1e3 * float(np.mean(sl_ms))
+
+    def op(us, nbytes, rows):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "rows_per_s": round(rows / (us * 1e-6), 1), "bytes": nbytes}
+
+    ops = {"l2_rows_res_8192x4096": op(l2_us, l2_bytes, ROWS),
+           "slerp_rows_8192x4096": op(sl_us, sl_bytes, ROWS)}
+
+    # ---- the weight op, rotating 3 copies of the 48 matrices (3 x 510 MB)
+    rn = inputs.make("rownorm_gain_12x4_d768")
+    rn_sets = []
+    for _ in range(3):
+        ws = [torch.from_numpy(w).to(dev) for w in rn.w]
+        gs = [torch.from_numpy(g).to(dev) for g in rn.gain]
+        ns = [torch.empty(w.shape[0], dtype=torch.float32, device=dev) for w in rn.w]
+        es = [torch.empty(w.shape, dtype=torch.int16, device=dev) for w in rn.w]
+        descs = (B.RownormDesc * len(ws))()
+        for i in range(len(ws)):
+            descs[i] = B.RownormDesc(ws[i].data_ptr(), gs[i].data_ptr(), 1.0, ns[i].data_ptr(),
+                                     es[i].data_ptr(), ws[i].shape[0], ws[i].shape[1])
+        rn_sets.append((descs, ws, gs, ns, es))
+    n_rn = len(rn.w)
+    for i in range(10):
+        assert L.ds_weight_rownorm_gain(rn_sets[i % 3][0], n_rn, sp) == 0
+    torch.cuda.synchronize()
+    rn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(60)]
+    for i, (a, b) in enumerate(rn_ev):
+        a.record(stream)
+        assert L.ds_weight_rownorm_gain(rn_sets[i % 3][0], n_rn, sp) == 0
+        b.record(stream)
+    torch.cuda.synchronize()
+    rn_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in rn_ev]))
+    rn_bytes = rn.total_elems * 6 + rn.total_rows * 8
+    ops["weight_rownorm_gain_12x4_d768"] = op(rn_us, rn_bytes, rn.total_rows)
+    ops["weight_rownorm_gain_12x4_d768"]["note"] = "includes the descriptor-table copy"
+
+    # ---- a plain device copy of the same bytes as l2_rows moves (reference ceiling)
+    src = torch.empty(l2_bytes // 2, dtype=torch.uint8, device=dev)   # read + write = l2_bytes
+    dsts = [torch.empty_like(src) for _ in range(4)]
+    srcs = [torch.empty_like(src) for _ in range(4)]
+    for i in range(5):
+        dsts[i % 4].copy_(srcs[i % 4])
+    torch.cuda.synchronize()
+    cp_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(40)]
+    for i, (a, b) in enumerate(cp_ev):
+        a.record(stream)
+        dsts[i % 4].copy_(srcs[i % 4])
+        b.record(stream)
+    torch.cuda.synchronize()
+    cp_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in cp_ev]))
+    ops["torch_copy_same_bytes"] = op(cp_us, 2 * src.numel(), ROWS)
+    del srcs, dsts, src
+
+    dominant = "slerp_rows_8192x4096" if sl_us >= l2_us else "l2_rows_res_8192x4096"
+    kname = {"slerp_rows_8192x4096": "slerp_rows_kernel",
+             "l2_rows_res_8192x4096": "l2_rows_kernel"}[dominant]
+    d = ops[dominant]
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": d["frac"],
+                "traffic": traffic_for(kname, d["bytes"]),
+                "algorithmic_bytes_per_launch": d["bytes"]}
+
+    result = {
+        "metric": "achieved HBM GB/s (% of peak) for bf16 l2_rows/slerp_rows at 8192x4096",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "l2_rows with fused residual + slerp_rows, 8192 x 4096 rows",
+                   "rows": ROWS, "cols": COLS, "io": "bf16", "eps": EPS,
+                   "buffer_sets": args.sets,
+                   "bytes_per_step": step_bytes,
+                   "frac_of_peak": round(value / HBM_PEAK_GBPS, 4)},
+        "roofline": roofline,
+        "ops": ops,
+    }
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(l2c, slc, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

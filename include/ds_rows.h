@@ -1,0 +1,174 @@
+/*
+ * ds_rows.h -- row-wise L2 normalisation on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Plain pointers and sizes; no HIP or
+ * torch types except an opaque stream handle.  All element buffers are device
+ * memory unless stated otherwise.
+ *
+ * Operations (cited by page and section):
+ *
+ *  ds_l2_rows             TensorFold PR #1260, the commit adding the two
+ *                         unit-sphere row kernels of the looped nGPT model:
+ *                         y = bf16(s / sqrt(sum(s^2) + eps)), s = x, or
+ *                         s = bf16(x + r) with a residual (the loop entry
+ *                         l2(state + input); with no residual, the loop exit).
+ *  ds_slerp_rows          same commit: the nGPT residual update
+ *                         h = bf16(l2(a + |alpha| (b - a))), a = bf16(l2(res)),
+ *                         b = bf16(l2(out)), the lerp in fp32 steps.
+ *  ds_weight_rownorm_gain DragonScale README, "What DragonScale changes":
+ *                         W_eff = diag(g) r W / ||W||_row over a ragged batch of
+ *                         weight matrices in one call ("Kernels and speed": the
+ *                         weights of every layer in a few launches).
+ *
+ * Numerics.  bf16 values are passed as their 16-bit patterns; every rounding
+ * to bf16 is to nearest, ties to even.  Sums of squares accumulate in fp32
+ * (the DragonScale README's eager reference: fp32 accumulation).  eps is
+ * added to the sum of squares, as an fp32 value.  The inverse length is
+ * 1 / sqrt(S + eps), each step correctly rounded in fp32, and each output is
+ * one fp32 product rounded to bf16.  A row whose fp32 sum of squares would
+ * overflow, or whose sum plus eps falls below 2^-96, is rescaled by a power
+ * of two before summing, so every finite input row gives the float64 result
+ * to within the stated rounding.  NaN and infinity propagate as in IEEE
+ * arithmetic (a row holding an infinity maps its finite entries to 0 and the
+ * infinity to NaN; a row holding a NaN maps to NaN).
+ *
+ * Determinism.  The bits of output row i depend only on row i's inputs, cols,
+ * eps (and alpha, gain, radius): not on the row count, the row's position,
+ * the grid, the other matrices of a ragged call, or the stream.  Repeated
+ * calls give identical bits.
+ *
+ * Errors.  Every argument is validated before anything is enqueued; a call
+ * that returns an error has enqueued nothing.  Launch failures reported by
+ * the runtime right after the launch return DS_ERR_LAUNCH.  No exception or
+ * abort crosses the ABI.  Calls are thread-safe.
+ *
+ * Ownership.  The caller owns every device buffer and keeps it alive until
+ * the stream has run the kernels.  The library keeps no caller pointer after
+ * the call returns, except inside the kernels it has enqueued.
+ */
+#ifndef DS_ROWS_H
+#define DS_ROWS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS_ROWS_VERSION 10000          /* major * 10000 + minor * 100 + patch */
+#define DS_MAX_COLS 65536              /* widest row any entry point accepts */
+
+/* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
+typedef void* ds_stream_t;
+
+/* Status codes returned by every entry point. */
+enum {
+  DS_OK = 0,
+  DS_ERR_NULL = -1,    /* a required pointer is NULL */
+  DS_ERR_SHAPE = -2,   /* rows < 0, cols not a multiple of 8 (bf16 rows) or 4
+                          (fp32 weight rows), cols below that multiple or above
+                          DS_MAX_COLS, or sizes that overflow */
+  DS_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned (gain and norm_out:
+                          4-byte aligned) */
+  DS_ERR_ARG = -4,     /* eps negative or not finite, radius not finite,
+                          n < 0, or buffers that partly overlap */
+  DS_ERR_ALLOC = -5,   /* the descriptor staging area could not be allocated */
+  DS_ERR_LAUNCH = -6,  /* the HIP runtime reported an error for the launch,
+                          the copy or the stream */
+  DS_ERR_DEVICE = -7   /* no usable HIP device */
+};
+
+/*
+ * ds_l2_rows -- unit-length activation rows, optionally with a fused residual.
+ * (TensorFold PR #1260, the l2 row kernel.)
+ *
+ *   s = x               when r == NULL
+ *   s = bf16(x + r)     otherwise (the sum in fp32, rounded once to bf16)
+ *   y = bf16(s / sqrt(sum_j s_j^2 + eps))          for every row
+ *
+ * x, r, y : row-major [rows, cols] bf16 bit patterns, contiguous, 16-byte
+ *           aligned.  y may be the same buffer as x or r (each row is read
+ *           whole before it is written); any other overlap is refused.
+ * rows    : >= 0; 0 enqueues nothing and returns DS_OK (pointers unchecked).
+ * cols    : multiple of 8, 8 <= cols <= DS_MAX_COLS.
+ * eps     : finite, >= 0 (1e-6 in the pages' models).
+ * stream  : the hipStream_t to launch on.
+ */
+int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y,
+               int64_t rows, int64_t cols, float eps, ds_stream_t stream);
+
+/*
+ * ds_slerp_rows -- the nGPT residual update on unit rows.
+ * (TensorFold PR #1260, the slerp row kernel.)
+ *
+ *   a = bf16(l2(res)),  b = bf16(l2(out))               (l2 as in ds_l2_rows)
+ *   u_j = a_j + |alpha_j| * (b_j - a_j)    three fp32 operations, in this
+ *                                          order, each rounded; u unrounded
+ *   h = bf16(l2(u))
+ *
+ * res, out, h : row-major [rows, cols] bf16 bit patterns, contiguous, 16-byte
+ *               aligned; h may be the same buffer as res or out.
+ * alpha       : [cols] fp32, one value per column shared by all rows (the
+ *               caller forms it; the kernel takes its absolute value);
+ *               16-byte aligned; must not overlap h.
+ * rows, cols, eps, stream : as for ds_l2_rows.
+ */
+int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha,
+                  uint16_t* h, int64_t rows, int64_t cols, float eps,
+                  ds_stream_t stream);
+
+/*
+ * One weight matrix of a ds_weight_rownorm_gain call.
+ *
+ * w        : [rows, cols] fp32, row-major, contiguous, 16-byte aligned.
+ * gain     : [rows] fp32, one learned gain per row; 4-byte aligned.
+ * radius   : the row radius r: 1 for linears and convs, sqrt(cols) for
+ *            embeddings (rows of unit RMS).  Finite.
+ * norm_out : [rows] fp32, receives ||W_i|| (fp32 sum of squares, fp32
+ *            square root); may be NULL; 4-byte aligned.
+ * w_eff    : [rows, cols] bf16 bit patterns, receives
+ *            bf16(W_i * (g_i * radius / ||W_i||)); 16-byte aligned; must not
+ *            overlap w, gain or norm_out.  A zero row gives a zero row.
+ * rows     : >= 0.
+ * cols     : multiple of 4, 4 <= cols <= DS_MAX_COLS.
+ */
+typedef struct ds_rownorm_desc {
+  const float* w;
+  const float* gain;
+  float radius;
+  float* norm_out;
+  uint16_t* w_eff;
+  int64_t rows;
+  int64_t cols;
+} ds_rownorm_desc;
+
+/*
+ * ds_weight_rownorm_gain -- unit-length weight rows times one gain per row,
+ * over a ragged batch of n matrices, in one launch per row-width class.
+ * (DragonScale README, "What DragonScale changes": W_eff = diag(g) r W/||W||;
+ * no eps in the formula.)
+ *
+ * descs  : host array of n descriptors, read during the call only.  All n
+ *          are validated before anything is enqueued.
+ * n      : >= 0; 0 enqueues nothing.
+ * stream : the hipStream_t to launch on.
+ *
+ * The library stages a small device table of the descriptors through a
+ * library-owned pinned buffer, which it keeps until the stream has consumed
+ * it (an event recorded behind the launches); a slot whose copy or launch
+ * fails is returned at once.  DS_ERR_ALLOC if that buffer cannot be made.
+ */
+int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n,
+                           ds_stream_t stream);
+
+/* A static, human-readable string for a status code (never NULL). */
+const char* ds_status_string(int status);
+
+/* DS_ROWS_VERSION of the built library. */
+int ds_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_ROWS_H */

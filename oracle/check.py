@@ -47,7 +47,7 @@ F64_WIDEN = 2.0 ** -46     # covers float64 rounding inside the bound arithmetic
 
 __all__ = ["contract_bf16", "contract_rel", "Report", "admissible_l2_rows",
            "admissible_slerp_rows", "admissible_rownorm", "default_depth",
-           "ordered"]
+           "ordered", "slerp_unique_mask"]
 
 
 def default_depth(cols: int) -> int:
@@ -283,6 +283,30 @@ def admissible_slerp_rows(got_bits, res_bits, out_bits, alpha, eps: float = 1e-6
         for j in bad[: max(0, 20 - len(rep.first_bad))]:
             rep.first_bad.append(int(base + j))
     return rep
+
+
+def slerp_unique_mask(res_bits, out_bits, eps: float = 1e-6,
+                      depth: Optional[int] = None) -> np.ndarray:
+    """Elements whose a and b each have exactly one admissible bf16 value.
+
+    Where a_j or b_j lies so near a bf16 midpoint that an fp32 run may round
+    it either way, both choices are correct, and the lerp can amplify the
+    one-ulp difference (b - a cancels): h_j is then not unique, and only the
+    admissible-set check applies.  Elsewhere the 1-ulp contract applies.
+    """
+    res = bf16_value(np.atleast_2d(res_bits))
+    out = bf16_value(np.atleast_2d(out_bits))
+    cols = res.shape[1]
+    depth = default_depth(cols) if depth is None else depth
+    eps64 = eps_as_passed(eps)
+    mask = np.ones(res.shape, bool)
+    for i in range(res.shape[0]):
+        for v in (res[i], out[i]):
+            if not np.isfinite(v).all():
+                continue
+            lo, hi = _l2_value_bounds(v, eps64, depth)
+            mask[i] &= ordered(bf16_rne(lo)) == ordered(bf16_rne(hi))
+    return mask
 
 
 def admissible_rownorm(got_norm, got_weff_bits, w, g, rho: float = 1.0,

@@ -1,0 +1,208 @@
+"""ctypes binding of libdsrows.so (include/ds_rows.h): argument marshalling only.
+
+Every computation runs in the library's HIP kernels.  The functions take
+torch tensors on a HIP device, check dtype/shape/contiguity/device, pass raw
+pointers and the current stream, and raise ``RuntimeError`` with the
+library's status string on a nonzero status.  Loading fails loudly if the
+library has not been built (``python -m scale_invariant_row_amd.build``).
+
+bf16 tensors may be ``torch.bfloat16`` or ``torch.int16``/``torch.uint16``
+holding the bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Sequence, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "_lib", "libdsrows.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "ds_rows.h")
+
+DS_OK = 0
+DS_ERR_NULL = -1
+DS_ERR_SHAPE = -2
+DS_ERR_ALIGN = -3
+DS_ERR_ARG = -4
+DS_ERR_ALLOC = -5
+DS_ERR_LAUNCH = -6
+DS_ERR_DEVICE = -7
+
+
+class RownormDesc(ctypes.Structure):
+    """ds_rownorm_desc."""
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("gain", ctypes.c_void_p),
+        ("radius", ctypes.c_float),
+        ("norm_out", ctypes.c_void_p),
+        ("w_eff", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m scale_invariant_row_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+        L.ds_l2_rows.argtypes = [vp, vp, vp, i64, i64, f32, vp]
+        L.ds_l2_rows.restype = ctypes.c_int
+        L.ds_slerp_rows.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
+        L.ds_slerp_rows.restype = ctypes.c_int
+        L.ds_weight_rownorm_gain.argtypes = [ctypes.POINTER(RownormDesc), ctypes.c_int32, vp]
+        L.ds_weight_rownorm_gain.restype = ctypes.c_int
+        L.ds_status_string.argtypes = [ctypes.c_int]
+        L.ds_status_string.restype = ctypes.c_char_p
+        L.ds_version.argtypes = []
+        L.ds_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> List[str]:
+    """Names of the functions include/ds_rows.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ds_\w+)\s*\(", text, re.M)))
+
+
+def ds_status_string(status: int) -> str:
+    return lib().ds_status_string(int(status)).decode()
+
+
+def ds_version() -> int:
+    return lib().ds_version()
+
+
+def _check(status: int, what: str) -> None:
+    if status != DS_OK:
+        raise RuntimeError(f"{what}: {ds_status_string(status)}")
+
+
+# --------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bf16_2d(t, name):
+    torch = _torch()
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected bf16 data (bfloat16 or 16-bit int bits), got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D [rows, cols] tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on a HIP device")
+
+
+def _same(a, b, name):
+    if b.shape != a.shape or b.device != a.device:
+        raise ValueError(f"{name}: shape/device mismatch {tuple(b.shape)} vs {tuple(a.shape)}")
+
+
+def _stream_of(t, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def ds_l2_rows(x, r=None, eps: float = 1e-6, out=None, stream=None):
+    """y = bf16(s / sqrt(sum(s^2) + eps)) per row, s = x or bf16(x + r).
+
+    Returns ``out`` (allocated like ``x`` when not given; may be ``x`` or ``r``).
+    """
+    torch = _torch()
+    _bf16_2d(x, "x")
+    if r is not None:
+        _bf16_2d(r, "r")
+        _same(x, r, "r")
+    if out is None:
+        out = torch.empty_like(x)
+    _bf16_2d(out, "out")
+    _same(x, out, "out")
+    with torch.cuda.device(x.device):
+        st = lib().ds_l2_rows(x.data_ptr(), None if r is None else r.data_ptr(), out.data_ptr(),
+                              x.shape[0], x.shape[1], float(eps), _stream_of(x, stream))
+    _check(st, "ds_l2_rows")
+    return out
+
+
+def ds_slerp_rows(res, out_rows, alpha, eps: float = 1e-6, h=None, stream=None):
+    """h = bf16(l2(a + |alpha| (b - a))), a = bf16(l2(res)), b = bf16(l2(out_rows))."""
+    torch = _torch()
+    _bf16_2d(res, "res")
+    _bf16_2d(out_rows, "out")
+    _same(res, out_rows, "out")
+    if alpha.dtype != torch.float32 or alpha.dim() != 1 or alpha.shape[0] != res.shape[1] \
+            or not alpha.is_contiguous() or alpha.device != res.device:
+        raise ValueError("alpha: expected a contiguous fp32 [cols] tensor on the rows' device")
+    if h is None:
+        h = torch.empty_like(res)
+    _bf16_2d(h, "h")
+    _same(res, h, "h")
+    with torch.cuda.device(res.device):
+        st = lib().ds_slerp_rows(res.data_ptr(), out_rows.data_ptr(), alpha.data_ptr(),
+                                 h.data_ptr(), res.shape[0], res.shape[1], float(eps),
+                                 _stream_of(res, stream))
+    _check(st, "ds_slerp_rows")
+    return h
+
+
+def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Sequence[float]] = None,
+                           norm_out: Optional[Sequence] = None, w_eff: Optional[Sequence] = None,
+                           stream=None) -> Tuple[list, list]:
+    """Per matrix: ||W_i|| (fp32) and bf16(W_i * g_i * radius / ||W_i||), in one call.
+
+    ``ws``: fp32 [rows, cols] tensors; ``gains``: fp32 [rows].  Returns
+    (norms, w_effs); w_effs are bfloat16 tensors unless given.
+    """
+    torch = _torch()
+    n = len(ws)
+    if len(gains) != n:
+        raise ValueError("one gain vector per matrix")
+    radius = [1.0] * n if radius is None else list(radius)
+    if norm_out is None:
+        norm_out = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device) for w in ws]
+    if w_eff is None:
+        w_eff = [torch.empty(w.shape, dtype=torch.bfloat16, device=w.device) for w in ws]
+    descs = (RownormDesc * max(n, 1))()
+    dev = None
+    for i, (w, g) in enumerate(zip(ws, gains)):
+        if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+            raise ValueError(f"ws[{i}]: expected a contiguous fp32 [rows, cols] tensor")
+        if g.dtype != torch.float32 or g.shape != (w.shape[0],) or not g.is_contiguous():
+            raise ValueError(f"gains[{i}]: expected a contiguous fp32 [rows] tensor")
+        _bf16_2d(w_eff[i], f"w_eff[{i}]")
+        if tuple(w_eff[i].shape) != tuple(w.shape):
+            raise ValueError(f"w_eff[{i}]: shape mismatch")
+        if norm_out[i] is not None and (norm_out[i].dtype != torch.float32
+                                        or norm_out[i].shape != (w.shape[0],)):
+            raise ValueError(f"norm_out[{i}]: expected fp32 [rows]")
+        for t in (w, g, w_eff[i]) + ((norm_out[i],) if norm_out[i] is not None else ()):
+            if t.device.type != "cuda" or (dev is not None and t.device != dev):
+                raise ValueError("all tensors must be on one HIP device")
+            dev = t.device
+        descs[i] = RownormDesc(w.data_ptr(), g.data_ptr(), float(radius[i]),
+                               None if norm_out[i] is None else norm_out[i].data_ptr(),
+                               w_eff[i].data_ptr(), w.shape[0], w.shape[1])
+    if n == 0:
+        return [], []
+    with torch.cuda.device(dev):
+        st = lib().ds_weight_rownorm_gain(descs, n, _stream_of(ws[0], stream))
+    _check(st, "ds_weight_rownorm_gain")
+    return list(norm_out), list(w_eff)

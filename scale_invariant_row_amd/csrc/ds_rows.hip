@@ -1,0 +1,344 @@
+// The C ABI of include/ds_rows.h: argument checks, kernel shape and grid
+// choice, and the staging of ragged weight descriptors.
+//
+// Every check runs before the first HIP call, so a refused call has touched
+// neither the device nor the stream.
+#include "ds_rows.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "launch.hpp"
+#include "row_kernels.hpp"
+
+namespace {
+
+using dsr::Shape;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+// Output buffer may be exactly the input buffer, or disjoint from it.
+bool same_or_disjoint(const void* out, const void* in, size_t n) {
+  return in == nullptr || out == in || !overlaps(out, n, in, n);
+}
+
+bool finite_nonneg(float v) { return std::isfinite(v) && v >= 0.f; }
+
+// rows x cols elements of `esize` bytes; cols a multiple of `mult`.
+int check_matrix(int64_t rows, int64_t cols, int64_t mult, int64_t esize) {
+  if (rows < 0 || cols < mult || cols > DS_MAX_COLS || cols % mult != 0) return DS_ERR_SHAPE;
+  if (rows > (INT64_MAX / 8) / (cols * esize)) return DS_ERR_SHAPE;
+  return DS_OK;
+}
+
+// Compute units of the current device, cached per device.
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return DS_ERR_DEVICE;
+    it = cache.emplace(dev, n).first;
+  }
+  *cus = it->second;
+  return DS_OK;
+}
+
+// Workgroups for `units` row groups: one per group up to a cap well above
+// what the chip holds at once; past it the kernels loop (grid-stride).
+int grid_for(int64_t units, int cus) {
+  int64_t cap = (int64_t)cus * 64;
+  return (int)std::max<int64_t>(1, std::min(units, cap));
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DS_OK : DS_ERR_LAUNCH; }
+
+// ----------------------------------------------------- descriptor staging
+//
+// A ring of pinned host + device buffers per device.  A slot is filled on the
+// host, copied to the device on the caller's stream, read by the kernels, and
+// handed out again only after an event recorded behind those kernels has
+// completed; a slot whose copy or launch failed is returned at once.
+
+constexpr int kSlots = 8;
+
+struct Slot {
+  void* host = nullptr;
+  void* dev = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool busy = false;      // handed out, not yet returned
+  bool pending = false;   // returned with work in flight behind `ev`
+};
+
+struct Ring {
+  std::mutex mu;
+  Slot slot[kSlots];
+  int next = 0;
+};
+
+Ring* ring_for_current_device() {
+  static std::mutex mu;
+  static std::map<int, Ring*> rings;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  Ring*& r = rings[dev];
+  if (r == nullptr) r = new Ring();   // lives until the process ends
+  return r;
+}
+
+int grow(Slot& s, size_t bytes) {
+  if (s.ev == nullptr && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
+    s.ev = nullptr;
+    return DS_ERR_ALLOC;
+  }
+  if (s.cap >= bytes) return DS_OK;
+  size_t cap = std::max<size_t>(bytes, 4096);
+  void* h = nullptr;
+  void* d = nullptr;
+  if (hipHostMalloc(&h, cap, hipHostMallocDefault) != hipSuccess) return DS_ERR_ALLOC;
+  if (hipMalloc(&d, cap) != hipSuccess) {
+    (void)hipHostFree(h);
+    return DS_ERR_ALLOC;
+  }
+  if (s.host) (void)hipHostFree(s.host);
+  if (s.dev) (void)hipFree(s.dev);
+  s.host = h;
+  s.dev = d;
+  s.cap = cap;
+  return DS_OK;
+}
+
+int acquire(Ring& r, size_t bytes, int* out) {
+  std::lock_guard<std::mutex> lock(r.mu);
+  int pick = -1;
+  for (int t = 0; t < kSlots && pick < 0; ++t) {
+    int i = (r.next + t) % kSlots;
+    Slot& s = r.slot[i];
+    if (s.busy) continue;
+    if (s.pending) {
+      if (hipEventQuery(s.ev) != hipSuccess) continue;   // still in flight
+      s.pending = false;
+    }
+    pick = i;
+  }
+  if (pick < 0) {                 // every slot in flight: wait for the oldest one
+    for (int t = 0; t < kSlots && pick < 0; ++t) {
+      int i = (r.next + t) % kSlots;
+      if (!r.slot[i].busy) pick = i;
+    }
+    if (pick < 0) return DS_ERR_ALLOC;
+    if (hipEventSynchronize(r.slot[pick].ev) != hipSuccess) return DS_ERR_LAUNCH;
+    r.slot[pick].pending = false;
+  }
+  int st = grow(r.slot[pick], bytes);
+  if (st != DS_OK) return st;
+  r.slot[pick].busy = true;
+  r.next = (pick + 1) % kSlots;
+  *out = pick;
+  return DS_OK;
+}
+
+// Return a slot: with `enqueued` work behind an event on `stream`, else at once.
+void release(Ring& r, int i, bool enqueued, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(r.mu);
+  Slot& s = r.slot[i];
+  if (enqueued) {
+    if (hipEventRecord(s.ev, stream) == hipSuccess) {
+      s.pending = true;
+    } else {
+      (void)hipStreamSynchronize(stream);   // no event: wait the work out here
+      s.pending = false;
+    }
+  }
+  s.busy = false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ds_version(void) { return DS_ROWS_VERSION; }
+
+const char* ds_status_string(int status) {
+  switch (status) {
+    case DS_OK: return "DS_OK: success";
+    case DS_ERR_NULL: return "DS_ERR_NULL: a required pointer is NULL";
+    case DS_ERR_SHAPE: return "DS_ERR_SHAPE: rows/cols out of range or cols not a multiple of the vector width";
+    case DS_ERR_ALIGN: return "DS_ERR_ALIGN: a pointer is misaligned";
+    case DS_ERR_ARG: return "DS_ERR_ARG: invalid eps/radius/count, or partly overlapping buffers";
+    case DS_ERR_ALLOC: return "DS_ERR_ALLOC: could not allocate the descriptor staging buffer";
+    case DS_ERR_LAUNCH: return "DS_ERR_LAUNCH: the HIP runtime reported an error";
+    case DS_ERR_DEVICE: return "DS_ERR_DEVICE: no usable HIP device";
+    default: return "unknown ds_rows status";
+  }
+}
+
+int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t rows, int64_t cols,
+               float eps, ds_stream_t stream) {
+  int st = check_matrix(rows, cols, 8, 2);
+  if (st != DS_OK) return st;
+  if (!finite_nonneg(eps)) return DS_ERR_ARG;
+  if (rows == 0) return DS_OK;
+  if (x == nullptr || y == nullptr) return DS_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || (r != nullptr && !aligned(r, 16))) return DS_ERR_ALIGN;
+  const size_t bytes = (size_t)rows * (size_t)cols * 2;
+  if (!same_or_disjoint(y, x, bytes) || !same_or_disjoint(y, r, bytes)) return DS_ERR_ARG;
+
+  const Shape s = dsr::pick_shape(cols / 8, dsr::kVmaxL2);
+  if (!s.ok()) return DS_ERR_SHAPE;
+  int cus = 0;
+  if ((st = device_cus(&cus)) != DS_OK) return st;
+  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  (void)hipGetLastError();   // start from a clean error state
+  return launch_status(dsr::launch_l2_rows(s, x, r, y, rows, (int)(cols / 8), eps,
+                                           grid_for(units, cus), (hipStream_t)stream));
+}
+
+int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha, uint16_t* h,
+                  int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
+  int st = check_matrix(rows, cols, 8, 2);
+  if (st != DS_OK) return st;
+  if (!finite_nonneg(eps)) return DS_ERR_ARG;
+  if (rows == 0) return DS_OK;
+  if (res == nullptr || out == nullptr || alpha == nullptr || h == nullptr) return DS_ERR_NULL;
+  if (!aligned(res, 16) || !aligned(out, 16) || !aligned(alpha, 16) || !aligned(h, 16))
+    return DS_ERR_ALIGN;
+  const size_t bytes = (size_t)rows * (size_t)cols * 2;
+  if (!same_or_disjoint(h, res, bytes) || !same_or_disjoint(h, out, bytes)) return DS_ERR_ARG;
+  if (overlaps(h, bytes, alpha, (size_t)cols * 4)) return DS_ERR_ARG;
+
+  const Shape s = dsr::pick_shape(cols / 8, dsr::kVmaxSlerp);
+  if (!s.ok()) return DS_ERR_SHAPE;
+  int cus = 0;
+  if ((st = device_cus(&cus)) != DS_OK) return st;
+  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  (void)hipGetLastError();
+  return launch_status(dsr::launch_slerp_rows(s, res, out, alpha, h, rows, (int)(cols / 8), eps,
+                                              grid_for(units, cus), (hipStream_t)stream));
+}
+
+int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t stream) {
+  if (n < 0) return DS_ERR_ARG;
+  if (n == 0) return DS_OK;
+  if (descs == nullptr) return DS_ERR_NULL;
+
+  // 1. validate every descriptor; collect output ranges
+  std::vector<std::pair<uintptr_t, uintptr_t>> outs;
+  for (int32_t i = 0; i < n; ++i) {
+    const ds_rownorm_desc& d = descs[i];
+    int st = check_matrix(d.rows, d.cols, 4, 4);
+    if (st != DS_OK) return st;
+    if (!std::isfinite(d.radius)) return DS_ERR_ARG;
+    if (d.rows == 0) continue;
+    if (d.w == nullptr || d.gain == nullptr || d.w_eff == nullptr) return DS_ERR_NULL;
+    if (!aligned(d.w, 16) || !aligned(d.w_eff, 16) || !aligned(d.gain, 4) ||
+        (d.norm_out != nullptr && !aligned(d.norm_out, 4)))
+      return DS_ERR_ALIGN;
+    const size_t nel = (size_t)d.rows * (size_t)d.cols;
+    const size_t weff_b = nel * 2, w_b = nel * 4, row_b = (size_t)d.rows * 4;
+    if (overlaps(d.w_eff, weff_b, d.w, w_b) || overlaps(d.w_eff, weff_b, d.gain, row_b))
+      return DS_ERR_ARG;
+    if (d.norm_out != nullptr &&
+        (overlaps(d.norm_out, row_b, d.w, w_b) || overlaps(d.norm_out, row_b, d.gain, row_b) ||
+         overlaps(d.norm_out, row_b, d.w_eff, weff_b)))
+      return DS_ERR_ARG;
+    auto a = reinterpret_cast<uintptr_t>(d.w_eff);
+    outs.emplace_back(a, a + weff_b);
+    if (d.norm_out != nullptr) {
+      auto b = reinterpret_cast<uintptr_t>(d.norm_out);
+      outs.emplace_back(b, b + row_b);
+    }
+  }
+  // no two matrices may write the same bytes
+  std::sort(outs.begin(), outs.end());
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (outs[i].first < outs[i - 1].second) return DS_ERR_ARG;
+
+  // 2. group the matrices by kernel shape (a function of cols alone)
+  std::map<int, std::vector<int32_t>> classes;
+  for (int32_t i = 0; i < n; ++i) {
+    if (descs[i].rows == 0) continue;
+    Shape s = dsr::pick_shape(descs[i].cols / 4, dsr::kVmaxRownorm);
+    if (!s.ok()) return DS_ERR_SHAPE;
+    classes[s.G * 100 + s.V].push_back(i);
+  }
+  if (classes.empty()) return DS_OK;
+
+  std::vector<dsr::RownormTask> table;
+  struct Launch { Shape s; size_t first; int ntasks; int nitems; };
+  std::vector<Launch> launches;
+  for (auto& kv : classes) {
+    Shape s{kv.first / 100, kv.first % 100};
+    const int R = s.rows_per_block();
+    Launch L{s, table.size(), 0, 0};
+    int64_t items = 0;
+    for (int32_t i : kv.second) {
+      const ds_rownorm_desc& d = descs[i];
+      dsr::RownormTask t{};
+      t.w = d.w;
+      t.gain = d.gain;
+      t.norm_out = d.norm_out;
+      t.w_eff = d.w_eff;
+      t.rows = d.rows;
+      t.cols = (int32_t)d.cols;
+      t.radius = d.radius;
+      t.item_begin = (int32_t)items;
+      items += (d.rows + R - 1) / R;
+      if (items > INT32_MAX) return DS_ERR_SHAPE;
+      table.push_back(t);
+    }
+    L.ntasks = (int)kv.second.size();
+    L.nitems = (int)items;
+    launches.push_back(L);
+  }
+
+  // 3. stage the table, launch one kernel per shape class
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st != DS_OK) return st;
+  Ring* ring = ring_for_current_device();
+  if (ring == nullptr) return DS_ERR_DEVICE;
+  const size_t bytes = table.size() * sizeof(dsr::RownormTask);
+  int slot = -1;
+  if ((st = acquire(*ring, bytes, &slot)) != DS_OK) return st;
+  Slot& sl = ring->slot[slot];
+  std::memcpy(sl.host, table.data(), bytes);
+  hipStream_t hs = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
+    release(*ring, slot, false, hs);          // nothing enqueued: refund the slot
+    return DS_ERR_LAUNCH;
+  }
+  const auto* dev_tasks = static_cast<const dsr::RownormTask*>(sl.dev);
+  int result = DS_OK;
+  for (const Launch& L : launches) {
+    hipError_t e = dsr::launch_rownorm(L.s, dev_tasks + L.first, L.ntasks, L.nitems,
+                                       grid_for(L.nitems, cus), hs);
+    if (e != hipSuccess) { result = DS_ERR_LAUNCH; break; }
+  }
+  release(*ring, slot, true, hs);             // the copy is in flight either way
+  return result;
+}
+
+}  // extern "C"

@@ -1,0 +1,557 @@
+// Row-L2 kernels for gfx950 (CDNA4, wave64).
+//
+// One wave group of G waves owns one row at a time; each lane holds V
+// 16-byte vectors of the row in VGPRs, so every input byte is read from HBM
+// once and every output byte written once.  Vector v of wave g in a row is
+// the row's 16-byte vector number (v * G + g) * 64 + lane: at every v the
+// group reads one contiguous stretch of 1 KiB per wave.
+//
+// Sums of squares accumulate in fp32 with fused multiply-adds in two chains
+// per lane (even and odd elements), then a fixed wave64 tree (DPP quad
+// swaps and mirrors inside each 16-lane row, then gfx950's permlane16/32
+// swaps across rows), then, for G > 1, a fixed sequential sum of the G wave
+// totals through LDS.  The tree depends on cols alone (cols picks G and V),
+// so a row's bits never depend on the row count, the grid or the batch.
+//
+// The ops (TensorFold PR #1260's two unit-sphere row kernels, the DragonScale
+// README's unit-row weight op):
+//   l2_rows     y = bf16(s * (1 / sqrt(S + eps))), s = x or bf16(x + r)
+//   slerp_rows  a = bf16(l2(res)), b = bf16(l2(out)),
+//               u = a + |alpha| * (b - a) in three rounded fp32 steps,
+//               h = bf16(l2(u))
+//   rownorm     n = sqrt(S), c = (g * rho) / n, W_eff = bf16(w * c)
+//
+// Range.  When S + eps overflows fp32 or falls below 2^-96 (where squares
+// may have lost bits to underflow), the row is summed again scaled by 2^k,
+// k chosen from max(max|s|, sqrt(eps)) so the scaled maximum lies in [1, 2):
+// a power-of-two scaling is exact, so the result is the unscaled one.  That
+// branch depends only on the row's own sum and is uniform over the group.
+//
+// This file is compiled with -ffp-contract=off: only the explicit fmaf calls
+// fuse, so the lerp's three steps stay three roundings.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsr {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kTiny = 0x1p-96f;   // below this, S + eps is recomputed scaled
+
+// ------------------------------------------------------- buffer resources
+//
+// Each row is read and written through its own buffer resource (base = the
+// row's first byte, size = the row's bytes).  Offsets are per-lane VGPRs, so
+// the hardware range check covers them: loads past the row return 0 and
+// stores past it are dropped, which handles a ragged last vector group with
+// no predicate.  Streaming accesses carry the non-temporal hint.
+#ifndef DSR_CPOL
+#define DSR_CPOL 2            // aux bits: 2 = nt (streaming)
+#endif
+constexpr int kCpol = DSR_CPOL;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+struct RowBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ RowBuf(const void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3)) {}
+  __device__ __forceinline__ u32x4_t ld16(int off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpol);
+  }
+  __device__ __forceinline__ f32x4_t ld16f(int off) const {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpol));
+  }
+  __device__ __forceinline__ f32x4_t ld16f_cached(int off) const {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ void st16(u32x4_t v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpol);
+  }
+  __device__ __forceinline__ void st8(u32x2_t v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpol);
+  }
+};
+
+// ---------------------------------------------------------------- bf16 pack
+
+__device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// Two fp32 values -> two bf16 (round to nearest even), low half first.
+// gfx950 does this in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// ------------------------------------------------------------- reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Pairs each lane with the lane 16 (permlane16_swap) or 32 (permlane32_swap)
+// away and returns (low partner, high partner): identical in both lanes.
+__device__ __forceinline__ f32x2_t swap16(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return f32x2_t{__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+__device__ __forceinline__ f32x2_t swap32(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return f32x2_t{__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+
+// Sum over the 64 lanes; every lane gets the same bits (each step adds two
+// equal-bit partial sums, and fp32 addition is commutative).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = v + dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = v + dpp_f<0x141>(v);   // row_half_mirror
+  v = v + dpp_f<0x140>(v);   // row_mirror
+  f32x2_t p = swap16(v);
+  v = p.x + p.y;
+  p = swap32(v);
+  return p.x + p.y;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  f32x2_t p = swap16(v);
+  v = fmaxf(p.x, p.y);
+  p = swap32(v);
+  return fmaxf(p.x, p.y);
+}
+
+// Combine the G wave totals of a row through LDS (G > 1): every wave sums
+// them in the order 0..G-1.  `slot` is G floats of LDS used by this call
+// only; the caller alternates two slots so one barrier per combine suffices.
+template <int G, int N>
+__device__ __forceinline__ void group_sum(float (&v)[N], float* slot, int g, int lane) {
+  if constexpr (G > 1) {
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) slot[i * G + g] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float t = slot[i * G];
+#pragma unroll
+      for (int k = 1; k < G; ++k) t = t + slot[i * G + k];
+      v[i] = t;
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ float group_max(float v, float* slot, int g, int lane) {
+  if constexpr (G > 1) {
+    if (lane == 0) slot[g] = v;
+    __syncthreads();
+    float t = slot[0];
+#pragma unroll
+    for (int k = 1; k < G; ++k) t = fmaxf(t, slot[k]);
+    return t;
+  }
+  return v;
+}
+
+// Round-robin LDS slots for the group combines (two buffers of 2*G floats).
+template <int G>
+struct GroupScratch {
+  float buf[2][2 * G];
+  __device__ __forceinline__ float* next(int& k) { float* p = buf[k]; k ^= 1; return p; }
+};
+
+// Geometry of one launch: which row this wave works on, and its lane/wave.
+template <int G>
+struct Geo {
+  static constexpr int R = (G == 1) ? 4 : 1;        // rows per workgroup pass
+  static constexpr int THREADS = 64 * G * R;
+  int lane, g, rr;
+  __device__ __forceinline__ Geo() {
+    lane = threadIdx.x & 63;
+    // the wave index is uniform within a wave; saying so keeps row addresses
+    // and buffer resources in SGPRs
+    int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    g = (G == 1) ? 0 : wave;
+    rr = (G == 1) ? wave : 0;
+  }
+  __device__ __forceinline__ int vec_index(int v) const { return (v * G + g) * 64 + lane; }
+  template <int V>
+  __device__ __forceinline__ void offsets(int (&off)[V], int vbytes) const {
+#pragma unroll
+    for (int v = 0; v < V; ++v) off[v] = vec_index(v) * vbytes;
+  }
+};
+
+// Scale exponent for a rescued row: -floor(log2(max(m, sqrt(eps)))).
+__device__ __forceinline__ int rescue_shift(float m, float eps) {
+  float M = fmaxf(m, sqrtf(eps));
+  int e;
+  (void)frexpf(M, &e);          // M = f * 2^e, f in [0.5, 1)
+  return 1 - e;                 // M * 2^(1-e) lies in [1, 2)
+}
+
+// ------------------------------------------------- packed-bf16 row in VGPRs
+
+// V 16-byte vectors per lane = 8 bf16 each, held as 4 packed uint32.
+template <int V>
+struct Bf16Row {
+  uint32_t p[V][4];
+
+  __device__ __forceinline__ void load(const RowBuf& b, const int (&off)[V]) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      u32x4_t t = b.ld16(off[v]);
+      p[v][0] = t.x; p[v][1] = t.y; p[v][2] = t.z; p[v][3] = t.w;
+    }
+  }
+
+  // Sum of squares in two fma chains (even, odd elements); the squares of
+  // bf16 values are exact in fp32, so each step rounds once.
+  __device__ __forceinline__ float sumsq() const {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float lo = bf_lo(p[v][k]), hi = bf_hi(p[v][k]);
+        a0 = __builtin_fmaf(lo, lo, a0);
+        a1 = __builtin_fmaf(hi, hi, a1);
+      }
+    return a0 + a1;
+  }
+
+  __device__ __forceinline__ float sumsq_scaled(int sh) const {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float lo = ldexpf(bf_lo(p[v][k]), sh), hi = ldexpf(bf_hi(p[v][k]), sh);
+        a0 = __builtin_fmaf(lo, lo, a0);
+        a1 = __builtin_fmaf(hi, hi, a1);
+      }
+    return a0 + a1;
+  }
+
+  // Forget every value derived from p so far.  Without this the compiler keeps
+  // the 8V unpacked fp32 values of the sum alive until the epilogue instead of
+  // unpacking again (two ALU ops), which doubles the VGPRs and halves the
+  // waves that keep loads in flight.  Emits no instruction.
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(p[v][k]));
+  }
+
+  __device__ __forceinline__ float maxabs() const {
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        m = fmaxf(m, fmaxf(fabsf(bf_lo(p[v][k])), fabsf(bf_hi(p[v][k]))));
+    return m;
+  }
+
+  // p <- bf16(p * inv), or bf16((p * 2^sh) * inv) when scaled.
+  __device__ __forceinline__ void scale(float inv, bool scaled, int sh) {
+    if (!scaled) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          p[v][k] = pack_bf16(bf_lo(p[v][k]) * inv, bf_hi(p[v][k]) * inv);
+    } else {
+      fence();    // keeps the two branches from sharing (and hoisting) their unpacking
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          p[v][k] = pack_bf16(ldexpf(bf_lo(p[v][k]), sh) * inv, ldexpf(bf_hi(p[v][k]), sh) * inv);
+    }
+  }
+
+  __device__ __forceinline__ void store(const RowBuf& b, const int (&off)[V]) const {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      u32x4_t t = {p[v][0], p[v][1], p[v][2], p[v][3]};
+      b.st16(t, off[v]);
+    }
+  }
+};
+
+// Normalise a packed-bf16 row in place: p <- bf16(p / sqrt(S + eps)), where
+// S is the row's (group-combined) fp32 sum of squares.
+template <int G, int V>
+__device__ __forceinline__ void l2_in_place(Bf16Row<V>& s, float S, float eps,
+                                            GroupScratch<G>& gs, int& slot,
+                                            const Geo<G>& geo) {
+  float T = S + eps;
+  bool scaled = false;
+  int sh = 0;
+  if (T == __builtin_inff() || T < kTiny) {       // uniform over the group
+    float m = group_max<G>(wave_max(s.maxabs()), gs.next(slot), geo.g, geo.lane);
+    s.fence();
+    if (m > 0.f && m < __builtin_inff()) {
+      sh = rescue_shift(m, eps);
+      float t[1] = {wave_sum(s.sumsq_scaled(sh))};
+      group_sum<G, 1>(t, gs.next(slot), geo.g, geo.lane);
+      T = t[0] + ldexpf(eps, 2 * sh);
+      scaled = true;
+    }
+  }
+  float inv = 1.0f / sqrtf(T);
+  s.fence();      // the epilogue unpacks again rather than share the rare branch's values
+  s.scale(inv, scaled, sh);
+}
+
+// ------------------------------------------------------------------ l2_rows
+
+template <int G, int V, bool RES>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+l2_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int nvec, float eps) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  int off[V];
+  geo.offsets(off, 16);
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+
+  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
+    const int64_t row = base + geo.rr;
+    if (G == 1 && row >= rows) break;             // waves of a G == 1 group are independent
+    Bf16Row<V> s;
+    s.load(RowBuf(x + row * nvec, row_bytes), off);
+    if constexpr (RES) {
+      Bf16Row<V> rv;
+      rv.load(RowBuf(r + row * nvec, row_bytes), off);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          s.p[v][k] = pack_bf16(bf_lo(s.p[v][k]) + bf_lo(rv.p[v][k]),
+                                bf_hi(s.p[v][k]) + bf_hi(rv.p[v][k]));
+    }
+    float S[1] = {wave_sum(s.sumsq())};
+    s.fence();
+    group_sum<G, 1>(S, gs.next(slot), geo.g, geo.lane);
+    l2_in_place<G, V>(s, S[0], eps, gs, slot, geo);
+    s.store(RowBuf(y + row * nvec, row_bytes), off);
+  }
+}
+
+// --------------------------------------------------------------- slerp_rows
+
+template <int G, int V>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, u32x4_t* h,
+                  int64_t rows, int nvec, float eps) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  int off[V];
+  geo.offsets(off, 16);
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  const RowBuf abuf(alpha, row_bytes * 2u);        // alpha: cols fp32 = 2 x row_bytes
+
+  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
+    const int64_t row = base + geo.rr;
+    if (G == 1 && row >= rows) break;
+    Bf16Row<V> a, b;
+    a.load(RowBuf(res + row * nvec, row_bytes), off);
+    b.load(RowBuf(out + row * nvec, row_bytes), off);
+    float S[2] = {wave_sum(a.sumsq()), wave_sum(b.sumsq())};
+    a.fence();
+    b.fence();
+    group_sum<G, 2>(S, gs.next(slot), geo.g, geo.lane);
+    l2_in_place<G, V>(a, S[0], eps, gs, slot, geo);   // a = bf16(l2(res))
+    l2_in_place<G, V>(b, S[1], eps, gs, slot, geo);   // b = bf16(l2(out))
+
+    // u = a + |alpha| * (b - a), three rounded fp32 steps; kept in VGPRs.
+    float u[V][8];
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const f32x4_t al0 = abuf.ld16f_cached(2 * off[v]);
+      const f32x4_t al1 = abuf.ld16f_cached(2 * off[v] + 16);
+      const float al[8] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float alo = bf_lo(a.p[v][k]), ahi = bf_hi(a.p[v][k]);
+        float blo = bf_lo(b.p[v][k]), bhi = bf_hi(b.p[v][k]);
+        float dlo = blo - alo, dhi = bhi - ahi;
+        float tlo = fabsf(al[2 * k]) * dlo, thi = fabsf(al[2 * k + 1]) * dhi;
+        float ulo = alo + tlo, uhi = ahi + thi;
+        u[v][2 * k] = ulo;
+        u[v][2 * k + 1] = uhi;
+        a0 = __builtin_fmaf(ulo, ulo, a0);
+        a1 = __builtin_fmaf(uhi, uhi, a1);
+      }
+    }
+    float Su[1] = {wave_sum(a0 + a1)};
+    group_sum<G, 1>(Su, gs.next(slot), geo.g, geo.lane);
+
+    float T = Su[0] + eps;
+    bool scaled = false;
+    int sh = 0;
+    if (T == __builtin_inff() || T < kTiny) {
+      float m = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(u[v][k]));
+      m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
+      if (m > 0.f && m < __builtin_inff()) {
+        sh = rescue_shift(m, eps);
+        float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float lo = ldexpf(u[v][2 * k], sh), hi = ldexpf(u[v][2 * k + 1], sh);
+            c0 = __builtin_fmaf(lo, lo, c0);
+            c1 = __builtin_fmaf(hi, hi, c1);
+          }
+        float t[1] = {wave_sum(c0 + c1)};
+        group_sum<G, 1>(t, gs.next(slot), geo.g, geo.lane);
+        T = t[0] + ldexpf(eps, 2 * sh);
+        scaled = true;
+      }
+    }
+    const float inv = 1.0f / sqrtf(T);
+    const RowBuf hb(h + row * nvec, row_bytes);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      uint32_t q[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float lo = u[v][2 * k], hi = u[v][2 * k + 1];
+        if (scaled) { lo = ldexpf(lo, sh); hi = ldexpf(hi, sh); }
+        q[k] = pack_bf16(lo * inv, hi * inv);
+      }
+      u32x4_t t = {q[0], q[1], q[2], q[3]};
+      hb.st16(t, off[v]);
+    }
+  }
+}
+
+// ------------------------------------------------------- weight rownorm+gain
+
+// One matrix of a ragged call, as the kernel reads it.  Items are groups of
+// R rows; matrix m owns items [item_begin, item_begin + ceil(rows / R)).
+struct RownormTask {
+  const float* w;
+  const float* gain;
+  float* norm_out;      // may be null
+  uint16_t* w_eff;
+  int64_t rows;
+  int32_t cols;
+  float radius;
+  int32_t item_begin;
+  int32_t pad_;
+};
+
+template <int G, int V>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+rownorm_kernel(const RownormTask* tasks, int ntasks, int nitems) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  int off[V];
+  geo.offsets(off, 16);
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    // the task owning this item: last task with item_begin <= item
+    int lo = 0, hi = ntasks - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (tasks[mid].item_begin <= item) lo = mid; else hi = mid - 1;
+    }
+    const RownormTask t = tasks[lo];
+    const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
+    if (G == 1 && row >= t.rows) continue;          // independent waves only
+    const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
+    float w[V][4];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const f32x4_t q = wb.ld16f(off[v]);
+      w[v][0] = q.x; w[v][1] = q.y; w[v][2] = q.z; w[v][3] = q.w;
+    }
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      a0 = __builtin_fmaf(w[v][0], w[v][0], a0);
+      a1 = __builtin_fmaf(w[v][1], w[v][1], a1);
+      a0 = __builtin_fmaf(w[v][2], w[v][2], a0);
+      a1 = __builtin_fmaf(w[v][3], w[v][3], a1);
+    }
+    float S[1] = {wave_sum(a0 + a1)};
+    group_sum<G, 1>(S, gs.next(slot), geo.g, geo.lane);
+    float T = S[0];
+    bool scaled = false;
+    int sh = 0;
+    if (T == __builtin_inff() || T < kTiny) {
+      float m = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(w[v][k]));
+      m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
+      if (m > 0.f && m < __builtin_inff()) {
+        sh = rescue_shift(m, 0.f);
+        float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float q0 = ldexpf(w[v][0], sh), q1 = ldexpf(w[v][1], sh);
+          float q2 = ldexpf(w[v][2], sh), q3 = ldexpf(w[v][3], sh);
+          c0 = __builtin_fmaf(q0, q0, c0);
+          c1 = __builtin_fmaf(q1, q1, c1);
+          c0 = __builtin_fmaf(q2, q2, c0);
+          c1 = __builtin_fmaf(q3, q3, c1);
+        }
+        float tt[1] = {wave_sum(c0 + c1)};
+        group_sum<G, 1>(tt, gs.next(slot), geo.g, geo.lane);
+        T = tt[0];
+        scaled = true;
+      }
+    }
+    const float rn = sqrtf(T);                       // length (of the scaled row)
+    if (t.norm_out != nullptr && geo.g == 0 && geo.lane == 0)
+      t.norm_out[row] = scaled ? ldexpf(rn, -sh) : rn;
+    const float gr = t.gain[row] * t.radius;
+    const float c = (rn == 0.f) ? 0.f : gr / rn;
+    const RowBuf eb(t.w_eff + row * t.cols, (uint32_t)t.cols * 2u);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float q[4] = {w[v][0], w[v][1], w[v][2], w[v][3]};
+      if (scaled) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = ldexpf(q[k], sh);
+      }
+      u32x2_t o = {pack_bf16(q[0] * c, q[1] * c), pack_bf16(q[2] * c, q[3] * c)};
+      eb.st8(o, off[v] / 2);
+    }
+  }
+}
+
+}  // namespace dsr

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: symbols, status strings and argument validation.
+
+Every refused call returns before its first HIP call, so these run anywhere
+(fake pointer values are never dereferenced).  Calls with valid arguments are
+made only where no HIP device exists, where they must stop at DS_ERR_DEVICE.
+"""
+import ctypes
+import os
+
+import pytest
+
+from scale_invariant_row_amd import binding as B
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="library not built (python -m scale_invariant_row_amd.build)")
+
+
+def no_device():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = B.header_functions()
+    assert set(names) == {"ds_l2_rows", "ds_slerp_rows", "ds_weight_rownorm_gain",
+                          "ds_status_string", "ds_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(L):
+    assert B.ds_version() == 10000
+    for code in range(0, -8, -1):
+        s = B.ds_status_string(code)
+        assert s.startswith("DS_"), s
+    assert "unknown" in B.ds_status_string(42)
+
+
+A = 0x10000          # fake, 16-byte aligned addresses; never dereferenced
+Bp = 0x20000000
+C = 0x40000000
+
+
+@pytest.mark.parametrize("rows,cols,code", [
+    (-1, 64, B.DS_ERR_SHAPE), (4, 0, B.DS_ERR_SHAPE), (4, 12, B.DS_ERR_SHAPE),
+    (4, 65544, B.DS_ERR_SHAPE), (4, 4, B.DS_ERR_SHAPE), (1 << 60, 64, B.DS_ERR_SHAPE)])
+def test_l2_shape(L, rows, cols, code):
+    assert L.ds_l2_rows(A, None, Bp, rows, cols, 1e-6, None) == code
+
+
+def test_l2_eps(L):
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert L.ds_l2_rows(A, None, Bp, 4, 64, eps, None) == B.DS_ERR_ARG
+
+
+def test_l2_pointers(L):
+    assert L.ds_l2_rows(None, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert L.ds_l2_rows(A, None, None, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert L.ds_l2_rows(A + 8, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert L.ds_l2_rows(A, A + 2, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert L.ds_l2_rows(A, None, Bp + 4, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    # y partly overlapping x or r
+    assert L.ds_l2_rows(A, None, A + 16, 4, 64, 1e-6, None) == B.DS_ERR_ARG
+    assert L.ds_l2_rows(A, C, C + 256, 4, 64, 1e-6, None) == B.DS_ERR_ARG
+
+
+def test_l2_zero_rows_is_noop(L):
+    assert L.ds_l2_rows(None, None, None, 0, 64, 1e-6, None) == B.DS_OK
+
+
+@pytest.mark.skipif("not no_device()")
+def test_l2_valid_args_reach_device_lookup(L):
+    assert L.ds_l2_rows(A, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE
+    assert L.ds_l2_rows(A, C, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE     # y == x is allowed
+    assert L.ds_slerp_rows(A, Bp, C, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE
+
+
+def test_slerp_validation(L):
+    f = L.ds_slerp_rows
+    assert f(A, Bp, None, C, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert f(A, Bp, C + 4, C + 4096, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert f(A, Bp, C, C + 64, 4, 64, 1e-6, None) == B.DS_ERR_ARG     # alpha overlaps h
+    assert f(A, Bp, C, A + 32, 4, 64, 1e-6, None) == B.DS_ERR_ARG     # h partly over res
+    assert f(A, Bp, C, C + 4096, 4, 60, 1e-6, None) == B.DS_ERR_SHAPE
+    assert f(A, Bp, C, C + 4096, 4, 64, -1.0, None) == B.DS_ERR_ARG
+    assert f(None, None, None, None, 0, 64, 1e-6, None) == B.DS_OK
+
+
+def _descs(*items):
+    arr = (B.RownormDesc * len(items))()
+    for i, d in enumerate(items):
+        arr[i] = B.RownormDesc(*d)
+    return arr
+
+
+def test_rownorm_validation(L):
+    f = L.ds_weight_rownorm_gain
+    good = (A, Bp, 1.0, Bp + 4096, C, 16, 64)
+    assert f(_descs(good), -1, None) == B.DS_ERR_ARG
+    assert f(None, 0, None) == B.DS_OK
+    assert f(None, 2, None) == B.DS_ERR_NULL
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 6)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_descs((A, Bp, float("inf"), None, C, 16, 64)), 1, None) == B.DS_ERR_ARG
+    assert f(_descs((A, None, 1.0, None, C, 16, 64)), 1, None) == B.DS_ERR_NULL
+    assert f(_descs((A + 4, Bp, 1.0, None, C, 16, 64)), 1, None) == B.DS_ERR_ALIGN
+    assert f(_descs((A, Bp, 1.0, Bp + 4098, C, 16, 64)), 1, None) == B.DS_ERR_ALIGN
+    assert f(_descs((A, Bp, 1.0, None, A + 64, 16, 64)), 1, None) == B.DS_ERR_ARG   # w_eff over w
+    # two matrices writing the same bytes
+    assert f(_descs(good, (A, Bp, 1.0, None, C + 512, 16, 64)), 2, None) == B.DS_ERR_ARG
+    # a bad descriptor anywhere refuses the whole call
+    assert f(_descs(good, (A, Bp, 1.0, None, C + 65536, -3, 64)), 2, None) == B.DS_ERR_SHAPE
+    # zero-row descriptors are skipped, pointers unchecked
+    assert f(_descs((None, None, 1.0, None, None, 0, 64)), 1, None) == B.DS_OK
+
+
+@pytest.mark.skipif("not no_device()")
+def test_rownorm_valid_args_reach_device_lookup(L):
+    good = (A, Bp, 1.0, Bp + 4096, C, 16, 64)
+    shared_w = (A, Bp, 1.0, None, C + 65536, 16, 64)      # tied weights: same w, two outputs
+    assert L.ds_weight_rownorm_gain(_descs(good, shared_w), 2, None) == B.DS_ERR_DEVICE
+
+
+def test_binding_raises_on_missing_library(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libdsrows.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
