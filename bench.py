@@ -83,7 +83,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=ROWS)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -132,35 +132,46 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # timed region: exactly K steps, events at its two ends only
+    t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
         s = sets[i % len(sets)]
-        e = ev[i]
-        e[0].record(stream)
         st1 = l2(s)
-        e[1].record(stream)
-        e[2].record(stream)
         st2 = slerp(s)
-        e[3].record(stream)
         if st1 or st2:
             raise RuntimeError(f"launch failed: {B.ds_status_string(st1 or st2)}")
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    l2_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    sl_ms = [e[2].elapsed_time(e[3]) for e in ev]
     ms_per_step = total_ms / K
+
+    # per-kernel duration: K back-to-back launches of one kernel between two
+    # events on the launch stream (an event between every pair of launches
+    # would add its own ~2 us to each)
+    def batch_us(fn):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(K):
+            if fn(sets[i % len(sets)]):
+                raise RuntimeError("launch failed")
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / K
+
+    l2_us = batch_us(l2)
+    sl_us = batch_us(slerp)
 
     l2_bytes = ROWS * COLS * 2 * 3                      # x, r read; y written
     sl_bytes = ROWS * COLS * 2 * 3 + COLS * 4           # res, out read; h written; alpha once
     step_bytes = l2_bytes + sl_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    l2_us = 1e3 * float(np.mean(l2_ms))
-    sl_us = 1e3 * float(np.mean(sl_ms))
 
     def op(us, nbytes, rows):
         gbps = nbytes / (us * 1e-6) / 1e9
@@ -187,17 +198,17 @@ def main():
     for i in range(10):
         assert L.ds_weight_rownorm_gain(rn_sets[i % 3][0], n_rn, sp) == 0
     torch.cuda.synchronize()
-    rn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(60)]
-    for i, (a, b) in enumerate(rn_ev):
-        a.record(stream)
+    a, b = ev(), ev()
+    a.record(stream)
+    for i in range(60):
         assert L.ds_weight_rownorm_gain(rn_sets[i % 3][0], n_rn, sp) == 0
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
-    rn_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in rn_ev]))
+    rn_us = a.elapsed_time(b) * 1e3 / 60
     rn_bytes = rn.total_elems * 6 + rn.total_rows * 8
     ops["weight_rownorm_gain_12x4_d768"] = op(rn_us, rn_bytes, rn.total_rows)
-    ops["weight_rownorm_gain_12x4_d768"]["note"] = "includes the descriptor-table copy"
+    ops["weight_rownorm_gain_12x4_d768"]["note"] = ("one call: the descriptor-table copy and one "
+                                                    "launch per row-width class")
 
     # ---- a plain device copy of the same bytes as l2_rows moves (reference ceiling)
     src = torch.empty(l2_bytes // 2, dtype=torch.uint8, device=dev)   # read + write = l2_bytes
@@ -206,14 +217,13 @@ def main():
     for i in range(5):
         dsts[i % 4].copy_(srcs[i % 4])
     torch.cuda.synchronize()
-    cp_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(40)]
-    for i, (a, b) in enumerate(cp_ev):
-        a.record(stream)
+    a, b = ev(), ev()
+    a.record(stream)
+    for i in range(40):
         dsts[i % 4].copy_(srcs[i % 4])
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
-    cp_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in cp_ev]))
+    cp_us = a.elapsed_time(b) * 1e3 / 40
     ops["torch_copy_same_bytes"] = op(cp_us, 2 * src.numel(), ROWS)
     del srcs, dsts, src
 

@@ -313,17 +313,21 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     launches.push_back(L);
   }
 
-  // 3. stage the table, launch one kernel per shape class
+  // 3. stage the table (tasks, then each task's first item as a compact int32
+  //    array for the kernels' lookup), launch one kernel per shape class
   int cus = 0;
   int st = device_cus(&cus);
   if (st != DS_OK) return st;
   Ring* ring = ring_for_current_device();
   if (ring == nullptr) return DS_ERR_DEVICE;
-  const size_t bytes = table.size() * sizeof(dsr::RownormTask);
+  const size_t task_bytes = table.size() * sizeof(dsr::RownormTask);
+  const size_t bytes = task_bytes + table.size() * sizeof(int32_t);
   int slot = -1;
   if ((st = acquire(*ring, bytes, &slot)) != DS_OK) return st;
   Slot& sl = ring->slot[slot];
-  std::memcpy(sl.host, table.data(), bytes);
+  std::memcpy(sl.host, table.data(), task_bytes);
+  int32_t* begins_host = reinterpret_cast<int32_t*>(static_cast<char*>(sl.host) + task_bytes);
+  for (size_t i = 0; i < table.size(); ++i) begins_host[i] = table[i].item_begin;
   hipStream_t hs = (hipStream_t)stream;
   (void)hipGetLastError();
   if (hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
@@ -331,10 +335,12 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     return DS_ERR_LAUNCH;
   }
   const auto* dev_tasks = static_cast<const dsr::RownormTask*>(sl.dev);
+  const auto* dev_begins =
+      reinterpret_cast<const int32_t*>(static_cast<const char*>(sl.dev) + task_bytes);
   int result = DS_OK;
   for (const Launch& L : launches) {
-    hipError_t e = dsr::launch_rownorm(L.s, dev_tasks + L.first, L.ntasks, L.nitems,
-                                       grid_for(L.nitems, cus), hs);
+    hipError_t e = dsr::launch_rownorm(L.s, dev_tasks + L.first, dev_begins + L.first, L.ntasks,
+                                       L.nitems, grid_for(L.nitems, cus), hs);
     if (e != hipSuccess) { result = DS_ERR_LAUNCH; break; }
   }
   release(*ring, slot, true, hs);             // the copy is in flight either way

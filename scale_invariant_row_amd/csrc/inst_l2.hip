@@ -23,24 +23,12 @@ hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_
   switch (s.G * 100 + s.V) {
     case 101: return run<1, 1>(x, r, y, rows, nvec, eps, grid, stream);
     case 102: return run<1, 2>(x, r, y, rows, nvec, eps, grid, stream);
-    case 103: return run<1, 3>(x, r, y, rows, nvec, eps, grid, stream);
-    case 104: return run<1, 4>(x, r, y, rows, nvec, eps, grid, stream);
-    case 105: return run<1, 5>(x, r, y, rows, nvec, eps, grid, stream);
-    case 106: return run<1, 6>(x, r, y, rows, nvec, eps, grid, stream);
-    case 107: return run<1, 7>(x, r, y, rows, nvec, eps, grid, stream);
-    case 108: return run<1, 8>(x, r, y, rows, nvec, eps, grid, stream);
-    case 205: return run<2, 5>(x, r, y, rows, nvec, eps, grid, stream);
-    case 206: return run<2, 6>(x, r, y, rows, nvec, eps, grid, stream);
-    case 207: return run<2, 7>(x, r, y, rows, nvec, eps, grid, stream);
-    case 208: return run<2, 8>(x, r, y, rows, nvec, eps, grid, stream);
-    case 405: return run<4, 5>(x, r, y, rows, nvec, eps, grid, stream);
-    case 406: return run<4, 6>(x, r, y, rows, nvec, eps, grid, stream);
-    case 407: return run<4, 7>(x, r, y, rows, nvec, eps, grid, stream);
-    case 408: return run<4, 8>(x, r, y, rows, nvec, eps, grid, stream);
-    case 805: return run<8, 5>(x, r, y, rows, nvec, eps, grid, stream);
-    case 806: return run<8, 6>(x, r, y, rows, nvec, eps, grid, stream);
-    case 807: return run<8, 7>(x, r, y, rows, nvec, eps, grid, stream);
-    case 808: return run<8, 8>(x, r, y, rows, nvec, eps, grid, stream);
+    case 202: return run<2, 2>(x, r, y, rows, nvec, eps, grid, stream);
+    case 402: return run<4, 2>(x, r, y, rows, nvec, eps, grid, stream);
+    case 802: return run<8, 2>(x, r, y, rows, nvec, eps, grid, stream);
+    case 1602: return run<16, 2>(x, r, y, rows, nvec, eps, grid, stream);
+    case 1603: return run<16, 3>(x, r, y, rows, nvec, eps, grid, stream);
+    case 1604: return run<16, 4>(x, r, y, rows, nvec, eps, grid, stream);
     case 1605: return run<16, 5>(x, r, y, rows, nvec, eps, grid, stream);
     case 1606: return run<16, 6>(x, r, y, rows, nvec, eps, grid, stream);
     case 1607: return run<16, 7>(x, r, y, rows, nvec, eps, grid, stream);

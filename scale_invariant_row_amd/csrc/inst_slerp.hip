@@ -21,14 +21,10 @@ hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const fl
   switch (s.G * 100 + s.V) {
     case 101: return run<1, 1>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 102: return run<1, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 103: return run<1, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 104: return run<1, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 203: return run<2, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 204: return run<2, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 403: return run<4, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 404: return run<4, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 803: return run<8, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 804: return run<8, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 202: return run<2, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 402: return run<4, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 802: return run<8, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 1602: return run<16, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 1603: return run<16, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 1604: return run<16, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 1605: return run<16, 5>(res, out, alpha, h, rows, nvec, eps, grid, stream);

@@ -19,10 +19,13 @@ struct Shape {
 
 // Largest V per lane for each op (registers hold the whole row): the shape is
 // the smallest G in {1, 2, 4, 8, 16} whose V = ceil(vectors / (64 G)) fits.
-constexpr int kVmaxL2 = 8;
-constexpr int kVmaxSlerp = 4;
-constexpr int kVmaxRownorm = 12;
-constexpr int kVmaxWide = 16;     // G = 16 may go up to here (DS_MAX_COLS)
+// Measured on MI355X: rows spread over more, lighter waves (V <= 2) stream
+// best for bf16 rows from 1,024 to 8,192 wide; only rows wider than 16,384
+// fall back to G = 16 with up to 8 vectors per lane.
+constexpr int kVmaxL2 = 2;
+constexpr int kVmaxSlerp = 2;
+constexpr int kVmaxRownorm = 6;
+constexpr int kVmaxWide = 16;     // G = 16 may go up to here (DS_MAX_COLS fp32 rows)
 
 // Shape for a row of `vectors` 16-byte vectors; a function of the width only.
 inline Shape pick_shape(int64_t vectors, int vmax) {
@@ -38,7 +41,7 @@ hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_
 hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const float* alpha,
                              void* h, int64_t rows, int nvec, float eps, int grid,
                              hipStream_t stream);
-hipError_t launch_rownorm(Shape s, const RownormTask* tasks, int ntasks, int nitems, int grid,
-                          hipStream_t stream);
+hipError_t launch_rownorm(Shape s, const RownormTask* tasks, const int32_t* begins, int ntasks,
+                          int nitems, int grid, hipStream_t stream);
 
 }  // namespace dsr

@@ -51,10 +51,14 @@ constexpr float kTiny = 0x1p-96f;   // below this, S + eps is recomputed scaled
 // the hardware range check covers them: loads past the row return 0 and
 // stores past it are dropped, which handles a ragged last vector group with
 // no predicate.  Streaming accesses carry the non-temporal hint.
-#ifndef DSR_CPOL
-#define DSR_CPOL 2            // aux bits: 2 = nt (streaming)
+#ifndef DSR_CPOL_LD
+#define DSR_CPOL_LD 2         // aux bits of streaming loads: 2 = nt
 #endif
-constexpr int kCpol = DSR_CPOL;
+#ifndef DSR_CPOL_ST
+#define DSR_CPOL_ST 2         // aux bits of streaming stores: 2 = nt
+#endif
+constexpr int kCpolLd = DSR_CPOL_LD;
+constexpr int kCpolSt = DSR_CPOL_ST;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 
 struct RowBuf {
@@ -62,19 +66,19 @@ struct RowBuf {
   __device__ __forceinline__ RowBuf(const void* base, uint32_t bytes)
       : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3)) {}
   __device__ __forceinline__ u32x4_t ld16(int off) const {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpol);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolLd);
   }
   __device__ __forceinline__ f32x4_t ld16f(int off) const {
-    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpol));
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolLd));
   }
   __device__ __forceinline__ f32x4_t ld16f_cached(int off) const {
     return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   }
   __device__ __forceinline__ void st16(u32x4_t v, int off) const {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpol);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSt);
   }
   __device__ __forceinline__ void st8(u32x2_t v, int off) const {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpol);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolSt);
   }
 };
 
@@ -470,9 +474,24 @@ struct RownormTask {
   int32_t pad_;
 };
 
+// Index of the task owning `item`: the number of tasks whose first item is
+// <= item, minus one.  `begins` holds the tasks' item_begin in ascending
+// order; each lane tests one task and a ballot counts them, 64 per load.
+__device__ __forceinline__ int owning_task(const int32_t* begins, int ntasks, int item, int lane) {
+  int count = 0;
+  for (int base = 0; base < ntasks; base += 64) {
+    const int k = base + lane;
+    const int b = (k < ntasks) ? begins[k] : 0x7fffffff;
+    const int c = __popcll(__ballot(b <= item));
+    count += c;
+    if (c < 64) break;                        // uniform: the ballot is the same in every lane
+  }
+  return count - 1;
+}
+
 template <int G, int V>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
-rownorm_kernel(const RownormTask* tasks, int ntasks, int nitems) {
+rownorm_kernel(const RownormTask* tasks, const int32_t* begins, int ntasks, int nitems) {
   constexpr int R = Geo<G>::R;
   const Geo<G> geo;
   __shared__ GroupScratch<G> gs;
@@ -481,12 +500,7 @@ rownorm_kernel(const RownormTask* tasks, int ntasks, int nitems) {
   geo.offsets(off, 16);
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    // the task owning this item: last task with item_begin <= item
-    int lo = 0, hi = ntasks - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (tasks[mid].item_begin <= item) lo = mid; else hi = mid - 1;
-    }
+    const int lo = __builtin_amdgcn_readfirstlane(owning_task(begins, ntasks, item, geo.lane));
     const RownormTask t = tasks[lo];
     const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
     if (G == 1 && row >= t.rows) continue;          // independent waves only
