@@ -10,7 +10,10 @@ every launch streams from HBM.  The weight op (ds_weight_rownorm_gain over a
 reported beside them.
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (each input
-read once, each output written once) over its time, in GB/s.
+read once, each output written once) over its time, in GB/s.  The K steps are
+timed with events at the two ends of the region only; each kernel's average
+duration (``ops``, ``roofline``) comes from K back-to-back launches of that
+kernel between two events on the launch stream.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu]
 """
@@ -30,7 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 ROWS, COLS = 8192, 4096
 EPS = 1e-6
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_l2_slerp_rownorm.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
                   "inst_rownorm.hip", "ds_rows.hip"]
 
@@ -43,17 +46,23 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, per_launch_algo: float):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
-    when they are missing or were taken from different kernel sources."""
+def traffic_for(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each calibrated on a copy of known size), or
+    None when it is missing or was taken from different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            lines = f.read().splitlines()
+    except OSError:
         return None
-    if t.get("kernel_hash") != kernel_hash() or kernel not in t.get("kernels", {}):
-        return None
-    return t["kernels"][kernel]["bytes_per_dispatch"]
+    found, khash = None, None
+    for line in lines:
+        parts = line.split()
+        if len(parts) == 2 and parts[0] == "kernel_hash":
+            khash = parts[1]
+        if len(parts) == 3 and parts[0] == "traffic" and parts[1] == kernel:
+            found = int(parts[2])
+    return found if khash == kernel_hash() else None
 
 
 def cpu_baseline(l2c, slc, rows: int):
@@ -233,7 +242,7 @@ def main():
     d = ops[dominant]
     roofline = {"bound": "hbm", "kernel": kname, "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": d["frac"],
-                "traffic": traffic_for(kname, d["bytes"]),
+                "traffic": traffic_for(kname),
                 "algorithmic_bytes_per_launch": d["bytes"]}
 
     result = {
