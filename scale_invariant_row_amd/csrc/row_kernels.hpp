@@ -41,6 +41,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kTiny = 0x1p-96f;   // below this, S + eps is recomputed scaled
 
@@ -264,14 +265,19 @@ struct Bf16Row {
       for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(p[v][k]));
   }
 
+  // Largest |value| of the row, on the packed bits: with the sign cleared, a
+  // bf16 pattern orders like its magnitude (infinity above every finite
+  // value), so a packed unsigned 16-bit max needs no unpacking.  Only used
+  // when the sum is finite, i.e. the row holds no NaN.
   __device__ __forceinline__ float maxabs() const {
-    float m = 0.f;
+    u16x2_t mx = {0, 0};
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        m = fmaxf(m, fmaxf(fabsf(bf_lo(p[v][k])), fabsf(bf_hi(p[v][k]))));
-    return m;
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, p[v][k] & 0x7fff7fffu));
+    const uint32_t top = mx.x > mx.y ? mx.x : mx.y;
+    return __uint_as_float(top << 16);
   }
 
   // p <- bf16(p * inv), or bf16((p * 2^sh) * inv) when scaled.
@@ -364,6 +370,26 @@ l2_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int
 
 // --------------------------------------------------------------- slerp_rows
 
+// |alpha| for this lane's columns: loaded once, before any row, when it fits
+// in registers (V <= 4); wider shapes load it next to each row's lerp.
+template <int V>
+struct AbsAlpha {
+  static constexpr bool kHeld = V <= 4;
+  float a[kHeld ? V : 1][8];
+  __device__ __forceinline__ void load_into(float (&dst)[8], const RowBuf& b, int off) const {
+    const f32x4_t a0 = b.ld16f_cached(2 * off);
+    const f32x4_t a1 = b.ld16f_cached(2 * off + 16);
+    dst[0] = fabsf(a0.x); dst[1] = fabsf(a0.y); dst[2] = fabsf(a0.z); dst[3] = fabsf(a0.w);
+    dst[4] = fabsf(a1.x); dst[5] = fabsf(a1.y); dst[6] = fabsf(a1.z); dst[7] = fabsf(a1.w);
+  }
+  __device__ __forceinline__ void init(const RowBuf& b, const int (&off)[V]) {
+    if constexpr (kHeld) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) load_into(a[v], b, off[v]);
+    }
+  }
+};
+
 template <int G, int V>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
 slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, u32x4_t* h,
@@ -376,6 +402,8 @@ slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, 
   geo.offsets(off, 16);
   const uint32_t row_bytes = (uint32_t)nvec * 16u;
   const RowBuf abuf(alpha, row_bytes * 2u);        // alpha: cols fp32 = 2 x row_bytes
+  AbsAlpha<V> al;
+  al.init(abuf, off);
 
   for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
     const int64_t row = base + geo.rr;
@@ -390,25 +418,54 @@ slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, 
     l2_in_place<G, V>(a, S[0], eps, gs, slot, geo);   // a = bf16(l2(res))
     l2_in_place<G, V>(b, S[1], eps, gs, slot, geo);   // b = bf16(l2(out))
 
-    // u = a + |alpha| * (b - a), three rounded fp32 steps; kept in VGPRs.
-    float u[V][8];
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const f32x4_t al0 = abuf.ld16f_cached(2 * off[v]);
-      const f32x4_t al1 = abuf.ld16f_cached(2 * off[v] + 16);
-      const float al[8] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
+    // u = a + |alpha| * (b - a), three rounded fp32 steps.  Narrow shapes keep
+    // u in VGPRs; wide ones (V > 4) recompute it, bit for bit, when storing.
+    constexpr bool kKeepU = V <= 4;
+    float u[kKeepU ? V : 1][8];
+    // Wide shapes unpack a and b and re-load alpha (an L2 hit) in each pass:
+    // the fences and the empty asm with a memory clobber stop the compiler
+    // from keeping the first pass's unpacked values and alpha alive instead,
+    // which would spill.  None of them emits an instruction.
+    auto reload_point = [&]() {
+      if constexpr (!kKeepU) {
+        a.fence();
+        b.fence();
+        asm volatile("" ::: "memory");
+      }
+    };
+    auto lerp = [&](int v, float (&uv)[8]) {
+      float tmp[8];
+      if constexpr (!kKeepU) asm volatile("" ::: "memory");   // one vector's alpha at a time
+      if constexpr (!AbsAlpha<V>::kHeld) al.load_into(tmp, abuf, off[v]);
+      const float* alv = AbsAlpha<V>::kHeld ? al.a[AbsAlpha<V>::kHeld ? v : 0] : tmp;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float alo = bf_lo(a.p[v][k]), ahi = bf_hi(a.p[v][k]);
-        float blo = bf_lo(b.p[v][k]), bhi = bf_hi(b.p[v][k]);
-        float dlo = blo - alo, dhi = bhi - ahi;
-        float tlo = fabsf(al[2 * k]) * dlo, thi = fabsf(al[2 * k + 1]) * dhi;
-        float ulo = alo + tlo, uhi = ahi + thi;
-        u[v][2 * k] = ulo;
-        u[v][2 * k + 1] = uhi;
-        a0 = __builtin_fmaf(ulo, ulo, a0);
-        a1 = __builtin_fmaf(uhi, uhi, a1);
+        const float alo = bf_lo(a.p[v][k]), ahi = bf_hi(a.p[v][k]);
+        const float blo = bf_lo(b.p[v][k]), bhi = bf_hi(b.p[v][k]);
+        const float dlo = blo - alo, dhi = bhi - ahi;
+        const float tlo = alv[2 * k] * dlo, thi = alv[2 * k + 1] * dhi;
+        uv[2 * k] = alo + tlo;
+        uv[2 * k + 1] = ahi + thi;
+      }
+    };
+    float a0 = 0.f, a1 = 0.f;
+    float m = 0.f;
+    reload_point();
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float t[8];
+      lerp(v, t);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a0 = __builtin_fmaf(t[2 * k], t[2 * k], a0);
+        a1 = __builtin_fmaf(t[2 * k + 1], t[2 * k + 1], a1);
+      }
+      if constexpr (kKeepU) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) u[v][k] = t[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(t[k]));
       }
     }
     float Su[1] = {wave_sum(a0 + a1)};
@@ -417,43 +474,61 @@ slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, 
     float T = Su[0] + eps;
     bool scaled = false;
     int sh = 0;
-    if (T == __builtin_inff() || T < kTiny) {
-      float m = 0.f;
+    if (T == __builtin_inff() || T < kTiny) {          // uniform over the group
+      if constexpr (kKeepU) {
 #pragma unroll
-      for (int v = 0; v < V; ++v)
+        for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(u[v][k]));
+          for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(u[v][k]));
+      }
       m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
       if (m > 0.f && m < __builtin_inff()) {
         sh = rescue_shift(m, eps);
         float c0 = 0.f, c1 = 0.f;
+        reload_point();
 #pragma unroll
-        for (int v = 0; v < V; ++v)
+        for (int v = 0; v < V; ++v) {
+          float t[8];
+          if constexpr (kKeepU) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) t[k] = u[v][k];
+          } else {
+            lerp(v, t);
+          }
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            float lo = ldexpf(u[v][2 * k], sh), hi = ldexpf(u[v][2 * k + 1], sh);
+            const float lo = ldexpf(t[2 * k], sh), hi = ldexpf(t[2 * k + 1], sh);
             c0 = __builtin_fmaf(lo, lo, c0);
             c1 = __builtin_fmaf(hi, hi, c1);
           }
-        float t[1] = {wave_sum(c0 + c1)};
-        group_sum<G, 1>(t, gs.next(slot), geo.g, geo.lane);
-        T = t[0] + ldexpf(eps, 2 * sh);
+        }
+        float tt[1] = {wave_sum(c0 + c1)};
+        group_sum<G, 1>(tt, gs.next(slot), geo.g, geo.lane);
+        T = tt[0] + ldexpf(eps, 2 * sh);
         scaled = true;
       }
     }
     const float inv = 1.0f / sqrtf(T);
     const RowBuf hb(h + row * nvec, row_bytes);
+    reload_point();
 #pragma unroll
     for (int v = 0; v < V; ++v) {
+      float t[8];
+      if constexpr (kKeepU) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t[k] = u[v][k];
+      } else {
+        lerp(v, t);
+      }
       uint32_t q[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float lo = u[v][2 * k], hi = u[v][2 * k + 1];
+        float lo = t[2 * k], hi = t[2 * k + 1];
         if (scaled) { lo = ldexpf(lo, sh); hi = ldexpf(hi, sh); }
         q[k] = pack_bf16(lo * inv, hi * inv);
       }
-      u32x4_t t = {q[0], q[1], q[2], q[3]};
-      hb.st16(t, off[v]);
+      u32x4_t w = {q[0], q[1], q[2], q[3]};
+      hb.st16(w, off[v]);
     }
   }
 }
