@@ -75,7 +75,9 @@ enum {
   DS_ERR_ALLOC = -5,   /* the descriptor staging area could not be allocated */
   DS_ERR_LAUNCH = -6,  /* the HIP runtime reported an error for the launch,
                           the copy or the stream */
-  DS_ERR_DEVICE = -7   /* no usable HIP device */
+  DS_ERR_DEVICE = -7,  /* no usable HIP device */
+  DS_ERR_CAPTURE = -8  /* ds_weight_rownorm_gain on a capturing stream with more
+                          than 48 matrices of one width (see that function) */
 };
 
 /*
@@ -153,10 +155,13 @@ typedef struct ds_rownorm_desc {
  * n      : >= 0; 0 enqueues nothing.
  * stream : the hipStream_t to launch on.
  *
- * The library stages a small device table of the descriptors through a
- * library-owned pinned buffer, which it keeps until the stream has consumed
- * it (an event recorded behind the launches); a slot whose copy or launch
- * fails is returned at once.  DS_ERR_ALLOC if that buffer cannot be made.
+ * Matrices are grouped by row width; a group of at most 48 matrices travels
+ * inside the kernel arguments (no copy, no allocation; such calls may be
+ * captured into a HIP graph).  A larger group's descriptors are staged in a
+ * device table through a library-owned pinned buffer, kept until the stream
+ * has consumed it (an event recorded behind the launches); a slot whose copy
+ * fails is returned at once.  DS_ERR_ALLOC if that buffer cannot be made;
+ * DS_ERR_CAPTURE if it would be needed while the stream is capturing.
  */
 int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n,
                            ds_stream_t stream);

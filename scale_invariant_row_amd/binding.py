@@ -28,6 +28,7 @@ DS_ERR_ARG = -4
 DS_ERR_ALLOC = -5
 DS_ERR_LAUNCH = -6
 DS_ERR_DEVICE = -7
+DS_ERR_CAPTURE = -8
 
 
 class RownormDesc(ctypes.Structure):

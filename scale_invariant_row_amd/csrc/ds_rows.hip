@@ -190,6 +190,7 @@ const char* ds_status_string(int status) {
     case DS_ERR_ALLOC: return "DS_ERR_ALLOC: could not allocate the descriptor staging buffer";
     case DS_ERR_LAUNCH: return "DS_ERR_LAUNCH: the HIP runtime reported an error";
     case DS_ERR_DEVICE: return "DS_ERR_DEVICE: no usable HIP device";
+    case DS_ERR_CAPTURE: return "DS_ERR_CAPTURE: a ragged call with more than 48 matrices of one width cannot be captured into a graph";
     default: return "unknown ds_rows status";
   }
 }
@@ -313,37 +314,79 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     launches.push_back(L);
   }
 
-  // 3. stage the table (tasks, then each task's first item as a compact int32
-  //    array for the kernels' lookup), launch one kernel per shape class
+  // 3. launch one kernel per shape class.  A class of at most kInlineTasks
+  //    matrices carries its table inside the kernel arguments; larger classes
+  //    share one table (tasks, then their first items as a compact int32
+  //    array) staged through the ring and copied on the stream first.
   int cus = 0;
   int st = device_cus(&cus);
   if (st != DS_OK) return st;
-  Ring* ring = ring_for_current_device();
-  if (ring == nullptr) return DS_ERR_DEVICE;
-  const size_t task_bytes = table.size() * sizeof(dsr::RownormTask);
-  const size_t bytes = task_bytes + table.size() * sizeof(int32_t);
-  int slot = -1;
-  if ((st = acquire(*ring, bytes, &slot)) != DS_OK) return st;
-  Slot& sl = ring->slot[slot];
-  std::memcpy(sl.host, table.data(), task_bytes);
-  int32_t* begins_host = reinterpret_cast<int32_t*>(static_cast<char*>(sl.host) + task_bytes);
-  for (size_t i = 0; i < table.size(); ++i) begins_host[i] = table[i].item_begin;
   hipStream_t hs = (hipStream_t)stream;
+  size_t staged_tasks = 0;
+  for (const Launch& L : launches)
+    if (L.ntasks > dsr::kInlineTasks) staged_tasks += (size_t)L.ntasks;
+
+  if (staged_tasks > 0) {
+    // a staged table is copied from a reusable host slot: a graph replay
+    // would copy whatever that slot holds by then
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return DS_ERR_LAUNCH;
+    if (cap != hipStreamCaptureStatusNone) return DS_ERR_CAPTURE;
+  }
+  Ring* ring = nullptr;
+  int slot = -1;
+  const dsr::RownormTask* dev_tasks = nullptr;
+  const int32_t* dev_begins = nullptr;
   (void)hipGetLastError();
-  if (hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
-    release(*ring, slot, false, hs);          // nothing enqueued: refund the slot
-    return DS_ERR_LAUNCH;
+  if (staged_tasks > 0) {
+    ring = ring_for_current_device();
+    if (ring == nullptr) return DS_ERR_DEVICE;
+    const size_t task_bytes = staged_tasks * sizeof(dsr::RownormTask);
+    const size_t bytes = task_bytes + staged_tasks * sizeof(int32_t);
+    if ((st = acquire(*ring, bytes, &slot)) != DS_OK) return st;
+    Slot& sl = ring->slot[slot];
+    auto* host_tasks = static_cast<dsr::RownormTask*>(sl.host);
+    auto* host_begins = reinterpret_cast<int32_t*>(static_cast<char*>(sl.host) + task_bytes);
+    size_t k = 0;
+    for (const Launch& L : launches) {
+      if (L.ntasks <= dsr::kInlineTasks) continue;
+      for (int i = 0; i < L.ntasks; ++i, ++k) {
+        host_tasks[k] = table[L.first + i];
+        host_begins[k] = table[L.first + i].item_begin;
+      }
+    }
+    if (hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
+      release(*ring, slot, false, hs);        // nothing enqueued: refund the slot
+      return DS_ERR_LAUNCH;
+    }
+    dev_tasks = static_cast<const dsr::RownormTask*>(sl.dev);
+    dev_begins = reinterpret_cast<const int32_t*>(static_cast<const char*>(sl.dev) + task_bytes);
   }
-  const auto* dev_tasks = static_cast<const dsr::RownormTask*>(sl.dev);
-  const auto* dev_begins =
-      reinterpret_cast<const int32_t*>(static_cast<const char*>(sl.dev) + task_bytes);
+
   int result = DS_OK;
+  size_t staged_at = 0;
   for (const Launch& L : launches) {
-    hipError_t e = dsr::launch_rownorm(L.s, dev_tasks + L.first, dev_begins + L.first, L.ntasks,
-                                       L.nitems, grid_for(L.nitems, cus), hs);
-    if (e != hipSuccess) { result = DS_ERR_LAUNCH; break; }
+    dsr::RownormArgs args{};
+    args.ntasks = L.ntasks;
+    args.nitems = L.nitems;
+    if (L.ntasks <= dsr::kInlineTasks) {
+      args.tasks = nullptr;
+      args.begins = nullptr;
+      for (int i = 0; i < L.ntasks; ++i) {
+        args.inline_tasks[i] = table[L.first + i];
+        args.inline_begins[i] = table[L.first + i].item_begin;
+      }
+    } else {
+      args.tasks = dev_tasks + staged_at;
+      args.begins = dev_begins + staged_at;
+      staged_at += (size_t)L.ntasks;
+    }
+    if (dsr::launch_rownorm(L.s, args, grid_for(L.nitems, cus), hs) != hipSuccess) {
+      result = DS_ERR_LAUNCH;
+      break;
+    }
   }
-  release(*ring, slot, true, hs);             // the copy is in flight either way
+  if (ring != nullptr) release(*ring, slot, true, hs);   // the copy is in flight either way
   return result;
 }
 

@@ -92,18 +92,16 @@ hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const fl
 '''
     rn = HEAD.format(what="weight rownorm+gain") + '''
 template <int G, int V>
-static hipError_t run(const RownormTask* tasks, const int32_t* begins, int ntasks, int nitems,
-                      int grid, hipStream_t stream) {
+static hipError_t run(const RownormArgs& args, int grid, hipStream_t stream) {
   constexpr int T = Geo<G>::THREADS;
-  rownorm_kernel<G, V><<<grid, T, 0, stream>>>(tasks, begins, ntasks, nitems);
+  rownorm_kernel<G, V><<<grid, T, 0, stream>>>(args);
   return hipGetLastError();
 }
 
-hipError_t launch_rownorm(Shape s, const RownormTask* tasks, const int32_t* begins, int ntasks,
-                          int nitems, int grid, hipStream_t stream) {
+hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_t stream) {
   switch (s.G * 100 + s.V) {
 ''' + cases(shapes(vrn, min(vwide, rn_wide)),
-            "return run<{G}, {V}>(tasks, begins, ntasks, nitems, grid, stream);") + '''
+            "return run<{G}, {V}>(args, grid, stream);") + '''
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,7 +6,7 @@
 
 namespace dsr {
 
-struct RownormTask;
+struct RownormArgs;
 
 // Kernel shape: G waves per row, V 16-byte vectors per lane.
 struct Shape {
@@ -41,7 +41,6 @@ hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_
 hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const float* alpha,
                              void* h, int64_t rows, int nvec, float eps, int grid,
                              hipStream_t stream);
-hipError_t launch_rownorm(Shape s, const RownormTask* tasks, const int32_t* begins, int ntasks,
-                          int nitems, int grid, hipStream_t stream);
+hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_t stream);
 
 }  // namespace dsr

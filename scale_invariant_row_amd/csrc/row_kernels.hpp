@@ -549,14 +549,29 @@ struct RownormTask {
   int32_t pad_;
 };
 
+// The tasks of one launch.  Up to kInlineTasks of them travel inside the
+// kernel arguments (no copy, no device allocation, safe to capture in a
+// graph); larger batches point at a table staged in device memory.
+constexpr int kInlineTasks = 48;
+struct RownormArgs {
+  const RownormTask* tasks;      // staged table, or null: use the inline arrays
+  const int32_t* begins;         // staged item_begin array (with `tasks`)
+  int32_t ntasks;
+  int32_t nitems;
+  int32_t inline_begins[kInlineTasks];
+  RownormTask inline_tasks[kInlineTasks];
+};
+static_assert(sizeof(RownormArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
 // Index of the task owning `item`: the number of tasks whose first item is
-// <= item, minus one.  `begins` holds the tasks' item_begin in ascending
-// order; each lane tests one task and a ballot counts them, 64 per load.
-__device__ __forceinline__ int owning_task(const int32_t* begins, int ntasks, int item, int lane) {
+// <= item, minus one.  Tasks are in ascending item_begin order; each lane
+// tests one task and a ballot counts them, 64 per pass.
+__device__ __forceinline__ int owning_task(const RownormArgs& a, int item, int lane) {
+  const int32_t* begins = a.tasks != nullptr ? a.begins : a.inline_begins;
   int count = 0;
-  for (int base = 0; base < ntasks; base += 64) {
+  for (int base = 0; base < a.ntasks; base += 64) {
     const int k = base + lane;
-    const int b = (k < ntasks) ? begins[k] : 0x7fffffff;
+    const int b = (k < a.ntasks) ? begins[k] : 0x7fffffff;
     const int c = __popcll(__ballot(b <= item));
     count += c;
     if (c < 64) break;                        // uniform: the ballot is the same in every lane
@@ -566,19 +581,23 @@ __device__ __forceinline__ int owning_task(const int32_t* begins, int ntasks, in
 
 template <int G, int V>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
-rownorm_kernel(const RownormTask* tasks, const int32_t* begins, int ntasks, int nitems) {
+rownorm_kernel(const RownormArgs args) {
   constexpr int R = Geo<G>::R;
   const Geo<G> geo;
   __shared__ GroupScratch<G> gs;
   int slot = 0;
   int off[V];
   geo.offsets(off, 16);
+  const int nitems = args.nitems;
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int lo = __builtin_amdgcn_readfirstlane(owning_task(begins, ntasks, item, geo.lane));
-    const RownormTask t = tasks[lo];
+    const int lo = __builtin_amdgcn_readfirstlane(owning_task(args, item, geo.lane));
+    const RownormTask t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
     const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
     if (G == 1 && row >= t.rows) continue;          // independent waves only
+    // the gain is read with the row, ahead of any store (a later read could
+    // not move above the norm store, and would add a memory round trip)
+    const float gr = t.gain[row] * t.radius;
     const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
     float w[V][4];
 #pragma unroll
@@ -627,7 +646,6 @@ rownorm_kernel(const RownormTask* tasks, const int32_t* begins, int ntasks, int 
     const float rn = sqrtf(T);                       // length (of the scaled row)
     if (t.norm_out != nullptr && geo.g == 0 && geo.lane == 0)
       t.norm_out[row] = scaled ? ldexpf(rn, -sh) : rn;
-    const float gr = t.gain[row] * t.radius;
     const float c = (rn == 0.f) ? 0.f : gr / rn;
     const RowBuf eb(t.w_eff + row * t.cols, (uint32_t)t.cols * 2u);
 #pragma unroll

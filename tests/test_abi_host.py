@@ -35,7 +35,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_strings(L):
     assert B.ds_version() == 10000
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
     assert "unknown" in B.ds_status_string(42)

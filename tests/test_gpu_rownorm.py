@@ -117,3 +117,17 @@ def test_zero_tiny_huge_and_nonfinite_rows(B):
     g4, r4 = bf16_value(we[0][4]), bf16_value(w_ref[0][4])
     assert np.array_equal(np.isnan(g4), np.isnan(r4)) and np.isinf(n[0][4])
     assert np.isnan(bf16_value(we[0][5])).all() and np.isnan(n[0][5])
+
+
+def test_staged_table_many_matrices(B):
+    """More than 48 matrices of one width go through the staged device table."""
+    shapes = [(17 + i % 5, 768) for i in range(60)] + [(9, 256)] * 5
+    case = inputs.rownorm_case(shapes, 813)
+    announce("rownorm staged table", len(shapes))
+    n, w = run(B, case)
+    for i, (wm, gm) in enumerate(zip(case.w, case.gain)):
+        check_matrix(n[i], w[i], wm, gm, 1.0, np.arange(wm.shape[0]), f"staged {i}")
+    for i in (0, 31, 59, 62):
+        one = inputs.RownormCase("one", [case.w[i]], [case.gain[i]], [1.0])
+        n1, w1 = run(B, one)
+        assert np.array_equal(n1[0], n[i]) and np.array_equal(w1[0], w[i])
