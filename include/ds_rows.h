@@ -23,9 +23,12 @@
  * Numerics.  bf16 values are passed as their 16-bit patterns; every rounding
  * to bf16 is to nearest, ties to even.  Sums of squares accumulate in fp32
  * (the DragonScale README's eager reference: fp32 accumulation).  eps is
- * added to the sum of squares, as an fp32 value.  The inverse length is
- * 1 / sqrt(S + eps), each step correctly rounded in fp32, and each output is
- * one fp32 product rounded to bf16.  A row whose fp32 sum of squares would
+ * added to the sum of squares, as an fp32 value.  The inverse length
+ * 1 / sqrt(S + eps) of an activation row is computed to within 1.5 units of
+ * fp32 rounding (hardware estimate plus one Newton step); a weight row's
+ * length is a correctly rounded fp32 square root and its scale g * r / length
+ * a correctly rounded division.  Each output is one fp32 product rounded to
+ * bf16.  A row whose fp32 sum of squares would
  * overflow, or whose sum plus eps falls below 2^-96, is rescaled by a power
  * of two before summing, so every finite input row gives the float64 result
  * to within the stated rounding.  NaN and infinity propagate as in IEEE
