@@ -206,7 +206,7 @@ int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t rows, 
   const size_t bytes = (size_t)rows * (size_t)cols * 2;
   if (!same_or_disjoint(y, x, bytes) || !same_or_disjoint(y, r, bytes)) return DS_ERR_ARG;
 
-  const Shape s = dsr::pick_shape(cols / 8, dsr::kVmaxL2);
+  const Shape s = dsr::pick_bf16_shape(cols / 8);
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
@@ -229,7 +229,7 @@ int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha, 
   if (!same_or_disjoint(h, res, bytes) || !same_or_disjoint(h, out, bytes)) return DS_ERR_ARG;
   if (overlaps(h, bytes, alpha, (size_t)cols * 4)) return DS_ERR_ARG;
 
-  const Shape s = dsr::pick_shape(cols / 8, dsr::kVmaxSlerp);
+  const Shape s = dsr::pick_bf16_shape(cols / 8);
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
@@ -280,7 +280,7 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
   std::map<int, std::vector<int32_t>> classes;
   for (int32_t i = 0; i < n; ++i) {
     if (descs[i].rows == 0) continue;
-    Shape s = dsr::pick_shape(descs[i].cols / 4, dsr::kVmaxRownorm);
+    Shape s = dsr::pick_rownorm_shape(descs[i].cols / 4);
     if (!s.ok()) return DS_ERR_SHAPE;
     classes[s.G * 100 + s.V].push_back(i);
   }

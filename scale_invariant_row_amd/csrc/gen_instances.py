@@ -1,30 +1,51 @@
 """Writes inst_l2.hip, inst_slerp.hip and inst_rownorm.hip: one launcher per op
 with a case for every kernel shape (G waves per row, V vectors per lane) that
-launch.hpp's pick_shape() can return for that op's V limit.  Run it after a
-change of kVmaxL2 / kVmaxSlerp / kVmaxRownorm / kVmaxWide."""
+launch.hpp's shape policy returns for some width up to DS_MAX_COLS, found by
+evaluating the policy (reproduced below from launch.hpp's constants) at every
+width.  Run it after a change of the policy."""
 import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+MAX_COLS = 65536
 
 
 def limits():
     text = open(os.path.join(HERE, "launch.hpp")).read()
     get = lambda name: int(re.search(rf"{name}\s*=\s*(\d+)", text).group(1))
-    return get("kVmaxL2"), get("kVmaxSlerp"), get("kVmaxRownorm"), get("kVmaxWide")
+    return {k: get(k) for k in ("kBf16SmallVectors", "kVmaxBf16Small", "kVmaxBf16Large",
+                                "kVmaxRownorm", "kVmaxWide")}
 
 
-def shapes(vmax, wide):
-    """(G, V) pairs reachable for rows of up to DS_MAX_COLS columns."""
-    out = []
+def pick_shape(vectors, vmax, wide):
+    """launch.hpp's pick_shape, in Python."""
     for G in (1, 2, 4, 8, 16):
-        lo = 1 if G == 1 else vmax // 2 + 1
-        hi = vmax if G < 16 else max(vmax, wide)
-        out += [(G, V) for V in range(lo, hi + 1)]
-    return out
+        V = -(-vectors // (64 * G))
+        if V <= vmax or (G == 16 and V <= wide):
+            return G, V
+    return None
 
 
-HEAD = '''// {what}: one launcher over every kernel shape pick_shape() can return.
+def bf16_shape(vectors, lim):
+    vmax = lim["kVmaxBf16Small"] if vectors <= lim["kBf16SmallVectors"] else lim["kVmaxBf16Large"]
+    return pick_shape(vectors, vmax, lim["kVmaxWide"])
+
+
+def rownorm_shape(vectors, lim):
+    return pick_shape(vectors, lim["kVmaxRownorm"], lim["kVmaxWide"])
+
+
+def bf16_shapes(lim):
+    """Every shape the bf16 policy returns for rows up to MAX_COLS columns."""
+    return sorted({bf16_shape(n, lim) for n in range(1, MAX_COLS // 8 + 1)})
+
+
+def rownorm_shapes(lim):
+    """Every shape the fp32 weight policy returns for rows up to MAX_COLS columns."""
+    return sorted({rownorm_shape(n, lim) for n in range(1, MAX_COLS // 4 + 1)})
+
+
+HEAD = '''// {what}: one launcher over every kernel shape the shape policy can return.
 // Written by gen_instances.py.
 #include "row_kernels.hpp"
 #include "launch.hpp"
@@ -38,10 +59,9 @@ def cases(lst, call):
 
 
 def main():
-    vl2, vsl, vrn, vwide = limits()
-    # widest rows: 65536 bf16 = 8192 vectors (l2, slerp); 65536 fp32 = 16384 (rownorm)
-    l2_wide = -(-8192 // (64 * 16))
-    rn_wide = -(-16384 // (64 * 16))
+    lim = limits()
+    bf16 = bf16_shapes(lim)
+    rown = rownorm_shapes(lim)
     l2 = HEAD.format(what="l2_rows") + '''
 template <int G, int V>
 static hipError_t run(const void* x, const void* r, void* y, int64_t rows, int nvec, float eps,
@@ -59,8 +79,7 @@ static hipError_t run(const void* x, const void* r, void* y, int64_t rows, int n
 hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_t rows,
                           int nvec, float eps, int grid, hipStream_t stream) {
   switch (s.G * 100 + s.V) {
-''' + cases(shapes(vl2, min(vwide, l2_wide)),
-            "return run<{G}, {V}>(x, r, y, rows, nvec, eps, grid, stream);") + '''
+''' + cases(bf16, "return run<{G}, {V}>(x, r, y, rows, nvec, eps, grid, stream);") + '''
     default: return hipErrorInvalidValue;
   }
 }
@@ -82,8 +101,7 @@ hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const fl
                              void* h, int64_t rows, int nvec, float eps, int grid,
                              hipStream_t stream) {
   switch (s.G * 100 + s.V) {
-''' + cases(shapes(vsl, min(vwide, l2_wide)),
-            "return run<{G}, {V}>(res, out, alpha, h, rows, nvec, eps, grid, stream);") + '''
+''' + cases(bf16, "return run<{G}, {V}>(res, out, alpha, h, rows, nvec, eps, grid, stream);") + '''
     default: return hipErrorInvalidValue;
   }
 }
@@ -100,8 +118,7 @@ static hipError_t run(const RownormArgs& args, int grid, hipStream_t stream) {
 
 hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_t stream) {
   switch (s.G * 100 + s.V) {
-''' + cases(shapes(vrn, min(vwide, rn_wide)),
-            "return run<{G}, {V}>(args, grid, stream);") + '''
+''' + cases(rown, "return run<{G}, {V}>(args, grid, stream);") + '''
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,4 +1,4 @@
-// l2_rows: one launcher over every kernel shape pick_shape() can return.
+// l2_rows: one launcher over every kernel shape the shape policy can return.
 // Written by gen_instances.py.
 #include "row_kernels.hpp"
 #include "launch.hpp"
@@ -25,8 +25,10 @@ hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_
     case 102: return run<1, 2>(x, r, y, rows, nvec, eps, grid, stream);
     case 202: return run<2, 2>(x, r, y, rows, nvec, eps, grid, stream);
     case 402: return run<4, 2>(x, r, y, rows, nvec, eps, grid, stream);
-    case 802: return run<8, 2>(x, r, y, rows, nvec, eps, grid, stream);
-    case 1602: return run<16, 2>(x, r, y, rows, nvec, eps, grid, stream);
+    case 403: return run<4, 3>(x, r, y, rows, nvec, eps, grid, stream);
+    case 404: return run<4, 4>(x, r, y, rows, nvec, eps, grid, stream);
+    case 803: return run<8, 3>(x, r, y, rows, nvec, eps, grid, stream);
+    case 804: return run<8, 4>(x, r, y, rows, nvec, eps, grid, stream);
     case 1603: return run<16, 3>(x, r, y, rows, nvec, eps, grid, stream);
     case 1604: return run<16, 4>(x, r, y, rows, nvec, eps, grid, stream);
     case 1605: return run<16, 5>(x, r, y, rows, nvec, eps, grid, stream);

@@ -1,4 +1,4 @@
-// weight rownorm+gain: one launcher over every kernel shape pick_shape() can return.
+// weight rownorm+gain: one launcher over every kernel shape the shape policy can return.
 // Written by gen_instances.py.
 #include "row_kernels.hpp"
 #include "launch.hpp"

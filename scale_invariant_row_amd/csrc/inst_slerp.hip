@@ -1,4 +1,4 @@
-// slerp_rows: one launcher over every kernel shape pick_shape() can return.
+// slerp_rows: one launcher over every kernel shape the shape policy can return.
 // Written by gen_instances.py.
 #include "row_kernels.hpp"
 #include "launch.hpp"
@@ -23,8 +23,10 @@ hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const fl
     case 102: return run<1, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 202: return run<2, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 402: return run<4, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 802: return run<8, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
-    case 1602: return run<16, 2>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 403: return run<4, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 404: return run<4, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 803: return run<8, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
+    case 804: return run<8, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 1603: return run<16, 3>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 1604: return run<16, 4>(res, out, alpha, h, rows, nvec, eps, grid, stream);
     case 1605: return run<16, 5>(res, out, alpha, h, rows, nvec, eps, grid, stream);

@@ -17,17 +17,21 @@ struct Shape {
   bool ok() const { return G > 0; }
 };
 
-// Largest V per lane for each op (registers hold the whole row): the shape is
-// the smallest G in {1, 2, 4, 8, 16} whose V = ceil(vectors / (64 G)) fits.
-// Measured on MI355X: rows spread over more, lighter waves (V <= 2) stream
-// best for bf16 rows from 1,024 to 8,192 wide; only rows wider than 16,384
-// fall back to G = 16 with up to 8 vectors per lane.
-constexpr int kVmaxL2 = 2;
-constexpr int kVmaxSlerp = 2;
+// Shape policy, measured on MI355X.  A row is spread over the smallest wave
+// group G in {1, 2, 4, 8, 16} whose V = ceil(vectors / (64 G)) fits a limit:
+//   bf16 rows (l2_rows, slerp_rows): V <= 2 up to 512 vectors (4,096
+//     columns), V <= 4 beyond -- more, lighter waves stream best at these
+//     widths, and slerp's per-row work favours V = 4 once rows are wider;
+//   fp32 weight rows: V <= 6;
+//   G = 16 may take V up to 16 (rows up to DS_MAX_COLS).
+// The shape is a function of the width alone.  gen_instances.py evaluates
+// these same rules over every width to list the kernels to instantiate.
+constexpr int kBf16SmallVectors = 512;
+constexpr int kVmaxBf16Small = 2;
+constexpr int kVmaxBf16Large = 4;
 constexpr int kVmaxRownorm = 6;
-constexpr int kVmaxWide = 16;     // G = 16 may go up to here (DS_MAX_COLS fp32 rows)
+constexpr int kVmaxWide = 16;
 
-// Shape for a row of `vectors` 16-byte vectors; a function of the width only.
 inline Shape pick_shape(int64_t vectors, int vmax) {
   for (int G = 1; G <= 16; G *= 2) {
     int64_t V = (vectors + 64 * G - 1) / (64 * G);
@@ -35,6 +39,14 @@ inline Shape pick_shape(int64_t vectors, int vmax) {
   }
   return Shape{};
 }
+
+// bf16 rows of `vectors` 16-byte vectors (8 columns each)
+inline Shape pick_bf16_shape(int64_t vectors) {
+  return pick_shape(vectors, vectors <= kBf16SmallVectors ? kVmaxBf16Small : kVmaxBf16Large);
+}
+
+// fp32 weight rows of `vectors` 16-byte vectors (4 columns each)
+inline Shape pick_rownorm_shape(int64_t vectors) { return pick_shape(vectors, kVmaxRownorm); }
 
 hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_t rows,
                           int nvec, float eps, int grid, hipStream_t stream);

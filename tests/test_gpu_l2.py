@@ -41,7 +41,10 @@ def full_check(got, x, r, eps, label):
     assert rep.ok, f"{label}: {rep}"
 
 
-COLS = [8, 64, 520, 1024, 2048, 4096, 4104, 7168, 8192, 12296, 65528, 65536]
+# every side of the shape policy's class boundaries (64, 128, 256, 512, 1024,
+# 2048 and 4096 vectors of 8 columns), the widths of the pages, and the limit
+COLS = [8, 64, 512, 520, 1024, 1032, 2048, 2056, 4096, 4104, 7168, 8192, 8200, 12296,
+        16384, 16392, 32768, 32776, 65528, 65536]
 
 
 @pytest.mark.parametrize("cols", COLS)

@@ -43,7 +43,8 @@ def full_check(got, res, out, alpha, eps, label):
     assert rep.ok, f"{label}: {rep}"
 
 
-@pytest.mark.parametrize("cols", [8, 64, 1024, 2056, 4096, 7168, 8192, 16392, 65536])
+@pytest.mark.parametrize("cols", [8, 64, 520, 1024, 1032, 2056, 4096, 4104, 7168, 8192, 8200,
+                                  16392, 32776, 65536])
 def test_small_shapes(B, cols):
     rows = 29 if cols <= 8192 else 4
     c = inputs.slerp_case(rows, cols, 700 + cols % 89)

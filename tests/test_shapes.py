@@ -1,0 +1,55 @@
+"""The generated kernel launchers cover every shape the policy can return.
+
+The shape (G waves per row, V vectors per lane) is chosen from the row width
+alone, so each row's reduction tree -- and its bits -- never depends on the
+row count.  A width whose shape had no kernel would fail at launch; this
+checks the generated launch switches against the policy at every width.
+"""
+import os
+import re
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                    "scale_invariant_row_amd", "csrc")
+sys.path.insert(0, CSRC)
+import gen_instances as gen  # noqa: E402
+
+
+def cases(name):
+    text = open(os.path.join(CSRC, name)).read()
+    return {(int(c) // 100, int(c) % 100) for c in re.findall(r"case (\d+):", text)}
+
+
+def test_bf16_launchers_cover_policy():
+    lim = gen.limits()
+    need = {gen.bf16_shape(n, lim) for n in range(1, 65536 // 8 + 1)}
+    assert None not in need
+    assert need <= cases("inst_l2.hip")
+    assert need <= cases("inst_slerp.hip")
+
+
+def test_rownorm_launcher_covers_policy():
+    lim = gen.limits()
+    need = {gen.rownorm_shape(n, lim) for n in range(1, 65536 // 4 + 1)}
+    assert None not in need
+    assert need <= cases("inst_rownorm.hip")
+
+
+def test_policy_is_measured_choice():
+    """The widths of the workloads map to the shapes measured fastest."""
+    lim = gen.limits()
+    assert gen.bf16_shape(1024 // 8, lim) == (1, 2)
+    assert gen.bf16_shape(4096 // 8, lim) == (4, 2)
+    assert gen.bf16_shape(7168 // 8, lim) == (4, 4)
+    assert gen.bf16_shape(8192 // 8, lim) == (4, 4)
+    assert gen.rownorm_shape(768 // 4, lim) == (1, 3)
+    assert gen.rownorm_shape(3072 // 4, lim) == (2, 6)
+
+
+def test_reduction_depth_bound():
+    """Deepest sum path (two fma chains, wave tree, group sum) stays <= 64."""
+    lim = gen.limits()
+    for G, V in gen.bf16_shapes(lim):
+        assert 4 * V + 1 + 6 + (G - 1) <= 64
+    for G, V in gen.rownorm_shapes(lim):
+        assert 2 * V + 1 + 6 + (G - 1) <= 64
