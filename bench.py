@@ -236,6 +236,36 @@ def main():
     ops["torch_copy_same_bytes"] = op(cp_us, 2 * src.numel(), ROWS)
     del srcs, dsts, src
 
+    # ---- the other workloads' shapes, beside the headline (random bf16 rows of
+    # the same shapes; one buffer set rotation each): reported, not in `value`
+    def shaped_us(rows, cols, fn, nsets, n=40):
+        bufs = [[torch.randn(rows, cols, device=dev).to(torch.bfloat16) for _ in range(3)]
+                for _ in range(nsets)]
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert fn(bufs[i % nsets], rows, cols) == 0
+        a, b = ev(), ev()
+        a.record(stream)
+        for i in range(n):
+            fn(bufs[i % nsets], rows, cols)
+        b.record(stream)
+        torch.cuda.synchronize()
+        del bufs
+        torch.cuda.empty_cache()
+        return a.elapsed_time(b) * 1e3 / n
+
+    alpha7 = (torch.rand(7168, device=dev) - 0.5) * 0.4
+    c1_us = shaped_us(64, 1024, lambda t, r, c: L.ds_l2_rows(
+        t[0].data_ptr(), None, t[2].data_ptr(), r, c, eps, sp), 4, n=200)
+    c3_us = shaped_us(8192, 7168, lambda t, r, c: L.ds_slerp_rows(
+        t[0].data_ptr(), t[1].data_ptr(), alpha7.data_ptr(), t[2].data_ptr(), r, c, eps, sp), 4)
+    c5_us = shaped_us(32768, 8192, lambda t, r, c: L.ds_l2_rows(
+        t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), r, c, eps, sp), 2, n=20)
+    ops["l2_rows_64x1024"] = op(c1_us, 64 * 1024 * 4, 64)
+    ops["l2_rows_64x1024"]["note"] = "latency-bound: one small launch"
+    ops["slerp_rows_8192x7168"] = op(c3_us, 8192 * 7168 * 6 + 7168 * 4, 8192)
+    ops["l2_rows_res_32768x8192"] = op(c5_us, 32768 * 8192 * 6, 32768)
+
     dominant = "slerp_rows_8192x4096" if sl_us >= l2_us else "l2_rows_res_8192x4096"
     kname = {"slerp_rows_8192x4096": "slerp_rows_kernel",
              "l2_rows_res_8192x4096": "l2_rows_kernel"}[dominant]

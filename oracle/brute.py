@@ -20,7 +20,8 @@ from fractions import Fraction
 from typing import List, Optional, Sequence, Tuple
 
 __all__ = ["bits_to_fraction", "round_fraction", "bf16_of", "fp32_of",
-           "l2_row", "slerp_row", "rownorm_row", "NEAR_TIE_REL"]
+           "l2_row", "slerp_row", "rownorm_row", "l2_backward_row", "rownorm_backward_row",
+           "NEAR_TIE_REL"]
 
 PREC = 60
 NEAR_TIE_REL = Fraction(1, 10 ** 12)     # flag values this close to a midpoint
@@ -162,3 +163,71 @@ def rownorm_row(w: Sequence[float], g: float, rho: float
             out.append(r)
             near = near or n
     return n32, out, near
+
+
+# The float64 oracle forms each gradient element as a difference of two terms
+# that may cancel; its error is then a few float64 units of the terms, not of
+# the result.  An element is flagged when rounding cannot be decided within
+# SLACK_REL times the size of those terms.
+SLACK_REL = Fraction(1, 2 ** 48)
+
+
+def _round_with_slack(v: Fraction, slack: Fraction, fmt) -> Tuple[Fraction, bool]:
+    r, near = fmt(v)
+    if slack > 0 and (fmt(v - slack)[0] != r or fmt(v + slack)[0] != r):
+        near = True
+    return r, near
+
+
+def l2_backward_row(x_bits: Sequence[int], r_bits: Optional[Sequence[int]],
+                    dy_bits: Sequence[int], eps32: float) -> Tuple[List[Fraction], List[bool]]:
+    """One row of the l2_rows gradient, exactly: bf16((dy - s <s, dy> / D^2) / D)."""
+    x = [bits_to_fraction(int(b)) for b in x_bits]
+    if r_bits is not None:
+        s = [bf16_of(xj + bits_to_fraction(int(rb)))[0] for xj, rb in zip(x, r_bits)]
+    else:
+        s = x
+    dy = [bits_to_fraction(int(b)) for b in dy_bits]
+    eps = f32_to_fraction(eps32)
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        d2 = sum((v * v for v in s), Fraction(0)) + eps
+        p = sum((a * b for a, b in zip(s, dy)), Fraction(0))
+        pa = sum((abs(a * b) for a, b in zip(s, dy)), Fraction(0))
+        root = _dec(d2).sqrt()
+        out, near = [], []
+        for sj, gj in zip(s, dy):
+            num = gj - sj * p / d2                  # exact
+            terms = abs(gj) + abs(sj) * pa / d2
+            v, n = _round_with_slack(Fraction(_dec(num) / root),
+                                     SLACK_REL * Fraction(_dec(terms) / root), bf16_of)
+            out.append(v)
+            near.append(n)
+    return out, near
+
+
+def rownorm_backward_row(w: Sequence[float], g: float, rho: float, dwe_bits: Sequence[int]
+                         ) -> Tuple[List[Fraction], Fraction, List[bool], bool]:
+    """One weight row's gradients exactly: fp32(dW) with per-element flags, fp32(dg), flag."""
+    wf = [f32_to_fraction(float(x)) for x in w]
+    de = [bits_to_fraction(int(b)) for b in dwe_bits]
+    grho = f32_to_fraction(g) * f32_to_fraction(rho)
+    rho_f = f32_to_fraction(rho)
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        ss = sum((v * v for v in wf), Fraction(0))
+        if ss == 0:
+            return [Fraction(0)] * len(wf), Fraction(0), [False] * len(wf), False
+        p = sum((a * b for a, b in zip(wf, de)), Fraction(0))
+        pa = sum((abs(a * b) for a, b in zip(wf, de)), Fraction(0))
+        root = _dec(ss).sqrt()
+        dg, near_g = fp32_of(Fraction(_dec(rho_f * p) / root))
+        out, near = [], []
+        for wj, ej in zip(wf, de):
+            num = grho * (ej - wj * p / ss)          # exact
+            terms = abs(grho) * (abs(ej) + abs(wj) * pa / ss)
+            v, n = _round_with_slack(Fraction(_dec(num) / root),
+                                     SLACK_REL * Fraction(_dec(terms) / root), fp32_of)
+            out.append(v)
+            near.append(n)
+    return out, dg, near, near_g

@@ -38,7 +38,8 @@ import numpy as np
 from .bf16 import bf16_rne, bf16_value
 
 __all__ = ["eps_as_passed", "l2_rows", "slerp_rows", "slerp_rows_detail",
-           "weight_rownorm_gain", "sum_sq"]
+           "weight_rownorm_gain", "sum_sq", "l2_backward_values", "l2_rows_backward",
+           "rownorm_backward_values", "weight_rownorm_gain_backward"]
 
 
 def eps_as_passed(eps: float) -> float:
@@ -146,3 +147,72 @@ def weight_rownorm_gain(w: Sequence[np.ndarray], gain: Sequence[np.ndarray],
         norms.append(n.astype(np.float32))
         weffs.append(bf16_rne(weff))
     return norms, weffs
+
+
+# ------------------------------------------------------------------ backward
+#
+# Readings: the gradient is that of the unrounded forward function at the
+# forward's inputs; a rounding to bf16 passes the gradient through unchanged
+# (so x and r of l2_rows receive the same gradient ds).  A zero weight row,
+# which the forward scales by 0, receives zero gradients.
+
+def l2_backward_values(s: np.ndarray, dy: np.ndarray, eps64: float) -> np.ndarray:
+    """ds = (dy - yhat <yhat, dy>) / D per row, yhat = s / D, D = sqrt(sum s^2 + eps).
+
+    The Jacobian of s -> s / D is (I - yhat yhat^T) / D, applied to dy.
+    Products of two bf16 values are exact in float64, so the sums are the
+    correctly rounded float64 sums of the exact products.
+    """
+    out = np.empty_like(s)
+    with np.errstate(all="ignore"):
+        for i in range(s.shape[0]):
+            d2 = sum_sq(s[i]) + eps64
+            p = math.fsum(s[i] * dy[i])
+            out[i] = (dy[i] - s[i] * (p / d2)) / math.sqrt(d2)
+    return out
+
+
+def l2_rows_backward(x_bits: np.ndarray, r_bits: Optional[np.ndarray], dy_bits: np.ndarray,
+                     eps: float = 1e-6) -> np.ndarray:
+    """bf16 bits of ds, the gradient of l2_rows with respect to s (and to x, r)."""
+    x = bf16_value(np.atleast_2d(x_bits))
+    if r_bits is not None:
+        with np.errstate(all="ignore"):
+            s = bf16_value(bf16_rne(x + bf16_value(np.atleast_2d(r_bits))))
+    else:
+        s = x
+    dy = bf16_value(np.atleast_2d(dy_bits))
+    return bf16_rne(l2_backward_values(s, dy, eps_as_passed(eps))).reshape(np.shape(x_bits))
+
+
+def rownorm_backward_values(w64: np.ndarray, g64: np.ndarray, rho64: float, dwe: np.ndarray):
+    """Per row: dW = (g rho / n) (dWe - w <w, dWe> / n^2), dg = rho <w, dWe> / n.
+
+    DragonScale README, "What DragonScale changes": the gradient reaching W is
+    (g r / ||W||) (I - w_hat w_hat^T) dL/dW_eff, tangent to the row; dg follows
+    from W_eff = g r w_hat by the chain rule.  n = 0 gives zeros.
+    """
+    dw = np.zeros_like(w64)
+    dg = np.zeros(w64.shape[0])
+    with np.errstate(all="ignore"):
+        for i in range(w64.shape[0]):
+            ss = sum_sq(w64[i])
+            n = math.sqrt(ss)
+            if n == 0.0:
+                continue
+            p = math.fsum(w64[i] * dwe[i])
+            dg[i] = rho64 * p / n
+            dw[i] = (g64[i] * rho64 / n) * (dwe[i] - w64[i] * (p / ss))
+    return dw, dg
+
+
+def weight_rownorm_gain_backward(w: Sequence[np.ndarray], gain: Sequence[np.ndarray],
+                                 radius: Sequence[float], dweff_bits: Sequence[np.ndarray]):
+    """Per matrix: (dW fp32, dg fp32) from bf16 dL/dW_eff; the float64 values rounded once."""
+    dws, dgs = [], []
+    for wm, gm, rho, de in zip(w, gain, radius, dweff_bits):
+        dw, dg = rownorm_backward_values(np.asarray(wm, np.float64), np.asarray(gm, np.float64),
+                                         float(np.float32(rho)), bf16_value(de))
+        dws.append(dw.astype(np.float32))
+        dgs.append(dg.astype(np.float32))
+    return dws, dgs

@@ -1,4 +1,4 @@
-"""Reader for tests/golden/closed_forms.json: builds input rows and expected rows."""
+"""Reader for the fixtures in tests/golden/: builds input rows and expected rows."""
 import json
 import os
 
@@ -7,8 +7,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def load():
-    with open(os.path.join(HERE, "golden", "closed_forms.json")) as f:
+def load(name="closed_forms.json"):
+    with open(os.path.join(HERE, "golden", name)) as f:
         return json.load(f)["cases"]
 
 
