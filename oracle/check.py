@@ -47,7 +47,9 @@ F64_WIDEN = 2.0 ** -46     # covers float64 rounding inside the bound arithmetic
 
 __all__ = ["contract_bf16", "contract_rel", "Report", "admissible_l2_rows",
            "admissible_slerp_rows", "admissible_rownorm", "default_depth",
-           "ordered", "slerp_unique_mask"]
+           "ordered", "slerp_unique_mask", "GRAD_SLACK", "l2_grad_terms",
+           "rownorm_grad_terms", "contract_grad", "admissible_l2_backward",
+           "admissible_rownorm_backward"]
 
 
 def default_depth(cols: int) -> int:
@@ -100,6 +102,7 @@ class Report:
     outside: int = 0          # result not in its admissible set
     two: int = 0              # elements whose set has two values (near-ties)
     loose: int = 0            # sets wider than two values (bound too loose)
+    wide: int = 0             # gradient sets wider than two values (cancellation)
     first_bad: list = field(default_factory=list)
 
     @property
@@ -111,12 +114,13 @@ class Report:
         self.outside += other.outside
         self.two += other.two
         self.loose += other.loose
+        self.wide += other.wide
         self.first_bad = (self.first_bad + other.first_bad)[:20]
         return self
 
     def __str__(self) -> str:
         return (f"n={self.n} outside={self.outside} two={self.two} "
-                f"loose={self.loose} first_bad={self.first_bad[:5]}")
+                f"loose={self.loose} wide={self.wide} first_bad={self.first_bad[:5]}")
 
 
 def _sum_bounds(sq_lo: np.ndarray, sq_hi: np.ndarray, depth: int):
@@ -151,7 +155,7 @@ def _product_bounds(v_lo, v_hi, c_lo, c_hi):
 
 
 def _judge(got_bits, lo, hi, exact_bits, exact_mask, zero_any_sign,
-           base_index, report: Report):
+           base_index, report: Report, wide_ok: bool = False):
     """Compare one row: interval elements and exactly-determined elements."""
     lo_b = bf16_rne(lo)
     hi_b = bf16_rne(hi)
@@ -174,7 +178,10 @@ def _judge(got_bits, lo, hi, exact_bits, exact_mask, zero_any_sign,
     report.n += n
     report.outside += bad.size
     report.two += int((width == 2).sum())
-    report.loose += int((width > 2).sum())
+    if wide_ok:
+        report.wide += int((width > 2).sum())
+    else:
+        report.loose += int((width > 2).sum())
     for j in bad[: max(0, 20 - len(report.first_bad))]:
         report.first_bad.append(int(base_index + j))
 
@@ -368,3 +375,220 @@ def admissible_rownorm(got_norm, got_weff_bits, w, g, rho: float = 1.0,
         zero = row == 0
         _judge(got_w[i], lo, hi, np.zeros(cols, np.uint16), zero, True, base, rw)
     return rn, rw
+
+
+# ------------------------------------------------------------------ backward
+#
+# A gradient element is a difference of two terms (dy_j and s_j <s,dy>/D^2
+# for l2_rows; dWe_j and w_j <w,dWe>/||w||^2 for the weights) that may cancel,
+# so an fp32 run's error is a few fp32 units of the larger term, not of the
+# result.  The contract therefore allows, beyond the output format's own
+# rounding (one bf16 ulp, or 2e-6 relative for fp32), GRAD_SLACK times the
+# size of those terms: 2**-16 = 256 fp32 units, enough for fp32 sums whose
+# tree is up to ~250 additions deep (a kernel reducing a row of 65,536 columns
+# over 1,024 lanes needs about 100).
+
+GRAD_SLACK = 2.0 ** -16
+
+
+def l2_grad_terms(s: np.ndarray, dy: np.ndarray, eps64: float) -> np.ndarray:
+    """Per element (|dy_j| + |s_j| sum|s dy| / D^2) / D: the size of ds_j's terms."""
+    out = np.empty(s.shape)
+    with np.errstate(all="ignore"):
+        for i in range(s.shape[0]):
+            d2 = sum_sq(s[i]) + eps64
+            a = math.fsum(np.abs(s[i] * dy[i]))
+            out[i] = (np.abs(dy[i]) + np.abs(s[i]) * (a / d2)) / math.sqrt(d2)
+    return out
+
+
+def rownorm_grad_terms(w: np.ndarray, g: np.ndarray, rho: float, dwe: np.ndarray):
+    """(per element |g rho| / n (|dWe_j| + |w_j| sum|w dWe| / n^2), per row |rho| sum|w dWe| / n)."""
+    tw = np.zeros(w.shape)
+    tg = np.zeros(w.shape[0])
+    with np.errstate(all="ignore"):
+        for i in range(w.shape[0]):
+            ss = sum_sq(w[i])
+            n = math.sqrt(ss)
+            if n == 0.0:
+                continue
+            a = math.fsum(np.abs(w[i] * dwe[i]))
+            tw[i] = abs(g[i] * rho) / n * (np.abs(dwe[i]) + np.abs(w[i]) * (a / ss))
+            tg[i] = abs(rho) * a / n
+    return tw, tg
+
+
+def contract_grad(got, want, terms, fmt: str = "bf16") -> np.ndarray:
+    """Boolean mask of gradient elements that MEET the contract.
+
+    ``got``/``want`` are bf16 bits (fmt "bf16") or fp32/float64 values (fmt
+    "f32"); ``terms`` from l2_grad_terms / rownorm_grad_terms.  NaN must match
+    NaN and infinities must match; the sign of a zero is not compared (a
+    cancelling difference may give either).
+    """
+    if fmt == "bf16":
+        g, w = bf16_value(got), bf16_value(want)
+        with np.errstate(all="ignore"):
+            tol = bf16_ulp(w) + GRAD_SLACK * terms
+    else:
+        g = np.asarray(got, np.float64)
+        w = np.asarray(want, np.float64)
+        with np.errstate(all="ignore"):
+            tol = 2e-6 * np.abs(w) + GRAD_SLACK * terms
+    gn, wn = np.isnan(g), np.isnan(w)
+    with np.errstate(all="ignore"):
+        near = np.abs(g - w) <= tol
+    inf = np.isinf(g) | np.isinf(w)
+    ok = np.where(inf, g == w, near)
+    return np.where(gn | wn, gn & wn, ok)
+
+
+def _mixed_sum_bounds(terms: np.ndarray, depth: int):
+    """Bounds of an fp32 sum of float64-exact terms of any sign.
+
+    Each term may be rounded once to fp32 (a product) and every leaf passes
+    through at most ``depth`` rounded additions, so the error is at most
+    ((1 + u)^(depth + 1) - 1) sum|t|, plus 2**-149 per term for products in
+    fp32's subnormal range.
+    """
+    p = math.fsum(terms)
+    a = math.fsum(np.abs(terms))
+    err = (((1 + U) ** (depth + 1) - 1) * a + terms.size * ETA) * (1 + F64_WIDEN) \
+        + abs(p) * 2.0 ** -52
+    return p - err, p + err
+
+
+def _corner_bounds(a_lo, a_hi, b_lo, b_hi):
+    """Bounds of fl(a * b) for a, b in intervals of any sign (arrays broadcast)."""
+    return _product_bounds(np.asarray(a_lo, np.float64), np.asarray(a_hi, np.float64),
+                           b_lo, b_hi)
+
+
+def _diff_bounds(a, m_lo, m_hi):
+    """Bounds of fl(a - m) for exact a and m in [m_lo, m_hi] (one rounding)."""
+    lo = a - m_hi
+    hi = a - m_lo
+    lo = np.where(lo >= 0, lo * (1 - U), lo * (1 + U)) * (1 + np.sign(-lo) * F64_WIDEN)
+    hi = np.where(hi >= 0, hi * (1 + U), hi * (1 - U)) * (1 + np.sign(hi) * F64_WIDEN)
+    return lo, hi
+
+
+def _tangent_bounds(v, d, k_lo, k_hi, c_lo, c_hi):
+    """Bounds of fl(c * fl(d - fl(v * k))) per element (v, d exact arrays)."""
+    with np.errstate(all="ignore"):
+        m = np.stack([v * k_lo, v * k_hi])
+    m_lo, m_hi = m.min(axis=0), m.max(axis=0)
+    m_lo = np.where(m_lo >= 0, m_lo * (1 - U), m_lo * (1 + U)) * (1 - np.sign(m_lo) * F64_WIDEN) - ETA
+    m_hi = np.where(m_hi >= 0, m_hi * (1 + U), m_hi * (1 - U)) * (1 + np.sign(m_hi) * F64_WIDEN) + ETA
+    t_lo, t_hi = _diff_bounds(d, m_lo, m_hi)
+    return _corner_bounds(t_lo, t_hi, c_lo, c_hi)
+
+
+def _scalar(lo_hi):
+    lo, hi = lo_hi
+    return float(np.min(lo)), float(np.max(hi))
+
+
+def admissible_l2_backward(got_bits, x_bits, r_bits, dy_bits, eps: float = 1e-6,
+                           depth: Optional[int] = None, row_ids=None) -> Report:
+    """Strict check of l2_rows gradients ``got_bits`` (bf16 bits).
+
+    The fp32 run modelled: S and P = <s, dy> summed as above (depth
+    additions); inv = 1/sqrt(S + eps) as in the forward; k = fl(fl(P inv) inv);
+    ds_j = fl(fl(dy_j - fl(s_j k)) inv), or any fusing of those steps.  A set
+    of more than two bf16 values is counted in ``wide`` (cancellation makes
+    it legitimate), not as a failure.
+    """
+    from .rows import l2_rows_backward as ref
+    x = bf16_value(np.atleast_2d(x_bits))
+    if r_bits is not None:
+        with np.errstate(all="ignore"):
+            s = bf16_value(bf16_rne(x + bf16_value(np.atleast_2d(r_bits))))
+    else:
+        s = x
+    dy = bf16_value(np.atleast_2d(dy_bits))
+    got = np.atleast_2d(got_bits)
+    cols = s.shape[1]
+    depth = default_depth(cols) if depth is None else depth
+    eps64 = eps_as_passed(eps)
+    rep = Report()
+    for i in range(s.shape[0]):
+        base = (row_ids[i] if row_ids is not None else i) * cols
+        row, d = s[i], dy[i]
+        if not (np.isfinite(row).all() and np.isfinite(d).all()) or (eps64 == 0 and not row.any()):
+            exact = ref(np.atleast_2d(x_bits)[i:i + 1],
+                        None if r_bits is None else np.atleast_2d(r_bits)[i:i + 1],
+                        np.atleast_2d(dy_bits)[i:i + 1], eps)[0]
+            _judge(got[i], row, row, exact, np.ones(cols, bool), True, base, rep)
+            continue
+        sq = row ** 2
+        s_lo, s_hi = _sum_bounds(sq, sq, depth)
+        inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, eps64)
+        p_lo, p_hi = _mixed_sum_bounds(row * d, depth)
+        q = _scalar(_corner_bounds([p_lo], [p_hi], inv_lo, inv_hi))
+        k_lo, k_hi = _scalar(_corner_bounds([q[0]], [q[1]], inv_lo, inv_hi))
+        lo, hi = _tangent_bounds(row, d, k_lo, k_hi, inv_lo, inv_hi)
+        _judge(got[i], lo, hi, None, None, True, base, rep, wide_ok=True)
+    return rep
+
+
+def admissible_rownorm_backward(got_dw, got_dg, w, g, rho, dweff_bits,
+                                depth: Optional[int] = None, row_offset: int = 0):
+    """Strict check of one matrix's weight gradients: (dW Report, dg Report).
+
+    fp32 outputs must lie inside the interval itself.  The fp32 run
+    modelled: S = sum w^2 and P = <w, dWe> as above; inv = 1/sqrt(S) with at
+    most three roundings; dg = fl(fl(rho P) inv); c = fl(fl(g rho) inv);
+    k = fl(fl(P inv) inv); dW_j = fl(c fl(dWe_j - fl(w_j k))), or any fusing
+    of those steps.  A zero row must give exact zeros.
+    """
+    from .rows import rownorm_backward_values as ref
+    w64 = np.asarray(w, dtype=np.float64)
+    g64 = np.asarray(g, dtype=np.float64)
+    rho64 = float(np.float32(rho))
+    de = bf16_value(np.asarray(dweff_bits))
+    rows, cols = w64.shape
+    depth = default_depth(cols) if depth is None else depth
+    gw = np.atleast_2d(np.asarray(got_dw, np.float64))
+    gg = np.asarray(got_dg, np.float64)
+    rw, rg = Report(), Report()
+
+    def mark(rep, bad, base):
+        rep.n += bad.size
+        idx = np.nonzero(bad)[0]
+        rep.outside += idx.size
+        for j in idx[: max(0, 20 - len(rep.first_bad))]:
+            rep.first_bad.append(int(base + j))
+
+    for i in range(rows):
+        row, d = w64[i], de[i]
+        base = (row_offset + i) * cols
+        if not (np.isfinite(row).all() and np.isfinite(d).all() and np.isfinite(g64[i])):
+            dw_ref, dg_ref = ref(row[None], g64[i:i + 1], rho64, d[None])
+            want = dw_ref[0].astype(np.float32).astype(np.float64)
+            mark(rw, ~((gw[i] == want) | (np.isnan(gw[i]) & np.isnan(want))), base)
+            wg = float(np.float32(dg_ref[0]))
+            mark(rg, np.array([not (gg[i] == wg or (np.isnan(gg[i]) and np.isnan(wg)))]),
+                 row_offset + i)
+            continue
+        sq = row ** 2
+        s_lo, s_hi = _sum_bounds(sq, sq, depth)
+        if s_hi == 0:
+            mark(rw, gw[i] != 0, base)
+            mark(rg, np.array([gg[i] != 0]), row_offset + i)
+            continue
+        inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, 0.0)
+        p_lo, p_hi = _mixed_sum_bounds(row * d, depth)
+        rp = _scalar(_corner_bounds([p_lo], [p_hi], rho64, rho64))
+        if rho64 == 1.0:
+            rp = (p_lo, p_hi)
+        dg_lo, dg_hi = _scalar(_corner_bounds([rp[0]], [rp[1]], inv_lo, inv_hi))
+        mark(rg, np.array([not (dg_lo <= gg[i] <= dg_hi)]), row_offset + i)
+        gr = g64[i] * rho64
+        gr_lo, gr_hi = (gr, gr) if rho64 == 1.0 else _scalar(_corner_bounds([gr], [gr], 1.0, 1.0))
+        c_lo, c_hi = _scalar(_corner_bounds([gr_lo], [gr_hi], inv_lo, inv_hi))
+        q = _scalar(_corner_bounds([p_lo], [p_hi], inv_lo, inv_hi))
+        k_lo, k_hi = _scalar(_corner_bounds([q[0]], [q[1]], inv_lo, inv_hi))
+        lo, hi = _tangent_bounds(row, d, k_lo, k_hi, c_lo, c_hi)
+        mark(rw, ~((gw[i] >= lo) & (gw[i] <= hi)), base)
+    return rw, rg

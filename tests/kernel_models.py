@@ -18,20 +18,24 @@ def bf16_of_f32(v32):
 
 def lane_sum_sq(s32, acc="f32"):
     """Row sums of squares: 64 lane accumulators, then a pairwise tree."""
-    rows, cols = s32.shape
+    return lane_sum((s32 * s32).astype(np.float32), acc)
+
+
+def lane_sum(sq, acc="f32"):
+    """Row sums of fp32 terms: 64 lane accumulators, then a pairwise tree."""
+    rows, cols = sq.shape
     pad = (-cols) % 64
-    s = np.concatenate([s32, np.zeros((rows, pad), np.float32)], axis=1)
-    sq = (s * s).astype(np.float32)
+    sq = np.concatenate([sq.astype(np.float32), np.zeros((rows, pad), np.float32)], axis=1)
     if acc == "f16":
         a = np.zeros((rows, 64), np.float16)
         with np.errstate(over="ignore"):
-            for c in range(0, s.shape[1], 64):
+            for c in range(0, sq.shape[1], 64):
                 a = (a + sq[:, c:c + 64].astype(np.float16)).astype(np.float16)
             while a.shape[1] > 1:
                 a = (a[:, 0::2] + a[:, 1::2]).astype(np.float16)
         return a[:, 0].astype(np.float32)
     a = np.zeros((rows, 64), np.float32)
-    for c in range(0, s.shape[1], 64):
+    for c in range(0, sq.shape[1], 64):
         a = a + sq[:, c:c + 64]
         if acc == "bf16":
             a = bf16_of_f32(a)
@@ -79,3 +83,53 @@ def rownorm_model(w, g, rho=1.0):
     with np.errstate(all="ignore"):
         c = np.where(n > 0, (np.asarray(g, np.float32) * np.float32(rho)) / n, np.float32(0))
     return n, bf16_rne((w32 * c[:, None].astype(np.float32)).astype(np.float64))
+
+
+# ------------------------------------------------------------------ backward
+
+def l2_backward_model(x_bits, r_bits, dy_bits, eps=1e-6, round_s=True, acc="f32",
+                      proj="s", use_eps=True):
+    """ds = (dy - s k) inv, k = P inv inv; controls: an unrounded s, a narrow
+    accumulator, the projection taken on the rounded output y (proj="y"),
+    eps left out."""
+    x = bf16_value(x_bits).astype(np.float32)
+    s = x if r_bits is None else x + bf16_value(r_bits).astype(np.float32)
+    if r_bits is not None and round_s:
+        s = bf16_of_f32(s)
+    dy = bf16_value(dy_bits).astype(np.float32)
+    inv = inv_norm(lane_sum_sq(s, acc), eps if use_eps else 0.0)[:, None]
+    with np.errstate(all="ignore"):
+        if proj == "y":
+            y = bf16_of_f32(s * inv)
+            py = lane_sum((y * dy).astype(np.float32), acc)[:, None]
+            ds = (dy - y * py) * inv
+        else:
+            p = lane_sum((s * dy).astype(np.float32), acc)[:, None]
+            k = (p * inv) * inv
+            ds = (dy - s * k) * inv
+    return bf16_rne(ds.astype(np.float32).astype(np.float64))
+
+
+def rownorm_backward_model(w, g, rho, dwe_bits, acc="f32", proj="w"):
+    """dW = c (dWe - w k), c = g rho inv, dg = rho P inv; controls: a narrow
+    accumulator, the projection taken on bf16(W_eff / (g rho)) (proj="weff")."""
+    w32 = np.asarray(w, np.float32)
+    de = bf16_value(dwe_bits).astype(np.float32)
+    g32 = np.asarray(g, np.float32)[:, None]
+    r32 = np.float32(rho)
+    with np.errstate(all="ignore"):
+        inv = (np.float32(1) / np.sqrt(lane_sum_sq(w32, acc)))[:, None]
+        if proj == "weff":
+            wh = bf16_of_f32(w32 * inv)
+            pw = lane_sum((wh * de).astype(np.float32), acc)[:, None]
+            dg = r32 * pw
+            dw = (g32 * r32) * inv * (de - wh * pw)
+        else:
+            p = lane_sum((w32 * de).astype(np.float32), acc)[:, None]
+            dg = (r32 * p) * inv
+            k = (p * inv) * inv
+            dw = ((g32 * r32) * inv) * (de - w32 * k)
+    zero = ~w32.any(axis=1)
+    dw[zero] = 0
+    dg[zero] = 0
+    return dw.astype(np.float32), dg[:, 0].astype(np.float32)
