@@ -19,6 +19,15 @@
  *                         W_eff = diag(g) r W / ||W||_row over a ragged batch of
  *                         weight matrices in one call ("Kernels and speed": the
  *                         weights of every layer in a few launches).
+ *  ds_l2_rows_backward    the gradient of ds_l2_rows' s -> s / sqrt(sum s^2 +
+ *                         eps): ds = (dy - s <s,dy> / D^2) / D, shared by x
+ *                         and r (the bf16 rounding of s passes it through).
+ *  ds_weight_rownorm_gain_backward
+ *                         DragonScale README, "What DragonScale changes": the
+ *                         gradient reaching W is (g r / ||W||) times dL/dW_eff
+ *                         with its component along the row removed; the gain's
+ *                         gradient follows by the chain rule through W_eff.
+ *                         Both for a ragged batch in one call.
  *
  * Numerics.  bf16 values are passed as their 16-bit patterns; every rounding
  * to bf16 is to nearest, ties to even.  Sums of squares accumulate in fp32
@@ -34,6 +43,12 @@
  * to within the stated rounding.  NaN and infinity propagate as in IEEE
  * arithmetic (a row holding an infinity maps its finite entries to 0 and the
  * infinity to NaN; a row holding a NaN maps to NaN).
+ *
+ * Gradients are those of the unrounded forward function, evaluated at the
+ * forward's inputs (which the gradient calls take again: nothing is saved
+ * between calls).  A gradient element is a difference of two terms that may
+ * cancel; its error is within one unit of the output format's rounding plus
+ * a few fp32 units of the larger term.
  *
  * Determinism.  The bits of output row i depend only on row i's inputs, cols,
  * eps (and alpha, gain, radius): not on the row count, the row's position,
@@ -58,7 +73,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10000          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10100          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -71,16 +86,17 @@ enum {
   DS_ERR_SHAPE = -2,   /* rows < 0, cols not a multiple of 8 (bf16 rows) or 4
                           (fp32 weight rows), cols below that multiple or above
                           DS_MAX_COLS, or sizes that overflow */
-  DS_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned (gain and norm_out:
-                          4-byte aligned) */
+  DS_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned (gain, norm_out and
+                          dgain: 4-byte aligned) */
   DS_ERR_ARG = -4,     /* eps negative or not finite, radius not finite,
                           n < 0, or buffers that partly overlap */
   DS_ERR_ALLOC = -5,   /* the descriptor staging area could not be allocated */
   DS_ERR_LAUNCH = -6,  /* the HIP runtime reported an error for the launch,
                           the copy or the stream */
   DS_ERR_DEVICE = -7,  /* no usable HIP device */
-  DS_ERR_CAPTURE = -8  /* ds_weight_rownorm_gain on a capturing stream with more
-                          than 48 matrices of one width (see that function) */
+  DS_ERR_CAPTURE = -8  /* a ragged weight call on a capturing stream with more
+                          than 48 matrices of one width (see
+                          ds_weight_rownorm_gain) */
 };
 
 /*
@@ -168,6 +184,67 @@ typedef struct ds_rownorm_desc {
  */
 int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n,
                            ds_stream_t stream);
+
+/*
+ * ds_l2_rows_backward -- the gradient of ds_l2_rows.
+ *
+ *   s  = x, or bf16(x + r)                       (as in ds_l2_rows)
+ *   D  = sqrt(sum_j s_j^2 + eps)
+ *   dx = bf16((dy - s * <s, dy> / D^2) / D)       for every row
+ *
+ * (I - y y^T) / D with y = s / D is the Jacobian of s -> s / D; the rounding
+ * of x + r to bf16 passes the gradient through, so dx is the gradient with
+ * respect to x and also, when r is given, with respect to r.
+ *
+ * x, r, dy, dx : row-major [rows, cols] bf16 bit patterns, contiguous,
+ *                16-byte aligned.  x and r are the forward call's inputs, dy
+ *                the gradient reaching its output y.  dx may be the same
+ *                buffer as x, r or dy; any other overlap is refused.
+ * rows, cols, eps, stream : as for ds_l2_rows (eps must be the forward's).
+ */
+int ds_l2_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy,
+                        uint16_t* dx, int64_t rows, int64_t cols, float eps,
+                        ds_stream_t stream);
+
+/*
+ * One weight matrix of a ds_weight_rownorm_gain_backward call.
+ *
+ * w, gain, radius : the forward call's inputs (as in ds_rownorm_desc).
+ * dw_eff   : [rows, cols] bf16 bit patterns, dL/dW_eff; 16-byte aligned.
+ * dw       : [rows, cols] fp32, receives dL/dW; 16-byte aligned.
+ * dgain    : [rows] fp32, receives dL/dg; may be NULL; 4-byte aligned.
+ * rows, cols : as in ds_rownorm_desc.
+ * dw and dgain must not overlap any input or output of the call.
+ */
+typedef struct ds_rownorm_grad_desc {
+  const float* w;
+  const float* gain;
+  float radius;
+  const uint16_t* dw_eff;
+  float* dw;
+  float* dgain;
+  int64_t rows;
+  int64_t cols;
+} ds_rownorm_grad_desc;
+
+/*
+ * ds_weight_rownorm_gain_backward -- gradients of ds_weight_rownorm_gain over
+ * a ragged batch of n matrices.
+ * (DragonScale README, "What DragonScale changes": the gradient reaching W is
+ * tangent to its rows.)
+ *
+ * Per row i, with n_i = ||W_i|| and P_i = <W_i, dW_eff_i>:
+ *   dw_i    = (g_i r / n_i) (dW_eff_i - W_i P_i / n_i^2)     fp32
+ *   dgain_i = r P_i / n_i                                     fp32
+ * A zero row (n_i = 0, scaled by the constant 0 in the forward) gets zero
+ * gradients.
+ *
+ * descs, n, stream : as for ds_weight_rownorm_gain, including the grouping by
+ *                    row width, the 48-matrix inline limit, the staged table
+ *                    and DS_ERR_CAPTURE.
+ */
+int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,
+                                    ds_stream_t stream);
 
 /* A static, human-readable string for a status code (never NULL). */
 const char* ds_status_string(int status);

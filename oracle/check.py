@@ -484,6 +484,20 @@ def _tangent_bounds(v, d, k_lo, k_hi, c_lo, c_hi):
     return _corner_bounds(t_lo, t_hi, c_lo, c_hi)
 
 
+F32_OVERFLOW = (2.0 - 2.0 ** -24) * 2.0 ** 127    # fp32 rounding sends |v| >= this to inf
+
+
+def _f32_inside(got, lo, hi):
+    """fp32 results inside [lo, hi]; an infinity is inside when the interval
+    reaches the overflow threshold on its side."""
+    got = np.asarray(got, np.float64)
+    with np.errstate(invalid="ignore"):
+        ok = (got >= lo) & (got <= hi)
+    ok |= (got == np.inf) & (hi >= F32_OVERFLOW)
+    ok |= (got == -np.inf) & (lo <= -F32_OVERFLOW)
+    return ok
+
+
 def _scalar(lo_hi):
     lo, hi = lo_hi
     return float(np.min(lo)), float(np.max(hi))
@@ -583,12 +597,12 @@ def admissible_rownorm_backward(got_dw, got_dg, w, g, rho, dweff_bits,
         if rho64 == 1.0:
             rp = (p_lo, p_hi)
         dg_lo, dg_hi = _scalar(_corner_bounds([rp[0]], [rp[1]], inv_lo, inv_hi))
-        mark(rg, np.array([not (dg_lo <= gg[i] <= dg_hi)]), row_offset + i)
+        mark(rg, ~_f32_inside(np.array([gg[i]]), dg_lo, dg_hi), row_offset + i)
         gr = g64[i] * rho64
         gr_lo, gr_hi = (gr, gr) if rho64 == 1.0 else _scalar(_corner_bounds([gr], [gr], 1.0, 1.0))
         c_lo, c_hi = _scalar(_corner_bounds([gr_lo], [gr_hi], inv_lo, inv_hi))
         q = _scalar(_corner_bounds([p_lo], [p_hi], inv_lo, inv_hi))
         k_lo, k_hi = _scalar(_corner_bounds([q[0]], [q[1]], inv_lo, inv_hi))
         lo, hi = _tangent_bounds(row, d, k_lo, k_hi, c_lo, c_hi)
-        mark(rw, ~((gw[i] >= lo) & (gw[i] <= hi)), base)
+        mark(rw, ~_f32_inside(gw[i], lo, hi), base)
     return rw, rg

@@ -213,6 +213,7 @@ def weight_rownorm_gain_backward(w: Sequence[np.ndarray], gain: Sequence[np.ndar
     for wm, gm, rho, de in zip(w, gain, radius, dweff_bits):
         dw, dg = rownorm_backward_values(np.asarray(wm, np.float64), np.asarray(gm, np.float64),
                                          float(np.float32(rho)), bf16_value(de))
-        dws.append(dw.astype(np.float32))
-        dgs.append(dg.astype(np.float32))
+        with np.errstate(over="ignore"):          # beyond fp32's range: +-inf
+            dws.append(dw.astype(np.float32))
+            dgs.append(dg.astype(np.float32))
     return dws, dgs

@@ -44,6 +44,20 @@ class RownormDesc(ctypes.Structure):
     ]
 
 
+class RownormGradDesc(ctypes.Structure):
+    """ds_rownorm_grad_desc."""
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("gain", ctypes.c_void_p),
+        ("radius", ctypes.c_float),
+        ("dw_eff", ctypes.c_void_p),
+        ("dw", ctypes.c_void_p),
+        ("dgain", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -55,6 +69,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m scale_invariant_row_amd.build` (there is no fallback)")
+        # torch first: it maps its own HIP runtime (same soname), and the
+        # library then binds to that one, so the kernels, the tensors' memory
+        # and the streams all live in one HIP runtime.  Loaded the other way
+        # round, the process would hold two runtimes and the library's own
+        # would not share torch's device state.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
         L.ds_l2_rows.argtypes = [vp, vp, vp, i64, i64, f32, vp]
@@ -63,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.ds_slerp_rows.restype = ctypes.c_int
         L.ds_weight_rownorm_gain.argtypes = [ctypes.POINTER(RownormDesc), ctypes.c_int32, vp]
         L.ds_weight_rownorm_gain.restype = ctypes.c_int
+        L.ds_l2_rows_backward.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
+        L.ds_l2_rows_backward.restype = ctypes.c_int
+        L.ds_weight_rownorm_gain_backward.argtypes = [ctypes.POINTER(RownormGradDesc),
+                                                      ctypes.c_int32, vp]
+        L.ds_weight_rownorm_gain_backward.restype = ctypes.c_int
         L.ds_status_string.argtypes = [ctypes.c_int]
         L.ds_status_string.restype = ctypes.c_char_p
         L.ds_version.argtypes = []
@@ -207,3 +232,78 @@ def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Seque
         st = lib().ds_weight_rownorm_gain(descs, n, _stream_of(ws[0], stream))
     _check(st, "ds_weight_rownorm_gain")
     return list(norm_out), list(w_eff)
+
+
+def ds_l2_rows_backward(x, r, dy, eps: float = 1e-6, out=None, stream=None):
+    """dx = bf16((dy - s <s,dy>/D^2) / D), the gradient of ds_l2_rows(x, r, eps)
+    with respect to x (and to r when given).  Returns ``out`` (allocated like
+    ``dy`` when not given; may be ``x``, ``r`` or ``dy``)."""
+    torch = _torch()
+    _bf16_2d(x, "x")
+    _bf16_2d(dy, "dy")
+    _same(x, dy, "dy")
+    if r is not None:
+        _bf16_2d(r, "r")
+        _same(x, r, "r")
+    if out is None:
+        out = torch.empty_like(dy)
+    _bf16_2d(out, "out")
+    _same(x, out, "out")
+    with torch.cuda.device(x.device):
+        st = lib().ds_l2_rows_backward(x.data_ptr(), None if r is None else r.data_ptr(),
+                                       dy.data_ptr(), out.data_ptr(), x.shape[0], x.shape[1],
+                                       float(eps), _stream_of(x, stream))
+    _check(st, "ds_l2_rows_backward")
+    return out
+
+
+def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequence,
+                                    radius: Optional[Sequence[float]] = None,
+                                    dw: Optional[Sequence] = None,
+                                    dgain: Optional[Sequence] = None,
+                                    want_dgain: bool = True, stream=None) -> Tuple[list, list]:
+    """Per matrix: dL/dW (fp32) and dL/dg (fp32) from dL/dW_eff (bf16), in one call.
+
+    Returns (dws, dgains); a dgain entry is None when ``want_dgain`` is false
+    and none was given.
+    """
+    torch = _torch()
+    n = len(ws)
+    if len(gains) != n or len(dw_effs) != n:
+        raise ValueError("one gain vector and one dW_eff per matrix")
+    radius = [1.0] * n if radius is None else list(radius)
+    if dw is None:
+        dw = [torch.empty(w.shape, dtype=torch.float32, device=w.device) for w in ws]
+    if dgain is None:
+        dgain = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device) if want_dgain
+                 else None for w in ws]
+    descs = (RownormGradDesc * max(n, 1))()
+    dev = None
+    for i, (w, g, de) in enumerate(zip(ws, gains, dw_effs)):
+        if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+            raise ValueError(f"ws[{i}]: expected a contiguous fp32 [rows, cols] tensor")
+        if g.dtype != torch.float32 or g.shape != (w.shape[0],) or not g.is_contiguous():
+            raise ValueError(f"gains[{i}]: expected a contiguous fp32 [rows] tensor")
+        _bf16_2d(de, f"dw_effs[{i}]")
+        if tuple(de.shape) != tuple(w.shape):
+            raise ValueError(f"dw_effs[{i}]: shape mismatch")
+        if dw[i].dtype != torch.float32 or tuple(dw[i].shape) != tuple(w.shape) \
+                or not dw[i].is_contiguous():
+            raise ValueError(f"dw[{i}]: expected a contiguous fp32 tensor shaped like ws[{i}]")
+        if dgain[i] is not None and (dgain[i].dtype != torch.float32
+                                     or dgain[i].shape != (w.shape[0],)):
+            raise ValueError(f"dgain[{i}]: expected fp32 [rows]")
+        for t in (w, g, de, dw[i]) + ((dgain[i],) if dgain[i] is not None else ()):
+            if t.device.type != "cuda" or (dev is not None and t.device != dev):
+                raise ValueError("all tensors must be on one HIP device")
+            dev = t.device
+        descs[i] = RownormGradDesc(w.data_ptr(), g.data_ptr(), float(radius[i]), de.data_ptr(),
+                                   dw[i].data_ptr(),
+                                   None if dgain[i] is None else dgain[i].data_ptr(),
+                                   w.shape[0], w.shape[1])
+    if n == 0:
+        return [], []
+    with torch.cuda.device(dev):
+        st = lib().ds_weight_rownorm_gain_backward(descs, n, _stream_of(ws[0], stream))
+    _check(st, "ds_weight_rownorm_gain_backward")
+    return list(dw), list(dgain)

@@ -174,6 +174,159 @@ void release(Ring& r, int i, bool enqueued, hipStream_t stream) {
   s.busy = false;
 }
 
+
+// ------------------------------------------------------ ragged weight calls
+
+// Byte ranges [first, second) that a call reads and writes.
+using Range = std::pair<uintptr_t, uintptr_t>;
+
+void add_range(std::vector<Range>& v, const void* p, size_t bytes) {
+  if (p == nullptr || bytes == 0) return;
+  auto a = reinterpret_cast<uintptr_t>(p);
+  v.emplace_back(a, a + bytes);
+}
+
+// No two output ranges share a byte, and no output shares a byte with any
+// input (of its own matrix or another's): every matrix of a ragged call runs
+// concurrently with the others.
+bool outputs_disjoint(std::vector<Range>& outs, std::vector<Range>& ins) {
+  std::sort(outs.begin(), outs.end());
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (outs[i].first < outs[i - 1].second) return false;
+  std::sort(ins.begin(), ins.end());
+  size_t j = 0;
+  uintptr_t reach = 0;          // furthest end among inputs starting before the current output
+  for (const Range& o : outs) {
+    while (j < ins.size() && ins[j].first < o.second) reach = std::max(reach, ins[j++].second);
+    if (reach > o.first) return false;
+  }
+  return true;
+}
+
+template <class Task>
+using RaggedLauncher = hipError_t (*)(Shape, const dsr::TaskArgs<Task>&, int, hipStream_t);
+
+// One launch per kernel shape class over the matrices' tasks.  A class of at
+// most kInlineTasks matrices carries its table inside the kernel arguments;
+// larger classes share one table (tasks, then their first items as a compact
+// int32 array) staged through the ring and copied on the stream first.
+template <class Task>
+int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLauncher<Task> launch,
+                  hipStream_t hs) {
+  std::map<int, std::vector<size_t>> classes;     // shape key -> indices into mats
+  for (size_t i = 0; i < mats.size(); ++i)
+    classes[mats[i].first.G * 100 + mats[i].first.V].push_back(i);
+  if (classes.empty()) return DS_OK;
+
+  std::vector<Task> table;
+  struct Launch { Shape s; size_t first; int ntasks; int nitems; };
+  std::vector<Launch> launches;
+  for (auto& kv : classes) {
+    const Shape s{kv.first / 100, kv.first % 100};
+    const int R = s.rows_per_block();
+    Launch L{s, table.size(), 0, 0};
+    int64_t items = 0;
+    for (size_t i : kv.second) {
+      Task t = mats[i].second;
+      t.item_begin = (int32_t)items;
+      items += (t.rows + R - 1) / R;
+      if (items > INT32_MAX) return DS_ERR_SHAPE;
+      table.push_back(t);
+    }
+    L.ntasks = (int)kv.second.size();
+    L.nitems = (int)items;
+    launches.push_back(L);
+  }
+
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st != DS_OK) return st;
+  size_t staged_tasks = 0;
+  for (const Launch& L : launches)
+    if (L.ntasks > dsr::kInlineTasks) staged_tasks += (size_t)L.ntasks;
+
+  if (staged_tasks > 0) {
+    // a staged table is copied from a reusable host slot: a graph replay
+    // would copy whatever that slot holds by then
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return DS_ERR_LAUNCH;
+    if (cap != hipStreamCaptureStatusNone) return DS_ERR_CAPTURE;
+  }
+  Ring* ring = nullptr;
+  int slot = -1;
+  const Task* dev_tasks = nullptr;
+  const int32_t* dev_begins = nullptr;
+  (void)hipGetLastError();
+  if (staged_tasks > 0) {
+    ring = ring_for_current_device();
+    if (ring == nullptr) return DS_ERR_DEVICE;
+    const size_t task_bytes = staged_tasks * sizeof(Task);
+    const size_t bytes = task_bytes + staged_tasks * sizeof(int32_t);
+    if ((st = acquire(*ring, bytes, &slot)) != DS_OK) return st;
+    Slot& sl = ring->slot[slot];
+    auto* host_tasks = static_cast<Task*>(sl.host);
+    auto* host_begins = reinterpret_cast<int32_t*>(static_cast<char*>(sl.host) + task_bytes);
+    size_t k = 0;
+    for (const Launch& L : launches) {
+      if (L.ntasks <= dsr::kInlineTasks) continue;
+      for (int i = 0; i < L.ntasks; ++i, ++k) {
+        host_tasks[k] = table[L.first + i];
+        host_begins[k] = table[L.first + i].item_begin;
+      }
+    }
+    if (hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
+      release(*ring, slot, false, hs);        // nothing enqueued: refund the slot
+      return DS_ERR_LAUNCH;
+    }
+    dev_tasks = static_cast<const Task*>(sl.dev);
+    dev_begins = reinterpret_cast<const int32_t*>(static_cast<const char*>(sl.dev) + task_bytes);
+  }
+
+  int result = DS_OK;
+  size_t staged_at = 0;
+  for (const Launch& L : launches) {
+    dsr::TaskArgs<Task> args{};
+    args.ntasks = L.ntasks;
+    args.nitems = L.nitems;
+    if (L.ntasks <= dsr::kInlineTasks) {
+      args.tasks = nullptr;
+      args.begins = nullptr;
+      for (int i = 0; i < L.ntasks; ++i) {
+        args.inline_tasks[i] = table[L.first + i];
+        args.inline_begins[i] = table[L.first + i].item_begin;
+      }
+    } else {
+      args.tasks = dev_tasks + staged_at;
+      args.begins = dev_begins + staged_at;
+      staged_at += (size_t)L.ntasks;
+    }
+    if (launch(L.s, args, grid_for(L.nitems, cus), hs) != hipSuccess) {
+      result = DS_ERR_LAUNCH;
+      break;
+    }
+  }
+  if (ring != nullptr) release(*ring, slot, true, hs);   // the copy is in flight either way
+  return result;
+}
+
+// The l2_rows gradient's buffers: dx may be exactly x, r or dy (each row is
+// held in registers before its store), or disjoint from all three.
+int check_l2_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy, uint16_t* dx,
+                      int64_t rows, int64_t cols, float eps) {
+  int st = check_matrix(rows, cols, 8, 2);
+  if (st != DS_OK) return st;
+  if (!finite_nonneg(eps)) return DS_ERR_ARG;
+  if (rows == 0) return DS_OK;
+  if (x == nullptr || dy == nullptr || dx == nullptr) return DS_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || (r != nullptr && !aligned(r, 16)))
+    return DS_ERR_ALIGN;
+  const size_t bytes = (size_t)rows * (size_t)cols * 2;
+  if (!same_or_disjoint(dx, x, bytes) || !same_or_disjoint(dx, r, bytes) ||
+      !same_or_disjoint(dx, dy, bytes))
+    return DS_ERR_ARG;
+  return DS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,7 +343,7 @@ const char* ds_status_string(int status) {
     case DS_ERR_ALLOC: return "DS_ERR_ALLOC: could not allocate the descriptor staging buffer";
     case DS_ERR_LAUNCH: return "DS_ERR_LAUNCH: the HIP runtime reported an error";
     case DS_ERR_DEVICE: return "DS_ERR_DEVICE: no usable HIP device";
-    case DS_ERR_CAPTURE: return "DS_ERR_CAPTURE: a ragged call with more than 48 matrices of one width cannot be captured into a graph";
+    case DS_ERR_CAPTURE: return "DS_ERR_CAPTURE: a ragged weight call with more than 48 matrices of one width cannot be captured into a graph";
     default: return "unknown ds_rows status";
   }
 }
@@ -244,8 +397,9 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
   if (n == 0) return DS_OK;
   if (descs == nullptr) return DS_ERR_NULL;
 
-  // 1. validate every descriptor; collect output ranges
-  std::vector<std::pair<uintptr_t, uintptr_t>> outs;
+  // validate every descriptor before anything is enqueued
+  std::vector<Range> outs, ins;
+  std::vector<std::pair<Shape, dsr::RownormTask>> mats;
   for (int32_t i = 0; i < n; ++i) {
     const ds_rownorm_desc& d = descs[i];
     int st = check_matrix(d.rows, d.cols, 4, 4);
@@ -257,137 +411,81 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
         (d.norm_out != nullptr && !aligned(d.norm_out, 4)))
       return DS_ERR_ALIGN;
     const size_t nel = (size_t)d.rows * (size_t)d.cols;
-    const size_t weff_b = nel * 2, w_b = nel * 4, row_b = (size_t)d.rows * 4;
-    if (overlaps(d.w_eff, weff_b, d.w, w_b) || overlaps(d.w_eff, weff_b, d.gain, row_b))
-      return DS_ERR_ARG;
-    if (d.norm_out != nullptr &&
-        (overlaps(d.norm_out, row_b, d.w, w_b) || overlaps(d.norm_out, row_b, d.gain, row_b) ||
-         overlaps(d.norm_out, row_b, d.w_eff, weff_b)))
-      return DS_ERR_ARG;
-    auto a = reinterpret_cast<uintptr_t>(d.w_eff);
-    outs.emplace_back(a, a + weff_b);
-    if (d.norm_out != nullptr) {
-      auto b = reinterpret_cast<uintptr_t>(d.norm_out);
-      outs.emplace_back(b, b + row_b);
-    }
-  }
-  // no two matrices may write the same bytes
-  std::sort(outs.begin(), outs.end());
-  for (size_t i = 1; i < outs.size(); ++i)
-    if (outs[i].first < outs[i - 1].second) return DS_ERR_ARG;
-
-  // 2. group the matrices by kernel shape (a function of cols alone)
-  std::map<int, std::vector<int32_t>> classes;
-  for (int32_t i = 0; i < n; ++i) {
-    if (descs[i].rows == 0) continue;
-    Shape s = dsr::pick_rownorm_shape(descs[i].cols / 4);
+    add_range(ins, d.w, nel * 4);
+    add_range(ins, d.gain, (size_t)d.rows * 4);
+    add_range(outs, d.w_eff, nel * 2);
+    add_range(outs, d.norm_out, (size_t)d.rows * 4);
+    const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
     if (!s.ok()) return DS_ERR_SHAPE;
-    classes[s.G * 100 + s.V].push_back(i);
+    dsr::RownormTask t{};
+    t.w = d.w;
+    t.gain = d.gain;
+    t.norm_out = d.norm_out;
+    t.w_eff = d.w_eff;
+    t.rows = d.rows;
+    t.cols = (int32_t)d.cols;
+    t.radius = d.radius;
+    mats.emplace_back(s, t);
   }
-  if (classes.empty()) return DS_OK;
+  if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
+  return launch_ragged<dsr::RownormTask>(mats, dsr::launch_rownorm, (hipStream_t)stream);
+}
 
-  std::vector<dsr::RownormTask> table;
-  struct Launch { Shape s; size_t first; int ntasks; int nitems; };
-  std::vector<Launch> launches;
-  for (auto& kv : classes) {
-    Shape s{kv.first / 100, kv.first % 100};
-    const int R = s.rows_per_block();
-    Launch L{s, table.size(), 0, 0};
-    int64_t items = 0;
-    for (int32_t i : kv.second) {
-      const ds_rownorm_desc& d = descs[i];
-      dsr::RownormTask t{};
-      t.w = d.w;
-      t.gain = d.gain;
-      t.norm_out = d.norm_out;
-      t.w_eff = d.w_eff;
-      t.rows = d.rows;
-      t.cols = (int32_t)d.cols;
-      t.radius = d.radius;
-      t.item_begin = (int32_t)items;
-      items += (d.rows + R - 1) / R;
-      if (items > INT32_MAX) return DS_ERR_SHAPE;
-      table.push_back(t);
-    }
-    L.ntasks = (int)kv.second.size();
-    L.nitems = (int)items;
-    launches.push_back(L);
-  }
-
-  // 3. launch one kernel per shape class.  A class of at most kInlineTasks
-  //    matrices carries its table inside the kernel arguments; larger classes
-  //    share one table (tasks, then their first items as a compact int32
-  //    array) staged through the ring and copied on the stream first.
+int ds_l2_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy, uint16_t* dx,
+                        int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
+  int st = check_l2_backward(x, r, dy, dx, rows, cols, eps);
+  if (st != DS_OK || rows == 0) return st;
+  const Shape s = dsr::pick_bf16_shape(cols / 8);
+  if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
-  int st = device_cus(&cus);
-  if (st != DS_OK) return st;
-  hipStream_t hs = (hipStream_t)stream;
-  size_t staged_tasks = 0;
-  for (const Launch& L : launches)
-    if (L.ntasks > dsr::kInlineTasks) staged_tasks += (size_t)L.ntasks;
-
-  if (staged_tasks > 0) {
-    // a staged table is copied from a reusable host slot: a graph replay
-    // would copy whatever that slot holds by then
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return DS_ERR_LAUNCH;
-    if (cap != hipStreamCaptureStatusNone) return DS_ERR_CAPTURE;
-  }
-  Ring* ring = nullptr;
-  int slot = -1;
-  const dsr::RownormTask* dev_tasks = nullptr;
-  const int32_t* dev_begins = nullptr;
+  if ((st = device_cus(&cus)) != DS_OK) return st;
+  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
   (void)hipGetLastError();
-  if (staged_tasks > 0) {
-    ring = ring_for_current_device();
-    if (ring == nullptr) return DS_ERR_DEVICE;
-    const size_t task_bytes = staged_tasks * sizeof(dsr::RownormTask);
-    const size_t bytes = task_bytes + staged_tasks * sizeof(int32_t);
-    if ((st = acquire(*ring, bytes, &slot)) != DS_OK) return st;
-    Slot& sl = ring->slot[slot];
-    auto* host_tasks = static_cast<dsr::RownormTask*>(sl.host);
-    auto* host_begins = reinterpret_cast<int32_t*>(static_cast<char*>(sl.host) + task_bytes);
-    size_t k = 0;
-    for (const Launch& L : launches) {
-      if (L.ntasks <= dsr::kInlineTasks) continue;
-      for (int i = 0; i < L.ntasks; ++i, ++k) {
-        host_tasks[k] = table[L.first + i];
-        host_begins[k] = table[L.first + i].item_begin;
-      }
-    }
-    if (hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
-      release(*ring, slot, false, hs);        // nothing enqueued: refund the slot
-      return DS_ERR_LAUNCH;
-    }
-    dev_tasks = static_cast<const dsr::RownormTask*>(sl.dev);
-    dev_begins = reinterpret_cast<const int32_t*>(static_cast<const char*>(sl.dev) + task_bytes);
-  }
+  return launch_status(dsr::launch_l2_rows_backward(s, x, r, dy, dx, rows, (int)(cols / 8), eps,
+                                                    grid_for(units, cus), (hipStream_t)stream));
+}
 
-  int result = DS_OK;
-  size_t staged_at = 0;
-  for (const Launch& L : launches) {
-    dsr::RownormArgs args{};
-    args.ntasks = L.ntasks;
-    args.nitems = L.nitems;
-    if (L.ntasks <= dsr::kInlineTasks) {
-      args.tasks = nullptr;
-      args.begins = nullptr;
-      for (int i = 0; i < L.ntasks; ++i) {
-        args.inline_tasks[i] = table[L.first + i];
-        args.inline_begins[i] = table[L.first + i].item_begin;
-      }
-    } else {
-      args.tasks = dev_tasks + staged_at;
-      args.begins = dev_begins + staged_at;
-      staged_at += (size_t)L.ntasks;
-    }
-    if (dsr::launch_rownorm(L.s, args, grid_for(L.nitems, cus), hs) != hipSuccess) {
-      result = DS_ERR_LAUNCH;
-      break;
-    }
+int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,
+                                    ds_stream_t stream) {
+  if (n < 0) return DS_ERR_ARG;
+  if (n == 0) return DS_OK;
+  if (descs == nullptr) return DS_ERR_NULL;
+
+  std::vector<Range> outs, ins;
+  std::vector<std::pair<Shape, dsr::RownormGradTask>> mats;
+  for (int32_t i = 0; i < n; ++i) {
+    const ds_rownorm_grad_desc& d = descs[i];
+    int st = check_matrix(d.rows, d.cols, 4, 4);
+    if (st != DS_OK) return st;
+    if (!std::isfinite(d.radius)) return DS_ERR_ARG;
+    if (d.rows == 0) continue;
+    if (d.w == nullptr || d.gain == nullptr || d.dw_eff == nullptr || d.dw == nullptr)
+      return DS_ERR_NULL;
+    if (!aligned(d.w, 16) || !aligned(d.dw_eff, 16) || !aligned(d.dw, 16) ||
+        !aligned(d.gain, 4) || (d.dgain != nullptr && !aligned(d.dgain, 4)))
+      return DS_ERR_ALIGN;
+    const size_t nel = (size_t)d.rows * (size_t)d.cols;
+    add_range(ins, d.w, nel * 4);
+    add_range(ins, d.gain, (size_t)d.rows * 4);
+    add_range(ins, d.dw_eff, nel * 2);
+    add_range(outs, d.dw, nel * 4);
+    add_range(outs, d.dgain, (size_t)d.rows * 4);
+    const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
+    if (!s.ok()) return DS_ERR_SHAPE;
+    dsr::RownormGradTask t{};
+    t.w = d.w;
+    t.gain = d.gain;
+    t.dw_eff = d.dw_eff;
+    t.dw = d.dw;
+    t.dgain = d.dgain;
+    t.rows = d.rows;
+    t.cols = (int32_t)d.cols;
+    t.radius = d.radius;
+    mats.emplace_back(s, t);
   }
-  if (ring != nullptr) release(*ring, slot, true, hs);   // the copy is in flight either way
-  return result;
+  if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
+  return launch_ragged<dsr::RownormGradTask>(mats, dsr::launch_rownorm_backward,
+                                             (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -1,4 +1,5 @@
-"""Writes inst_l2.hip, inst_slerp.hip and inst_rownorm.hip: one launcher per op
+"""Writes inst_l2.hip, inst_slerp.hip, inst_rownorm.hip, inst_l2_bwd.hip and
+inst_rownorm_bwd.hip: one launcher per op
 with a case for every kernel shape (G waves per row, V vectors per lane) that
 launch.hpp's shape policy returns for some width up to DS_MAX_COLS, found by
 evaluating the policy (reproduced below from launch.hpp's constants) at every
@@ -125,7 +126,51 @@ hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_
 
 }  // namespace dsr
 '''
-    for name, text in (("inst_l2.hip", l2), ("inst_slerp.hip", sl), ("inst_rownorm.hip", rn)):
+    l2b = HEAD.format(what="l2_rows gradient") + '''
+template <int G, int V>
+static hipError_t run(const void* x, const void* r, const void* dy, void* dx, int64_t rows,
+                      int nvec, float eps, int grid, hipStream_t stream) {
+  constexpr int T = Geo<G>::THREADS;
+  if (r != nullptr)
+    l2_rows_backward_kernel<G, V, true><<<grid, T, 0, stream>>>(
+        (const u32x4_t*)x, (const u32x4_t*)r, (const u32x4_t*)dy, (u32x4_t*)dx, rows, nvec, eps);
+  else
+    l2_rows_backward_kernel<G, V, false><<<grid, T, 0, stream>>>(
+        (const u32x4_t*)x, nullptr, (const u32x4_t*)dy, (u32x4_t*)dx, rows, nvec, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_l2_rows_backward(Shape s, const void* x, const void* r, const void* dy,
+                                   void* dx, int64_t rows, int nvec, float eps, int grid,
+                                   hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(bf16, "return run<{G}, {V}>(x, r, dy, dx, rows, nvec, eps, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsr
+'''
+    rnb = HEAD.format(what="weight rownorm+gain gradient") + '''
+template <int G, int V>
+static hipError_t run(const RownormGradArgs& args, int grid, hipStream_t stream) {
+  constexpr int T = Geo<G>::THREADS;
+  rownorm_backward_kernel<G, V><<<grid, T, 0, stream>>>(args);
+  return hipGetLastError();
+}
+
+hipError_t launch_rownorm_backward(Shape s, const RownormGradArgs& args, int grid,
+                                   hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(rown, "return run<{G}, {V}>(args, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsr
+'''
+    for name, text in (("inst_l2.hip", l2), ("inst_slerp.hip", sl), ("inst_rownorm.hip", rn),
+                       ("inst_l2_bwd.hip", l2b), ("inst_rownorm_bwd.hip", rnb)):
         with open(os.path.join(HERE, name), "w") as f:
             f.write(text)
 

@@ -6,7 +6,10 @@
 
 namespace dsr {
 
-struct RownormArgs;
+template <class Task>
+struct TaskArgs;
+struct RownormTask;
+struct RownormGradTask;
 
 // Kernel shape: G waves per row, V 16-byte vectors per lane.
 struct Shape {
@@ -17,7 +20,8 @@ struct Shape {
   bool ok() const { return G > 0; }
 };
 
-// Shape policy, measured on MI355X.  A row is spread over the smallest wave
+// Shape policy, measured on MI355X (the gradients use the same rules as
+// their forward ops).  A row is spread over the smallest wave
 // group G in {1, 2, 4, 8, 16} whose V = ceil(vectors / (64 G)) fits a limit:
 //   bf16 rows (l2_rows, slerp_rows): V <= 2 up to 512 vectors (4,096
 //     columns), V <= 4 beyond -- more, lighter waves stream best at these
@@ -53,6 +57,12 @@ hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_
 hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const float* alpha,
                              void* h, int64_t rows, int nvec, float eps, int grid,
                              hipStream_t stream);
-hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_t stream);
+hipError_t launch_rownorm(Shape s, const TaskArgs<RownormTask>& args, int grid,
+                          hipStream_t stream);
+hipError_t launch_l2_rows_backward(Shape s, const void* x, const void* r, const void* dy,
+                                   void* dx, int64_t rows, int nvec, float eps, int grid,
+                                   hipStream_t stream);
+hipError_t launch_rownorm_backward(Shape s, const TaskArgs<RownormGradTask>& args, int grid,
+                                   hipStream_t stream);
 
 }  // namespace dsr

@@ -20,12 +20,23 @@
 //               u = a + |alpha| * (b - a) in three rounded fp32 steps,
 //               h = bf16(l2(u))
 //   rownorm     n = sqrt(S), c = (g * rho) / n, W_eff = bf16(w * c)
+// and their gradients (the gradient of the unrounded function at the
+// forward's inputs; a bf16 rounding passes the gradient through):
+//   l2_rows     ds = bf16((dy - s k) inv), inv = 1/sqrt(S + eps),
+//               k = <s, dy> inv^2 -- the Jacobian of s * inv is
+//               (I - y y^T) inv, and x and r share ds
+//   rownorm     dW = (g rho inv) (dWe - w k), k = <w, dWe> inv^2,
+//               dg = rho <w, dWe> inv, inv = 1/||w|| -- the DragonScale
+//               README's gradient tangent to the rows ("What DragonScale
+//               changes"), and the chain rule through g
 //
 // Range.  When S + eps overflows fp32 or falls below 2^-96 (where squares
 // may have lost bits to underflow), the row is summed again scaled by 2^k,
 // k chosen from max(max|s|, sqrt(eps)) so the scaled maximum lies in [1, 2):
 // a power-of-two scaling is exact, so the result is the unscaled one.  That
 // branch depends only on the row's own sum and is uniform over the group.
+// Afterwards the sum handed to inv_sqrt is >= 2^-96, or 0 (a zero row with
+// eps = 0), infinite or NaN.
 //
 // This file is compiled with -ffp-contract=off: only the explicit fmaf calls
 // fuse, so the lerp's three steps stay three roundings.
@@ -74,6 +85,9 @@ struct RowBuf {
   }
   __device__ __forceinline__ f32x4_t ld16f_cached(int off) const {
     return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ u32x2_t ld8(int off) const {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolLd);
   }
   __device__ __forceinline__ void st16(u32x4_t v, int off) const {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSt);
@@ -174,6 +188,25 @@ __device__ __forceinline__ float group_max(float v, float* slot, int g, int lane
   return v;
 }
 
+// Two maxima combined at once (slot: 2 G floats).
+template <int G>
+__device__ __forceinline__ void group_max2(float (&v)[2], float* slot, int g, int lane) {
+  if constexpr (G > 1) {
+    if (lane == 0) {
+      slot[g] = v[0];
+      slot[G + g] = v[1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float t = slot[i * G];
+#pragma unroll
+      for (int k = 1; k < G; ++k) t = fmaxf(t, slot[i * G + k]);
+      v[i] = t;
+    }
+  }
+}
+
 // Round-robin LDS slots for the group combines (two buffers of 2*G floats).
 template <int G>
 struct GroupScratch {
@@ -219,12 +252,24 @@ __device__ __forceinline__ float inv_sqrt(float T) {
   return (T > 0.f && T < __builtin_inff()) ? r : y;
 }
 
-// Scale exponent for a rescued row: -floor(log2(max(m, sqrt(eps)))).
+// floor(log2(x)) for finite x > 0, normal or subnormal, from the bits.
+__device__ __forceinline__ int floor_log2(float x) {
+  const uint32_t b = __float_as_uint(x) & 0x7fffffffu;
+  const int e = (int)(b >> 23);
+  return e != 0 ? e - 127 : -118 - __builtin_clz(b);
+}
+
+// Scale exponent for a rescued row: k = -floor(log2(max(m, sqrt(eps)))), so
+// that max(m, sqrt(eps)) * 2^k lies in [1, 2); floor(log2(sqrt(eps))) is
+// floor(floor(log2(eps)) / 2).  Needs m > 0 or eps > 0, both finite.
 __device__ __forceinline__ int rescue_shift(float m, float eps) {
-  float M = fmaxf(m, sqrtf(eps));
-  int e;
-  (void)frexpf(M, &e);          // M = f * 2^e, f in [0.5, 1)
-  return 1 - e;                 // M * 2^(1-e) lies in [1, 2)
+  int E = -1000;
+  if (m > 0.f) E = floor_log2(m);
+  if (eps > 0.f) {
+    const int le = floor_log2(eps);
+    E = max(E, le >= 0 ? le / 2 : -((1 - le) / 2));
+  }
+  return -E;
 }
 
 // ------------------------------------------------- packed-bf16 row in VGPRs
@@ -266,6 +311,31 @@ struct Bf16Row {
         float lo = ldexpf(bf_lo(p[v][k]), sh), hi = ldexpf(bf_hi(p[v][k]), sh);
         a0 = __builtin_fmaf(lo, lo, a0);
         a1 = __builtin_fmaf(hi, hi, a1);
+      }
+    return a0 + a1;
+  }
+
+  // <p, d> in two fma chains; products of two bf16 values are exact in fp32.
+  __device__ __forceinline__ float dot(const Bf16Row& d) const {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a0 = __builtin_fmaf(bf_lo(p[v][k]), bf_lo(d.p[v][k]), a0);
+        a1 = __builtin_fmaf(bf_hi(p[v][k]), bf_hi(d.p[v][k]), a1);
+      }
+    return a0 + a1;
+  }
+
+  __device__ __forceinline__ float dot_scaled(const Bf16Row& d, int sa, int sb) const {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a0 = __builtin_fmaf(ldexpf(bf_lo(p[v][k]), sa), ldexpf(bf_lo(d.p[v][k]), sb), a0);
+        a1 = __builtin_fmaf(ldexpf(bf_hi(p[v][k]), sa), ldexpf(bf_hi(d.p[v][k]), sb), a1);
       }
     return a0 + a1;
   }
@@ -335,7 +405,7 @@ __device__ __forceinline__ void l2_in_place(Bf16Row<V>& s, float S, float eps,
   if (T == __builtin_inff() || T < kTiny) {       // uniform over the group
     float m = group_max<G>(wave_max(s.maxabs()), gs.next(slot), geo.g, geo.lane);
     s.fence();
-    if (m > 0.f && m < __builtin_inff()) {
+    if ((m > 0.f || eps > 0.f) && m < __builtin_inff()) {
       sh = rescue_shift(m, eps);
       float t[1] = {wave_sum(s.sumsq_scaled(sh))};
       group_sum<G, 1>(t, gs.next(slot), geo.g, geo.lane);
@@ -381,6 +451,97 @@ l2_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int
     group_sum<G, 1>(S, gs.next(slot), geo.g, geo.lane);
     l2_in_place<G, V>(s, S[0], eps, gs, slot, geo);
     s.store(RowBuf(y + row * nvec, row_bytes), off);
+  }
+}
+
+// --------------------------------------------------------- l2_rows gradient
+//
+// Holds the row s (x, or bf16(x + r)) and dy packed in VGPRs; one reduction
+// pass gives S = sum s^2 and P = <s, dy>.  When S + eps or P is out of fp32's
+// comfortable range (S + eps overflowing or below 2^-96, P overflowing), both
+// are summed again with s scaled by 2^sa and dy by 2^sb (sa from
+// max(max|s|, sqrt(eps)), sb from max|dy|, bringing each maximum to [1, 2)):
+// the scaled row gives ds * 2^(sb - sa) exactly, undone by one ldexp.
+
+template <int G, int V, bool RES>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+l2_rows_backward_kernel(const u32x4_t* x, const u32x4_t* r, const u32x4_t* dy, u32x4_t* dx,
+                        int64_t rows, int nvec, float eps) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  int off[V];
+  geo.offsets(off, 16);
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+
+  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
+    const int64_t row = base + geo.rr;
+    if (G == 1 && row >= rows) break;
+    Bf16Row<V> s, d;
+    s.load(RowBuf(x + row * nvec, row_bytes), off);
+    if constexpr (RES) {
+      Bf16Row<V> rv;
+      rv.load(RowBuf(r + row * nvec, row_bytes), off);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          s.p[v][k] = pack_bf16(bf_lo(s.p[v][k]) + bf_lo(rv.p[v][k]),
+                                bf_hi(s.p[v][k]) + bf_hi(rv.p[v][k]));
+    }
+    d.load(RowBuf(dy + row * nvec, row_bytes), off);
+    float acc[2] = {wave_sum(s.sumsq()), wave_sum(s.dot(d))};
+    s.fence();
+    d.fence();
+    group_sum<G, 2>(acc, gs.next(slot), geo.g, geo.lane);
+    float T = acc[0] + eps;
+    float P = acc[1];
+    bool scaled = false;
+    int sa = 0, sb = 0;
+    // uniform over the group; NaN sums enter too, and leave with no rescue
+    if (!(T >= kTiny && T < __builtin_inff() && fabsf(P) < __builtin_inff())) {
+      float m[2] = {wave_max(s.maxabs()), wave_max(d.maxabs())};
+      group_max2<G>(m, gs.next(slot), geo.g, geo.lane);
+      s.fence();
+      d.fence();
+      if ((m[0] > 0.f || eps > 0.f) && m[0] < __builtin_inff() && m[1] < __builtin_inff()) {
+        sa = rescue_shift(m[0], eps);
+        sb = (m[1] > 0.f) ? rescue_shift(m[1], 0.f) : 0;
+        float t[2] = {wave_sum(s.sumsq_scaled(sa)), wave_sum(s.dot_scaled(d, sa, sb))};
+        group_sum<G, 2>(t, gs.next(slot), geo.g, geo.lane);
+        T = t[0] + ldexpf(eps, 2 * sa);
+        P = t[1];
+        scaled = true;
+      }
+    }
+    const float inv = inv_sqrt(T);
+    const float kk = (P * inv) * inv;
+    s.fence();
+    d.fence();
+    if (!scaled) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __builtin_fmaf(-bf_lo(s.p[v][k]), kk, bf_lo(d.p[v][k])) * inv;
+          const float hi = __builtin_fmaf(-bf_hi(s.p[v][k]), kk, bf_hi(d.p[v][k])) * inv;
+          d.p[v][k] = pack_bf16(lo, hi);
+        }
+    } else {
+      const int sh = sa - sb;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float slo = ldexpf(bf_lo(s.p[v][k]), sa), shi = ldexpf(bf_hi(s.p[v][k]), sa);
+          const float dlo = ldexpf(bf_lo(d.p[v][k]), sb), dhi = ldexpf(bf_hi(d.p[v][k]), sb);
+          const float lo = ldexpf(__builtin_fmaf(-slo, kk, dlo) * inv, sh);
+          const float hi = ldexpf(__builtin_fmaf(-shi, kk, dhi) * inv, sh);
+          d.p[v][k] = pack_bf16(lo, hi);
+        }
+    }
+    d.store(RowBuf(dx + row * nvec, row_bytes), off);
   }
 }
 
@@ -498,7 +659,7 @@ slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, 
           for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(u[v][k]));
       }
       m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
-      if (m > 0.f && m < __builtin_inff()) {
+      if ((m > 0.f || eps > 0.f) && m < __builtin_inff()) {
         sh = rescue_shift(m, eps);
         float c0 = 0.f, c1 = 0.f;
         reload_point();
@@ -565,24 +726,43 @@ struct RownormTask {
   int32_t pad_;
 };
 
+// One matrix of a ragged gradient call.
+struct RownormGradTask {
+  const float* w;
+  const float* gain;
+  const uint16_t* dw_eff;
+  float* dw;
+  float* dgain;         // may be null
+  int64_t rows;
+  int32_t cols;
+  float radius;
+  int32_t item_begin;
+  int32_t pad_;
+};
+
 // The tasks of one launch.  Up to kInlineTasks of them travel inside the
 // kernel arguments (no copy, no device allocation, safe to capture in a
 // graph); larger batches point at a table staged in device memory.
 constexpr int kInlineTasks = 48;
-struct RownormArgs {
-  const RownormTask* tasks;      // staged table, or null: use the inline arrays
+template <class Task>
+struct TaskArgs {
+  const Task* tasks;             // staged table, or null: use the inline arrays
   const int32_t* begins;         // staged item_begin array (with `tasks`)
   int32_t ntasks;
   int32_t nitems;
   int32_t inline_begins[kInlineTasks];
-  RownormTask inline_tasks[kInlineTasks];
+  Task inline_tasks[kInlineTasks];
 };
+using RownormArgs = TaskArgs<RownormTask>;
+using RownormGradArgs = TaskArgs<RownormGradTask>;
 static_assert(sizeof(RownormArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+static_assert(sizeof(RownormGradArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Index of the task owning `item`: the number of tasks whose first item is
 // <= item, minus one.  Tasks are in ascending item_begin order; each lane
 // tests one task and a ballot counts them, 64 per pass.
-__device__ __forceinline__ int owning_task(const RownormArgs& a, int item, int lane) {
+template <class Task>
+__device__ __forceinline__ int owning_task(const TaskArgs<Task>& a, int item, int lane) {
   const int32_t* begins = a.tasks != nullptr ? a.begins : a.inline_begins;
   int count = 0;
   for (int base = 0; base < a.ntasks; base += 64) {
@@ -673,6 +853,128 @@ rownorm_kernel(const RownormArgs args) {
       }
       u32x2_t o = {pack_bf16(q[0] * c, q[1] * c), pack_bf16(q[2] * c, q[3] * c)};
       eb.st8(o, off[v] / 2);
+    }
+  }
+}
+
+// ------------------------------------------------ weight rownorm gradient
+//
+// Per row: S = sum w^2 and P = <w, dWe> in one pass (w fp32, dWe bf16), then
+// dg = (rho P) inv, k = (P inv) inv, c = (g rho) inv and
+// dW_j = c (dWe_j - w_j k).  Out-of-range sums are recomputed with w scaled
+// by 2^sa and dWe by 2^sb (as for l2_rows' gradient; no eps here).  A zero
+// row gets exact zeros: the forward scales it by the constant 0.
+
+template <int G, int V>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+rownorm_backward_kernel(const RownormGradArgs args) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  int off[V];
+  geo.offsets(off, 16);
+  const int nitems = args.nitems;
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int lo = __builtin_amdgcn_readfirstlane(owning_task(args, item, geo.lane));
+    const RownormGradTask t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
+    const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
+    if (G == 1 && row >= t.rows) continue;
+    const float gr = t.gain[row] * t.radius;
+    const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
+    const RowBuf eb(t.dw_eff + row * t.cols, (uint32_t)t.cols * 2u);
+    float w[V][4];
+    uint32_t e[V][2];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const f32x4_t q = wb.ld16f(off[v]);
+      w[v][0] = q.x; w[v][1] = q.y; w[v][2] = q.z; w[v][3] = q.w;
+      const u32x2_t b = eb.ld8(off[v] / 2);
+      e[v][0] = b.x; e[v][1] = b.y;
+    }
+    float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      a0 = __builtin_fmaf(w[v][0], w[v][0], a0);
+      a1 = __builtin_fmaf(w[v][1], w[v][1], a1);
+      a0 = __builtin_fmaf(w[v][2], w[v][2], a0);
+      a1 = __builtin_fmaf(w[v][3], w[v][3], a1);
+      p0 = __builtin_fmaf(w[v][0], bf_lo(e[v][0]), p0);
+      p1 = __builtin_fmaf(w[v][1], bf_hi(e[v][0]), p1);
+      p0 = __builtin_fmaf(w[v][2], bf_lo(e[v][1]), p0);
+      p1 = __builtin_fmaf(w[v][3], bf_hi(e[v][1]), p1);
+    }
+    float acc[2] = {wave_sum(a0 + a1), wave_sum(p0 + p1)};
+    group_sum<G, 2>(acc, gs.next(slot), geo.g, geo.lane);
+    float T = acc[0];
+    float P = acc[1];
+    bool scaled = false;
+    int sa = 0, sb = 0;
+    if (!(T >= kTiny && T < __builtin_inff() && fabsf(P) < __builtin_inff())) {
+      float m[2] = {0.f, 0.f};
+      u16x2_t mx = {0, 0};
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m[0] = fmaxf(m[0], fabsf(w[v][k]));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, e[v][0] & 0x7fff7fffu));
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, e[v][1] & 0x7fff7fffu));
+      }
+      m[1] = __uint_as_float((uint32_t)(mx.x > mx.y ? mx.x : mx.y) << 16);
+      m[0] = wave_max(m[0]);
+      m[1] = wave_max(m[1]);
+      group_max2<G>(m, gs.next(slot), geo.g, geo.lane);
+      if (m[0] > 0.f && m[0] < __builtin_inff() && m[1] < __builtin_inff()) {
+        sa = rescue_shift(m[0], 0.f);
+        sb = (m[1] > 0.f) ? rescue_shift(m[1], 0.f) : 0;
+        float c0 = 0.f, c1 = 0.f, q0 = 0.f, q1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const float w0 = ldexpf(w[v][0], sa), w1 = ldexpf(w[v][1], sa);
+          const float w2 = ldexpf(w[v][2], sa), w3 = ldexpf(w[v][3], sa);
+          c0 = __builtin_fmaf(w0, w0, c0);
+          c1 = __builtin_fmaf(w1, w1, c1);
+          c0 = __builtin_fmaf(w2, w2, c0);
+          c1 = __builtin_fmaf(w3, w3, c1);
+          q0 = __builtin_fmaf(w0, ldexpf(bf_lo(e[v][0]), sb), q0);
+          q1 = __builtin_fmaf(w1, ldexpf(bf_hi(e[v][0]), sb), q1);
+          q0 = __builtin_fmaf(w2, ldexpf(bf_lo(e[v][1]), sb), q0);
+          q1 = __builtin_fmaf(w3, ldexpf(bf_hi(e[v][1]), sb), q1);
+        }
+        float tt[2] = {wave_sum(c0 + c1), wave_sum(q0 + q1)};
+        group_sum<G, 2>(tt, gs.next(slot), geo.g, geo.lane);
+        T = tt[0];
+        P = tt[1];
+        scaled = true;
+      }
+    }
+    const bool zero = T == 0.f;                     // after any rescue: every w is 0
+    const float inv = inv_sqrt(T);
+    float dg = (t.radius * P) * inv;
+    if (scaled) dg = ldexpf(dg, -sb);
+    const float kk = zero ? 0.f : (P * inv) * inv;
+    const float c = zero ? 0.f : gr * inv;
+    if (t.dgain != nullptr && geo.g == 0 && geo.lane == 0) t.dgain[row] = zero ? 0.f : dg;
+    const RowBuf ob(t.dw + row * t.cols, (uint32_t)t.cols * 4u);
+    const int sh = sa - sb;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float wv[4] = {w[v][0], w[v][1], w[v][2], w[v][3]};
+      float ev[4] = {bf_lo(e[v][0]), bf_hi(e[v][0]), bf_lo(e[v][1]), bf_hi(e[v][1])};
+      float o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (scaled) {
+          wv[k] = ldexpf(wv[k], sa);
+          ev[k] = ldexpf(ev[k], sb);
+        }
+        o[k] = c * __builtin_fmaf(-wv[k], kk, ev[k]);
+        if (scaled) o[k] = ldexpf(o[k], sh);
+        if (zero) o[k] = 0.f;
+      }
+      const f32x4_t ov = {o[0], o[1], o[2], o[3]};
+      ob.st16(__builtin_bit_cast(u32x4_t, ov), off[v]);
     }
   }
 }

@@ -32,7 +32,14 @@ l2_rows_res_stress        32768x8192: x ~ N(0,1), 1% of entries x1000; 327 rows
                           all-zero in x and r; 327 rows of integers in [-64, 64]
                           with r = 0; r ~ N(0,1) elsewhere
 slerp_rows_8192x4096      as slerp_rows_8192x7168 at width 4096
+l2_rows_res_bwd_8192x4096 x, r as l2_rows_res_8192x4096; upstream dy ~ N(0,1)
+rownorm_gain_bwd_12x4     rownorm_gain_12x4_d768's matrices; dL/dW_eff ~ N(0,1)
+rownorm_gain_bwd_11008x   one 11008x4096 matrix (the DragonScale README's
+4096                      kernel-speed shape), W ~ N(0, sd 0.02), g ~ U(0.5, 2),
+                          dL/dW_eff ~ N(0,1)
 ========================  =======================================================
+
+Upstream gradients (dy, dL/dW_eff) are bf16 values drawn like activations.
 """
 from __future__ import annotations
 
@@ -45,6 +52,7 @@ __all__ = [
     "L2Case", "SlerpCase", "RownormCase",
     "to_bf16_bits", "l2_case", "slerp_case", "rownorm_case",
     "transformer_linears", "stress_l2_case", "WORKLOADS", "make",
+    "L2GradCase", "RownormGradCase", "grad_bits", "l2_grad_case", "rownorm_grad_case",
 ]
 
 
@@ -91,6 +99,35 @@ class RownormCase:
     w: List[np.ndarray]               # float32 [rows_m, cols_m] each
     gain: List[np.ndarray]            # float32 [rows_m] each
     radius: List[float]
+
+    @property
+    def total_rows(self) -> int:
+        return sum(m.shape[0] for m in self.w)
+
+    @property
+    def total_elems(self) -> int:
+        return sum(m.size for m in self.w)
+
+
+@dataclass
+class L2GradCase:
+    """Inputs of the l2_rows gradient: the forward's x, r and the upstream dy."""
+    name: str
+    x: np.ndarray                     # uint16 [rows, cols]
+    r: Optional[np.ndarray]
+    dy: np.ndarray                    # uint16 [rows, cols]
+    eps: float = 1e-6
+    meta: dict = field(default_factory=dict)
+
+
+@dataclass
+class RownormGradCase:
+    """Inputs of the weight gradient: the forward's matrices and dL/dW_eff."""
+    name: str
+    w: List[np.ndarray]
+    gain: List[np.ndarray]
+    radius: List[float]
+    dwe: List[np.ndarray]             # uint16 bf16 bits, shaped like w
 
     @property
     def total_rows(self) -> int:
@@ -185,6 +222,29 @@ def stress_l2_case(rows: int = 32768, cols: int = 8192, seed: int = 1005,
                   xb, rb, eps, meta)
 
 
+def grad_bits(shape, seed: int, sd: float = 1.0) -> np.ndarray:
+    """An upstream gradient: N(0, sd) samples as bf16 bits."""
+    (g,) = _streams(seed, 1)
+    return to_bf16_bits(sd * g.standard_normal(shape))
+
+
+def l2_grad_case(rows: int, cols: int, seed: int, residual: bool = True,
+                 eps: float = 1e-6, name: Optional[str] = None) -> L2GradCase:
+    """x, r drawn as l2_case(rows, cols, seed) does, dy from the stream after them."""
+    fwd = l2_case(rows, cols, seed, residual, eps)
+    dy = grad_bits((rows, cols), seed + 7919)
+    return L2GradCase(name or f"l2_rows{'_res' if residual else ''}_bwd_{rows}x{cols}",
+                      fwd.x, fwd.r, dy, eps)
+
+
+def rownorm_grad_case(shapes, seed: int, radius: float = 1.0,
+                      name: Optional[str] = None) -> RownormGradCase:
+    fwd = rownorm_case(shapes, seed, radius=radius)
+    dwe = [grad_bits(w.shape, seed + 7919 + i) for i, w in enumerate(fwd.w)]
+    return RownormGradCase(name or f"rownorm_gain_bwd_{len(shapes)}", fwd.w, fwd.gain,
+                           fwd.radius, dwe)
+
+
 # name -> (description, builder, seed).  Seeds are 1000 + a fixed number.
 WORKLOADS = {
     "l2_rows_64x1024": (
@@ -209,6 +269,18 @@ WORKLOADS = {
         "slerp_rows, 8192 x 4096 bf16, res ~ N(0,1), out ~ N(0, sd 2), "
         "alpha ~ U(-0.2, 0.2) fp32, eps 1e-6",
         lambda: slerp_case(8192, 4096, 1006, name="slerp_rows_8192x4096")),
+    "l2_rows_res_bwd_8192x4096": (
+        "l2_rows gradient with residual, 8192 x 4096 bf16: x, r, dy ~ N(0,1), eps 1e-6",
+        lambda: l2_grad_case(8192, 4096, 1007, name="l2_rows_res_bwd_8192x4096")),
+    "rownorm_gain_bwd_12x4_d768": (
+        "weight rownorm + gain gradient over 12 pre-norm layers' linears (d 768, d_ff 3072): "
+        "W ~ N(0, sd 0.02), g ~ U(0.5, 2), rho 1, dL/dW_eff ~ N(0,1) bf16",
+        lambda: rownorm_grad_case(transformer_linears(), 1008,
+                                  name="rownorm_gain_bwd_12x4_d768")),
+    "rownorm_gain_bwd_11008x4096": (
+        "weight rownorm + gain gradient, one 11008 x 4096 matrix: W ~ N(0, sd 0.02), "
+        "g ~ U(0.5, 2), rho 1, dL/dW_eff ~ N(0,1) bf16",
+        lambda: rownorm_grad_case([(11008, 4096)], 1009, name="rownorm_gain_bwd_11008x4096")),
 }
 
 

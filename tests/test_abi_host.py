@@ -28,13 +28,14 @@ def L():
 def test_exports_every_declared_function(L):
     names = B.header_functions()
     assert set(names) == {"ds_l2_rows", "ds_slerp_rows", "ds_weight_rownorm_gain",
+                          "ds_l2_rows_backward", "ds_weight_rownorm_gain_backward",
                           "ds_status_string", "ds_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10000
+    assert B.ds_version() == 10100
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -123,6 +124,71 @@ def test_rownorm_valid_args_reach_device_lookup(L):
     good = (A, Bp, 1.0, Bp + 4096, C, 16, 64)
     shared_w = (A, Bp, 1.0, None, C + 65536, 16, 64)      # tied weights: same w, two outputs
     assert L.ds_weight_rownorm_gain(_descs(good, shared_w), 2, None) == B.DS_ERR_DEVICE
+
+
+def test_l2_backward_validation(L):
+    f = L.ds_l2_rows_backward
+    assert f(None, None, C, Bp, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert f(A, None, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert f(A, None, C, None, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert f(A, None, C + 2, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert f(A, Bp + 8, C, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert f(A, None, C, C + 16, 4, 64, 1e-6, None) == B.DS_ERR_ARG      # dx partly over dy
+    assert f(A, None, C, A + 256, 4, 64, 1e-6, None) == B.DS_ERR_ARG     # dx partly over x
+    assert f(A, None, C, Bp, 4, 60, 1e-6, None) == B.DS_ERR_SHAPE
+    assert f(A, None, C, Bp, 4, 64, float("nan"), None) == B.DS_ERR_ARG
+    assert f(None, None, None, None, 0, 64, 1e-6, None) == B.DS_OK
+
+
+@pytest.mark.skipif("not no_device()")
+def test_l2_backward_valid_args_reach_device_lookup(L):
+    f = L.ds_l2_rows_backward
+    assert f(A, None, C, Bp, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE
+    assert f(A, Bp, C, C, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE          # dx == dy
+    assert f(A, Bp, C, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE          # dx == x
+
+
+def _gdescs(*items):
+    arr = (B.RownormGradDesc * len(items))()
+    for i, d in enumerate(items):
+        arr[i] = B.RownormGradDesc(*d)
+    return arr
+
+
+def test_rownorm_backward_validation(L):
+    f = L.ds_weight_rownorm_gain_backward
+    # w, gain, radius, dw_eff, dw, dgain, rows, cols
+    good = (A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64)
+    assert f(_gdescs(good), -1, None) == B.DS_ERR_ARG
+    assert f(None, 0, None) == B.DS_OK
+    assert f(None, 1, None) == B.DS_ERR_NULL
+    assert f(_gdescs((A, Bp, 1.0, C, C + 65536, None, 16, 6)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_gdescs((A, Bp, float("nan"), C, C + 65536, None, 16, 64)), 1, None) == B.DS_ERR_ARG
+    assert f(_gdescs((A, Bp, 1.0, None, C + 65536, None, 16, 64)), 1, None) == B.DS_ERR_NULL
+    assert f(_gdescs((A, Bp, 1.0, C, None, None, 16, 64)), 1, None) == B.DS_ERR_NULL
+    assert f(_gdescs((A, Bp, 1.0, C + 8, C + 65536, None, 16, 64)), 1, None) == B.DS_ERR_ALIGN
+    assert f(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4098, 16, 64)), 1, None) == B.DS_ERR_ALIGN
+    # dw over dw_eff, dgain over gain, dw over w
+    assert f(_gdescs((A, Bp, 1.0, C, C + 512, None, 16, 64)), 1, None) == B.DS_ERR_ARG
+    assert f(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 16, 16, 64)), 1, None) == B.DS_ERR_ARG
+    assert f(_gdescs((A, Bp, 1.0, C, A, None, 16, 64)), 1, None) == B.DS_ERR_ARG
+    # one matrix's output over another matrix's input
+    other = (A + 8192, Bp + 1024, 1.0, C + 8192, A + 2048, None, 16, 64)
+    assert f(_gdescs(good, other), 2, None) == B.DS_ERR_ARG
+    assert f(_gdescs((None, None, 1.0, None, None, None, 0, 64)), 1, None) == B.DS_OK
+
+
+@pytest.mark.skipif("not no_device()")
+def test_rownorm_backward_valid_args_reach_device_lookup(L):
+    good = (A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64)
+    tied = (A, Bp, 1.0, C, C + 131072, None, 16, 64)       # same inputs, other outputs
+    assert L.ds_weight_rownorm_gain_backward(_gdescs(good, tied), 2, None) == B.DS_ERR_DEVICE
+
+
+def test_rownorm_output_over_other_input_refused(L):
+    good = (A, Bp, 1.0, Bp + 4096, C, 16, 64)
+    over = (A + 8192, Bp + 1024, 1.0, None, A, 16, 64)     # its W_eff over the first w
+    assert L.ds_weight_rownorm_gain(_descs(good, over), 2, None) == B.DS_ERR_ARG
 
 
 def test_binding_raises_on_missing_library(monkeypatch):

@@ -157,6 +157,7 @@ def test_extreme_magnitudes_and_eps(B):
     rows.append(big)
     sub = np.zeros(cols); sub[:7] = 2.0 ** -133 * np.arange(1, 8)       # bf16 subnormals
     rows.append(sub)
+    rows.append(np.zeros(cols))                                         # eps alone
     x = bf16_rne(np.array(rows))
     for eps in (1e-6, 0.0, 2.0 ** -140, 1.0, 3.0e38):
         announce("l2_rows extremes eps", eps)

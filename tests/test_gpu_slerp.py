@@ -113,3 +113,17 @@ def test_extreme_alpha_rescaled(B):
     alpha = np.full(c.cols, 3.0e37, np.float32)
     announce("slerp_rows huge alpha")
     full_check(run(B, c.res, c.out, alpha), c.res, c.out, alpha, 1e-6, "huge alpha")
+
+
+def test_zero_rows_tiny_eps(B):
+    """All-zero res/out rows with eps far below 2^-96 (down to fp32
+    subnormals): the inverse lengths come from eps alone, after rescaling."""
+    c = inputs.slerp_case(6, 512, 704)
+    res, out = c.res.copy(), c.out.copy()
+    res[0] = 0
+    out[1] = 0
+    res[2] = 0
+    out[2] = 0
+    for eps in (2.0 ** -100, 2.0 ** -140, 1e-6):
+        announce("slerp_rows zero rows eps", eps)
+        full_check(run(B, res, out, c.alpha, eps), res, out, c.alpha, eps, f"eps={eps}")
