@@ -3,6 +3,8 @@
 A step is one pass of the path over one batch at the workload the headline
 metric is quoted on: ds_l2_rows with the fused residual on 8192 x 4096 bf16
 rows, then ds_slerp_rows on 8192 x 4096 bf16 rows (synthetic, seeded inputs).
+The other shapes, the weight op and the gradients are timed after the
+headline steps and reported in ``ops``.
 Inputs are resident in HBM before timing starts; the steps rotate over
 several buffer sets whose total is well above the 256 MB last-level cache, so
 every launch streams from HBM.  The weight op (ds_weight_rownorm_gain over a
@@ -33,9 +35,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 ROWS, COLS = 8192, 4096
 EPS = 1e-6
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_l2_slerp_rownorm.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
-                  "inst_rownorm.hip", "ds_rows.hip"]
+                  "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "ds_rows.hip"]
 
 
 def kernel_hash() -> str:
@@ -238,8 +240,8 @@ def main():
 
     # ---- the other workloads' shapes, beside the headline (random bf16 rows of
     # the same shapes; one buffer set rotation each): reported, not in `value`
-    def shaped_us(rows, cols, fn, nsets, n=40):
-        bufs = [[torch.randn(rows, cols, device=dev).to(torch.bfloat16) for _ in range(3)]
+    def shaped_us(rows, cols, fn, nsets, n=40, ntens=3):
+        bufs = [[torch.randn(rows, cols, device=dev).to(torch.bfloat16) for _ in range(ntens)]
                 for _ in range(nsets)]
         torch.cuda.synchronize()
         for i in range(4):
@@ -261,6 +263,76 @@ def main():
         t[0].data_ptr(), t[1].data_ptr(), alpha7.data_ptr(), t[2].data_ptr(), r, c, eps, sp), 4)
     c5_us = shaped_us(32768, 8192, lambda t, r, c: L.ds_l2_rows(
         t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), r, c, eps, sp), 2, n=20)
+    # the l2_rows gradient at the headline shape: x, r, dy read, dx written
+    c2b_us = shaped_us(ROWS, COLS, lambda t, r, c: L.ds_l2_rows_backward(
+        t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), t[3].data_ptr(), r, c, eps, sp),
+        4, n=100, ntens=4)
+    ops["l2_rows_res_bwd_8192x4096"] = op(c2b_us, ROWS * COLS * 8, ROWS)
+
+    # ---- weight gradients: the 48 linears, and the one 11008 x 4096 matrix the
+    # DragonScale README times forward + backward (device-random fp32 weights
+    # N(0, 0.02), gains U(0.5, 2), bf16 upstream gradients N(0, 1))
+    gen = torch.Generator(device=dev).manual_seed(4242)
+
+    def weight_sets(shapes, nsets):
+        out = []
+        for _ in range(nsets):
+            ws = [0.02 * torch.randn(sh, device=dev, generator=gen) for sh in shapes]
+            gs = [0.5 + 1.5 * torch.rand(sh[0], device=dev, generator=gen) for sh in shapes]
+            de = [torch.randn(sh, device=dev, generator=gen).to(torch.bfloat16) for sh in shapes]
+            fw = (B.RownormDesc * len(ws))()
+            bw = (B.RownormGradDesc * len(ws))()
+            keep = [ws, gs, de]
+            for i, w in enumerate(ws):
+                n_out = torch.empty(w.shape[0], device=dev)
+                e_out = torch.empty(w.shape, dtype=torch.int16, device=dev)
+                dw = torch.empty_like(w)
+                dg = torch.empty(w.shape[0], device=dev)
+                keep += [n_out, e_out, dw, dg]
+                fw[i] = B.RownormDesc(w.data_ptr(), gs[i].data_ptr(), 1.0, n_out.data_ptr(),
+                                      e_out.data_ptr(), w.shape[0], w.shape[1])
+                bw[i] = B.RownormGradDesc(w.data_ptr(), gs[i].data_ptr(), 1.0, de[i].data_ptr(),
+                                          dw.data_ptr(), dg.data_ptr(), w.shape[0], w.shape[1])
+            out.append((fw, bw, len(ws), keep))
+        torch.cuda.synchronize()
+        return out
+
+    def ragged_us(wsets, which, n):
+        call = L.ds_weight_rownorm_gain if which == 0 else L.ds_weight_rownorm_gain_backward
+        for i in range(4):
+            assert call(wsets[i % len(wsets)][which], wsets[i % len(wsets)][2], sp) == 0
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for i in range(n):
+            call(wsets[i % len(wsets)][which], wsets[i % len(wsets)][2], sp)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    lin = inputs.transformer_linears()
+    n_el = sum(r * c for r, c in lin)
+    n_rows = sum(r for r, _ in lin)
+    wsets = weight_sets(lin, 3)
+    rnb_us = ragged_us(wsets, 1, 60)
+    ops["weight_rownorm_gain_bwd_12x4_d768"] = op(rnb_us, n_el * 10 + n_rows * 8, n_rows)
+    del wsets
+    big = [(11008, 4096)]
+    wsets = weight_sets(big, 4)
+    f_us = ragged_us(wsets, 0, 40)
+    b_us = ragged_us(wsets, 1, 40)
+    del wsets
+    torch.cuda.empty_cache()
+    n_big = 11008 * 4096
+    ops["weight_rownorm_gain_11008x4096"] = op(f_us, n_big * 6 + 11008 * 8, 11008)
+    ops["weight_rownorm_gain_bwd_11008x4096"] = op(b_us, n_big * 10 + 11008 * 8, 11008)
+    ops["weight_rownorm_gain_fwd_bwd_11008x4096"] = op(
+        f_us + b_us, n_big * 16 + 11008 * 16, 11008)
+    ops["weight_rownorm_gain_fwd_bwd_11008x4096"]["note"] = (
+        "forward (fp32 W read, bf16 W_eff and fp32 norms written) plus backward (W and bf16 "
+        "dW_eff read, fp32 dW and dg written): the op the DragonScale README reports at 85-96% "
+        "of the card's bandwidth on V100/2080 Ti/3090/4090, where its W_eff is fp32")
+
     ops["l2_rows_64x1024"] = op(c1_us, 64 * 1024 * 4, 64)
     ops["l2_rows_64x1024"]["note"] = "latency-bound: one small launch"
     ops["slerp_rows_8192x7168"] = op(c3_us, 8192 * 7168 * 6 + 7168 * 4, 8192)
