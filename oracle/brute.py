@@ -21,7 +21,7 @@ from typing import List, Optional, Sequence, Tuple
 
 __all__ = ["bits_to_fraction", "round_fraction", "bf16_of", "fp32_of",
            "l2_row", "slerp_row", "rownorm_row", "l2_backward_row", "rownorm_backward_row",
-           "NEAR_TIE_REL"]
+           "gate_row", "swiglu_row", "NEAR_TIE_REL"]
 
 PREC = 60
 NEAR_TIE_REL = Fraction(1, 10 ** 12)     # flag values this close to a midpoint
@@ -231,3 +231,44 @@ def rownorm_backward_row(w: Sequence[float], g: float, rho: float, dwe_bits: Seq
             out.append(v)
             near.append(n)
     return out, dg, near, near_g
+
+
+# ------------------------------------------------------- activation rows
+
+def _sigmoid_exact(x: Fraction) -> Fraction:
+    """1 / (1 + exp(-x)) at PREC digits (exp from the decimal module)."""
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        return Fraction(Decimal(1) / (Decimal(1) + (-_dec(x)).exp()))
+
+
+def _fp32_product(v_bits: int, scale: float) -> Fraction:
+    """The IEEE fp32 product of a bf16 value and an fp32 scale, exactly."""
+    return fp32_of(bits_to_fraction(int(v_bits)) * f32_to_fraction(float(scale)))[0]
+
+
+def gate_row(o_bits: Sequence[int], g_bits: Sequence[int], sg: Sequence[float], eps32: float
+             ) -> Tuple[List[Fraction], List[bool]]:
+    """bf16(l2(bf16(o * sigmoid(fp32(g * sg))))) exactly, with near-tie flags."""
+    t, near_t = [], []
+    for ob, gb, sc in zip(o_bits, g_bits, sg):
+        x = _fp32_product(gb, sc)
+        v, n = bf16_of(bits_to_fraction(int(ob)) * _sigmoid_exact(x))
+        t.append(v)
+        near_t.append(n)
+    y, near = _l2_exact(t, f32_to_fraction(eps32))
+    return y, [a or any(near_t) for a in near]
+
+
+def swiglu_row(g_bits: Sequence[int], u_bits: Sequence[int], sug: Sequence[float],
+               suu: Sequence[float], eps32: float) -> Tuple[List[Fraction], List[bool]]:
+    """bf16(l2(bf16(silu(a) * b))), a = bf16(fp32(g sug)), b = bf16(fp32(u suu)), exactly."""
+    p, near_p = [], []
+    for gb, ub, s1, s2 in zip(g_bits, u_bits, sug, suu):
+        a = bf16_of(_fp32_product(gb, s1))[0]
+        b = bf16_of(_fp32_product(ub, s2))[0]
+        v, n = bf16_of(a * _sigmoid_exact(a) * b)
+        p.append(v)
+        near_p.append(n)
+    y, near = _l2_exact(p, f32_to_fraction(eps32))
+    return y, [a or any(near_p) for a in near]

@@ -39,7 +39,8 @@ from .bf16 import bf16_rne, bf16_value
 
 __all__ = ["eps_as_passed", "l2_rows", "slerp_rows", "slerp_rows_detail",
            "weight_rownorm_gain", "sum_sq", "l2_backward_values", "l2_rows_backward",
-           "rownorm_backward_values", "weight_rownorm_gain_backward"]
+           "rownorm_backward_values", "weight_rownorm_gain_backward",
+           "gate_gated_row", "gate_l2_rows", "swiglu_product_row", "swiglu_l2_rows"]
 
 
 def eps_as_passed(eps: float) -> float:
@@ -217,3 +218,61 @@ def weight_rownorm_gain_backward(w: Sequence[np.ndarray], gain: Sequence[np.ndar
             dws.append(dw.astype(np.float32))
             dgs.append(dg.astype(np.float32))
     return dws, dgs
+
+
+# ------------------------------------------------------- activation rows
+#
+# TensorFold PR #1260, the commit adding two activation rows for Dory:
+#   gate_l2_rows    out = bf16(l2(bf16(o * sigmoid(g * sg))))   over the whole row
+#   swiglu_l2_rows  out = bf16(l2(bf16(silu(bf16(g * sug)) * bf16(u * suu))))
+# with sigmoid(x) = 1 / (1 + exp(-x)) and silu(x) = x / (1 + exp(-x)), and fp32
+# scale vectors (one value per column) formed by the caller.
+#
+# Readings: a product of a bf16 row by an fp32 scale vector is one IEEE fp32
+# multiply (the form torch computes bf16 * fp32 in), rounded to bf16 where
+# the formula names bf16; the oracle does that multiply in numpy float32.
+# Everything after it up to the next bf16 rounding is float64 (exp from the
+# float64 library, one rounding per operation).
+
+def _sigmoid64(x: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def _f32_scale(v_bits: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """fp32(bf16 value * fp32 scale), the product rounded once in binary32."""
+    with np.errstate(all="ignore"):
+        return (bf16_value(v_bits).astype(np.float32)
+                * np.asarray(scale, dtype=np.float32)).astype(np.float64)
+
+
+def gate_gated_row(o_bits: np.ndarray, g_bits: np.ndarray, sg: np.ndarray) -> np.ndarray:
+    """bf16 bits of the gated row t = bf16(o * sigmoid(fp32(g * sg)))."""
+    o = bf16_value(np.atleast_2d(o_bits))
+    x = _f32_scale(np.atleast_2d(g_bits), sg)
+    with np.errstate(all="ignore"):
+        return bf16_rne(o * _sigmoid64(x))
+
+
+def gate_l2_rows(o_bits: np.ndarray, g_bits: np.ndarray, sg: np.ndarray,
+                 eps: float = 1e-6) -> np.ndarray:
+    """bf16 bits of l2 over each gated row (all heads of the row at once)."""
+    t = bf16_value(gate_gated_row(o_bits, g_bits, sg))
+    return bf16_rne(_l2_of_values(t, eps_as_passed(eps))).reshape(np.shape(o_bits))
+
+
+def swiglu_product_row(g_bits: np.ndarray, u_bits: np.ndarray, sug: np.ndarray,
+                       suu: np.ndarray) -> np.ndarray:
+    """bf16 bits of p = bf16(silu(a) * b), a = bf16(fp32(g * sug)), b = bf16(fp32(u * suu))."""
+    a = bf16_value(bf16_rne(_f32_scale(np.atleast_2d(g_bits), sug)))
+    b = bf16_value(bf16_rne(_f32_scale(np.atleast_2d(u_bits), suu)))
+    with np.errstate(all="ignore"):
+        silu = a * _sigmoid64(a)
+        return bf16_rne(silu * b)
+
+
+def swiglu_l2_rows(g_bits: np.ndarray, u_bits: np.ndarray, sug: np.ndarray, suu: np.ndarray,
+                   eps: float = 1e-6) -> np.ndarray:
+    """bf16 bits of l2 over each SwiGLU product row."""
+    p = bf16_value(swiglu_product_row(g_bits, u_bits, sug, suu))
+    return bf16_rne(_l2_of_values(p, eps_as_passed(eps))).reshape(np.shape(g_bits))
