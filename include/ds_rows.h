@@ -19,6 +19,10 @@
  *                         W_eff = diag(g) r W / ||W||_row over a ragged batch of
  *                         weight matrices in one call ("Kernels and speed": the
  *                         weights of every layer in a few launches).
+ *  ds_gate_l2_rows        TensorFold PR #1260, the commit adding two activation
+ *  ds_swiglu_l2_rows      rows for Dory: the output gate and the scaled SwiGLU,
+ *                         each rounded to bf16 and then L2-normalised over the
+ *                         whole row.
  *  ds_l2_rows_backward    the gradient of ds_l2_rows' s -> s / sqrt(sum s^2 +
  *                         eps): ds = (dy - s <s,dy> / D^2) / D, shared by x
  *                         and r (the bf16 rounding of s passes it through).
@@ -73,7 +77,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10100          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10200          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -137,6 +141,46 @@ int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y,
 int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha,
                   uint16_t* h, int64_t rows, int64_t cols, float eps,
                   ds_stream_t stream);
+
+/*
+ * ds_gate_l2_rows -- the gated attention output, unit-length per row.
+ * (TensorFold PR #1260, the activation-row commit: Dory's output gate, then
+ * the row's L2 norm over all its heads.)
+ *
+ *   t_j = bf16(o_j * sigmoid(g_j * sg_j))    g_j * sg_j one fp32 product;
+ *                                            sigmoid(x) = 1 / (1 + expf(-x))
+ *                                            in fp32, IEEE division
+ *   y   = bf16(t / sqrt(sum_j t_j^2 + eps))
+ *
+ * o, g, y : row-major [rows, cols] bf16 bit patterns, contiguous, 16-byte
+ *           aligned; y may be the same buffer as o or g.
+ * sg      : [cols] fp32 scale vector shared by all rows (formed by the caller),
+ *           16-byte aligned, not overlapping y.
+ * rows, cols, eps, stream : as for ds_l2_rows.
+ *
+ * expf is the device library's (measured within 1 ulp on gfx950); an argument
+ * beyond fp32's exp range gives sigmoid 0, as fp32 arithmetic does.
+ */
+int ds_gate_l2_rows(const uint16_t* o, const uint16_t* g, const float* sg, uint16_t* y,
+                    int64_t rows, int64_t cols, float eps, ds_stream_t stream);
+
+/*
+ * ds_swiglu_l2_rows -- the scaled SwiGLU product, unit-length per row.
+ * (TensorFold PR #1260, the activation-row commit: Dory's MLP.)
+ *
+ *   a_j = bf16(g_j * sug_j),  b_j = bf16(u_j * suu_j)     fp32 products, rounded
+ *   p_j = bf16(silu(a_j) * b_j)        silu(x) = x / (1 + expf(-x)) in fp32,
+ *                                      IEEE division
+ *   y   = bf16(p / sqrt(sum_j p_j^2 + eps))
+ *
+ * g, u, y  : row-major [rows, cols] bf16 bit patterns, contiguous, 16-byte
+ *            aligned; y may be the same buffer as g or u.
+ * sug, suu : [cols] fp32 scale vectors shared by all rows, 16-byte aligned,
+ *            not overlapping y.
+ * rows, cols, eps, stream : as for ds_l2_rows.
+ */
+int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, const float* suu,
+                      uint16_t* y, int64_t rows, int64_t cols, float eps, ds_stream_t stream);
 
 /*
  * One weight matrix of a ds_weight_rownorm_gain call.

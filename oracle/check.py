@@ -49,7 +49,8 @@ __all__ = ["contract_bf16", "contract_rel", "Report", "admissible_l2_rows",
            "admissible_slerp_rows", "admissible_rownorm", "default_depth",
            "ordered", "slerp_unique_mask", "GRAD_SLACK", "l2_grad_terms",
            "rownorm_grad_terms", "contract_grad", "admissible_l2_backward",
-           "admissible_rownorm_backward"]
+           "admissible_rownorm_backward", "EXPF_ULPS", "gate_candidates", "swiglu_candidates",
+           "admissible_act_rows", "act_unique_mask"]
 
 
 def default_depth(cols: int) -> int:
@@ -606,3 +607,123 @@ def admissible_rownorm_backward(got_dw, got_dg, w, g, rho, dweff_bits,
         lo, hi = _tangent_bounds(row, d, k_lo, k_hi, c_lo, c_hi)
         mark(rw, ~_f32_inside(gw[i], lo, hi), base)
     return rw, rg
+
+
+# ---------------------------------------------------------- activation rows
+#
+# The fp32 run modelled for gate_l2_rows and swiglu_l2_rows: the products by
+# the fp32 scale vectors are IEEE multiplies (deterministic, as the oracle
+# does them); expf is within EXPF_ULPS units in the last place of exp, may
+# return +inf where exp exceeds fp32's largest value, and carries 2**-149
+# steps in the subnormal range; 1 + e, the IEEE division and the product by
+# o (or b) round once each.  That bounds the pre-norm value of each element;
+# its admissible bf16 values run from bf16(lo) to bf16(hi), and the output
+# is checked over every such choice as slerp's is over a and b.
+
+EXPF_ULPS = 2.0     # the device expf measured within 1.0 ulp over 23M arguments on gfx950
+F32_MAX = float(np.finfo(np.float32).max)
+
+
+def _expf_bounds(v):
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(v)
+        rel = EXPF_ULPS * 2.0 ** -23
+        lo = np.maximum(e * (1 - rel) - EXPF_ULPS * ETA, 0.0)
+        hi = e * (1 + rel) + EXPF_ULPS * ETA
+    return lo, np.where(hi >= F32_MAX, np.inf, hi)
+
+
+def _one_plus_bounds(e_lo, e_hi):
+    """Bounds of fl(1 + e), e >= 0."""
+    return (1 + e_lo) * (1 - U), (1 + e_hi) * (1 + U)
+
+
+def _outward(lo, hi):
+    lo = np.where(lo >= 0, lo * (1 - U), lo * (1 + U)) * (1 + np.sign(-lo) * F64_WIDEN) - ETA
+    hi = np.where(hi >= 0, hi * (1 + U), hi * (1 - U)) * (1 + np.sign(hi) * F64_WIDEN) + ETA
+    return lo, hi
+
+
+def gate_candidates(o_bits, g_bits, sg):
+    """Float64 values of the lowest and highest admissible gated-row bf16 value."""
+    from .rows import _f32_scale
+    o = bf16_value(np.atleast_2d(o_bits))
+    x = _f32_scale(np.atleast_2d(g_bits), sg)
+    e_lo, e_hi = _expf_bounds(-x)
+    d_lo, d_hi = _one_plus_bounds(e_lo, e_hi)
+    with np.errstate(all="ignore"):
+        r_lo, r_hi = _outward(1.0 / d_hi, 1.0 / d_lo)
+    r_lo = np.maximum(r_lo, 0.0)
+    lo, hi = _product_bounds(o, o, r_lo, r_hi)
+    return bf16_value(bf16_rne(lo)), bf16_value(bf16_rne(hi))
+
+
+def swiglu_candidates(g_bits, u_bits, sug, suu):
+    """Float64 values of the lowest and highest admissible SwiGLU product bf16 value."""
+    from .rows import _f32_scale
+    a = bf16_value(bf16_rne(_f32_scale(np.atleast_2d(g_bits), sug)))
+    b = bf16_value(bf16_rne(_f32_scale(np.atleast_2d(u_bits), suu)))
+    e_lo, e_hi = _expf_bounds(-a)
+    d_lo, d_hi = _one_plus_bounds(e_lo, e_hi)
+    with np.errstate(all="ignore"):
+        q1, q2 = a / d_hi, a / d_lo
+        s_lo, s_hi = _outward(np.minimum(q1, q2), np.maximum(q1, q2))
+        s_lo = np.where(a == 0, 0.0, s_lo)
+        s_hi = np.where(a == 0, 0.0, s_hi)
+    lo, hi = _product_bounds(s_lo, s_hi, b, b)
+    return bf16_value(bf16_rne(lo)), bf16_value(bf16_rne(hi))
+
+
+def act_unique_mask(c_lo, c_hi) -> np.ndarray:
+    """Elements whose pre-norm value has exactly one admissible bf16 value."""
+    return ordered(bf16_rne(c_lo)) == ordered(bf16_rne(c_hi))
+
+
+def admissible_act_rows(got_bits, c_lo, c_hi, exact_bits=None, finite_rows=None,
+                        eps: float = 1e-6, depth: Optional[int] = None) -> Report:
+    """Strict check of l2 over rows whose elements lie in [c_lo, c_hi] (bf16 values).
+
+    Rows flagged False in ``finite_rows`` are compared with ``exact_bits``
+    (NaN by position, values exactly).
+    """
+    got = np.atleast_2d(got_bits)
+    c_lo = np.atleast_2d(c_lo)
+    c_hi = np.atleast_2d(c_hi)
+    cols = got.shape[1]
+    depth = default_depth(cols) if depth is None else depth
+    eps64 = eps_as_passed(eps)
+    rep = Report()
+    for i in range(got.shape[0]):
+        base = i * cols
+        fin = np.isfinite(c_lo[i]).all() and np.isfinite(c_hi[i]).all()
+        if finite_rows is not None:
+            fin = fin and bool(finite_rows[i])
+        lo_i, hi_i = c_lo[i], c_hi[i]
+        if not fin or (eps64 == 0 and not (lo_i.any() or hi_i.any())):
+            _judge(got[i], lo_i, lo_i, exact_bits[i], np.ones(cols, bool), False, base, rep)
+            continue
+        sq_a, sq_b = lo_i ** 2, hi_i ** 2
+        sq_lo = np.where((lo_i <= 0) & (hi_i >= 0), 0.0, np.minimum(sq_a, sq_b))
+        s_lo, s_hi = _sum_bounds(sq_lo, np.maximum(sq_a, sq_b), depth)
+        inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, eps64)
+        g = ordered(got[i])
+        outs = []
+        width = np.zeros(cols, np.int64)
+        for c in (lo_i, hi_i):
+            lo, hi = _product_bounds(c, c, inv_lo, inv_hi)
+            ol, oh = ordered(bf16_rne(lo)), ordered(bf16_rne(hi))
+            outs.append((ol, oh))
+            width = np.maximum(width, oh - ol + 1)
+        hull_lo = np.minimum(outs[0][0], outs[1][0])
+        hull_hi = np.maximum(outs[0][1], outs[1][1])
+        inside = (g >= hull_lo) & (g <= hull_hi)
+        many = ordered(bf16_rne(hi_i)) - ordered(bf16_rne(lo_i)) > 1
+        bad = np.nonzero(~inside)[0]
+        rep.n += cols
+        rep.outside += bad.size
+        rep.two += int(((hull_hi - hull_lo) == 1).sum())
+        rep.loose += int((width > 2).sum())
+        rep.wide += int(many.sum())
+        for j in bad[: max(0, 20 - len(rep.first_bad))]:
+            rep.first_bad.append(int(base + j))
+    return rep

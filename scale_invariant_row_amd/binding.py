@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.ds_slerp_rows.restype = ctypes.c_int
         L.ds_weight_rownorm_gain.argtypes = [ctypes.POINTER(RownormDesc), ctypes.c_int32, vp]
         L.ds_weight_rownorm_gain.restype = ctypes.c_int
+        L.ds_gate_l2_rows.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
+        L.ds_gate_l2_rows.restype = ctypes.c_int
+        L.ds_swiglu_l2_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, vp]
+        L.ds_swiglu_l2_rows.restype = ctypes.c_int
         L.ds_l2_rows_backward.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
         L.ds_l2_rows_backward.restype = ctypes.c_int
         L.ds_weight_rownorm_gain_backward.argtypes = [ctypes.POINTER(RownormGradDesc),
@@ -307,3 +311,48 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
         st = lib().ds_weight_rownorm_gain_backward(descs, n, _stream_of(ws[0], stream))
     _check(st, "ds_weight_rownorm_gain_backward")
     return list(dw), list(dgain)
+
+
+def _col_vector(v, cols, like, name):
+    torch = _torch()
+    if v.dtype != torch.float32 or v.dim() != 1 or v.shape[0] != cols \
+            or not v.is_contiguous() or v.device != like.device:
+        raise ValueError(f"{name}: expected a contiguous fp32 [cols] tensor on the rows' device")
+
+
+def ds_gate_l2_rows(o, g, sg, eps: float = 1e-6, out=None, stream=None):
+    """y = bf16(l2(bf16(o * sigmoid(g * sg)))) per row (sg: fp32 [cols])."""
+    torch = _torch()
+    _bf16_2d(o, "o")
+    _bf16_2d(g, "g")
+    _same(o, g, "g")
+    _col_vector(sg, o.shape[1], o, "sg")
+    if out is None:
+        out = torch.empty_like(o)
+    _bf16_2d(out, "out")
+    _same(o, out, "out")
+    with torch.cuda.device(o.device):
+        st = lib().ds_gate_l2_rows(o.data_ptr(), g.data_ptr(), sg.data_ptr(), out.data_ptr(),
+                                   o.shape[0], o.shape[1], float(eps), _stream_of(o, stream))
+    _check(st, "ds_gate_l2_rows")
+    return out
+
+
+def ds_swiglu_l2_rows(g, u, sug, suu, eps: float = 1e-6, out=None, stream=None):
+    """y = bf16(l2(bf16(silu(bf16(g * sug)) * bf16(u * suu)))) per row."""
+    torch = _torch()
+    _bf16_2d(g, "g")
+    _bf16_2d(u, "u")
+    _same(g, u, "u")
+    _col_vector(sug, g.shape[1], g, "sug")
+    _col_vector(suu, g.shape[1], g, "suu")
+    if out is None:
+        out = torch.empty_like(g)
+    _bf16_2d(out, "out")
+    _same(g, out, "out")
+    with torch.cuda.device(g.device):
+        st = lib().ds_swiglu_l2_rows(g.data_ptr(), u.data_ptr(), sug.data_ptr(), suu.data_ptr(),
+                                     out.data_ptr(), g.shape[0], g.shape[1], float(eps),
+                                     _stream_of(g, stream))
+    _check(st, "ds_swiglu_l2_rows")
+    return out

@@ -392,6 +392,59 @@ int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha, 
                                               grid_for(units, cus), (hipStream_t)stream));
 }
 
+namespace {
+
+// Checks shared by the two activation rows: two bf16 input rows, one or two
+// fp32 column vectors, one bf16 output that may be exactly either input.
+int check_act(const uint16_t* a, const uint16_t* b, const float* s0, const float* s1, uint16_t* y,
+              int64_t rows, int64_t cols, float eps, bool two_scales) {
+  int st = check_matrix(rows, cols, 8, 2);
+  if (st != DS_OK) return st;
+  if (!finite_nonneg(eps)) return DS_ERR_ARG;
+  if (rows == 0) return DS_OK;
+  if (a == nullptr || b == nullptr || s0 == nullptr || y == nullptr || (two_scales && s1 == nullptr))
+    return DS_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(s0, 16) || !aligned(y, 16) ||
+      (two_scales && !aligned(s1, 16)))
+    return DS_ERR_ALIGN;
+  const size_t bytes = (size_t)rows * (size_t)cols * 2;
+  if (!same_or_disjoint(y, a, bytes) || !same_or_disjoint(y, b, bytes)) return DS_ERR_ARG;
+  if (overlaps(y, bytes, s0, (size_t)cols * 4) || (two_scales && overlaps(y, bytes, s1, (size_t)cols * 4)))
+    return DS_ERR_ARG;
+  return DS_OK;
+}
+
+}  // namespace
+
+int ds_gate_l2_rows(const uint16_t* o, const uint16_t* g, const float* sg, uint16_t* y,
+                    int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
+  int st = check_act(o, g, sg, nullptr, y, rows, cols, eps, false);
+  if (st != DS_OK || rows == 0) return st;
+  const Shape s = dsr::pick_bf16_shape(cols / 8);
+  if (!s.ok()) return DS_ERR_SHAPE;
+  int cus = 0;
+  if ((st = device_cus(&cus)) != DS_OK) return st;
+  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  (void)hipGetLastError();
+  return launch_status(dsr::launch_gate_l2_rows(s, o, g, sg, y, rows, (int)(cols / 8), eps,
+                                                grid_for(units, cus), (hipStream_t)stream));
+}
+
+int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, const float* suu,
+                      uint16_t* y, int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
+  int st = check_act(g, u, sug, suu, y, rows, cols, eps, true);
+  if (st != DS_OK || rows == 0) return st;
+  const Shape s = dsr::pick_bf16_shape(cols / 8);
+  if (!s.ok()) return DS_ERR_SHAPE;
+  int cus = 0;
+  if ((st = device_cus(&cus)) != DS_OK) return st;
+  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  (void)hipGetLastError();
+  return launch_status(dsr::launch_swiglu_l2_rows(s, g, u, sug, suu, y, rows, (int)(cols / 8),
+                                                  eps, grid_for(units, cus),
+                                                  (hipStream_t)stream));
+}
+
 int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t stream) {
   if (n < 0) return DS_ERR_ARG;
   if (n == 0) return DS_OK;

@@ -1,5 +1,5 @@
-"""Writes inst_l2.hip, inst_slerp.hip, inst_rownorm.hip, inst_l2_bwd.hip and
-inst_rownorm_bwd.hip: one launcher per op
+"""Writes inst_l2.hip, inst_slerp.hip, inst_rownorm.hip, inst_l2_bwd.hip,
+inst_rownorm_bwd.hip and inst_act.hip: one launcher per op
 with a case for every kernel shape (G waves per row, V vectors per lane) that
 launch.hpp's shape policy returns for some width up to DS_MAX_COLS, found by
 evaluating the policy (reproduced below from launch.hpp's constants) at every
@@ -169,8 +169,39 @@ hipError_t launch_rownorm_backward(Shape s, const RownormGradArgs& args, int gri
 
 }  // namespace dsr
 '''
+    act = HEAD.format(what="gate and SwiGLU activation rows") + '''
+template <int G, int V, Act A>
+static hipError_t run(const void* in0, const void* in1, const float* s0, const float* s1, void* y,
+                      int64_t rows, int nvec, float eps, int grid, hipStream_t stream) {
+  constexpr int T = Geo<G>::THREADS;
+  act_l2_rows_kernel<G, V, A><<<grid, T, 0, stream>>>(
+      (const u32x4_t*)in0, (const u32x4_t*)in1, (const f32x4_t*)s0, (const f32x4_t*)s1,
+      (u32x4_t*)y, rows, nvec, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_l2_rows(Shape s, const void* o, const void* g, const float* sg, void* y,
+                               int64_t rows, int nvec, float eps, int grid, hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(bf16, "return run<{G}, {V}, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const float* sug,
+                                 const float* suu, void* y, int64_t rows, int nvec, float eps,
+                                 int grid, hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(bf16, "return run<{G}, {V}, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsr
+'''
     for name, text in (("inst_l2.hip", l2), ("inst_slerp.hip", sl), ("inst_rownorm.hip", rn),
-                       ("inst_l2_bwd.hip", l2b), ("inst_rownorm_bwd.hip", rnb)):
+                       ("inst_l2_bwd.hip", l2b), ("inst_rownorm_bwd.hip", rnb),
+                       ("inst_act.hip", act)):
         with open(os.path.join(HERE, name), "w") as f:
             f.write(text)
 

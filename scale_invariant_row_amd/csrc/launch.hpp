@@ -59,6 +59,11 @@ hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const fl
                              hipStream_t stream);
 hipError_t launch_rownorm(Shape s, const TaskArgs<RownormTask>& args, int grid,
                           hipStream_t stream);
+hipError_t launch_gate_l2_rows(Shape s, const void* o, const void* g, const float* sg, void* y,
+                               int64_t rows, int nvec, float eps, int grid, hipStream_t stream);
+hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const float* sug,
+                                 const float* suu, void* y, int64_t rows, int nvec, float eps,
+                                 int grid, hipStream_t stream);
 hipError_t launch_l2_rows_backward(Shape s, const void* x, const void* r, const void* dy,
                                    void* dx, int64_t rows, int nvec, float eps, int grid,
                                    hipStream_t stream);

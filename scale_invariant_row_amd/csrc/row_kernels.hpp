@@ -710,6 +710,118 @@ slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, 
   }
 }
 
+// ---------------------------------------------------------- activation rows
+//
+// TensorFold PR #1260's two activation rows for Dory, each an elementwise
+// prologue in front of l2_rows' normalisation over the whole row:
+//   gate    t = bf16(o * sigmoid(g * sg)),                       y = bf16(l2(t))
+//   swiglu  a = bf16(g * sug), b = bf16(u * suu),
+//           p = bf16(silu(a) * b),                               y = bf16(l2(p))
+// sigmoid(x) = 1 / (1 + expf(-x)) and silu(x) = x / (1 + expf(-x)) in fp32
+// with IEEE division (torch's fp32 forms); expf is the device library's.
+// The scale vectors are fp32, one value per column, shared by every row.
+
+enum class Act { kGate, kSwiglu };
+
+// The fp32 column scales of this lane's columns: NV vectors of 8 values per
+// 16-byte row vector; held in VGPRs when the shape is narrow, else re-read
+// (from L2) next to each row.
+template <int V, int NS>
+struct ColScales {
+  static constexpr bool kHeld = V * NS <= 4;
+  float c[kHeld ? V : 1][NS][8];
+  __device__ __forceinline__ static void load_into(float (&dst)[8], const RowBuf& b, int off) {
+    const f32x4_t a0 = b.ld16f_cached(2 * off);
+    const f32x4_t a1 = b.ld16f_cached(2 * off + 16);
+    dst[0] = a0.x; dst[1] = a0.y; dst[2] = a0.z; dst[3] = a0.w;
+    dst[4] = a1.x; dst[5] = a1.y; dst[6] = a1.z; dst[7] = a1.w;
+  }
+  __device__ __forceinline__ void init(const RowBuf& b0, const RowBuf& b1, const int (&off)[V]) {
+    if constexpr (kHeld) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        load_into(c[v][0], b0, off[v]);
+        if constexpr (NS == 2) load_into(c[v][NS - 1], b1, off[v]);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float round_bf16(float x) { return bf_lo(pack_bf16(x, 0.f)); }
+
+// One row vector's 8 outputs of the prologue, packed: x0 and x1 hold the two
+// input rows' packed values (o, g for the gate; g, u for SwiGLU).
+template <Act A>
+__device__ __forceinline__ void act_prologue(uint32_t (&out)[4], const uint32_t (&x0)[4],
+                                             const uint32_t (&x1)[4], const float* s0,
+                                             const float* s1) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float r[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float v0 = h ? bf_hi(x0[k]) : bf_lo(x0[k]);
+      const float v1 = h ? bf_hi(x1[k]) : bf_lo(x1[k]);
+      const int j = 2 * k + h;
+      if constexpr (A == Act::kGate) {
+        const float x = v1 * s0[j];                       // g * sg
+        const float sig = 1.0f / (1.0f + expf(-x));
+        r[h] = v0 * sig;                                  // o * sigmoid, rounded below
+      } else {
+        const float a = round_bf16(v0 * s0[j]);           // bf16(g * sug)
+        const float b = round_bf16(v1 * s1[j]);           // bf16(u * suu)
+        const float silu = a / (1.0f + expf(-a));
+        r[h] = silu * b;                                  // rounded below
+      }
+    }
+    out[k] = pack_bf16(r[0], r[1]);
+  }
+}
+
+template <int G, int V, Act A>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
+                   const f32x4_t* sc1, u32x4_t* y, int64_t rows, int nvec, float eps) {
+  constexpr int R = Geo<G>::R;
+  constexpr int NS = (A == Act::kGate) ? 1 : 2;
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  int off[V];
+  geo.offsets(off, 16);
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  const RowBuf sb0(sc0, row_bytes * 2u);                        // cols fp32 = 2 x row bytes
+  const RowBuf sb1(NS == 2 ? sc1 : sc0, row_bytes * 2u);
+  ColScales<V, NS> cs;
+  cs.init(sb0, sb1, off);
+
+  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
+    const int64_t row = base + geo.rr;
+    if (G == 1 && row >= rows) break;
+    Bf16Row<V> t, q;
+    t.load(RowBuf(in0 + row * nvec, row_bytes), off);
+    q.load(RowBuf(in1 + row * nvec, row_bytes), off);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float tmp[NS][8];
+      if constexpr (!ColScales<V, NS>::kHeld) {
+        asm volatile("" ::: "memory");          // one vector's scales at a time
+        ColScales<V, NS>::load_into(tmp[0], sb0, off[v]);
+        if constexpr (NS == 2) ColScales<V, NS>::load_into(tmp[NS - 1], sb1, off[v]);
+      }
+      const float* s0 = ColScales<V, NS>::kHeld ? cs.c[ColScales<V, NS>::kHeld ? v : 0][0] : tmp[0];
+      const float* s1 = ColScales<V, NS>::kHeld ? cs.c[ColScales<V, NS>::kHeld ? v : 0][NS - 1]
+                                                : tmp[NS - 1];
+      act_prologue<A>(t.p[v], t.p[v], q.p[v], s0, s1);
+    }
+    float S[1] = {wave_sum(t.sumsq())};
+    t.fence();
+    group_sum<G, 1>(S, gs.next(slot), geo.g, geo.lane);
+    l2_in_place<G, V>(t, S[0], eps, gs, slot, geo);
+    t.store(RowBuf(y + row * nvec, row_bytes), off);
+  }
+}
+
 // ------------------------------------------------------- weight rownorm+gain
 
 // One matrix of a ragged call, as the kernel reads it.  Items are groups of

@@ -39,7 +39,12 @@ rownorm_gain_bwd_11008x   one 11008x4096 matrix (the DragonScale README's
                           dL/dW_eff ~ N(0,1)
 ========================  =======================================================
 
+gate_l2_rows_8192x4096    o, g ~ N(0,1) bf16; sg ~ U(0.5, 2) fp32 per column
+swiglu_l2_rows_8192x7168  g, u ~ N(0,1) bf16; sug, suu ~ U(0.5, 2) fp32 per column
+
 Upstream gradients (dy, dL/dW_eff) are bf16 values drawn like activations.
+The activation rows' widths are the Dory rows the TensorFold PR names (4,096
+over all heads, 7,168 for the MLP).
 """
 from __future__ import annotations
 
@@ -53,6 +58,7 @@ __all__ = [
     "to_bf16_bits", "l2_case", "slerp_case", "rownorm_case",
     "transformer_linears", "stress_l2_case", "WORKLOADS", "make",
     "L2GradCase", "RownormGradCase", "grad_bits", "l2_grad_case", "rownorm_grad_case",
+    "ActCase", "gate_case", "swiglu_case",
 ]
 
 
@@ -136,6 +142,18 @@ class RownormGradCase:
     @property
     def total_elems(self) -> int:
         return sum(m.size for m in self.w)
+
+
+@dataclass
+class ActCase:
+    """Inputs of an activation row: two bf16 rows and one or two fp32 column scales
+    (gate: a = o, b = g, s0 = sg; SwiGLU: a = g, b = u, s0 = sug, s1 = suu)."""
+    name: str
+    a: np.ndarray
+    b: np.ndarray
+    s0: np.ndarray
+    s1: Optional[np.ndarray]
+    eps: float = 1e-6
 
 
 def _streams(seed: int, n: int) -> List[np.random.Generator]:
@@ -245,6 +263,24 @@ def rownorm_grad_case(shapes, seed: int, radius: float = 1.0,
                            fwd.radius, dwe)
 
 
+def gate_case(rows: int, cols: int, seed: int, g_sd: float = 1.0,
+              name: Optional[str] = None) -> ActCase:
+    go, gg, gs = _streams(seed, 3)
+    o = to_bf16_bits(go.standard_normal((rows, cols)))
+    g = to_bf16_bits(g_sd * gg.standard_normal((rows, cols)))
+    sg = gs.uniform(0.5, 2.0, cols).astype(np.float32)
+    return ActCase(name or f"gate_l2_rows_{rows}x{cols}", o, g, sg, None)
+
+
+def swiglu_case(rows: int, cols: int, seed: int, name: Optional[str] = None) -> ActCase:
+    gg, gu, s1, s2 = _streams(seed, 4)
+    g = to_bf16_bits(gg.standard_normal((rows, cols)))
+    u = to_bf16_bits(gu.standard_normal((rows, cols)))
+    sug = s1.uniform(0.5, 2.0, cols).astype(np.float32)
+    suu = s2.uniform(0.5, 2.0, cols).astype(np.float32)
+    return ActCase(name or f"swiglu_l2_rows_{rows}x{cols}", g, u, sug, suu)
+
+
 # name -> (description, builder, seed).  Seeds are 1000 + a fixed number.
 WORKLOADS = {
     "l2_rows_64x1024": (
@@ -281,6 +317,14 @@ WORKLOADS = {
         "weight rownorm + gain gradient, one 11008 x 4096 matrix: W ~ N(0, sd 0.02), "
         "g ~ U(0.5, 2), rho 1, dL/dW_eff ~ N(0,1) bf16",
         lambda: rownorm_grad_case([(11008, 4096)], 1009, name="rownorm_gain_bwd_11008x4096")),
+    "gate_l2_rows_8192x4096": (
+        "gate_l2_rows, 8192 x 4096 bf16 (all heads of a row): o, g ~ N(0,1), "
+        "sg ~ U(0.5, 2) fp32, eps 1e-6",
+        lambda: gate_case(8192, 4096, 1010, name="gate_l2_rows_8192x4096")),
+    "swiglu_l2_rows_8192x7168": (
+        "swiglu_l2_rows, 8192 x 7168 bf16 (the MLP width): g, u ~ N(0,1), "
+        "sug, suu ~ U(0.5, 2) fp32, eps 1e-6",
+        lambda: swiglu_case(8192, 7168, 1011, name="swiglu_l2_rows_8192x7168")),
 }
 
 

@@ -133,3 +133,41 @@ def rownorm_backward_model(w, g, rho, dwe_bits, acc="f32", proj="w"):
     dw[zero] = 0
     dg[zero] = 0
     return dw.astype(np.float32), dg[:, 0].astype(np.float32)
+
+
+# ------------------------------------------------------------ activation rows
+
+def _l2_of_f32_rows(t32, eps):
+    inv = inv_norm(lane_sum_sq(t32), eps)
+    return bf16_rne((t32 * inv[:, None]).astype(np.float64))
+
+
+def gate_model(o_bits, g_bits, sg, eps=1e-6, round_t=True):
+    """fp32 steps of the gate row; the control leaves the gated row unrounded."""
+    o = bf16_value(o_bits).astype(np.float32)
+    g = bf16_value(g_bits).astype(np.float32)
+    with np.errstate(all="ignore"):
+        x = g * np.asarray(sg, np.float32)
+        sig = np.float32(1) / (np.float32(1) + np.exp(-x))
+        t = o * sig
+    if round_t:
+        t = bf16_of_f32(t)
+    return _l2_of_f32_rows(t.astype(np.float32), eps)
+
+
+def swiglu_model(g_bits, u_bits, sug, suu, eps=1e-6, round_a=True, round_b=True, round_p=True):
+    """fp32 steps of the SwiGLU row; each control leaves one rounding point out."""
+    g = bf16_value(g_bits).astype(np.float32)
+    u = bf16_value(u_bits).astype(np.float32)
+    with np.errstate(all="ignore"):
+        a = g * np.asarray(sug, np.float32)
+        b = u * np.asarray(suu, np.float32)
+        if round_a:
+            a = bf16_of_f32(a)
+        if round_b:
+            b = bf16_of_f32(b)
+        silu = a / (np.float32(1) + np.exp(-a))
+        p = silu * b
+    if round_p:
+        p = bf16_of_f32(p)
+    return _l2_of_f32_rows(p.astype(np.float32), eps)

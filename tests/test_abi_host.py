@@ -29,13 +29,14 @@ def test_exports_every_declared_function(L):
     names = B.header_functions()
     assert set(names) == {"ds_l2_rows", "ds_slerp_rows", "ds_weight_rownorm_gain",
                           "ds_l2_rows_backward", "ds_weight_rownorm_gain_backward",
+                          "ds_gate_l2_rows", "ds_swiglu_l2_rows",
                           "ds_status_string", "ds_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10100
+    assert B.ds_version() == 10200
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -189,6 +190,32 @@ def test_rownorm_output_over_other_input_refused(L):
     good = (A, Bp, 1.0, Bp + 4096, C, 16, 64)
     over = (A + 8192, Bp + 1024, 1.0, None, A, 16, 64)     # its W_eff over the first w
     assert L.ds_weight_rownorm_gain(_descs(good, over), 2, None) == B.DS_ERR_ARG
+
+
+def test_activation_validation(L):
+    gate, sw = L.ds_gate_l2_rows, L.ds_swiglu_l2_rows
+    S1, S2 = C + 0x100000, C + 0x200000
+    assert gate(A, Bp, None, C, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert gate(A, None, S1, C, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert gate(A, Bp, S1 + 4, C, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert gate(A, Bp, S1, C + 8, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert gate(A, Bp, S1, A + 64, 4, 64, 1e-6, None) == B.DS_ERR_ARG       # y partly over o
+    assert gate(A, Bp, C + 256, C, 4, 64, 1e-6, None) == B.DS_ERR_ARG       # sg inside y
+    assert gate(A, Bp, S1, C, 4, 12, 1e-6, None) == B.DS_ERR_SHAPE
+    assert gate(A, Bp, S1, C, 4, 64, -1.0, None) == B.DS_ERR_ARG
+    assert gate(None, None, None, None, 0, 64, 1e-6, None) == B.DS_OK
+    assert sw(A, Bp, S1, None, C, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert sw(A, Bp, S1, S2 + 8, C, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert sw(A, Bp, S1, C + 64, C, 4, 64, 1e-6, None) == B.DS_ERR_ARG      # suu inside y
+    assert sw(A, Bp, S1, S2, Bp + 32, 4, 64, 1e-6, None) == B.DS_ERR_ARG    # y partly over u
+    assert sw(None, None, None, None, None, 0, 64, 1e-6, None) == B.DS_OK
+
+
+@pytest.mark.skipif("not no_device()")
+def test_activation_valid_args_reach_device_lookup(L):
+    S1, S2 = C + 0x100000, C + 0x200000
+    assert L.ds_gate_l2_rows(A, Bp, S1, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE      # y == o
+    assert L.ds_swiglu_l2_rows(A, Bp, S1, S2, Bp, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE  # y == u
 
 
 def test_binding_raises_on_missing_library(monkeypatch):

@@ -1,0 +1,194 @@
+"""ds_gate_l2_rows and ds_swiglu_l2_rows on the GPU against the CPU oracle.
+
+The 1-ulp contract applies where the pre-norm row value (the gated row, the
+SwiGLU product) has one admissible bf16 value; the strict admissible set
+(an fp32 run's spread, the device expf within its ulp bound) applies to every
+element.  Full-size workloads are checked on sampled rows, and on every row
+through unit length.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import announce, depth_for, dev_bits, dev_f32, host_bits, sample_rows, unit_norm_ok
+from oracle.bf16 import bf16_rne, bf16_value
+from oracle.check import (act_unique_mask, admissible_act_rows, contract_bf16, gate_candidates,
+                          swiglu_candidates)
+from oracle.rows import gate_l2_rows, swiglu_l2_rows
+from scale_invariant_row_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from scale_invariant_row_amd import binding
+    binding.lib()
+    return binding
+
+
+def run_gate(B, o, g, sg, eps=1e-6):
+    import torch
+    y = B.ds_gate_l2_rows(dev_bits(o), dev_bits(g), dev_f32(sg), eps)
+    torch.cuda.synchronize()
+    return host_bits(y)
+
+
+def run_swiglu(B, g, u, sug, suu, eps=1e-6):
+    import torch
+    y = B.ds_swiglu_l2_rows(dev_bits(g), dev_bits(u), dev_f32(sug), dev_f32(suu), eps)
+    torch.cuda.synchronize()
+    return host_bits(y)
+
+
+def check(got, want, lo, hi, eps, label, min_unique=0.99):
+    uniq = act_unique_mask(lo, hi)
+    ok = contract_bf16(got, want)
+    bad = ~ok & uniq
+    assert not bad.any(), f"{label}: {np.count_nonzero(bad)} beyond 1 ulp, e.g. {np.argwhere(bad)[:4]}"
+    assert uniq.mean() >= min_unique, f"{label}: unique fraction {uniq.mean():.4f}"
+    finite = np.isfinite(lo).all(axis=1) & np.isfinite(hi).all(axis=1)
+    rep = admissible_act_rows(got, lo, hi, want, finite, eps, depth_for(got.shape[-1]))
+    assert rep.ok, f"{label}: {rep}"
+
+
+def check_gate(got, o, g, sg, eps, label, **kw):
+    lo, hi = gate_candidates(o, g, sg)
+    check(got, gate_l2_rows(o, g, sg, eps), lo, hi, eps, label, **kw)
+
+
+def check_swiglu(got, g, u, sug, suu, eps, label, **kw):
+    lo, hi = swiglu_candidates(g, u, sug, suu)
+    check(got, swiglu_l2_rows(g, u, sug, suu, eps), lo, hi, eps, label, **kw)
+
+
+WIDTHS = [8, 64, 520, 1024, 4096, 4104, 7168, 8192, 16392, 65536]
+
+
+@pytest.mark.parametrize("cols", WIDTHS)
+def test_gate_widths(B, cols):
+    rows = 29 if cols <= 8192 else 4
+    c = inputs.gate_case(rows, cols, 1500 + cols % 83)
+    announce("gate_l2_rows", rows, cols)
+    check_gate(run_gate(B, c.a, c.b, c.s0), c.a, c.b, c.s0, 1e-6, f"gate {rows}x{cols}")
+
+
+@pytest.mark.parametrize("cols", WIDTHS)
+def test_swiglu_widths(B, cols):
+    rows = 29 if cols <= 8192 else 4
+    c = inputs.swiglu_case(rows, cols, 1600 + cols % 83)
+    announce("swiglu_l2_rows", rows, cols)
+    check_swiglu(run_swiglu(B, c.a, c.b, c.s0, c.s1), c.a, c.b, c.s0, c.s1, 1e-6,
+                 f"swiglu {rows}x{cols}")
+
+
+def test_gate_workload(B):
+    import torch
+    c = inputs.make("gate_l2_rows_8192x4096")
+    announce("gate_l2_rows full", c.name)
+    od, gd, sd = dev_bits(c.a), dev_bits(c.b), dev_f32(c.s0)
+    y = B.ds_gate_l2_rows(od, gd, sd, 1e-6)
+    y2 = B.ds_gate_l2_rows(od, gd, sd, 1e-6)
+    part = B.ds_gate_l2_rows(od[77:1100], gd[77:1100], sd, 1e-6)
+    torch.cuda.synchronize()
+    got = host_bits(y)
+    assert np.array_equal(got, host_bits(y2))
+    assert np.array_equal(got[77:1100], host_bits(part))
+    assert unit_norm_ok(y)
+    rows = sample_rows(8192, 40, 1501)
+    check_gate(got[rows], c.a[rows], c.b[rows], c.s0, 1e-6, c.name)
+
+
+def test_swiglu_workload(B):
+    import torch
+    c = inputs.make("swiglu_l2_rows_8192x7168")
+    announce("swiglu_l2_rows full", c.name)
+    gd, ud, s0, s1 = dev_bits(c.a), dev_bits(c.b), dev_f32(c.s0), dev_f32(c.s1)
+    y = B.ds_swiglu_l2_rows(gd, ud, s0, s1, 1e-6)
+    y2 = B.ds_swiglu_l2_rows(gd, ud, s0, s1, 1e-6)
+    torch.cuda.synchronize()
+    got = host_bits(y)
+    assert np.array_equal(got, host_bits(y2))
+    assert unit_norm_ok(y)
+    rows = sample_rows(8192, 32, 1601)
+    check_swiglu(got[rows], c.a[rows], c.b[rows], c.s0, c.s1, 1e-6, c.name)
+
+
+def test_in_place(B):
+    import torch
+    c = inputs.gate_case(200, 4096, 1502)
+    want = run_gate(B, c.a, c.b, c.s0)
+    for target in ("o", "g"):
+        od, gd = dev_bits(c.a), dev_bits(c.b)
+        out = od if target == "o" else gd
+        announce("gate_l2_rows in place", target)
+        B.ds_gate_l2_rows(od, gd, dev_f32(c.s0), 1e-6, out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), want), target
+    s = inputs.swiglu_case(200, 7168, 1602)
+    want = run_swiglu(B, s.a, s.b, s.s0, s.s1)
+    for target in ("g", "u"):
+        gd, ud = dev_bits(s.a), dev_bits(s.b)
+        out = gd if target == "g" else ud
+        announce("swiglu_l2_rows in place", target)
+        B.ds_swiglu_l2_rows(gd, ud, dev_f32(s.s0), dev_f32(s.s1), 1e-6, out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), want), target
+
+
+def test_extremes(B):
+    """Saturated gates (exp beyond fp32's range), huge and tiny rows, zero rows."""
+    rng = np.random.default_rng(1503)
+    cols = 1024
+    o = rng.standard_normal((10, cols))
+    g = rng.standard_normal((10, cols))
+    g[0] *= 60                                     # |x| past exp's fp32 range on many entries
+    g[1] = -100.0
+    o[2] *= 2.0 ** 100                             # squares of the gated row overflow fp32
+    o[3] *= 2.0 ** -100                            # ... and underflow
+    o[4] = 0.0                                     # zero row: eps alone
+    g[5] = 0.0                                     # the half gate: exact halves
+    o[5] = rng.integers(-64, 65, cols)
+    o[6] *= 3.0e37
+    sg = rng.uniform(0.5, 2, cols).astype(np.float32)
+    sg[:8] = 0.0
+    ob, gb = bf16_rne(o), bf16_rne(g)
+    for eps in (1e-6, 0.0):
+        keep = np.array([eps > 0 or i != 4 for i in range(10)])
+        announce("gate_l2_rows extremes eps", eps)
+        got = run_gate(B, ob[keep], gb[keep], sg, eps)
+        check_gate(got, ob[keep], gb[keep], sg, eps, f"gate extremes eps={eps}", min_unique=0.9)
+    # SwiGLU: the same shapes of trouble on the gate input and the up row
+    u = rng.standard_normal((10, cols))
+    u[2] *= 2.0 ** 100
+    u[3] *= 2.0 ** -100
+    u[4] = 0.0
+    gs = rng.standard_normal((10, cols))
+    gs[0] *= 60
+    gs[1] = -100.0
+    gs[6] = 100.0
+    sug = rng.uniform(0.5, 2, cols).astype(np.float32)
+    suu = rng.uniform(0.5, 2, cols).astype(np.float32)
+    gsb, ub = bf16_rne(gs), bf16_rne(u)
+    for eps in (1e-6, 0.0):
+        keep = np.array([eps > 0 or i not in (1, 4) for i in range(10)])
+        announce("swiglu_l2_rows extremes eps", eps)
+        got = run_swiglu(B, gsb[keep], ub[keep], sug, suu, eps)
+        check_swiglu(got, gsb[keep], ub[keep], sug, suu, eps, f"swiglu extremes eps={eps}",
+                     min_unique=0.9)
+
+
+def test_nonfinite(B):
+    rng = np.random.default_rng(1504)
+    o = bf16_rne(rng.standard_normal((5, 256)))
+    g = bf16_rne(rng.standard_normal((5, 256)))
+    o[0, 3] = 0x7FC0                                # NaN in o
+    g[1, 7] = 0x7FC0                                # NaN in g
+    g[2, 9] = 0x7F80                                # +inf gate: sigmoid 1 exactly
+    g[3, 9] = 0xFF80                                # -inf gate: sigmoid 0 exactly
+    sg = np.ones(256, np.float32)
+    announce("gate_l2_rows non-finite")
+    got = run_gate(B, o, g, sg)
+    want = gate_l2_rows(o, g, sg)
+    gv, wv = bf16_value(got), bf16_value(want)
+    assert np.array_equal(np.isnan(gv), np.isnan(wv))
+    assert np.array_equal(gv[2:], wv[2:]) or contract_bf16(got[2:], want[2:]).all()

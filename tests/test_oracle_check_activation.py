@@ -1,0 +1,79 @@
+"""The activation-row checks themselves: a faithful fp32 run passes, and each
+of the pages' controls (TensorFold PR #1260's activation-row commit: drop the
+gated row's rounding, the scaled gate's, the scaled up's, or the product's)
+fails the strict check."""
+import numpy as np
+import pytest
+
+import kernel_models as km
+from oracle.bf16 import bf16_rne
+from oracle.check import (act_unique_mask, admissible_act_rows, contract_bf16, gate_candidates,
+                          swiglu_candidates)
+from oracle.rows import gate_l2_rows, swiglu_l2_rows
+
+
+@pytest.fixture(scope="module")
+def gate_in():
+    rng = np.random.default_rng(321)
+    o = bf16_rne(rng.standard_normal((64, 4096)))
+    g = bf16_rne(rng.standard_normal((64, 4096)) * 2)
+    sg = rng.uniform(0.5, 2.0, 4096).astype(np.float32)
+    return o, g, sg
+
+
+@pytest.fixture(scope="module")
+def swiglu_in():
+    rng = np.random.default_rng(322)
+    g = bf16_rne(rng.standard_normal((48, 7168)))
+    u = bf16_rne(rng.standard_normal((48, 7168)))
+    sug = rng.uniform(0.5, 3.0, 7168).astype(np.float32)
+    suu = rng.uniform(0.5, 3.0, 7168).astype(np.float32)
+    return g, u, sug, suu
+
+
+def test_faithful_gate_passes(gate_in):
+    o, g, sg = gate_in
+    y = km.gate_model(o, g, sg)
+    lo, hi = gate_candidates(o, g, sg)
+    rep = admissible_act_rows(y, lo, hi)
+    assert rep.ok, str(rep)
+    uniq = act_unique_mask(lo, hi)
+    assert uniq.mean() > 0.99
+    assert contract_bf16(y, gate_l2_rows(o, g, sg))[uniq].all()
+
+
+def test_gate_control_fails(gate_in):
+    o, g, sg = gate_in
+    y = km.gate_model(o, g, sg, round_t=False)
+    lo, hi = gate_candidates(o, g, sg)
+    rep = admissible_act_rows(y, lo, hi)
+    assert rep.outside > 100, str(rep)
+
+
+def test_faithful_swiglu_passes(swiglu_in):
+    g, u, sug, suu = swiglu_in
+    y = km.swiglu_model(g, u, sug, suu)
+    lo, hi = swiglu_candidates(g, u, sug, suu)
+    rep = admissible_act_rows(y, lo, hi)
+    assert rep.ok, str(rep)
+    uniq = act_unique_mask(lo, hi)
+    assert uniq.mean() > 0.99
+    assert contract_bf16(y, swiglu_l2_rows(g, u, sug, suu))[uniq].all()
+
+
+@pytest.mark.parametrize("drop", ["round_a", "round_b", "round_p"])
+def test_swiglu_controls_fail(swiglu_in, drop):
+    g, u, sug, suu = swiglu_in
+    y = km.swiglu_model(g, u, sug, suu, **{drop: False})
+    lo, hi = swiglu_candidates(g, u, sug, suu)
+    rep = admissible_act_rows(y, lo, hi)
+    assert rep.outside > 100, str(rep)
+
+
+def test_saturated_gate_admits_fp32_zero():
+    """exp beyond fp32's range: fp32 gives sigmoid 0, float64 a subnormal; both pass."""
+    o = bf16_rne(np.full((1, 64), 3.0e38))
+    g = bf16_rne(np.full((1, 64), -88.8))
+    sg = np.ones(64, np.float32)
+    lo, hi = gate_candidates(o, g, sg)
+    assert (lo[0] == 0).all() and (hi[0] > 0).all()
