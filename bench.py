@@ -37,7 +37,8 @@ ROWS, COLS = 8192, 4096
 EPS = 1e-6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
-                  "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "ds_rows.hip"]
+                  "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip",
+                  "ds_rows.hip"]
 
 
 def kernel_hash() -> str:
@@ -332,6 +333,19 @@ def main():
         "forward (fp32 W read, bf16 W_eff and fp32 norms written) plus backward (W and bf16 "
         "dW_eff read, fp32 dW and dg written): the op the DragonScale README reports at 85-96% "
         "of the card's bandwidth on V100/2080 Ti/3090/4090, where its W_eff is fp32")
+
+    # ---- activation rows at the Dory widths (o, g or g, u read; y written;
+    # fp32 column scales once per launch)
+    sg4 = 0.5 + 1.5 * torch.rand(4096, device=dev)
+    sug7 = 0.5 + 1.5 * torch.rand(7168, device=dev)
+    suu7 = 0.5 + 1.5 * torch.rand(7168, device=dev)
+    gate_us = shaped_us(ROWS, 4096, lambda t, r, c: L.ds_gate_l2_rows(
+        t[0].data_ptr(), t[1].data_ptr(), sg4.data_ptr(), t[2].data_ptr(), r, c, eps, sp), 5)
+    swiglu_us = shaped_us(ROWS, 7168, lambda t, r, c: L.ds_swiglu_l2_rows(
+        t[0].data_ptr(), t[1].data_ptr(), sug7.data_ptr(), suu7.data_ptr(), t[2].data_ptr(),
+        r, c, eps, sp), 4)
+    ops["gate_l2_rows_8192x4096"] = op(gate_us, ROWS * 4096 * 6 + 4096 * 4, ROWS)
+    ops["swiglu_l2_rows_8192x7168"] = op(swiglu_us, ROWS * 7168 * 6 + 7168 * 8, ROWS)
 
     ops["l2_rows_64x1024"] = op(c1_us, 64 * 1024 * 4, 64)
     ops["l2_rows_64x1024"]["note"] = "latency-bound: one small launch"

@@ -148,7 +148,7 @@ int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha,
  * the row's L2 norm over all its heads.)
  *
  *   t_j = bf16(o_j * sigmoid(g_j * sg_j))    g_j * sg_j one fp32 product;
- *                                            sigmoid(x) = 1 / (1 + expf(-x))
+ *                                            sigmoid(x) = 1 / (1 + exp(-x))
  *                                            in fp32, IEEE division
  *   y   = bf16(t / sqrt(sum_j t_j^2 + eps))
  *
@@ -158,8 +158,10 @@ int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha,
  *           16-byte aligned, not overlapping y.
  * rows, cols, eps, stream : as for ds_l2_rows.
  *
- * expf is the device library's (measured within 1 ulp on gfx950); an argument
- * beyond fp32's exp range gives sigmoid 0, as fp32 arithmetic does.
+ * exp is 2^(x log2 e) on the hardware exponential with log2 e split in two
+ * fp32 parts: within 1.22 ulp (measured) where the result is a normal fp32
+ * number; below that it may flush, which leaves 1 + exp(-x) = 1 unchanged.  An
+ * argument beyond fp32's exp range gives sigmoid 0, as fp32 arithmetic does.
  */
 int ds_gate_l2_rows(const uint16_t* o, const uint16_t* g, const float* sg, uint16_t* y,
                     int64_t rows, int64_t cols, float eps, ds_stream_t stream);
@@ -169,8 +171,8 @@ int ds_gate_l2_rows(const uint16_t* o, const uint16_t* g, const float* sg, uint1
  * (TensorFold PR #1260, the activation-row commit: Dory's MLP.)
  *
  *   a_j = bf16(g_j * sug_j),  b_j = bf16(u_j * suu_j)     fp32 products, rounded
- *   p_j = bf16(silu(a_j) * b_j)        silu(x) = x / (1 + expf(-x)) in fp32,
- *                                      IEEE division
+ *   p_j = bf16(silu(a_j) * b_j)        silu(x) = x / (1 + exp(-x)) in fp32,
+ *                                      IEEE division, exp as for the gate
  *   y   = bf16(p / sqrt(sum_j p_j^2 + eps))
  *
  * g, u, y  : row-major [rows, cols] bf16 bit patterns, contiguous, 16-byte

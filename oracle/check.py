@@ -613,14 +613,14 @@ def admissible_rownorm_backward(got_dw, got_dg, w, g, rho, dweff_bits,
 #
 # The fp32 run modelled for gate_l2_rows and swiglu_l2_rows: the products by
 # the fp32 scale vectors are IEEE multiplies (deterministic, as the oracle
-# does them); expf is within EXPF_ULPS units in the last place of exp, may
-# return +inf where exp exceeds fp32's largest value, and carries 2**-149
-# steps in the subnormal range; 1 + e, the IEEE division and the product by
-# o (or b) round once each.  That bounds the pre-norm value of each element;
+# does them); exp is within EXPF_ULPS units in the last place of exp where
+# the result is a normal fp32 number, anywhere in [0, 2**-126] below that,
+# and may return +inf where exp exceeds fp32's largest value; 1 + e, the IEEE
+# division and the product by o (or b) round once each.  That bounds the pre-norm value of each element;
 # its admissible bf16 values run from bf16(lo) to bf16(hi), and the output
 # is checked over every such choice as slerp's is over a and b.
 
-EXPF_ULPS = 2.0     # the device expf measured within 1.0 ulp over 23M arguments on gfx950
+EXPF_ULPS = 2.0     # the kernels' exp measured within 1.22 ulp over 23M arguments on gfx950
 F32_MAX = float(np.finfo(np.float32).max)
 
 
@@ -630,6 +630,9 @@ def _expf_bounds(v):
         rel = EXPF_ULPS * 2.0 ** -23
         lo = np.maximum(e * (1 - rel) - EXPF_ULPS * ETA, 0.0)
         hi = e * (1 + rel) + EXPF_ULPS * ETA
+        tiny = e < 2.0 ** -126
+        lo = np.where(tiny, 0.0, lo)
+        hi = np.where(tiny, 2.0 ** -126, hi)
     return lo, np.where(hi >= F32_MAX, np.inf, hi)
 
 

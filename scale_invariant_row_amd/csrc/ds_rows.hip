@@ -420,7 +420,7 @@ int ds_gate_l2_rows(const uint16_t* o, const uint16_t* g, const float* sg, uint1
                     int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
   int st = check_act(o, g, sg, nullptr, y, rows, cols, eps, false);
   if (st != DS_OK || rows == 0) return st;
-  const Shape s = dsr::pick_bf16_shape(cols / 8);
+  const Shape s = dsr::pick_act_shape(cols / 8);
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
@@ -434,7 +434,7 @@ int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, co
                       uint16_t* y, int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
   int st = check_act(g, u, sug, suu, y, rows, cols, eps, true);
   if (st != DS_OK || rows == 0) return st;
-  const Shape s = dsr::pick_bf16_shape(cols / 8);
+  const Shape s = dsr::pick_act_shape(cols / 8);
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;

@@ -15,7 +15,7 @@ def limits():
     text = open(os.path.join(HERE, "launch.hpp")).read()
     get = lambda name: int(re.search(rf"{name}\s*=\s*(\d+)", text).group(1))
     return {k: get(k) for k in ("kBf16SmallVectors", "kVmaxBf16Small", "kVmaxBf16Large",
-                                "kVmaxRownorm", "kVmaxWide")}
+                                "kVmaxAct", "kVmaxRownorm", "kVmaxWide")}
 
 
 def pick_shape(vectors, vmax, wide):
@@ -30,6 +30,15 @@ def pick_shape(vectors, vmax, wide):
 def bf16_shape(vectors, lim):
     vmax = lim["kVmaxBf16Small"] if vectors <= lim["kBf16SmallVectors"] else lim["kVmaxBf16Large"]
     return pick_shape(vectors, vmax, lim["kVmaxWide"])
+
+
+def act_shape(vectors, lim):
+    return pick_shape(vectors, lim["kVmaxAct"], lim["kVmaxWide"])
+
+
+def act_shapes(lim):
+    """Every shape the activation-row policy returns for rows up to MAX_COLS columns."""
+    return sorted({act_shape(n, lim) for n in range(1, MAX_COLS // 8 + 1)})
 
 
 def rownorm_shape(vectors, lim):
@@ -63,6 +72,7 @@ def main():
     lim = limits()
     bf16 = bf16_shapes(lim)
     rown = rownorm_shapes(lim)
+    actsh = act_shapes(lim)
     l2 = HEAD.format(what="l2_rows") + '''
 template <int G, int V>
 static hipError_t run(const void* x, const void* r, void* y, int64_t rows, int nvec, float eps,
@@ -183,7 +193,7 @@ static hipError_t run(const void* in0, const void* in1, const float* s0, const f
 hipError_t launch_gate_l2_rows(Shape s, const void* o, const void* g, const float* sg, void* y,
                                int64_t rows, int nvec, float eps, int grid, hipStream_t stream) {
   switch (s.G * 100 + s.V) {
-''' + cases(bf16, "return run<{G}, {V}, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);") + '''
+''' + cases(actsh, "return run<{G}, {V}, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);") + '''
     default: return hipErrorInvalidValue;
   }
 }
@@ -192,7 +202,7 @@ hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const fl
                                  const float* suu, void* y, int64_t rows, int nvec, float eps,
                                  int grid, hipStream_t stream) {
   switch (s.G * 100 + s.V) {
-''' + cases(bf16, "return run<{G}, {V}, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);") + '''
+''' + cases(actsh, "return run<{G}, {V}, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);") + '''
     default: return hipErrorInvalidValue;
   }
 }

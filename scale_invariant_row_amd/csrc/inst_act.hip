@@ -22,10 +22,8 @@ hipError_t launch_gate_l2_rows(Shape s, const void* o, const void* g, const floa
     case 102: return run<1, 2, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
     case 202: return run<2, 2, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
     case 402: return run<4, 2, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
-    case 403: return run<4, 3, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
-    case 404: return run<4, 4, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
-    case 803: return run<8, 3, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
-    case 804: return run<8, 4, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
+    case 802: return run<8, 2, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
+    case 1602: return run<16, 2, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
     case 1603: return run<16, 3, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
     case 1604: return run<16, 4, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
     case 1605: return run<16, 5, Act::kGate>(o, g, sg, nullptr, y, rows, nvec, eps, grid, stream);
@@ -44,10 +42,8 @@ hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const fl
     case 102: return run<1, 2, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
     case 202: return run<2, 2, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
     case 402: return run<4, 2, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
-    case 403: return run<4, 3, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
-    case 404: return run<4, 4, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
-    case 803: return run<8, 3, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
-    case 804: return run<8, 4, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
+    case 802: return run<8, 2, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
+    case 1602: return run<16, 2, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
     case 1603: return run<16, 3, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
     case 1604: return run<16, 4, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
     case 1605: return run<16, 5, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);

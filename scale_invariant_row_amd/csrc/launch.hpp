@@ -26,6 +26,8 @@ struct Shape {
 //   bf16 rows (l2_rows, slerp_rows): V <= 2 up to 512 vectors (4,096
 //     columns), V <= 4 beyond -- more, lighter waves stream best at these
 //     widths, and slerp's per-row work favours V = 4 once rows are wider;
+//   activation rows (gate, SwiGLU): V <= 2, so the fp32 column scales stay
+//     in VGPRs; these kernels are ALU-bound and gain from more, lighter waves;
 //   fp32 weight rows: V <= 6;
 //   G = 16 may take V up to 16 (rows up to DS_MAX_COLS).
 // The shape is a function of the width alone.  gen_instances.py evaluates
@@ -33,6 +35,7 @@ struct Shape {
 constexpr int kBf16SmallVectors = 512;
 constexpr int kVmaxBf16Small = 2;
 constexpr int kVmaxBf16Large = 4;
+constexpr int kVmaxAct = 2;
 constexpr int kVmaxRownorm = 6;
 constexpr int kVmaxWide = 16;
 
@@ -48,6 +51,9 @@ inline Shape pick_shape(int64_t vectors, int vmax) {
 inline Shape pick_bf16_shape(int64_t vectors) {
   return pick_shape(vectors, vectors <= kBf16SmallVectors ? kVmaxBf16Small : kVmaxBf16Large);
 }
+
+// activation rows of `vectors` 16-byte vectors (8 columns each)
+inline Shape pick_act_shape(int64_t vectors) { return pick_shape(vectors, kVmaxAct); }
 
 // fp32 weight rows of `vectors` 16-byte vectors (4 columns each)
 inline Shape pick_rownorm_shape(int64_t vectors) { return pick_shape(vectors, kVmaxRownorm); }

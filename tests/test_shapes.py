@@ -33,6 +33,16 @@ def test_rownorm_launcher_covers_policy():
     need = {gen.rownorm_shape(n, lim) for n in range(1, 65536 // 4 + 1)}
     assert None not in need
     assert need <= cases("inst_rownorm.hip")
+    assert need <= cases("inst_rownorm_bwd.hip")
+
+
+def test_gradient_and_activation_launchers_cover_policy():
+    lim = gen.limits()
+    need = {gen.bf16_shape(n, lim) for n in range(1, 65536 // 8 + 1)}
+    assert need <= cases("inst_l2_bwd.hip")
+    need = {gen.act_shape(n, lim) for n in range(1, 65536 // 8 + 1)}
+    assert None not in need
+    assert need <= cases("inst_act.hip")
 
 
 def test_policy_is_measured_choice():
@@ -44,6 +54,8 @@ def test_policy_is_measured_choice():
     assert gen.bf16_shape(8192 // 8, lim) == (4, 4)
     assert gen.rownorm_shape(768 // 4, lim) == (1, 3)
     assert gen.rownorm_shape(3072 // 4, lim) == (2, 6)
+    assert gen.act_shape(4096 // 8, lim) == (4, 2)
+    assert gen.act_shape(7168 // 8, lim) == (8, 2)
 
 
 def test_reduction_depth_bound():
@@ -53,3 +65,5 @@ def test_reduction_depth_bound():
         assert 4 * V + 1 + 6 + (G - 1) <= 64
     for G, V in gen.rownorm_shapes(lim):
         assert 2 * V + 1 + 6 + (G - 1) <= 64
+    for G, V in gen.act_shapes(lim):
+        assert 4 * V + 1 + 6 + (G - 1) <= 64
