@@ -21,7 +21,7 @@ from typing import List, Optional, Sequence, Tuple
 
 __all__ = ["bits_to_fraction", "round_fraction", "bf16_of", "fp32_of",
            "l2_row", "slerp_row", "rownorm_row", "l2_backward_row", "rownorm_backward_row",
-           "gate_row", "swiglu_row", "NEAR_TIE_REL"]
+           "gate_row", "swiglu_row", "qk_head", "NEAR_TIE_REL"]
 
 PREC = 60
 NEAR_TIE_REL = Fraction(1, 10 ** 12)     # flag values this close to a midpoint
@@ -272,3 +272,39 @@ def swiglu_row(g_bits: Sequence[int], u_bits: Sequence[int], sug: Sequence[float
         near_p.append(n)
     y, near = _l2_exact(p, f32_to_fraction(eps32))
     return y, [a or any(near_p) for a in near]
+
+
+# ------------------------------------------------------------------ q/k rows
+
+def qk_head(x_bits: Sequence[int], pos: int, inv_freq: Sequence[float], scale: Sequence[float],
+            eps32: float) -> Tuple[List[Fraction], List[Fraction], bool]:
+    """One head exactly: (normalized head n, bf16(fp32(n * scale)), near-tie flag).
+
+    The angle is the IEEE fp32 product fp32(pos) * inv_i; cos and sin of it at
+    50 digits (mpmath); rotation, sum and quotient exact or at 60 digits.
+    """
+    import mpmath
+    hd = len(x_bits)
+    h2 = hd // 2
+    x = [bits_to_fraction(int(b)) for b in x_bits]
+    p32 = fp32_of(Fraction(int(pos)))[0]
+    near = False
+    r = [Fraction(0)] * hd
+    with mpmath.workdps(50):
+        for i in range(h2):
+            th = fp32_of(p32 * f32_to_fraction(float(inv_freq[i])))[0]
+            t = mpmath.mpf(th.numerator) / th.denominator
+            c = Fraction(mpmath.nstr(mpmath.cos(t), 48, min_fixed=-1, max_fixed=1))
+            s = Fraction(mpmath.nstr(mpmath.sin(t), 48, min_fixed=-1, max_fixed=1))
+            v1, n1 = bf16_of(x[i] * c - x[i + h2] * s)
+            v2, n2 = bf16_of(x[i + h2] * c + x[i] * s)
+            r[i], r[i + h2] = v1, v2
+            near = near or n1 or n2
+    n, nn = _l2_exact(r, f32_to_fraction(eps32))
+    near = near or any(nn)
+    out = []
+    for v, sc in zip(n, scale):
+        o, f = bf16_of(fp32_of(v * f32_to_fraction(float(sc)))[0])
+        out.append(o)
+        near = near or f
+    return n, out, near

@@ -40,7 +40,8 @@ from .bf16 import bf16_rne, bf16_value
 __all__ = ["eps_as_passed", "l2_rows", "slerp_rows", "slerp_rows_detail",
            "weight_rownorm_gain", "sum_sq", "l2_backward_values", "l2_rows_backward",
            "rownorm_backward_values", "weight_rownorm_gain_backward",
-           "gate_gated_row", "gate_l2_rows", "swiglu_product_row", "swiglu_l2_rows"]
+           "gate_gated_row", "gate_l2_rows", "swiglu_product_row", "swiglu_l2_rows",
+           "rope_angles", "qk_rotated_heads", "qk_rows_l2"]
 
 
 def eps_as_passed(eps: float) -> float:
@@ -276,3 +277,60 @@ def swiglu_l2_rows(g_bits: np.ndarray, u_bits: np.ndarray, sug: np.ndarray, suu:
     """bf16 bits of l2 over each SwiGLU product row."""
     p = bf16_value(swiglu_product_row(g_bits, u_bits, sug, suu))
     return bf16_rne(_l2_of_values(p, eps_as_passed(eps))).reshape(np.shape(g_bits))
+
+
+# ------------------------------------------------------------------ q/k rows
+#
+# TensorFold PR #1260, the q/k commit (dory.py's order): rotate-half RoPE on
+# the projection's bf16 rows with the fp32 angle pos * inv, rounded to bf16
+# (the rotated head); then each head's L2 norm with eps on the sum, rounded to
+# bf16 (the normalized head); then q times an fp32 scale vector; k is its
+# normalized head.  For a head x = [x1, x2] (halves of head_dim / 2) and
+# frequency i:  rot_i = x1_i cos(t_i) - x2_i sin(t_i),
+#               rot_{i + hd/2} = x2_i cos(t_i) + x1_i sin(t_i).
+#
+# Readings: the angle is the fp32 product fp32(pos) * inv_freq_i (IEEE, as
+# torch forms it; numpy float32 here); cos and sin of that fp32 value are
+# float64.  The scale product is one fp32 multiply rounded to bf16, the form
+# of the other scaled rows.  The scale vector covers the whole q row
+# (n_q_heads * head_dim values).
+
+def rope_angles(positions: np.ndarray, inv_freq: np.ndarray) -> np.ndarray:
+    """float64 values of the fp32 angles fp32(pos) * inv_freq, [rows, hd/2]."""
+    p = np.asarray(positions).astype(np.float32)[:, None]
+    with np.errstate(all="ignore"):
+        return (p * np.asarray(inv_freq, np.float32)[None, :]).astype(np.float64)
+
+
+def qk_rotated_heads(x_bits: np.ndarray, theta: np.ndarray, head_dim: int) -> np.ndarray:
+    """bf16 bits of every head rotated (rounding point 1), same layout as x."""
+    x = bf16_value(np.atleast_2d(x_bits))
+    rows, width = x.shape
+    h2 = head_dim // 2
+    xh = x.reshape(rows, width // head_dim, head_dim)
+    x1, x2 = xh[..., :h2], xh[..., h2:]
+    c = np.cos(theta)[:, None, :]
+    s = np.sin(theta)[:, None, :]
+    with np.errstate(all="ignore"):
+        rot = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+    return bf16_rne(rot.reshape(rows, width))
+
+
+def _l2_heads(r_bits: np.ndarray, head_dim: int, eps: float) -> np.ndarray:
+    rows, width = r_bits.shape
+    r = bf16_value(r_bits).reshape(rows * (width // head_dim), head_dim)
+    return bf16_rne(_l2_of_values(r, eps_as_passed(eps))).reshape(rows, width)
+
+
+def qk_rows_l2(q_bits: np.ndarray, k_bits: Optional[np.ndarray], positions: np.ndarray,
+               inv_freq: np.ndarray, q_scale: np.ndarray, head_dim: int, eps: float = 1e-6):
+    """(q_out bits, k_out bits or None): RoPE, per-head L2, q scaled."""
+    theta = rope_angles(positions, inv_freq)
+    nq = _l2_heads(qk_rotated_heads(q_bits, theta, head_dim), head_dim, eps)
+    with np.errstate(all="ignore"):
+        q_out = bf16_rne((bf16_value(nq).astype(np.float32)
+                          * np.asarray(q_scale, np.float32)[None, :]).astype(np.float64))
+    k_out = None
+    if k_bits is not None and np.size(k_bits):
+        k_out = _l2_heads(qk_rotated_heads(k_bits, theta, head_dim), head_dim, eps)
+    return q_out, k_out
