@@ -23,6 +23,8 @@
  *  ds_swiglu_l2_rows      rows for Dory: the output gate and the scaled SwiGLU,
  *                         each rounded to bf16 and then L2-normalised over the
  *                         whole row.
+ *  ds_qk_rows_l2          same PR, the q/k commit: rotate-half RoPE, each
+ *                         head's L2 norm, q's scale vector (dory.py's order).
  *  ds_l2_rows_backward    the gradient of ds_l2_rows' s -> s / sqrt(sum s^2 +
  *                         eps): ds = (dy - s <s,dy> / D^2) / D, shared by x
  *                         and r (the bf16 rounding of s passes it through).
@@ -77,7 +79,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10200          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10300          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -183,6 +185,39 @@ int ds_gate_l2_rows(const uint16_t* o, const uint16_t* g, const float* sg, uint1
  */
 int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, const float* suu,
                       uint16_t* y, int64_t rows, int64_t cols, float eps, ds_stream_t stream);
+
+/*
+ * ds_qk_rows_l2 -- q and k heads of a token row: RoPE, unit-length heads, q scale.
+ * (TensorFold PR #1260, the q/k commit, in dory.py's order.)
+ *
+ * For each row (token) with position p and each head x of q and of k
+ * (head_dim = HD values, halves x1 = x[0 : HD/2], x2 = x[HD/2 : HD]):
+ *   t_i  = fp32(p) * inv_freq_i                            fp32 product
+ *   r    = bf16([x1 cos t - x2 sin t, x2 cos t + x1 sin t])  rotate-half RoPE,
+ *          each product and sum an fp32 operation; cos, sin: the device
+ *          library's sincosf of the fp32 angle
+ *   n    = bf16(r / sqrt(sum r^2 + eps))                    per head
+ *   q_out = bf16(n * q_scale)  (one fp32 product per element); k_out = n
+ *
+ * q, q_out : [rows, ldq] / [rows, ldq_out] bf16 bit patterns, the first
+ *            n_q_heads * head_dim elements of each row used; 16-byte aligned,
+ *            strides multiples of 8.  q_out may be q itself (with ldq_out ==
+ *            ldq); otherwise it must not overlap any input.
+ * k, k_out : likewise for the n_kv_heads heads of k (may be NULL when
+ *            n_kv_heads == 0).
+ * positions: [rows] int32 token positions (converted to fp32, exact below
+ *            2^24); 4-byte aligned.
+ * inv_freq : [head_dim / 2] fp32 (formed by the caller, e.g. theta^(-2i/HD));
+ *            16-byte aligned.
+ * q_scale  : [n_q_heads * head_dim] fp32 (formed by the caller); 16-byte aligned.
+ * head_dim : 128 or 256.  eps: finite, >= 0.  rows >= 0 (0: no-op).
+ * The KV-cache writes that follow in a serving stack are the caller's.
+ */
+int ds_qk_rows_l2(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk,
+                  const int32_t* positions, const float* inv_freq, const float* q_scale,
+                  uint16_t* q_out, int64_t ldq_out, uint16_t* k_out, int64_t ldk_out,
+                  int64_t rows, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                  float eps, ds_stream_t stream);
 
 /*
  * One weight matrix of a ds_weight_rownorm_gain call.

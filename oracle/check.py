@@ -50,7 +50,7 @@ __all__ = ["contract_bf16", "contract_rel", "Report", "admissible_l2_rows",
            "ordered", "slerp_unique_mask", "GRAD_SLACK", "l2_grad_terms",
            "rownorm_grad_terms", "contract_grad", "admissible_l2_backward",
            "admissible_rownorm_backward", "EXPF_ULPS", "gate_candidates", "swiglu_candidates",
-           "admissible_act_rows", "act_unique_mask"]
+           "admissible_act_rows", "act_unique_mask", "COSF_ULPS", "admissible_qk_rows"]
 
 
 def default_depth(cols: int) -> int:
@@ -730,3 +730,117 @@ def admissible_act_rows(got_bits, c_lo, c_hi, exact_bits=None, finite_rows=None,
         for j in bad[: max(0, 20 - len(rep.first_bad))]:
             rep.first_bad.append(int(base + j))
     return rep
+
+
+# ------------------------------------------------------------------ q/k rows
+#
+# The fp32 run modelled for qk_rows_l2: the angle is the IEEE product (as the
+# oracle forms it); cos and sin are within COSF_ULPS units in the last place
+# of the float64 values of the fp32 angle; each of the four products and the
+# two sums of the rotation rounds once; then the head's l2 over every
+# admissible rotated value (as for the activation rows); then q's scale is
+# one fp32 product rounded to bf16 -- a monotone map of the normalized value,
+# so the admissible q outputs are the images of the admissible n range.
+
+COSF_ULPS = 2.0
+
+
+def _trig_bounds(v):
+    a = np.abs(v)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 23)
+    d = COSF_ULPS * ulp + ETA
+    return v - d, v + d
+
+
+def _mul_iv(x, lo, hi):
+    """Bounds of fl(x * c) for exact x and c in [lo, hi]."""
+    with np.errstate(all="ignore"):
+        a, b = x * lo, x * hi
+    return _outward(np.minimum(a, b), np.maximum(a, b))
+
+
+def _l2_range(c_lo, c_hi, eps64, depth):
+    """Ordered bf16 bounds of bf16(l2) over heads whose values lie in [c_lo, c_hi]."""
+    sq_a, sq_b = c_lo ** 2, c_hi ** 2
+    sq_lo = np.where((c_lo <= 0) & (c_hi >= 0), 0.0, np.minimum(sq_a, sq_b))
+    s_lo, s_hi = _sum_bounds(sq_lo, np.maximum(sq_a, sq_b), depth)
+    inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, eps64)
+    outs = []
+    for c in (c_lo, c_hi):
+        lo, hi = _product_bounds(c, c, inv_lo, inv_hi)
+        outs.append((ordered(bf16_rne(lo)), ordered(bf16_rne(hi))))
+    return np.minimum(outs[0][0], outs[1][0]), np.maximum(outs[0][1], outs[1][1])
+
+
+def _ordered_to_bits(o):
+    o = np.asarray(o, np.int64)
+    return np.where(o < 0, 0x8000 | (-o), o).astype(np.uint16)
+
+
+def admissible_qk_rows(got_q, got_k, q_bits, k_bits, positions, inv_freq, q_scale, head_dim,
+                       eps: float = 1e-6, depth: Optional[int] = None):
+    """Strict check of qk_rows_l2: (q Report, k Report, q unique mask, k unique mask).
+
+    A unique element is one whose admissible output is a single bf16 value.
+    Heads holding a non-finite input are compared with the oracle exactly.
+    """
+    from .rows import qk_rows_l2 as ref
+    from .rows import rope_angles
+    hd, h2 = head_dim, head_dim // 2
+    depth = default_depth(hd) if depth is None else depth
+    eps64 = eps_as_passed(eps)
+    theta = rope_angles(positions, inv_freq)
+    c_lo, c_hi = _trig_bounds(np.cos(theta))
+    s_lo, s_hi = _trig_bounds(np.sin(theta))
+    reps, masks = [], []
+    for which, (got, x_bits) in enumerate(((got_q, q_bits), (got_k, k_bits))):
+        rep = Report()
+        if x_bits is None or not np.size(x_bits):
+            reps.append(rep)
+            masks.append(None)
+            continue
+        got = np.atleast_2d(got)
+        x = bf16_value(np.atleast_2d(x_bits))
+        rows, width = x.shape
+        uniq = np.zeros((rows, width), bool)
+        want_q, want_k = ref(q_bits, k_bits, positions, inv_freq, q_scale, hd, eps)
+        want = want_q if which == 0 else want_k
+        for i in range(rows):
+            for h in range(width // hd):
+                sl = slice(h * hd, (h + 1) * hd)
+                base = i * width + h * hd
+                xh = x[i, sl]
+                if not np.isfinite(xh).all():
+                    _judge(got[i, sl], xh, xh, want[i, sl], np.ones(hd, bool), True, base, rep)
+                    continue
+                x1, x2 = xh[:h2], xh[h2:]
+                a1, b1 = _mul_iv(x1, c_lo[i], c_hi[i])
+                a2, b2 = _mul_iv(x2, s_lo[i], s_hi[i])
+                lo1, hi1 = _outward(a1 - b2, b1 - a2)              # x1 c - x2 s
+                a3, b3 = _mul_iv(x2, c_lo[i], c_hi[i])
+                a4, b4 = _mul_iv(x1, s_lo[i], s_hi[i])
+                lo2, hi2 = _outward(a3 + a4, b3 + b4)              # x2 c + x1 s
+                r_lo = bf16_value(bf16_rne(np.concatenate([lo1, lo2])))
+                r_hi = bf16_value(bf16_rne(np.concatenate([hi1, hi2])))
+                ol, oh = _l2_range(r_lo, r_hi, eps64, depth)
+                if which == 0:
+                    sc = np.asarray(q_scale, np.float32)[sl]
+                    f = []
+                    for o in (ol, oh):
+                        nv = bf16_value(_ordered_to_bits(o)).astype(np.float32)
+                        with np.errstate(all="ignore"):
+                            f.append(ordered(bf16_rne((nv * sc).astype(np.float64))))
+                    ol, oh = np.minimum(f[0], f[1]), np.maximum(f[0], f[1])
+                g = ordered(got[i, sl])
+                inside = (g >= ol) & (g <= oh)
+                uniq[i, sl] = ol == oh
+                bad = np.nonzero(~inside)[0]
+                rep.n += hd
+                rep.outside += bad.size
+                rep.two += int(((oh - ol) == 1).sum())
+                rep.wide += int(((oh - ol) > 1).sum())
+                for j in bad[: max(0, 20 - len(rep.first_bad))]:
+                    rep.first_bad.append(int(base + j))
+        reps.append(rep)
+        masks.append(uniq)
+    return reps[0], reps[1], masks[0], masks[1]

@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.ds_gate_l2_rows.restype = ctypes.c_int
         L.ds_swiglu_l2_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, vp]
         L.ds_swiglu_l2_rows.restype = ctypes.c_int
+        i32 = ctypes.c_int32
+        L.ds_qk_rows_l2.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, vp, i64, i64,
+                                    i32, i32, i32, f32, vp]
+        L.ds_qk_rows_l2.restype = ctypes.c_int
         L.ds_l2_rows_backward.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
         L.ds_l2_rows_backward.restype = ctypes.c_int
         L.ds_weight_rownorm_gain_backward.argtypes = [ctypes.POINTER(RownormGradDesc),
@@ -356,3 +360,42 @@ def ds_swiglu_l2_rows(g, u, sug, suu, eps: float = 1e-6, out=None, stream=None):
                                      _stream_of(g, stream))
     _check(st, "ds_swiglu_l2_rows")
     return out
+
+
+def ds_qk_rows_l2(q, k, positions, inv_freq, q_scale, head_dim: int, eps: float = 1e-6,
+                  q_out=None, k_out=None, stream=None):
+    """RoPE, per-head L2 and q's scale on q [rows, >= nq*hd] and k [rows, >= nk*hd].
+
+    ``q``/``k`` may be strided row views (a fused projection's slices); the
+    number of heads is the used width / head_dim, given by ``q_scale``'s
+    length for q and by k's width for k.  Returns (q_out, k_out).
+    """
+    torch = _torch()
+    nq = q_scale.shape[0] // head_dim
+    rows = q.shape[0]
+    for t, name in ((q, "q"),) + (((k, "k"),) if k is not None else ()):
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or t.dim() != 2 \
+                or t.stride(1) != 1 or t.device.type != "cuda":
+            raise ValueError(f"{name}: expected a bf16 [rows, cols] HIP tensor with unit column stride")
+    nk = 0 if k is None else k.shape[1] // head_dim
+    if q.shape[1] < nq * head_dim or (k is not None and k.shape[1] % head_dim):
+        raise ValueError("q must hold n_q_heads * head_dim columns; k a whole number of heads")
+    if positions.dtype != torch.int32 or positions.shape != (rows,):
+        raise ValueError("positions: expected int32 [rows]")
+    if inv_freq.dtype != torch.float32 or inv_freq.shape != (head_dim // 2,):
+        raise ValueError("inv_freq: expected fp32 [head_dim / 2]")
+    if q_scale.dtype != torch.float32 or q_scale.dim() != 1:
+        raise ValueError("q_scale: expected fp32 [n_q_heads * head_dim]")
+    if q_out is None:
+        q_out = torch.empty(rows, nq * head_dim, dtype=q.dtype, device=q.device)
+    if k is not None and k_out is None:
+        k_out = torch.empty(rows, nk * head_dim, dtype=k.dtype, device=k.device)
+    with torch.cuda.device(q.device):
+        st = lib().ds_qk_rows_l2(
+            q.data_ptr(), q.stride(0), None if k is None else k.data_ptr(),
+            0 if k is None else k.stride(0), positions.data_ptr(), inv_freq.data_ptr(),
+            q_scale.data_ptr(), q_out.data_ptr(), q_out.stride(0),
+            None if k_out is None else k_out.data_ptr(), 0 if k_out is None else k_out.stride(0),
+            rows, nq, nk, head_dim, float(eps), _stream_of(q, stream))
+    _check(st, "ds_qk_rows_l2")
+    return q_out, k_out

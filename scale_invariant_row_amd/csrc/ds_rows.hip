@@ -445,6 +445,109 @@ int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, co
                                                   (hipStream_t)stream));
 }
 
+namespace {
+
+// Bytes a strided [rows, width] bf16 view spans.
+size_t span_bytes(int64_t rows, int64_t ld, int64_t width) {
+  return rows == 0 ? 0 : ((size_t)(rows - 1) * (size_t)ld + (size_t)width) * 2;
+}
+
+int64_t floor_div(int64_t a, int64_t b) { return a / b - ((a % b != 0) && ((a < 0) != (b < 0))); }
+
+// Two [rows, wa] and [rows, wb] bf16 views at a and b share an element.  With
+// one row stride ld (>= wa, wb) the test is exact: element (ra, ca) of a is
+// element (rb, cb) of b when (ra - rb) ld = de + cb - ca, de = (b - a) / 2,
+// so some multiple k ld with |k| < rows must lie in (de - wa, de + wb).
+// Otherwise it compares the spans.
+bool views_overlap(const void* a, int64_t lda, int64_t wa, const void* b, int64_t ldb, int64_t wb,
+                   int64_t rows) {
+  if (rows == 0 || wa == 0 || wb == 0 || a == nullptr || b == nullptr) return false;
+  const intptr_t d = reinterpret_cast<intptr_t>(b) - reinterpret_cast<intptr_t>(a);
+  if (lda != ldb || d % 2 != 0)
+    return overlaps(a, span_bytes(rows, lda, wa), b, span_bytes(rows, ldb, wb));
+  const int64_t de = d / 2, ld = lda;
+  const int64_t k_lo = std::max<int64_t>(floor_div(de - wa, ld) + 1, -(rows - 1));
+  const int64_t k_hi = std::min<int64_t>(floor_div(de + wb - 1, ld), rows - 1);
+  for (int64_t k = k_lo; k <= k_hi; ++k) {
+    const int64_t t = k * ld;          // t in [de - wa + 1, de + wb - 1] by construction
+    if (t > de - wa && t < de + wb) return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+int ds_qk_rows_l2(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk,
+                  const int32_t* positions, const float* inv_freq, const float* q_scale,
+                  uint16_t* q_out, int64_t ldq_out, uint16_t* k_out, int64_t ldk_out,
+                  int64_t rows, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                  float eps, ds_stream_t stream) {
+  if (rows < 0 || n_q_heads < 0 || n_kv_heads < 0) return DS_ERR_SHAPE;
+  if (head_dim != 128 && head_dim != 256) return DS_ERR_SHAPE;
+  if (!finite_nonneg(eps)) return DS_ERR_ARG;
+  const int64_t wq = (int64_t)n_q_heads * head_dim, wk = (int64_t)n_kv_heads * head_dim;
+  if (wq > (1 << 24) || wk > (1 << 24)) return DS_ERR_SHAPE;
+  if (rows == 0 || wq + wk == 0) return DS_OK;
+  if (positions == nullptr || inv_freq == nullptr) return DS_ERR_NULL;
+  if (wq > 0 && (q == nullptr || q_out == nullptr || q_scale == nullptr)) return DS_ERR_NULL;
+  if (wk > 0 && (k == nullptr || k_out == nullptr)) return DS_ERR_NULL;
+  if (wq > 0 && (ldq < wq || ldq_out < wq || ldq % 8 != 0 || ldq_out % 8 != 0)) return DS_ERR_SHAPE;
+  if (wk > 0 && (ldk < wk || ldk_out < wk || ldk % 8 != 0 || ldk_out % 8 != 0)) return DS_ERR_SHAPE;
+  const int64_t ldmax = std::max(std::max(ldq, ldq_out), std::max(ldk, ldk_out));
+  if (rows > (INT64_MAX / 8) / std::max<int64_t>(ldmax, 1)) return DS_ERR_SHAPE;
+  if (!aligned(positions, 4) || !aligned(inv_freq, 16) ||
+      (wq > 0 && (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(q_scale, 16))) ||
+      (wk > 0 && (!aligned(k, 16) || !aligned(k_out, 16))))
+    return DS_ERR_ALIGN;
+  // outputs: each exactly its input (same stride: in place) or sharing no element with
+  // it; never sharing an element with the other input, the other output or the vectors
+  // (q and k may be column slices of one fused projection row)
+  const size_t bqo = wq > 0 ? span_bytes(rows, ldq_out, wq) : 0;
+  const size_t bko = wk > 0 ? span_bytes(rows, ldk_out, wk) : 0;
+  auto vectors_clear = [&](const void* out, size_t nb) {
+    return !overlaps(out, nb, positions, (size_t)rows * 4) &&
+           !overlaps(out, nb, inv_freq, (size_t)head_dim * 2) &&
+           !(wq > 0 && overlaps(out, nb, q_scale, (size_t)wq * 4));
+  };
+  if (wq > 0) {
+    const bool in_place = q_out == q && ldq_out == ldq;
+    if (!in_place && views_overlap(q_out, ldq_out, wq, q, ldq, wq, rows)) return DS_ERR_ARG;
+    if (wk > 0 && views_overlap(q_out, ldq_out, wq, k, ldk, wk, rows)) return DS_ERR_ARG;
+    if (!vectors_clear(q_out, bqo)) return DS_ERR_ARG;
+  }
+  if (wk > 0) {
+    const bool in_place = k_out == k && ldk_out == ldk;
+    if (!in_place && views_overlap(k_out, ldk_out, wk, k, ldk, wk, rows)) return DS_ERR_ARG;
+    if (wq > 0 && views_overlap(k_out, ldk_out, wk, q, ldq, wq, rows)) return DS_ERR_ARG;
+    if (!vectors_clear(k_out, bko)) return DS_ERR_ARG;
+  }
+  if (wq > 0 && wk > 0 && views_overlap(q_out, ldq_out, wq, k_out, ldk_out, wk, rows))
+    return DS_ERR_ARG;
+
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st != DS_OK) return st;
+  dsr::QkArgs a{};
+  a.q = q;
+  a.k = k;
+  a.pos = positions;
+  a.inv_freq = inv_freq;
+  a.q_scale = q_scale;
+  a.qo = q_out;
+  a.ko = k_out;
+  a.ldq = ldq;
+  a.ldk = ldk;
+  a.ldqo = ldq_out;
+  a.ldko = ldk_out;
+  a.rows = rows;
+  a.nq = n_q_heads;
+  a.nk = n_kv_heads;
+  a.eps = eps;
+  (void)hipGetLastError();
+  return launch_status(dsr::launch_qk_rows_l2(head_dim, a, grid_for((rows + 3) / 4, cus),
+                                              (hipStream_t)stream));
+}
+
 int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t stream) {
   if (n < 0) return DS_ERR_ARG;
   if (n == 0) return DS_OK;

@@ -846,6 +846,175 @@ act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
   }
 }
 
+// ----------------------------------------------------------------- q/k rows
+//
+// TensorFold PR #1260's q/k row kernel, in dory.py's order: rotate-half RoPE
+// on the projection's bf16 heads with the fp32 angle fp32(pos) * inv_i,
+// rounded to bf16 (r); each head's L2 norm with eps, rounded (n); q's heads
+// times an fp32 scale vector, rounded; k's heads are n.
+//   r_i        = bf16(x_i cos t_i - x_{i+HD/2} sin t_i)        i < HD/2
+//   r_{i+HD/2} = bf16(x_{i+HD/2} cos t_i + x_i sin t_i)
+// each product and the sum rounded once in fp32 (no contraction).
+//
+// One wave per token row.  A head of HD values is spread over L = HD/4
+// lanes, four values (8 bytes) each: lane l of a head holds elements
+// 4 (l mod L/2) .. +3 of half l / (L/2), so its rotate-half partner is L/2
+// lanes away -- one permlane swap (32 for HD = 256, 16 for HD = 128) gives
+// every lane both halves, and 64/L heads go through the wave at a time.  A
+// lane's four frequencies are the same for every head of the row, so cos
+// and sin are computed once per row (the device library's sincosf, with its
+// full-range argument reduction) and reused for all q and k heads.  Heads
+// are loaded four wave-steps at a time to keep several loads in flight.
+
+struct QkArgs {
+  const uint16_t* q;
+  const uint16_t* k;            // may be null when nk == 0
+  const int32_t* pos;
+  const float* inv_freq;        // [HD/2]
+  const float* q_scale;         // [nq * HD]
+  uint16_t* qo;
+  uint16_t* ko;
+  int64_t ldq, ldk, ldqo, ldko; // row strides in elements
+  int64_t rows;
+  int32_t nq, nk;
+  float eps;
+};
+
+template <int L>
+__device__ __forceinline__ float head_sum(float v) {
+  if constexpr (L == 64) {
+    return wave_sum(v);
+  } else {                      // two heads per wave: sum each 32-lane half
+    v = v + dpp_f<0xB1>(v);
+    v = v + dpp_f<0x4E>(v);
+    v = v + dpp_f<0x141>(v);
+    v = v + dpp_f<0x140>(v);
+    const f32x2_t p = swap16(v);
+    return p.x + p.y;
+  }
+}
+
+template <int L>
+__device__ __forceinline__ float head_max(float v) {
+  if constexpr (L == 64) {
+    return wave_max(v);
+  } else {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    const f32x2_t p = swap16(v);
+    return fmaxf(p.x, p.y);
+  }
+}
+
+// (low-half value, high-half value) of a packed dword between rotate-half partners
+template <int L>
+__device__ __forceinline__ void partner_pair(uint32_t u, uint32_t& lo, uint32_t& hi) {
+  if constexpr (L == 64) {
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = p[0];
+    hi = p[1];
+  } else {
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = p[0];
+    hi = p[1];
+  }
+}
+
+template <int HD>
+__global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
+  constexpr int L = HD / 4;             // lanes per head
+  constexpr int HPW = 64 / L;           // heads per wave step
+  constexpr int CH = 4;                 // wave steps loaded at once
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ll = lane % L;              // lane within its head
+  const int hsub = lane / L;            // head within the wave step
+  const bool upper = ll >= L / 2;       // holds the second half of the head
+  const int e0 = (upper ? HD / 2 : 0) + 4 * (ll % (L / 2));    // first element of the lane
+  const int f0 = 4 * (ll % (L / 2));                           // first frequency of the lane
+  const RowBuf fb(a.inv_freq, (uint32_t)(HD / 2) * 4u);
+  const f32x4_t inv4 = fb.ld16f_cached(f0 * 4);
+  const float invf[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
+  const RowBuf sb(a.q_scale, (uint32_t)a.nq * (uint32_t)HD * 4u);
+  const int nsteps[2] = {(a.nq + HPW - 1) / HPW, (a.nk + HPW - 1) / HPW};
+
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
+    const float pf = (float)a.pos[row];
+    float c[4], s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sincosf(pf * invf[j], &s[j], &c[j]);
+
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {          // q's heads, then k's
+      const int nh = which == 0 ? a.nq : a.nk;
+      if (nh == 0) continue;
+      const uint16_t* src = which == 0 ? a.q + row * a.ldq : a.k + row * a.ldk;
+      uint16_t* dst = which == 0 ? a.qo + row * a.ldqo : a.ko + row * a.ldko;
+      const uint32_t bytes = (uint32_t)nh * (uint32_t)HD * 2u;
+      const RowBuf ib(src, bytes), ob(dst, bytes);
+      for (int st0 = 0; st0 < nsteps[which]; st0 += CH) {
+        u32x2_t x[CH];
+#pragma unroll
+        for (int c4 = 0; c4 < CH; ++c4) {
+          const int h = (st0 + c4) * HPW + hsub;      // past the row: the range check reads 0
+          x[c4] = ib.ld8((h * HD + e0) * 2);
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < CH; ++c4) {
+          if (st0 + c4 >= nsteps[which]) break;        // uniform
+          const int h = (st0 + c4) * HPW + hsub;
+          uint32_t lo0, hi0, lo1, hi1;
+          partner_pair<L>(x[c4].x, lo0, hi0);
+          partner_pair<L>(x[c4].y, lo1, hi1);
+          const float x1[4] = {bf_lo(lo0), bf_hi(lo0), bf_lo(lo1), bf_hi(lo1)};
+          const float x2[4] = {bf_lo(hi0), bf_hi(hi0), bf_lo(hi1), bf_hi(hi1)};
+          float rot[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p1 = (upper ? x2[j] : x1[j]) * c[j];
+            const float p2 = (upper ? x1[j] : x2[j]) * s[j];
+            rot[j] = upper ? p1 + p2 : p1 - p2;
+          }
+          uint32_t r[2] = {pack_bf16(rot[0], rot[1]), pack_bf16(rot[2], rot[3])};
+          float rv[4] = {bf_lo(r[0]), bf_hi(r[0]), bf_lo(r[1]), bf_hi(r[1])};
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(rv[j], rv[j], acc);
+          float T = head_sum<L>(acc) + a.eps;
+          int sh = 0;
+          const bool need = T == __builtin_inff() || T < kTiny;
+          if (__builtin_amdgcn_ballot_w64(need) != 0) {  // any head of this wave step
+            float m = fmaxf(fmaxf(fabsf(rv[0]), fabsf(rv[1])), fmaxf(fabsf(rv[2]), fabsf(rv[3])));
+            m = head_max<L>(m);
+            if (need && (m > 0.f || a.eps > 0.f) && m < __builtin_inff()) sh = rescue_shift(m, a.eps);
+            float acc2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float v = ldexpf(rv[j], sh);
+              acc2 = __builtin_fmaf(v, v, acc2);
+            }
+            const float T2 = head_sum<L>(acc2) + ldexpf(a.eps, 2 * sh);
+            if (sh != 0) T = T2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rv[j] = ldexpf(rv[j], sh);
+          }
+          const float inv = inv_sqrt(T);
+          uint32_t n[2] = {pack_bf16(rv[0] * inv, rv[1] * inv), pack_bf16(rv[2] * inv, rv[3] * inv)};
+          if (which == 0) {
+            const f32x4_t sc = sb.ld16f_cached((h * HD + e0) * 4);
+            n[0] = pack_bf16(bf_lo(n[0]) * sc.x, bf_hi(n[0]) * sc.y);
+            n[1] = pack_bf16(bf_lo(n[1]) * sc.z, bf_hi(n[1]) * sc.w);
+          }
+          const u32x2_t o = {n[0], n[1]};
+          ob.st8(o, (h * HD + e0) * 2);
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------- weight rownorm+gain
 
 // One matrix of a ragged call, as the kernel reads it.  Items are groups of

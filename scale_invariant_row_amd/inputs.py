@@ -39,6 +39,10 @@ rownorm_gain_bwd_11008x   one 11008x4096 matrix (the DragonScale README's
                           dL/dW_eff ~ N(0,1)
 ========================  =======================================================
 
+qk_rows_l2_8192_h16x4     8192 token rows, head_dim 256, 16 q heads, 4 kv heads:
+_d256                     q, k ~ N(0,1) bf16; positions 0.. for two thirds of
+                          the rows and 199,800.. for the last third; inv_freq =
+                          10000^(-2i/256) in fp32; q_scale ~ U(0.5, 2) fp32
 gate_l2_rows_8192x4096    o, g ~ N(0,1) bf16; sg ~ U(0.5, 2) fp32 per column
 swiglu_l2_rows_8192x7168  g, u ~ N(0,1) bf16; sug, suu ~ U(0.5, 2) fp32 per column
 
@@ -58,7 +62,7 @@ __all__ = [
     "to_bf16_bits", "l2_case", "slerp_case", "rownorm_case",
     "transformer_linears", "stress_l2_case", "WORKLOADS", "make",
     "L2GradCase", "RownormGradCase", "grad_bits", "l2_grad_case", "rownorm_grad_case",
-    "ActCase", "gate_case", "swiglu_case",
+    "ActCase", "gate_case", "swiglu_case", "QkCase", "qk_case", "rope_inv_freq",
 ]
 
 
@@ -153,6 +157,20 @@ class ActCase:
     b: np.ndarray
     s0: np.ndarray
     s1: Optional[np.ndarray]
+    eps: float = 1e-6
+
+
+@dataclass
+class QkCase:
+    """Inputs of qk_rows_l2: q and k rows (heads concatenated), positions,
+    the fp32 inverse frequencies and q's fp32 scale vector."""
+    name: str
+    q: np.ndarray                     # uint16 [rows, nq * hd]
+    k: Optional[np.ndarray]           # uint16 [rows, nk * hd]
+    pos: np.ndarray                   # int32 [rows]
+    inv_freq: np.ndarray              # float32 [hd / 2]
+    q_scale: np.ndarray               # float32 [nq * hd]
+    head_dim: int
     eps: float = 1e-6
 
 
@@ -281,6 +299,24 @@ def swiglu_case(rows: int, cols: int, seed: int, name: Optional[str] = None) -> 
     return ActCase(name or f"swiglu_l2_rows_{rows}x{cols}", g, u, sug, suu)
 
 
+def rope_inv_freq(head_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """theta^(-2i/head_dim), i < head_dim/2, in float64, rounded to fp32."""
+    return (theta ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)).astype(np.float32)
+
+
+def qk_case(rows: int, nq: int, nk: int, head_dim: int, seed: int, far: float = 1 / 3,
+            far_start: int = 199_800, name: Optional[str] = None) -> QkCase:
+    """Rows at positions 0, 1, ... and, for the last `far` of them, far_start, ..."""
+    gq, gk, gs = _streams(seed, 3)
+    q = to_bf16_bits(gq.standard_normal((rows, nq * head_dim)))
+    k = to_bf16_bits(gk.standard_normal((rows, nk * head_dim))) if nk else None
+    n_far = int(rows * far)
+    pos = np.concatenate([np.arange(rows - n_far), far_start + np.arange(n_far)]).astype(np.int32)
+    sc = gs.uniform(0.5, 2.0, nq * head_dim).astype(np.float32)
+    return QkCase(name or f"qk_rows_l2_{rows}_h{nq}x{nk}_d{head_dim}", q, k, pos,
+                  rope_inv_freq(head_dim), sc, head_dim)
+
+
 # name -> (description, builder, seed).  Seeds are 1000 + a fixed number.
 WORKLOADS = {
     "l2_rows_64x1024": (
@@ -325,6 +361,10 @@ WORKLOADS = {
         "swiglu_l2_rows, 8192 x 7168 bf16 (the MLP width): g, u ~ N(0,1), "
         "sug, suu ~ U(0.5, 2) fp32, eps 1e-6",
         lambda: swiglu_case(8192, 7168, 1011, name="swiglu_l2_rows_8192x7168")),
+    "qk_rows_l2_8192_h16x4_d256": (
+        "qk_rows_l2, 8192 token rows, head_dim 256, 16 q heads over 4 kv heads, a third "
+        "of the rows past position 199,800, inv_freq 10000^(-2i/256), q_scale ~ U(0.5, 2)",
+        lambda: qk_case(8192, 16, 4, 256, 1012, name="qk_rows_l2_8192_h16x4_d256")),
 }
 
 

@@ -171,3 +171,33 @@ def swiglu_model(g_bits, u_bits, sug, suu, eps=1e-6, round_a=True, round_b=True,
     if round_p:
         p = bf16_of_f32(p)
     return _l2_of_f32_rows(p.astype(np.float32), eps)
+
+
+# ------------------------------------------------------------------ q/k rows
+
+def qk_model(q_bits, k_bits, positions, inv_freq, q_scale, hd, eps=1e-6,
+             round_r=True, round_n=True):
+    """fp32 steps of qk_rows_l2; the controls leave the rotated head or the
+    normalized head unrounded."""
+    th = (np.asarray(positions).astype(np.float32)[:, None]
+          * np.asarray(inv_freq, np.float32)[None, :]).astype(np.float32)
+    c, s = np.cos(th)[:, None, :], np.sin(th)[:, None, :]
+
+    def heads(x_bits):
+        x = bf16_value(x_bits).astype(np.float32)
+        rows, width = x.shape
+        xh = x.reshape(rows, width // hd, hd)
+        x1, x2 = xh[..., :hd // 2], xh[..., hd // 2:]
+        rot = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1).astype(np.float32)
+        r = bf16_of_f32(rot) if round_r else rot
+        r2 = r.reshape(-1, hd)
+        inv = inv_norm(lane_sum_sq(r2), eps)
+        n = (r2 * inv[:, None]).astype(np.float32)
+        if round_n:
+            n = bf16_of_f32(n)
+        return n.reshape(rows, width)
+
+    nq = heads(q_bits)
+    q_out = bf16_rne((nq * np.asarray(q_scale, np.float32)).astype(np.float32).astype(np.float64))
+    k_out = bf16_rne(heads(k_bits).astype(np.float64)) if k_bits is not None else None
+    return q_out, k_out

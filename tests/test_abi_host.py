@@ -29,14 +29,14 @@ def test_exports_every_declared_function(L):
     names = B.header_functions()
     assert set(names) == {"ds_l2_rows", "ds_slerp_rows", "ds_weight_rownorm_gain",
                           "ds_l2_rows_backward", "ds_weight_rownorm_gain_backward",
-                          "ds_gate_l2_rows", "ds_swiglu_l2_rows",
+                          "ds_gate_l2_rows", "ds_swiglu_l2_rows", "ds_qk_rows_l2",
                           "ds_status_string", "ds_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10200
+    assert B.ds_version() == 10300
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -216,6 +216,43 @@ def test_activation_valid_args_reach_device_lookup(L):
     S1, S2 = C + 0x100000, C + 0x200000
     assert L.ds_gate_l2_rows(A, Bp, S1, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE      # y == o
     assert L.ds_swiglu_l2_rows(A, Bp, S1, S2, Bp, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE  # y == u
+
+
+def _qk(L, q=A, ldq=4096, k=Bp, ldk=1024, pos=C, inv=C + 0x10000, sc=C + 0x20000,
+        qo=C + 0x100000, ldqo=4096, ko=C + 0x4000000, ldko=1024, rows=4, nq=16, nk=4, hd=256,
+        eps=1e-6):
+    return L.ds_qk_rows_l2(q, ldq, k, ldk, pos, inv, sc, qo, ldqo, ko, ldko, rows, nq, nk, hd,
+                           eps, None)
+
+
+def test_qk_validation(L):
+    assert _qk(L, hd=64) == B.DS_ERR_SHAPE
+    assert _qk(L, nq=-1) == B.DS_ERR_SHAPE
+    assert _qk(L, ldq=4000) == B.DS_ERR_SHAPE                   # stride below the width
+    assert _qk(L, ldk=1028) == B.DS_ERR_SHAPE                   # stride not a multiple of 8
+    assert _qk(L, eps=-1.0) == B.DS_ERR_ARG
+    assert _qk(L, pos=None) == B.DS_ERR_NULL
+    assert _qk(L, sc=None) == B.DS_ERR_NULL
+    assert _qk(L, ko=None) == B.DS_ERR_NULL
+    assert _qk(L, inv=C + 0x10008) == B.DS_ERR_ALIGN
+    assert _qk(L, qo=C + 0x100008) == B.DS_ERR_ALIGN
+    assert _qk(L, qo=A + 64) == B.DS_ERR_ARG                    # q_out partly over q
+    assert _qk(L, ko=A + 2048) == B.DS_ERR_ARG                  # k_out over q
+    assert _qk(L, qo=A, ldqo=4104) == B.DS_ERR_ARG              # same base, other stride
+    assert _qk(L, rows=0, q=None, k=None, pos=None, inv=None) == B.DS_OK
+    assert _qk(L, nq=0, nk=0) == B.DS_OK
+
+
+@pytest.mark.skipif("not no_device()")
+def test_qk_fused_views_reach_device_lookup(L):
+    """q and k as column slices of one [rows, 6144] projection, updated in place."""
+    base = 0x60000000
+    q, k = base, base + 4096 * 2
+    assert _qk(L, q=q, ldq=6144, k=k, ldk=6144, qo=q, ldqo=6144, ko=k, ldko=6144) == \
+        B.DS_ERR_DEVICE
+    # writing q's output over k's slice is refused
+    assert _qk(L, q=q, ldq=6144, k=k, ldk=6144, qo=k - 2048, ldqo=6144, ko=k, ldko=6144) == \
+        B.DS_ERR_ARG
 
 
 def test_binding_raises_on_missing_library(monkeypatch):

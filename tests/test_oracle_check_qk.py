@@ -1,0 +1,53 @@
+"""The q/k check itself: a faithful fp32 run passes; the pages' two controls
+(TensorFold PR #1260's q/k commit: drop the rotated head's rounding, or q's
+normalized head's) fail the strict check."""
+import numpy as np
+import pytest
+
+import kernel_models as km
+from oracle.bf16 import bf16_rne
+from oracle.check import admissible_qk_rows, contract_bf16
+from oracle.rows import qk_rows_l2
+
+
+@pytest.fixture(scope="module")
+def qk_in():
+    rng = np.random.default_rng(331)
+    hd, rows = 256, 24
+    q = bf16_rne(rng.standard_normal((rows, 4 * hd)))
+    k = bf16_rne(rng.standard_normal((rows, 1 * hd)))
+    pos = np.concatenate([np.arange(16), 199_800 + np.arange(8)])
+    inv = (10000.0 ** (-np.arange(0, hd, 2) / hd)).astype(np.float32)
+    sc = rng.uniform(0.5, 3.0, 4 * hd).astype(np.float32)
+    return q, k, pos, inv, sc, hd
+
+
+def test_faithful_passes(qk_in):
+    q, k, pos, inv, sc, hd = qk_in
+    qo, ko = km.qk_model(q, k, pos, inv, sc, hd)
+    rq, rk, uq, uk = admissible_qk_rows(qo, ko, q, k, pos, inv, sc, hd)
+    assert rq.ok and rk.ok, (str(rq), str(rk))
+    assert uq.mean() > 0.97 and uk.mean() > 0.97
+    wq, wk = qk_rows_l2(q, k, pos, inv, sc, hd)
+    assert contract_bf16(qo, wq)[uq].all() and contract_bf16(ko, wk)[uk].all()
+
+
+@pytest.mark.parametrize("drop", ["round_r", "round_n"])
+def test_controls_fail(qk_in, drop):
+    q, k, pos, inv, sc, hd = qk_in
+    qo, ko = km.qk_model(q, k, pos, inv, sc, hd, **{drop: False})
+    rq, rk, _, _ = admissible_qk_rows(qo, ko, q, k, pos, inv, sc, hd)
+    assert rq.outside > 100, str(rq)
+
+
+def test_integer_heads_at_position_zero_are_exact():
+    """The pages' gate 4 for q/k: integer heads, no rotation, exact fp32 sums."""
+    rng = np.random.default_rng(332)
+    hd = 128
+    q = bf16_rne(rng.integers(-64, 65, (4, 2 * hd)).astype(float))
+    pos = np.zeros(4, np.int64)
+    inv = np.ones(hd // 2, np.float32)
+    sc = np.ones(2 * hd, np.float32)
+    qo, _ = km.qk_model(q, None, pos, inv, sc, hd)
+    rq, _, uq, _ = admissible_qk_rows(qo, None, q, None, pos, inv, sc, hd, depth=0)
+    assert rq.ok, str(rq)
