@@ -38,7 +38,7 @@ EPS = 1e-6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
                   "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip",
-                  "ds_rows.hip"]
+                  "inst_qk.hip", "ds_rows.hip"]
 
 
 def kernel_hash() -> str:
@@ -345,6 +345,38 @@ def main():
         t[0].data_ptr(), t[1].data_ptr(), sug7.data_ptr(), suu7.data_ptr(), t[2].data_ptr(),
         r, c, eps, sp), 4)
     ops["gate_l2_rows_8192x4096"] = op(gate_us, ROWS * 4096 * 6 + 4096 * 4, ROWS)
+
+    # ---- q/k rows: 16 q heads over 4 kv heads of 256, a third of the rows far
+    # along (positions 199,800..); q and k read and written, positions once per row
+    nq, nk, hd = 16, 4, 256
+    posv = torch.cat([torch.arange(ROWS - ROWS // 3), 199_800 + torch.arange(ROWS // 3)]).to(
+        device=dev, dtype=torch.int32)
+    invf = torch.from_numpy(inputs.rope_inv_freq(hd)).to(dev)
+    qsc = 0.5 + 1.5 * torch.rand(nq * hd, device=dev)
+    qk_sets = [(torch.randn(ROWS, nq * hd, device=dev).to(torch.bfloat16),
+                torch.randn(ROWS, nk * hd, device=dev).to(torch.bfloat16),
+                torch.empty(ROWS, nq * hd, dtype=torch.bfloat16, device=dev),
+                torch.empty(ROWS, nk * hd, dtype=torch.bfloat16, device=dev)) for _ in range(6)]
+
+    def qk(t):
+        return L.ds_qk_rows_l2(t[0].data_ptr(), nq * hd, t[1].data_ptr(), nk * hd,
+                               posv.data_ptr(), invf.data_ptr(), qsc.data_ptr(),
+                               t[2].data_ptr(), nq * hd, t[3].data_ptr(), nk * hd,
+                               ROWS, nq, nk, hd, eps, sp)
+    for i in range(4):
+        assert qk(qk_sets[i % 6]) == 0
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record(stream)
+    for i in range(60):
+        qk(qk_sets[i % 6])
+    b.record(stream)
+    torch.cuda.synchronize()
+    qk_us = a.elapsed_time(b) * 1e3 / 60
+    del qk_sets
+    torch.cuda.empty_cache()
+    qk_bytes = ROWS * (nq + nk) * hd * 2 * 2 + ROWS * 4 + hd // 2 * 4 + nq * hd * 4
+    ops["qk_rows_l2_8192_h16x4_d256"] = op(qk_us, qk_bytes, ROWS)
     ops["swiglu_l2_rows_8192x7168"] = op(swiglu_us, ROWS * 7168 * 6 + 7168 * 8, ROWS)
 
     ops["l2_rows_64x1024"] = op(c1_us, 64 * 1024 * 4, 64)
