@@ -21,7 +21,7 @@ from typing import List, Optional, Sequence, Tuple
 
 __all__ = ["bits_to_fraction", "round_fraction", "bf16_of", "fp32_of",
            "l2_row", "slerp_row", "rownorm_row", "l2_backward_row", "rownorm_backward_row",
-           "gate_row", "swiglu_row", "qk_head", "NEAR_TIE_REL"]
+           "gate_row", "swiglu_row", "qk_head", "rescale_row", "NEAR_TIE_REL"]
 
 PREC = 60
 NEAR_TIE_REL = Fraction(1, 10 ** 12)     # flag values this close to a midpoint
@@ -308,3 +308,39 @@ def qk_head(x_bits: Sequence[int], pos: int, inv_freq: Sequence[float], scale: S
         out.append(o)
         near = near or f
     return n, out, near
+
+
+# ------------------------------------------------------------ rescale method
+
+def rescale_row(w: Sequence[float], v: Optional[Sequence[float]], rho: float
+                ) -> Tuple[List[Fraction], Optional[List[Fraction]], List[bool]]:
+    """One row exactly: (fp32(rho w/||w||), fp32(v - w <w,v>/||w||^2) or None, flags).
+
+    Flags mark elements whose projection float64 cannot round within
+    SLACK_REL of its cancelling terms, or whose rescaled value is near a tie.
+    """
+    wf = [f32_to_fraction(float(x)) for x in w]
+    ss = sum((x * x for x in wf), Fraction(0))
+    if ss == 0:
+        return wf, None if v is None else [f32_to_fraction(float(x)) for x in v], [False] * len(wf)
+    near = [False] * len(wf)
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        root = _dec(ss).sqrt()
+        rf = f32_to_fraction(float(rho))
+        w_out = []
+        for j, x in enumerate(wf):
+            r, n = fp32_of(Fraction(_dec(rf * x) / root))
+            w_out.append(r)
+            near[j] = near[j] or n
+    v_out = None
+    if v is not None:
+        vf = [f32_to_fraction(float(x)) for x in v]
+        p = sum((a * b for a, b in zip(wf, vf)), Fraction(0))
+        pa = sum((abs(a * b) for a, b in zip(wf, vf)), Fraction(0))
+        v_out = []
+        for j, (x, y) in enumerate(zip(wf, vf)):
+            r, n = _round_with_slack(y - x * p / ss, SLACK_REL * (abs(y) + abs(x) * pa / ss), fp32_of)
+            v_out.append(r)
+            near[j] = near[j] or n
+    return w_out, v_out, near

@@ -41,7 +41,8 @@ __all__ = ["eps_as_passed", "l2_rows", "slerp_rows", "slerp_rows_detail",
            "weight_rownorm_gain", "sum_sq", "l2_backward_values", "l2_rows_backward",
            "rownorm_backward_values", "weight_rownorm_gain_backward",
            "gate_gated_row", "gate_l2_rows", "swiglu_product_row", "swiglu_l2_rows",
-           "rope_angles", "qk_rotated_heads", "qk_rows_l2"]
+           "rope_angles", "qk_rotated_heads", "qk_rows_l2",
+           "rescale_project_values", "rescale_project", "rescale_after_step"]
 
 
 def eps_as_passed(eps: float) -> float:
@@ -334,3 +335,53 @@ def qk_rows_l2(q_bits: np.ndarray, k_bits: Optional[np.ndarray], positions: np.n
     if k_bits is not None and np.size(k_bits):
         k_out = _l2_heads(qk_rotated_heads(k_bits, theta, head_dim), head_dim, eps)
     return q_out, k_out
+
+
+# ------------------------------------------------------------ rescale method
+#
+# DragonScale README, "Optimizer" (and the `method` option of "Patching
+# options": raw rows, rescaled by the optimizer after each step).  Per row of
+# a raw weight w, with w_hat = w / ||w||:
+#   before the step: g <- g - w_hat <w_hat, g>       (the gradient's radial part)
+#   after the step:  m <- m - w_hat <w_hat, m>       (the momentum's, same part)
+#                    w <- radius * w_hat             (back to its radius)
+# Readings: after the step the direction is the stepped row's (rescaling
+# does not change it); a zero row has no direction and is left as it is.
+
+def rescale_project_values(w64: np.ndarray, v64: np.ndarray) -> np.ndarray:
+    """v - w <w, v> / ||w||^2 per row (float64); rows with ||w|| = 0 unchanged."""
+    out = np.array(v64, dtype=np.float64, copy=True)
+    with np.errstate(all="ignore"):
+        for i in range(w64.shape[0]):
+            ss = sum_sq(w64[i])
+            if ss == 0.0:
+                continue
+            p = math.fsum(w64[i] * v64[i])
+            out[i] = v64[i] - w64[i] * (p / ss)
+    return out
+
+
+def rescale_project(w: Sequence[np.ndarray], v: Sequence[np.ndarray]):
+    """Per matrix: fp32 v with its radial part removed (products of two fp32
+    values are exact in float64, so each sum is the correctly rounded one)."""
+    return [rescale_project_values(np.asarray(wm, np.float64), np.asarray(vm, np.float64))
+            .astype(np.float32) for wm, vm in zip(w, v)]
+
+
+def rescale_after_step(w: Sequence[np.ndarray], m: Sequence[Optional[np.ndarray]],
+                       radius: Sequence[float]):
+    """Per matrix: (fp32 w rescaled to its radius, fp32 m projected or None)."""
+    ws, ms = [], []
+    for wm, mm, rho in zip(w, m, radius):
+        w64 = np.asarray(wm, np.float64)
+        ms.append(None if mm is None else
+                  rescale_project_values(w64, np.asarray(mm, np.float64)).astype(np.float32))
+        out = np.array(w64, copy=True)
+        r64 = float(np.float32(rho))
+        with np.errstate(all="ignore"):
+            for i in range(w64.shape[0]):
+                n = math.sqrt(sum_sq(w64[i]))
+                if n != 0.0:
+                    out[i] = w64[i] * (r64 / n)
+        ws.append(out.astype(np.float32))
+    return ws, ms
