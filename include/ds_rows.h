@@ -25,6 +25,11 @@
  *                         whole row.
  *  ds_qk_rows_l2          same PR, the q/k commit: rotate-half RoPE, each
  *                         head's L2 norm, q's scale vector (dory.py's order).
+ *  ds_rescale_project     DragonScale README, "Optimizer" (method "rescale":
+ *  ds_rescale_after_step  raw rows kept at their radius by the optimizer):
+ *                         remove the radial part of each gradient before a
+ *                         step; after it, of the momentum, and rescale each
+ *                         row to its radius.  Ragged, like the weight op.
  *  ds_l2_rows_backward    the gradient of ds_l2_rows' s -> s / sqrt(sum s^2 +
  *                         eps): ds = (dy - s <s,dy> / D^2) / D, shared by x
  *                         and r (the bf16 rounding of s passes it through).
@@ -79,7 +84,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10300          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10400          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -326,6 +331,51 @@ typedef struct ds_rownorm_grad_desc {
  */
 int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,
                                     ds_stream_t stream);
+
+/*
+ * One weight matrix of a rescale-method call.
+ *
+ * w      : [rows, cols] fp32 raw rows, row-major, contiguous, 16-byte aligned.
+ * v      : [rows, cols] fp32, the gradient (ds_rescale_project) or the
+ *          momentum (ds_rescale_after_step: Adam's exp_avg, SGD's or Muon's
+ *          momentum buffer; may be NULL there); updated in place; 16-byte
+ *          aligned; must not overlap any w or other v of the call.
+ * radius : the row radius after a step (1 for linears and convs, sqrt(cols)
+ *          for embeddings); finite.  Unused by ds_rescale_project.
+ * rows, cols : rows >= 0; cols a multiple of 4, 4 <= cols <= DS_MAX_COLS.
+ */
+typedef struct ds_rescale_desc {
+  float* w;
+  float* v;
+  float radius;
+  int64_t rows;
+  int64_t cols;
+} ds_rescale_desc;
+
+/*
+ * ds_rescale_project -- before an optimizer step: remove from each gradient
+ * row the part that would change the row's length.
+ * (DragonScale README, "Optimizer".)
+ *
+ *   v_i <- v_i - w_i <w_i, v_i> / ||w_i||^2        fp32, per row; w read only
+ *
+ * A zero row of w leaves v's row unchanged.  descs, n, stream: as for
+ * ds_weight_rownorm_gain (grouping by width, the 48-matrix inline limit,
+ * the staged table, DS_ERR_CAPTURE).
+ */
+int ds_rescale_project(const ds_rescale_desc* descs, int32_t n, ds_stream_t stream);
+
+/*
+ * ds_rescale_after_step -- after an optimizer step: remove the same part from
+ * the momentum, then rescale each row to its radius.
+ * (DragonScale README, "Optimizer"; second moments are left alone.)
+ *
+ *   v_i <- v_i - w_i <w_i, v_i> / ||w_i||^2        when v is given
+ *   w_i <- radius * w_i / ||w_i||                  (the stepped row's direction)
+ *
+ * A zero row is left as it is.  descs, n, stream: as for ds_rescale_project.
+ */
+int ds_rescale_after_step(const ds_rescale_desc* descs, int32_t n, ds_stream_t stream);
 
 /* A static, human-readable string for a status code (never NULL). */
 const char* ds_status_string(int status);

@@ -50,7 +50,8 @@ __all__ = ["contract_bf16", "contract_rel", "Report", "admissible_l2_rows",
            "ordered", "slerp_unique_mask", "GRAD_SLACK", "l2_grad_terms",
            "rownorm_grad_terms", "contract_grad", "admissible_l2_backward",
            "admissible_rownorm_backward", "EXPF_ULPS", "gate_candidates", "swiglu_candidates",
-           "admissible_act_rows", "act_unique_mask", "COSF_ULPS", "admissible_qk_rows"]
+           "admissible_act_rows", "act_unique_mask", "COSF_ULPS", "admissible_qk_rows",
+           "rescale_terms", "admissible_rescale"]
 
 
 def default_depth(cols: int) -> int:
@@ -844,3 +845,78 @@ def admissible_qk_rows(got_q, got_k, q_bits, k_bits, positions, inv_freq, q_scal
         reps.append(rep)
         masks.append(uniq)
     return reps[0], reps[1], masks[0], masks[1]
+
+
+# ------------------------------------------------------------ rescale method
+#
+# The projection v - w <w, v> / ||w||^2 cancels like a gradient (contract:
+# 2e-6 relative plus GRAD_SLACK of its terms |v_j| + |w_j| sum|w v| / ||w||^2);
+# the rescaled row w rho / ||w|| is within 2e-6 relative.  The fp32 run
+# modelled: S, P as for the gradients; inv = 1/sqrt(S) (three roundings);
+# k = fl(fl(P inv) inv); v_j = fl(v_j - fl(w_j k)); w_j = fl(w_j fl(rho inv)).
+
+def rescale_terms(w: np.ndarray, v: np.ndarray) -> np.ndarray:
+    out = np.zeros(w.shape)
+    with np.errstate(all="ignore"):
+        for i in range(w.shape[0]):
+            ss = sum_sq(w[i])
+            if ss == 0.0:
+                continue
+            a = math.fsum(np.abs(w[i] * v[i]))
+            out[i] = np.abs(v[i]) + np.abs(w[i]) * (a / ss)
+    return out
+
+
+def admissible_rescale(got_w, got_v, w, v, rho: float = 1.0, after_step: bool = True,
+                       depth: Optional[int] = None):
+    """Strict check of one matrix: (w Report, v Report)."""
+    from .rows import rescale_after_step as ref
+    w64 = np.asarray(w, dtype=np.float64)
+    v64 = None if v is None else np.asarray(v, dtype=np.float64)
+    rho64 = float(np.float32(rho))
+    rows, cols = w64.shape
+    depth = default_depth(cols) if depth is None else depth
+    gw = np.atleast_2d(np.asarray(got_w, np.float64))
+    gv = None if got_v is None else np.atleast_2d(np.asarray(got_v, np.float64))
+    rw, rv = Report(), Report()
+
+    def mark(rep, bad, base):
+        rep.n += bad.size
+        idx = np.nonzero(bad)[0]
+        rep.outside += idx.size
+        for j in idx[: max(0, 20 - len(rep.first_bad))]:
+            rep.first_bad.append(int(base + j))
+
+    for i in range(rows):
+        row = w64[i]
+        base = i * cols
+        vr = None if v64 is None else v64[i]
+        if not (np.isfinite(row).all() and (vr is None or np.isfinite(vr).all())):
+            ws, ms = ref([w[i:i + 1]], [None if v is None else v[i:i + 1]], [rho])
+            exact_w = ws[0][0].astype(np.float64) if after_step else row
+            if after_step:
+                mark(rw, ~((gw[i] == exact_w) | (np.isnan(gw[i]) & np.isnan(exact_w))), base)
+            if vr is not None:
+                ev = ms[0][0].astype(np.float64)
+                mark(rv, ~((gv[i] == ev) | (np.isnan(gv[i]) & np.isnan(ev))), base)
+            continue
+        sq = row ** 2
+        s_lo, s_hi = _sum_bounds(sq, sq, depth)
+        if s_hi == 0:                                   # a zero row stays as it is
+            if after_step:
+                mark(rw, gw[i] != row, base)
+            if vr is not None:
+                mark(rv, gv[i] != vr, base)
+            continue
+        inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, 0.0)
+        if after_step:
+            c_lo, c_hi = _scalar(_corner_bounds([rho64], [rho64], inv_lo, inv_hi))
+            lo, hi = _corner_bounds(row, row, c_lo, c_hi)
+            mark(rw, ~_f32_inside(gw[i], lo, hi), base)
+        if vr is not None:
+            p_lo, p_hi = _mixed_sum_bounds(row * vr, depth)
+            q = _scalar(_corner_bounds([p_lo], [p_hi], inv_lo, inv_hi))
+            k_lo, k_hi = _scalar(_corner_bounds([q[0]], [q[1]], inv_lo, inv_hi))
+            lo, hi = _tangent_bounds(row, vr, k_lo, k_hi, 1.0, 1.0)
+            mark(rv, ~_f32_inside(gv[i], lo, hi), base)
+    return rw, rv

@@ -58,6 +58,17 @@ class RownormGradDesc(ctypes.Structure):
     ]
 
 
+class RescaleDesc(ctypes.Structure):
+    """ds_rescale_desc."""
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("radius", ctypes.c_float),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -91,6 +102,9 @@ def lib() -> ctypes.CDLL:
         L.ds_qk_rows_l2.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, vp, i64, i64,
                                     i32, i32, i32, f32, vp]
         L.ds_qk_rows_l2.restype = ctypes.c_int
+        for name in ("ds_rescale_project", "ds_rescale_after_step"):
+            getattr(L, name).argtypes = [ctypes.POINTER(RescaleDesc), ctypes.c_int32, vp]
+            getattr(L, name).restype = ctypes.c_int
         L.ds_l2_rows_backward.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
         L.ds_l2_rows_backward.restype = ctypes.c_int
         L.ds_weight_rownorm_gain_backward.argtypes = [ctypes.POINTER(RownormGradDesc),
@@ -399,3 +413,42 @@ def ds_qk_rows_l2(q, k, positions, inv_freq, q_scale, head_dim: int, eps: float 
             rows, nq, nk, head_dim, float(eps), _stream_of(q, stream))
     _check(st, "ds_qk_rows_l2")
     return q_out, k_out
+
+
+def _rescale(ws, vs, radius, after_step, stream):
+    torch = _torch()
+    n = len(ws)
+    vs = [None] * n if vs is None else list(vs)
+    radius = [1.0] * n if radius is None else list(radius)
+    descs = (RescaleDesc * max(n, 1))()
+    dev = None
+    for i, w in enumerate(ws):
+        for t, name in ((w, "w"), (vs[i], "v")):
+            if t is None:
+                continue
+            if t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous() \
+                    or t.shape != w.shape or t.device.type != "cuda" \
+                    or (dev is not None and t.device != dev):
+                raise ValueError(f"{name}[{i}]: expected a contiguous fp32 HIP tensor shaped like w")
+            dev = t.device
+        descs[i] = RescaleDesc(w.data_ptr(), None if vs[i] is None else vs[i].data_ptr(),
+                               float(radius[i]), w.shape[0], w.shape[1])
+    if n == 0:
+        return
+    with torch.cuda.device(dev):
+        fn = lib().ds_rescale_after_step if after_step else lib().ds_rescale_project
+        st = fn(descs, n, _stream_of(ws[0], stream))
+    _check(st, "ds_rescale_after_step" if after_step else "ds_rescale_project")
+
+
+def ds_rescale_project(ws: Sequence, grads: Sequence, stream=None) -> None:
+    """In place, per matrix: grad <- grad - w <w, grad> / ||w||^2 per row."""
+    if len(grads) != len(ws):
+        raise ValueError("one gradient per matrix")
+    _rescale(ws, grads, None, False, stream)
+
+
+def ds_rescale_after_step(ws: Sequence, moms: Optional[Sequence] = None,
+                          radius: Optional[Sequence[float]] = None, stream=None) -> None:
+    """In place, per matrix: project the momentum (if given), then w <- radius w/||w||."""
+    _rescale(ws, moms, radius, True, stream)

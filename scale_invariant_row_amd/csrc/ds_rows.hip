@@ -644,4 +644,51 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
                                              (hipStream_t)stream);
 }
 
+namespace {
+
+// The rescale method's ragged calls: `project` writes v only (w is read);
+// `after_step` writes w and, when given, v.
+int rescale_call(const ds_rescale_desc* descs, int32_t n, bool after_step, ds_stream_t stream) {
+  if (n < 0) return DS_ERR_ARG;
+  if (n == 0) return DS_OK;
+  if (descs == nullptr) return DS_ERR_NULL;
+  std::vector<Range> outs, ins;
+  std::vector<std::pair<Shape, dsr::RescaleTask>> mats;
+  for (int32_t i = 0; i < n; ++i) {
+    const ds_rescale_desc& d = descs[i];
+    int st = check_matrix(d.rows, d.cols, 4, 4);
+    if (st != DS_OK) return st;
+    if (after_step && !std::isfinite(d.radius)) return DS_ERR_ARG;
+    if (d.rows == 0) continue;
+    if (d.w == nullptr || (!after_step && d.v == nullptr)) return DS_ERR_NULL;
+    if (!aligned(d.w, 16) || (d.v != nullptr && !aligned(d.v, 16))) return DS_ERR_ALIGN;
+    const size_t nb = (size_t)d.rows * (size_t)d.cols * 4;
+    add_range(after_step ? outs : ins, d.w, nb);
+    add_range(outs, d.v, nb);
+    const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
+    if (!s.ok()) return DS_ERR_SHAPE;
+    dsr::RescaleTask t{};
+    t.w = d.w;
+    t.v = d.v;
+    t.rows = d.rows;
+    t.cols = (int32_t)d.cols;
+    t.radius = d.radius;
+    mats.emplace_back(s, t);
+  }
+  if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
+  return launch_ragged<dsr::RescaleTask>(
+      mats, after_step ? dsr::launch_rescale_after_step : dsr::launch_rescale_project,
+      (hipStream_t)stream);
+}
+
+}  // namespace
+
+int ds_rescale_project(const ds_rescale_desc* descs, int32_t n, ds_stream_t stream) {
+  return rescale_call(descs, n, false, stream);
+}
+
+int ds_rescale_after_step(const ds_rescale_desc* descs, int32_t n, ds_stream_t stream) {
+  return rescale_call(descs, n, true, stream);
+}
+
 }  // extern "C"

@@ -1,5 +1,5 @@
 """Writes inst_l2.hip, inst_slerp.hip, inst_rownorm.hip, inst_l2_bwd.hip,
-inst_rownorm_bwd.hip and inst_act.hip: one launcher per op
+inst_rownorm_bwd.hip, inst_act.hip and inst_rescale.hip: one launcher per op
 with a case for every kernel shape (G waves per row, V vectors per lane) that
 launch.hpp's shape policy returns for some width up to DS_MAX_COLS, found by
 evaluating the policy (reproduced below from launch.hpp's constants) at every
@@ -209,9 +209,34 @@ hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const fl
 
 }  // namespace dsr
 '''
+    rsc = HEAD.format(what="rescale method (projection; rescale after a step)") + '''
+template <int G, int V, bool RESCALE>
+static hipError_t run(const RescaleArgs& args, int grid, hipStream_t stream) {
+  constexpr int T = Geo<G>::THREADS;
+  rescale_kernel<G, V, RESCALE><<<grid, T, 0, stream>>>(args);
+  return hipGetLastError();
+}
+
+hipError_t launch_rescale_project(Shape s, const RescaleArgs& args, int grid, hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(rown, "return run<{G}, {V}, false>(args, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_rescale_after_step(Shape s, const RescaleArgs& args, int grid,
+                                     hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(rown, "return run<{G}, {V}, true>(args, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsr
+'''
     for name, text in (("inst_l2.hip", l2), ("inst_slerp.hip", sl), ("inst_rownorm.hip", rn),
                        ("inst_l2_bwd.hip", l2b), ("inst_rownorm_bwd.hip", rnb),
-                       ("inst_act.hip", act)):
+                       ("inst_act.hip", act), ("inst_rescale.hip", rsc)):
         with open(os.path.join(HERE, name), "w") as f:
             f.write(text)
 

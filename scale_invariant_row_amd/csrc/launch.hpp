@@ -11,6 +11,7 @@ struct TaskArgs;
 struct RownormTask;
 struct RownormGradTask;
 struct QkArgs;
+struct RescaleTask;
 
 // Kernel shape: G waves per row, V 16-byte vectors per lane.
 struct Shape {
@@ -71,6 +72,10 @@ hipError_t launch_gate_l2_rows(Shape s, const void* o, const void* g, const floa
 hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const float* sug,
                                  const float* suu, void* y, int64_t rows, int nvec, float eps,
                                  int grid, hipStream_t stream);
+hipError_t launch_rescale_project(Shape s, const TaskArgs<RescaleTask>& args, int grid,
+                                  hipStream_t stream);
+hipError_t launch_rescale_after_step(Shape s, const TaskArgs<RescaleTask>& args, int grid,
+                                     hipStream_t stream);
 hipError_t launch_qk_rows_l2(int head_dim, const QkArgs& args, int grid, hipStream_t stream);
 hipError_t launch_l2_rows_backward(Shape s, const void* x, const void* r, const void* dy,
                                    void* dx, int64_t rows, int nvec, float eps, int grid,

@@ -1286,4 +1286,135 @@ rownorm_backward_kernel(const RownormGradArgs args) {
   }
 }
 
+// ------------------------------------------------------------ rescale method
+//
+// DragonScale README, "Optimizer": with raw rows (method "rescale"), the
+// part of the gradient that would change a row's length is removed before
+// each step; after it the same part is removed from the momentum and the
+// row is rescaled to its radius.  Per row of fp32 w and v (a gradient or a
+// momentum), S = sum w^2 and P = <w, v> in one pass:
+//   v <- v - w k,  k = (P inv) inv,  inv = 1/sqrt(S)      (v may be absent)
+//   w <- w (rho inv)                                      (after a step only)
+// Sums out of fp32's range are recomputed with w scaled by 2^sa and v by
+// 2^sb, as for the weight gradient.  A zero row is left as it is.
+
+struct RescaleTask {
+  float* w;
+  float* v;             // may be null (after a step without momentum)
+  int64_t rows;
+  int32_t cols;
+  float radius;
+  int32_t item_begin;
+  int32_t pad_;
+};
+using RescaleArgs = TaskArgs<RescaleTask>;
+static_assert(sizeof(RescaleArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
+template <int G, int V, bool RESCALE>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+rescale_kernel(const RescaleArgs args) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  int off[V];
+  geo.offsets(off, 16);
+  const int nitems = args.nitems;
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int lo = __builtin_amdgcn_readfirstlane(owning_task(args, item, geo.lane));
+    const RescaleTask t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
+    const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
+    if (G == 1 && row >= t.rows) continue;
+    const bool has_v = t.v != nullptr;             // uniform
+    const uint32_t bytes = (uint32_t)t.cols * 4u;
+    const RowBuf wb(t.w + row * t.cols, bytes);
+    const RowBuf vb(has_v ? t.v + row * t.cols : t.w, has_v ? bytes : 0u);
+    float w[V][4], v[V][4];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const f32x4_t a = wb.ld16f(off[k]);
+      w[k][0] = a.x; w[k][1] = a.y; w[k][2] = a.z; w[k][3] = a.w;
+      const f32x4_t b = vb.ld16f(off[k]);          // zeros when there is no v
+      v[k][0] = b.x; v[k][1] = b.y; v[k][2] = b.z; v[k][3] = b.w;
+    }
+    float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      a0 = __builtin_fmaf(w[k][0], w[k][0], a0);
+      a1 = __builtin_fmaf(w[k][1], w[k][1], a1);
+      a0 = __builtin_fmaf(w[k][2], w[k][2], a0);
+      a1 = __builtin_fmaf(w[k][3], w[k][3], a1);
+      p0 = __builtin_fmaf(w[k][0], v[k][0], p0);
+      p1 = __builtin_fmaf(w[k][1], v[k][1], p1);
+      p0 = __builtin_fmaf(w[k][2], v[k][2], p0);
+      p1 = __builtin_fmaf(w[k][3], v[k][3], p1);
+    }
+    float acc[2] = {wave_sum(a0 + a1), wave_sum(p0 + p1)};
+    group_sum<G, 2>(acc, gs.next(slot), geo.g, geo.lane);
+    float T = acc[0];
+    float P = acc[1];
+    bool scaled = false;
+    int sa = 0, sb = 0;
+    if (!(T >= kTiny && T < __builtin_inff() && fabsf(P) < __builtin_inff())) {
+      float m[2] = {0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < V; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          m[0] = fmaxf(m[0], fabsf(w[k][j]));
+          m[1] = fmaxf(m[1], fabsf(v[k][j]));
+        }
+      m[0] = wave_max(m[0]);
+      m[1] = wave_max(m[1]);
+      group_max2<G>(m, gs.next(slot), geo.g, geo.lane);
+      if (m[0] > 0.f && m[0] < __builtin_inff() && m[1] < __builtin_inff()) {
+        sa = rescue_shift(m[0], 0.f);
+        sb = (m[1] > 0.f) ? rescue_shift(m[1], 0.f) : 0;
+        float c0 = 0.f, c1 = 0.f, q0 = 0.f, q1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+#pragma unroll
+          for (int j = 0; j < 4; j += 2) {
+            const float x0 = ldexpf(w[k][j], sa), x1 = ldexpf(w[k][j + 1], sa);
+            c0 = __builtin_fmaf(x0, x0, c0);
+            c1 = __builtin_fmaf(x1, x1, c1);
+            q0 = __builtin_fmaf(x0, ldexpf(v[k][j], sb), q0);
+            q1 = __builtin_fmaf(x1, ldexpf(v[k][j + 1], sb), q1);
+          }
+        }
+        float tt[2] = {wave_sum(c0 + c1), wave_sum(q0 + q1)};
+        group_sum<G, 2>(tt, gs.next(slot), geo.g, geo.lane);
+        T = tt[0];
+        P = tt[1];
+        scaled = true;
+      }
+    }
+    if (T == 0.f) continue;                        // a zero row: nothing to do (uniform)
+    const float inv = inv_sqrt(T);
+    const float kk = (P * inv) * inv;
+    const float c = t.radius * inv;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float ov[4], ow[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float wj = scaled ? ldexpf(w[k][j], sa) : w[k][j];
+        const float vj = scaled ? ldexpf(v[k][j], sb) : v[k][j];
+        const float r = __builtin_fmaf(-wj, kk, vj);
+        ov[j] = scaled ? ldexpf(r, -sb) : r;
+        ow[j] = wj * c;
+      }
+      if (has_v) {
+        const f32x4_t o = {ov[0], ov[1], ov[2], ov[3]};
+        vb.st16(__builtin_bit_cast(u32x4_t, o), off[k]);
+      }
+      if constexpr (RESCALE) {
+        const f32x4_t o = {ow[0], ow[1], ow[2], ow[3]};
+        wb.st16(__builtin_bit_cast(u32x4_t, o), off[k]);
+      }
+    }
+  }
+}
+
 }  // namespace dsr

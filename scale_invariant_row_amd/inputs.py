@@ -37,14 +37,16 @@ rownorm_gain_bwd_12x4     rownorm_gain_12x4_d768's matrices; dL/dW_eff ~ N(0,1)
 rownorm_gain_bwd_11008x   one 11008x4096 matrix (the DragonScale README's
 4096                      kernel-speed shape), W ~ N(0, sd 0.02), g ~ U(0.5, 2),
                           dL/dW_eff ~ N(0,1)
-========================  =======================================================
-
 qk_rows_l2_8192_h16x4     8192 token rows, head_dim 256, 16 q heads, 4 kv heads:
 _d256                     q, k ~ N(0,1) bf16; positions 0.. for two thirds of
                           the rows and 199,800.. for the last third; inv_freq =
                           10000^(-2i/256) in fp32; q_scale ~ U(0.5, 2) fp32
 gate_l2_rows_8192x4096    o, g ~ N(0,1) bf16; sg ~ U(0.5, 2) fp32 per column
 swiglu_l2_rows_8192x7168  g, u ~ N(0,1) bf16; sug, suu ~ U(0.5, 2) fp32 per column
+rescale_12x4_d768         the 48 linears of rownorm_gain_12x4_d768 as raw rows,
+                          W ~ N(0, sd 0.02) fp32, gradients / momenta
+                          ~ N(0, sd 1e-3) fp32, radius 1
+========================  =======================================================
 
 Upstream gradients (dy, dL/dW_eff) are bf16 values drawn like activations.
 The activation rows' widths are the Dory rows the TensorFold PR names (4,096
@@ -63,6 +65,7 @@ __all__ = [
     "transformer_linears", "stress_l2_case", "WORKLOADS", "make",
     "L2GradCase", "RownormGradCase", "grad_bits", "l2_grad_case", "rownorm_grad_case",
     "ActCase", "gate_case", "swiglu_case", "QkCase", "qk_case", "rope_inv_freq",
+    "RescaleCase", "rescale_case",
 ]
 
 
@@ -172,6 +175,16 @@ class QkCase:
     q_scale: np.ndarray               # float32 [nq * hd]
     head_dim: int
     eps: float = 1e-6
+
+
+@dataclass
+class RescaleCase:
+    """Inputs of the rescale method's row ops: raw rows and, per matrix, a
+    gradient or momentum of the same shape."""
+    name: str
+    w: List[np.ndarray]
+    v: List[np.ndarray]
+    radius: List[float]
 
 
 def _streams(seed: int, n: int) -> List[np.random.Generator]:
@@ -317,6 +330,16 @@ def qk_case(rows: int, nq: int, nk: int, head_dim: int, seed: int, far: float = 
                   rope_inv_freq(head_dim), sc, head_dim)
 
 
+def rescale_case(shapes, seed: int, w_sd: float = 0.02, v_sd: float = 1e-3,
+                 radius: float = 1.0, name: Optional[str] = None) -> RescaleCase:
+    gens = _streams(seed, 2 * len(shapes))
+    ws, vs = [], []
+    for i, (rows, cols) in enumerate(shapes):
+        ws.append((w_sd * gens[2 * i].standard_normal((rows, cols))).astype(np.float32))
+        vs.append((v_sd * gens[2 * i + 1].standard_normal((rows, cols))).astype(np.float32))
+    return RescaleCase(name or f"rescale_{len(shapes)}", ws, vs, [float(radius)] * len(shapes))
+
+
 # name -> (description, builder, seed).  Seeds are 1000 + a fixed number.
 WORKLOADS = {
     "l2_rows_64x1024": (
@@ -365,6 +388,10 @@ WORKLOADS = {
         "qk_rows_l2, 8192 token rows, head_dim 256, 16 q heads over 4 kv heads, a third "
         "of the rows past position 199,800, inv_freq 10000^(-2i/256), q_scale ~ U(0.5, 2)",
         lambda: qk_case(8192, 16, 4, 256, 1012, name="qk_rows_l2_8192_h16x4_d256")),
+    "rescale_12x4_d768": (
+        "rescale method over 12 pre-norm layers' linears (d 768, d_ff 3072): raw rows "
+        "W ~ N(0, sd 0.02) fp32, gradients / momenta ~ N(0, sd 1e-3) fp32, radius 1",
+        lambda: rescale_case(transformer_linears(), 1013, name="rescale_12x4_d768")),
 }
 
 

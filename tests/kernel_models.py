@@ -201,3 +201,23 @@ def qk_model(q_bits, k_bits, positions, inv_freq, q_scale, hd, eps=1e-6,
     q_out = bf16_rne((nq * np.asarray(q_scale, np.float32)).astype(np.float32).astype(np.float64))
     k_out = bf16_rne(heads(k_bits).astype(np.float64)) if k_bits is not None else None
     return q_out, k_out
+
+
+# ------------------------------------------------------------ rescale method
+
+def rescale_model(w, v, rho=1.0, after_step=True, k_over_norm=False, project=True):
+    """fp32 steps of the rescale row ops; controls: k = P/||w|| instead of
+    P/||w||^2, and no projection at all."""
+    w32 = np.asarray(w, np.float32)
+    v32 = None if v is None else np.asarray(v, np.float32)
+    with np.errstate(all="ignore"):
+        S = lane_sum_sq(w32)
+        inv = (np.float32(1) / np.sqrt(S)).astype(np.float32)[:, None]
+        zero = (S == 0)[:, None]
+        v_out = None
+        if v32 is not None:
+            P = lane_sum((w32 * v32).astype(np.float32))[:, None]
+            k = (P * inv) if k_over_norm else (P * inv) * inv
+            v_out = np.where(zero | (not project), v32, v32 - w32 * k).astype(np.float32)
+        w_out = np.where(zero, w32, w32 * (np.float32(rho) * inv)).astype(np.float32) if after_step else w32
+    return w_out, v_out

@@ -30,13 +30,14 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"ds_l2_rows", "ds_slerp_rows", "ds_weight_rownorm_gain",
                           "ds_l2_rows_backward", "ds_weight_rownorm_gain_backward",
                           "ds_gate_l2_rows", "ds_swiglu_l2_rows", "ds_qk_rows_l2",
+                          "ds_rescale_project", "ds_rescale_after_step",
                           "ds_status_string", "ds_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10300
+    assert B.ds_version() == 10400
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -253,6 +254,37 @@ def test_qk_fused_views_reach_device_lookup(L):
     # writing q's output over k's slice is refused
     assert _qk(L, q=q, ldq=6144, k=k, ldk=6144, qo=k - 2048, ldqo=6144, ko=k, ldko=6144) == \
         B.DS_ERR_ARG
+
+
+def _rdescs(*items):
+    arr = (B.RescaleDesc * len(items))()
+    for i, d in enumerate(items):
+        arr[i] = B.RescaleDesc(*d)
+    return arr
+
+
+def test_rescale_validation(L):
+    pr, af = L.ds_rescale_project, L.ds_rescale_after_step
+    good = (A, C, 1.0, 16, 64)                        # w, v, radius, rows, cols
+    assert pr(_rdescs(good), -1, None) == B.DS_ERR_ARG
+    assert pr(None, 0, None) == B.DS_OK and af(None, 0, None) == B.DS_OK
+    assert pr(None, 1, None) == B.DS_ERR_NULL
+    assert pr(_rdescs((A, None, 1.0, 16, 64)), 1, None) == B.DS_ERR_NULL      # project needs v
+    assert pr(_rdescs((A, C, 1.0, 16, 6)), 1, None) == B.DS_ERR_SHAPE
+    assert pr(_rdescs((A + 8, C, 1.0, 16, 64)), 1, None) == B.DS_ERR_ALIGN
+    assert pr(_rdescs((A, A + 1024, 1.0, 16, 64)), 1, None) == B.DS_ERR_ARG   # v over w
+    assert af(_rdescs((A, C, float("inf"), 16, 64)), 1, None) == B.DS_ERR_ARG
+    # after a step w is written too: two matrices sharing w are refused
+    assert af(_rdescs(good, (A, C + 65536, 1.0, 16, 64)), 2, None) == B.DS_ERR_ARG
+    assert af(_rdescs((None, None, 1.0, 0, 64)), 1, None) == B.DS_OK
+
+
+@pytest.mark.skipif("not no_device()")
+def test_rescale_valid_args_reach_device_lookup(L):
+    good = (A, C, 1.0, 16, 64)
+    tied = (A, C + 65536, 1.0, 16, 64)               # project: w shared (read only), two v
+    assert L.ds_rescale_project(_rdescs(good, tied), 2, None) == B.DS_ERR_DEVICE
+    assert L.ds_rescale_after_step(_rdescs((A, None, 2.0, 16, 64)), 1, None) == B.DS_ERR_DEVICE
 
 
 def test_binding_raises_on_missing_library(monkeypatch):
