@@ -38,7 +38,7 @@ EPS = 1e-6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
                   "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip",
-                  "inst_qk.hip", "ds_rows.hip"]
+                  "inst_qk.hip", "inst_rescale.hip", "ds_rows.hip"]
 
 
 def kernel_hash() -> str:
@@ -318,6 +318,39 @@ def main():
     rnb_us = ragged_us(wsets, 1, 60)
     ops["weight_rownorm_gain_bwd_12x4_d768"] = op(rnb_us, n_el * 10 + n_rows * 8, n_rows)
     del wsets
+    # ---- the rescale method on the 48 linears: project (W, G read; G written) and
+    # after a step (W, M read and written)
+    rs_sets = []
+    for _ in range(3):
+        ws = [0.02 * torch.randn(sh, device=dev, generator=gen) for sh in lin]
+        vs = [1e-3 * torch.randn(sh, device=dev, generator=gen) for sh in lin]
+        ms = [1e-3 * torch.randn(sh, device=dev, generator=gen) for sh in lin]
+        pd = (B.RescaleDesc * len(lin))()
+        ad = (B.RescaleDesc * len(lin))()
+        for i, (r, c) in enumerate(lin):
+            pd[i] = B.RescaleDesc(ws[i].data_ptr(), vs[i].data_ptr(), 1.0, r, c)
+            ad[i] = B.RescaleDesc(ws[i].data_ptr(), ms[i].data_ptr(), 1.0, r, c)
+        rs_sets.append((pd, ad, ws, vs, ms))
+    torch.cuda.synchronize()
+
+    def rescale_us(which, n=60):
+        call = L.ds_rescale_project if which == 0 else L.ds_rescale_after_step
+        for i in range(4):
+            assert call(rs_sets[i % 3][which], len(lin), sp) == 0
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for i in range(n):
+            call(rs_sets[i % 3][which], len(lin), sp)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    ops["rescale_project_12x4_d768"] = op(rescale_us(0), n_el * 12, n_rows)
+    ops["rescale_after_step_12x4_d768"] = op(rescale_us(1), n_el * 16, n_rows)
+    del rs_sets
+    torch.cuda.empty_cache()
+
     big = [(11008, 4096)]
     wsets = weight_sets(big, 4)
     f_us = ragged_us(wsets, 0, 40)
