@@ -21,7 +21,8 @@ from typing import List, Optional, Sequence, Tuple
 
 __all__ = ["bits_to_fraction", "round_fraction", "bf16_of", "fp32_of",
            "l2_row", "slerp_row", "rownorm_row", "l2_backward_row", "rownorm_backward_row",
-           "gate_row", "swiglu_row", "qk_head", "rescale_row", "NEAR_TIE_REL"]
+           "gate_row", "swiglu_row", "qk_head", "rescale_row", "rms_row", "rms_backward_row",
+           "NEAR_TIE_REL"]
 
 PREC = 60
 NEAR_TIE_REL = Fraction(1, 10 ** 12)     # flag values this close to a midpoint
@@ -344,3 +345,56 @@ def rescale_row(w: Sequence[float], v: Optional[Sequence[float]], rho: float
             v_out.append(r)
             near[j] = near[j] or n
     return w_out, v_out, near
+
+
+# ------------------------------------------------------------------ RMSNorm
+# The ternary/8-bit GPT model page's parameter-free rms_norm: y = s / sqrt(
+# sum(s^2) / n + eps), n the row's length, rounded once to bf16.
+
+def _s_exact(x_bits, r_bits):
+    x = [bits_to_fraction(int(b)) for b in x_bits]
+    if r_bits is None:
+        return x
+    return [bf16_of(xj + bits_to_fraction(int(rb)))[0] for xj, rb in zip(x, r_bits)]
+
+
+def rms_row(x_bits: Sequence[int], r_bits: Optional[Sequence[int]], eps32: float
+            ) -> Tuple[List[Fraction], List[bool]]:
+    """One row of rms_rows, exactly, with near-tie flags."""
+    s = _s_exact(x_bits, r_bits)
+    n = len(s)
+    eps = f32_to_fraction(eps32)
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        ms = sum((v * v for v in s), Fraction(0)) / n + eps
+        root = _dec(ms).sqrt()
+        out, near = [], []
+        for v in s:
+            r, fl = bf16_of(Fraction(_dec(v) / root))
+            out.append(r)
+            near.append(fl)
+    return out, near
+
+
+def rms_backward_row(x_bits: Sequence[int], r_bits: Optional[Sequence[int]],
+                     dy_bits: Sequence[int], eps32: float) -> Tuple[List[Fraction], List[bool]]:
+    """One row of the rms_rows gradient, exactly: bf16((dy - s <s,dy> / (n D^2)) / D)."""
+    s = _s_exact(x_bits, r_bits)
+    n = len(s)
+    dy = [bits_to_fraction(int(b)) for b in dy_bits]
+    eps = f32_to_fraction(eps32)
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        nd2 = sum((v * v for v in s), Fraction(0)) + n * eps        # n D^2, exact
+        p = sum((a * b for a, b in zip(s, dy)), Fraction(0))
+        pa = sum((abs(a * b) for a, b in zip(s, dy)), Fraction(0))
+        root = _dec(nd2 / n).sqrt()
+        out, near = [], []
+        for sj, gj in zip(s, dy):
+            num = gj - sj * p / nd2
+            terms = abs(gj) + abs(sj) * pa / nd2
+            v, fl = _round_with_slack(Fraction(_dec(num) / root),
+                                      SLACK_REL * Fraction(_dec(terms) / root), bf16_of)
+            out.append(v)
+            near.append(fl)
+    return out, near

@@ -188,21 +188,34 @@ def _judge(got_bits, lo, hi, exact_bits, exact_mask, zero_any_sign,
         report.first_bad.append(int(base_index + j))
 
 
-def _row_inv(s_row: np.ndarray, eps64: float, depth: int):
+def _mean_bounds(s_lo: float, s_hi: float, n: int):
+    """Bounds of fl(S / n) for S in [s_lo, s_hi] >= 0 (one rounding)."""
+    return (max(0.0, s_lo / n * (1 - U) * (1 - F64_WIDEN) - ETA),
+            s_hi / n * (1 + U) * (1 + F64_WIDEN) + ETA)
+
+
+def _row_inv(s_row: np.ndarray, eps64: float, depth: int, mean: bool = False):
     sq = s_row.astype(np.float64) ** 2
     s_lo, s_hi = _sum_bounds(sq, sq, depth)
+    if mean:
+        s_lo, s_hi = _mean_bounds(s_lo, s_hi, s_row.size)
     return _inv_bounds(s_lo, s_hi, eps64)
 
 
-def _l2_value_bounds(s_row: np.ndarray, eps64: float, depth: int):
-    inv_lo, inv_hi = _row_inv(s_row, eps64, depth)
+def _l2_value_bounds(s_row: np.ndarray, eps64: float, depth: int, mean: bool = False):
+    inv_lo, inv_hi = _row_inv(s_row, eps64, depth, mean)
     return _product_bounds(s_row, s_row, inv_lo, inv_hi)
 
 
 def admissible_l2_rows(got_bits, x_bits, r_bits=None, eps: float = 1e-6,
-                       depth: Optional[int] = None, row_ids=None) -> Report:
-    """Strict check of l2_rows outputs ``got_bits`` for the given input rows."""
-    from .rows import l2_rows as l2_ref
+                       depth: Optional[int] = None, row_ids=None, mean: bool = False) -> Report:
+    """Strict check of l2_rows outputs ``got_bits`` for the given input rows.
+
+    ``mean=True`` checks rms_rows instead: the fp32 sum is divided by the
+    row's length (one more rounding) before eps is added.
+    """
+    from .rows import l2_rows, rms_rows
+    l2_ref = rms_rows if mean else l2_rows
     x = bf16_value(np.atleast_2d(x_bits))
     if r_bits is not None:
         with np.errstate(all="ignore"):
@@ -222,7 +235,7 @@ def admissible_l2_rows(got_bits, x_bits, r_bits=None, eps: float = 1e-6,
                            None if r_bits is None else r_bits[i:i + 1], eps)[0]
             _judge(got[i], row, row, exact, np.ones(cols, bool), False, base, rep)
             continue
-        lo, hi = _l2_value_bounds(row, eps64, depth)
+        lo, hi = _l2_value_bounds(row, eps64, depth, mean)
         zero = row == 0
         exact = np.where(np.signbit(row), np.uint16(0x8000), np.uint16(0)).astype(np.uint16)
         _judge(got[i], lo, hi, exact, zero, False, base, rep)
@@ -393,14 +406,19 @@ def admissible_rownorm(got_norm, got_weff_bits, w, g, rho: float = 1.0,
 GRAD_SLACK = 2.0 ** -16
 
 
-def l2_grad_terms(s: np.ndarray, dy: np.ndarray, eps64: float) -> np.ndarray:
-    """Per element (|dy_j| + |s_j| sum|s dy| / D^2) / D: the size of ds_j's terms."""
+def l2_grad_terms(s: np.ndarray, dy: np.ndarray, eps64: float, mean: bool = False) -> np.ndarray:
+    """Per element (|dy_j| + |s_j| sum|s dy| / D^2) / D: the size of ds_j's terms.
+
+    With mean=True (the rms_rows gradient) D^2 = sum s^2 / n + eps and the
+    second term is |s_j| sum|s dy| / (n D^2).
+    """
     out = np.empty(s.shape)
+    n = s.shape[1] if mean else 1
     with np.errstate(all="ignore"):
         for i in range(s.shape[0]):
-            d2 = sum_sq(s[i]) + eps64
+            d2 = sum_sq(s[i]) / n + eps64
             a = math.fsum(np.abs(s[i] * dy[i]))
-            out[i] = (np.abs(dy[i]) + np.abs(s[i]) * (a / d2)) / math.sqrt(d2)
+            out[i] = (np.abs(dy[i]) + np.abs(s[i]) * (a / (n * d2))) / math.sqrt(d2)
     return out
 
 
@@ -506,16 +524,20 @@ def _scalar(lo_hi):
 
 
 def admissible_l2_backward(got_bits, x_bits, r_bits, dy_bits, eps: float = 1e-6,
-                           depth: Optional[int] = None, row_ids=None) -> Report:
+                           depth: Optional[int] = None, row_ids=None,
+                           mean: bool = False) -> Report:
     """Strict check of l2_rows gradients ``got_bits`` (bf16 bits).
 
     The fp32 run modelled: S and P = <s, dy> summed as above (depth
     additions); inv = 1/sqrt(S + eps) as in the forward; k = fl(fl(P inv) inv);
     ds_j = fl(fl(dy_j - fl(s_j k)) inv), or any fusing of those steps.  A set
     of more than two bf16 values is counted in ``wide`` (cancellation makes
-    it legitimate), not as a failure.
+    it legitimate), not as a failure.  ``mean=True`` checks the rms_rows
+    gradient: S and P are each divided by the row's length (one rounding
+    each) before inv and k are formed.
     """
-    from .rows import l2_rows_backward as ref
+    from .rows import l2_rows_backward, rms_rows_backward
+    ref = rms_rows_backward if mean else l2_rows_backward
     x = bf16_value(np.atleast_2d(x_bits))
     if r_bits is not None:
         with np.errstate(all="ignore"):
@@ -539,8 +561,11 @@ def admissible_l2_backward(got_bits, x_bits, r_bits, dy_bits, eps: float = 1e-6,
             continue
         sq = row ** 2
         s_lo, s_hi = _sum_bounds(sq, sq, depth)
-        inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, eps64)
         p_lo, p_hi = _mixed_sum_bounds(row * d, depth)
+        if mean:
+            s_lo, s_hi = _mean_bounds(s_lo, s_hi, cols)
+            p_lo, p_hi = _scalar(_corner_bounds([p_lo], [p_hi], 1.0 / cols, 1.0 / cols))
+        inv_lo, inv_hi = _inv_bounds(s_lo, s_hi, eps64)
         q = _scalar(_corner_bounds([p_lo], [p_hi], inv_lo, inv_hi))
         k_lo, k_hi = _scalar(_corner_bounds([q[0]], [q[1]], inv_lo, inv_hi))
         lo, hi = _tangent_bounds(row, d, k_lo, k_hi, inv_lo, inv_hi)

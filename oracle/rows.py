@@ -42,7 +42,8 @@ __all__ = ["eps_as_passed", "l2_rows", "slerp_rows", "slerp_rows_detail",
            "rownorm_backward_values", "weight_rownorm_gain_backward",
            "gate_gated_row", "gate_l2_rows", "swiglu_product_row", "swiglu_l2_rows",
            "rope_angles", "qk_rotated_heads", "qk_rows_l2",
-           "rescale_project_values", "rescale_project", "rescale_after_step"]
+           "rescale_project_values", "rescale_project", "rescale_after_step",
+           "rms_rows", "rms_backward_values", "rms_rows_backward"]
 
 
 def eps_as_passed(eps: float) -> float:
@@ -385,3 +386,64 @@ def rescale_after_step(w: Sequence[np.ndarray], m: Sequence[Optional[np.ndarray]
                     out[i] = w64[i] * (r64 / n)
         ws.append(out.astype(np.float32))
     return ws, ms
+
+
+# ------------------------------------------------------------------ RMSNorm
+#
+# The parameter-free RMSNorm of the ternary/8-bit GPT model page (its
+# `rms_norm`: torch's rms_norm over the last dimension, eps 1e-6):
+#   y = bf16(s / sqrt(mean(s^2) + eps)),   mean(s^2) = sum(s^2) / n
+# over a row of n values, with s = x, or s = bf16(x + r) given a residual, as
+# for l2_rows.  Readings: the mean divides the sum by the row's length; eps is
+# added to the mean, not to the sum; the output is rounded once to bf16.
+# Algebraically y = sqrt(n) * s / sqrt(sum(s^2) + n eps): l2_rows with eps
+# scaled by n, times sqrt(n).
+
+def _s_values(x_bits, r_bits):
+    x = bf16_value(np.atleast_2d(x_bits))
+    if r_bits is None:
+        return x
+    with np.errstate(all="ignore"):
+        return bf16_value(bf16_rne(x + bf16_value(np.atleast_2d(r_bits))))
+
+
+def _rms_of_values(s: np.ndarray, eps64: float) -> np.ndarray:
+    """Row-wise s / sqrt(sum(s^2) / n + eps) in float64 (not yet rounded)."""
+    out = np.empty_like(s)
+    n = s.shape[1]
+    with np.errstate(all="ignore"):
+        for i in range(s.shape[0]):
+            d = math.sqrt(sum_sq(s[i]) / n + eps64)
+            out[i] = s[i] / d
+    return out
+
+
+def rms_rows(x_bits: np.ndarray, r_bits: Optional[np.ndarray] = None,
+             eps: float = 1e-6) -> np.ndarray:
+    """y = bf16(s / sqrt(mean(s^2) + eps)), s = x or bf16(x + r); bf16 bits in/out."""
+    y = _rms_of_values(_s_values(x_bits, r_bits), eps_as_passed(eps))
+    return bf16_rne(y).reshape(np.shape(x_bits))
+
+
+def rms_backward_values(s: np.ndarray, dy: np.ndarray, eps64: float) -> np.ndarray:
+    """ds = (dy - s <s, dy> / (n D^2)) / D per row, D = sqrt(sum(s^2) / n + eps).
+
+    y = s / D with dD/ds_j = s_j / (n D), so the Jacobian is
+    (I - s s^T / (n D^2)) / D, symmetric, applied to dy.
+    """
+    out = np.empty_like(s)
+    n = s.shape[1]
+    with np.errstate(all="ignore"):
+        for i in range(s.shape[0]):
+            d2 = sum_sq(s[i]) / n + eps64
+            p = math.fsum(s[i] * dy[i])
+            out[i] = (dy[i] - s[i] * (p / (n * d2))) / math.sqrt(d2)
+    return out
+
+
+def rms_rows_backward(x_bits: np.ndarray, r_bits: Optional[np.ndarray], dy_bits: np.ndarray,
+                      eps: float = 1e-6) -> np.ndarray:
+    """bf16 bits of ds, the gradient of rms_rows with respect to s (and to x, r)."""
+    s = _s_values(x_bits, r_bits)
+    dy = bf16_value(np.atleast_2d(dy_bits))
+    return bf16_rne(rms_backward_values(s, dy, eps_as_passed(eps))).reshape(np.shape(x_bits))

@@ -51,12 +51,22 @@ def inv_norm(S32, eps):
         return np.float32(1.0) / np.sqrt((S32 + np.float32(eps)).astype(np.float32))
 
 
-def l2_model(x_bits, r_bits=None, eps=1e-6, round_s=True, acc="f32"):
+def l2_model(x_bits, r_bits=None, eps=1e-6, round_s=True, acc="f32", mean=False,
+             eps_on_sum=False):
+    """l2_rows, or rms_rows with mean=True (S / n in fp32 before eps); the
+    eps_on_sum control adds eps to the sum before dividing by n."""
     x = bf16_value(x_bits).astype(np.float32)
     s = x if r_bits is None else x + bf16_value(r_bits).astype(np.float32)
     if r_bits is not None and round_s:
         s = bf16_of_f32(s)
-    inv = inv_norm(lane_sum_sq(s, acc), eps)
+    S = lane_sum_sq(s, acc)
+    if mean:
+        n = np.float32(s.shape[1])
+        if eps_on_sum:
+            S, eps = (S + np.float32(eps)).astype(np.float32) / n, 0.0
+        else:
+            S = (S / n).astype(np.float32)
+    inv = inv_norm(S, eps)
     return bf16_rne((s * inv[:, None]).astype(np.float64))
 
 
@@ -88,16 +98,21 @@ def rownorm_model(w, g, rho=1.0):
 # ------------------------------------------------------------------ backward
 
 def l2_backward_model(x_bits, r_bits, dy_bits, eps=1e-6, round_s=True, acc="f32",
-                      proj="s", use_eps=True):
+                      proj="s", use_eps=True, mean=False, k_mean=True):
     """ds = (dy - s k) inv, k = P inv inv; controls: an unrounded s, a narrow
     accumulator, the projection taken on the rounded output y (proj="y"),
-    eps left out."""
+    eps left out.  mean=True models the rms_rows gradient (S / n and P / n in
+    fp32); its control k_mean=False leaves P undivided."""
     x = bf16_value(x_bits).astype(np.float32)
     s = x if r_bits is None else x + bf16_value(r_bits).astype(np.float32)
     if r_bits is not None and round_s:
         s = bf16_of_f32(s)
     dy = bf16_value(dy_bits).astype(np.float32)
-    inv = inv_norm(lane_sum_sq(s, acc), eps if use_eps else 0.0)[:, None]
+    n = np.float32(s.shape[1])
+    S = lane_sum_sq(s, acc)
+    if mean:
+        S = (S / n).astype(np.float32)
+    inv = inv_norm(S, eps if use_eps else 0.0)[:, None]
     with np.errstate(all="ignore"):
         if proj == "y":
             y = bf16_of_f32(s * inv)
@@ -105,6 +120,8 @@ def l2_backward_model(x_bits, r_bits, dy_bits, eps=1e-6, round_s=True, acc="f32"
             ds = (dy - y * py) * inv
         else:
             p = lane_sum((s * dy).astype(np.float32), acc)[:, None]
+            if mean and k_mean:
+                p = (p / n).astype(np.float32)
             k = (p * inv) * inv
             ds = (dy - s * k) * inv
     return bf16_rne(ds.astype(np.float32).astype(np.float64))
