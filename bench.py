@@ -38,7 +38,8 @@ EPS = 1e-6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
                   "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip",
-                  "inst_qk.hip", "inst_rescale.hip", "ds_rows.hip"]
+                  "inst_qk.hip", "inst_rescale.hip", "inst_rms.hip", "inst_rms_bwd.hip",
+                  "ds_rows.hip"]
 
 
 def kernel_hash() -> str:
@@ -269,6 +270,19 @@ def main():
         t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), t[3].data_ptr(), r, c, eps, sp),
         4, n=100, ntens=4)
     ops["l2_rows_res_bwd_8192x4096"] = op(c2b_us, ROWS * COLS * 8, ROWS)
+
+    # ---- RMSNorm rows: the GPT page's d_model 768 over 8 x 2048 tokens (x read,
+    # y written; the gradient reads x and dy, writes dx), and the headline shape
+    # with a residual for comparison with l2_rows
+    rms_f_us = shaped_us(16384, 768, lambda t, r, c: L.ds_rms_rows(
+        t[0].data_ptr(), None, t[1].data_ptr(), r, c, eps, sp), 8, n=100, ntens=2)
+    rms_b_us = shaped_us(16384, 768, lambda t, r, c: L.ds_rms_rows_backward(
+        t[0].data_ptr(), None, t[1].data_ptr(), t[2].data_ptr(), r, c, eps, sp), 8, n=100)
+    rms_h_us = shaped_us(ROWS, COLS, lambda t, r, c: L.ds_rms_rows(
+        t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), r, c, eps, sp), 4, n=100)
+    ops["rms_rows_16384x768"] = op(rms_f_us, 16384 * 768 * 4, 16384)
+    ops["rms_rows_bwd_16384x768"] = op(rms_b_us, 16384 * 768 * 6, 16384)
+    ops["rms_rows_res_8192x4096"] = op(rms_h_us, ROWS * COLS * 6, ROWS)
 
     # ---- weight gradients: the 48 linears, and the one 11008 x 4096 matrix the
     # DragonScale README times forward + backward (device-random fp32 weights

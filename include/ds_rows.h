@@ -25,6 +25,10 @@
  *                         whole row.
  *  ds_qk_rows_l2          same PR, the q/k commit: rotate-half RoPE, each
  *                         head's L2 norm, q's scale vector (dory.py's order).
+ *  ds_rms_rows            the parameter-free RMSNorm of the ternary/8-bit GPT
+ *                         model page (its rms_norm over the last dimension):
+ *                         y = bf16(s / sqrt(sum(s^2) / n + eps)), s as for
+ *                         ds_l2_rows; ds_rms_rows_backward is its gradient.
  *  ds_rescale_project     DragonScale README, "Optimizer" (method "rescale":
  *  ds_rescale_after_step  raw rows kept at their radius by the optimizer):
  *                         remove the radial part of each gradient before a
@@ -84,7 +88,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10400          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10500          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -128,6 +132,21 @@ enum {
  */
 int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y,
                int64_t rows, int64_t cols, float eps, ds_stream_t stream);
+
+/*
+ * ds_rms_rows -- RMS-normalised activation rows, optionally with a fused
+ * residual.  (The ternary/8-bit GPT model page: its parameter-free rms_norm,
+ * torch's rms_norm over the last dimension, eps 1e-6.)
+ *
+ *   s = x, or bf16(x + r)                          (as in ds_l2_rows)
+ *   y = bf16(s / sqrt(sum_j s_j^2 / cols + eps))   for every row
+ *
+ * The fp32 sum of squares is divided by cols (IEEE division) before eps is
+ * added; the rest is ds_l2_rows' arithmetic, rescue included.  Arguments,
+ * layout, aliasing and errors: as for ds_l2_rows.
+ */
+int ds_rms_rows(const uint16_t* x, const uint16_t* r, uint16_t* y,
+                int64_t rows, int64_t cols, float eps, ds_stream_t stream);
 
 /*
  * ds_slerp_rows -- the nGPT residual update on unit rows.
@@ -291,6 +310,20 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n,
 int ds_l2_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy,
                         uint16_t* dx, int64_t rows, int64_t cols, float eps,
                         ds_stream_t stream);
+
+/*
+ * ds_rms_rows_backward -- the gradient of ds_rms_rows.
+ *
+ *   D  = sqrt(sum_j s_j^2 / cols + eps)
+ *   dx = bf16((dy - s * <s, dy> / (cols * D^2)) / D)     for every row
+ *
+ * (I - s s^T / (cols D^2)) / D is the Jacobian of s -> s / D here.  The fp32
+ * sums S and <s, dy> are each divided by cols before use.  Arguments,
+ * layout, aliasing and errors: as for ds_l2_rows_backward.
+ */
+int ds_rms_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy,
+                         uint16_t* dx, int64_t rows, int64_t cols, float eps,
+                         ds_stream_t stream);
 
 /*
  * One weight matrix of a ds_weight_rownorm_gain_backward call.

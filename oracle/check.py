@@ -189,9 +189,15 @@ def _judge(got_bits, lo, hi, exact_bits, exact_mask, zero_any_sign,
 
 
 def _mean_bounds(s_lo: float, s_hi: float, n: int):
-    """Bounds of fl(S / n) for S in [s_lo, s_hi] >= 0 (one rounding)."""
-    return (max(0.0, s_lo / n * (1 - U) * (1 - F64_WIDEN) - ETA),
-            s_hi / n * (1 + U) * (1 + F64_WIDEN) + ETA)
+    """Bounds of fl(S / n) for S in [s_lo, s_hi] >= 0 (one rounding).
+
+    Relative error only, like the sum bounds: a row whose S / n + eps falls
+    below 2^-96 is summed again scaled by a power of two (the kernels'
+    rescue), so the quotient that decides the result is a normal fp32 value;
+    where eps keeps S / n + eps above 2^-96 without a rescue, an absolute
+    subnormal error in S / n is far below the 2u the inverse allows for.
+    """
+    return s_lo / n * (1 - U) * (1 - F64_WIDEN), s_hi / n * (1 + U) * (1 + F64_WIDEN)
 
 
 def _row_inv(s_row: np.ndarray, eps64: float, depth: int, mean: bool = False):

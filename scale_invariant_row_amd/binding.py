@@ -88,8 +88,9 @@ def lib() -> ctypes.CDLL:
         import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
-        L.ds_l2_rows.argtypes = [vp, vp, vp, i64, i64, f32, vp]
-        L.ds_l2_rows.restype = ctypes.c_int
+        for name in ("ds_l2_rows", "ds_rms_rows"):
+            getattr(L, name).argtypes = [vp, vp, vp, i64, i64, f32, vp]
+            getattr(L, name).restype = ctypes.c_int
         L.ds_slerp_rows.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
         L.ds_slerp_rows.restype = ctypes.c_int
         L.ds_weight_rownorm_gain.argtypes = [ctypes.POINTER(RownormDesc), ctypes.c_int32, vp]
@@ -105,8 +106,9 @@ def lib() -> ctypes.CDLL:
         for name in ("ds_rescale_project", "ds_rescale_after_step"):
             getattr(L, name).argtypes = [ctypes.POINTER(RescaleDesc), ctypes.c_int32, vp]
             getattr(L, name).restype = ctypes.c_int
-        L.ds_l2_rows_backward.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
-        L.ds_l2_rows_backward.restype = ctypes.c_int
+        for name in ("ds_l2_rows_backward", "ds_rms_rows_backward"):
+            getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
+            getattr(L, name).restype = ctypes.c_int
         L.ds_weight_rownorm_gain_backward.argtypes = [ctypes.POINTER(RownormGradDesc),
                                                       ctypes.c_int32, vp]
         L.ds_weight_rownorm_gain_backward.restype = ctypes.c_int
@@ -169,11 +171,7 @@ def _stream_of(t, stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def ds_l2_rows(x, r=None, eps: float = 1e-6, out=None, stream=None):
-    """y = bf16(s / sqrt(sum(s^2) + eps)) per row, s = x or bf16(x + r).
-
-    Returns ``out`` (allocated like ``x`` when not given; may be ``x`` or ``r``).
-    """
+def _norm_rows(name, x, r, eps, out, stream):
     torch = _torch()
     _bf16_2d(x, "x")
     if r is not None:
@@ -184,10 +182,34 @@ def ds_l2_rows(x, r=None, eps: float = 1e-6, out=None, stream=None):
     _bf16_2d(out, "out")
     _same(x, out, "out")
     with torch.cuda.device(x.device):
-        st = lib().ds_l2_rows(x.data_ptr(), None if r is None else r.data_ptr(), out.data_ptr(),
-                              x.shape[0], x.shape[1], float(eps), _stream_of(x, stream))
-    _check(st, "ds_l2_rows")
+        st = getattr(lib(), name)(x.data_ptr(), None if r is None else r.data_ptr(),
+                                  out.data_ptr(), x.shape[0], x.shape[1], float(eps),
+                                  _stream_of(x, stream))
+    _check(st, name)
     return out
+
+
+def ds_rms_rows(x, r=None, eps: float = 1e-6, out=None, stream=None):
+    """y = bf16(s / sqrt(sum(s^2) / cols + eps)) per row, s = x or bf16(x + r).
+
+    Returns ``out`` (allocated like ``x`` when not given; may be ``x`` or ``r``).
+    """
+    return _norm_rows("ds_rms_rows", x, r, eps, out, stream)
+
+
+def ds_rms_rows_backward(x, r, dy, eps: float = 1e-6, out=None, stream=None):
+    """dx = bf16((dy - s <s,dy>/(cols D^2)) / D), D^2 = sum(s^2)/cols + eps: the
+    gradient of ds_rms_rows(x, r, eps) with respect to x (and r).  Returns
+    ``out`` (allocated like ``dy`` when not given; may be ``x``, ``r`` or ``dy``)."""
+    return _norm_rows_backward("ds_rms_rows_backward", x, r, dy, eps, out, stream)
+
+
+def ds_l2_rows(x, r=None, eps: float = 1e-6, out=None, stream=None):
+    """y = bf16(s / sqrt(sum(s^2) + eps)) per row, s = x or bf16(x + r).
+
+    Returns ``out`` (allocated like ``x`` when not given; may be ``x`` or ``r``).
+    """
+    return _norm_rows("ds_l2_rows", x, r, eps, out, stream)
 
 
 def ds_slerp_rows(res, out_rows, alpha, eps: float = 1e-6, h=None, stream=None):
@@ -256,10 +278,7 @@ def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Seque
     return list(norm_out), list(w_eff)
 
 
-def ds_l2_rows_backward(x, r, dy, eps: float = 1e-6, out=None, stream=None):
-    """dx = bf16((dy - s <s,dy>/D^2) / D), the gradient of ds_l2_rows(x, r, eps)
-    with respect to x (and to r when given).  Returns ``out`` (allocated like
-    ``dy`` when not given; may be ``x``, ``r`` or ``dy``)."""
+def _norm_rows_backward(name, x, r, dy, eps, out, stream):
     torch = _torch()
     _bf16_2d(x, "x")
     _bf16_2d(dy, "dy")
@@ -272,11 +291,18 @@ def ds_l2_rows_backward(x, r, dy, eps: float = 1e-6, out=None, stream=None):
     _bf16_2d(out, "out")
     _same(x, out, "out")
     with torch.cuda.device(x.device):
-        st = lib().ds_l2_rows_backward(x.data_ptr(), None if r is None else r.data_ptr(),
-                                       dy.data_ptr(), out.data_ptr(), x.shape[0], x.shape[1],
-                                       float(eps), _stream_of(x, stream))
-    _check(st, "ds_l2_rows_backward")
+        st = getattr(lib(), name)(x.data_ptr(), None if r is None else r.data_ptr(),
+                                  dy.data_ptr(), out.data_ptr(), x.shape[0], x.shape[1],
+                                  float(eps), _stream_of(x, stream))
+    _check(st, name)
     return out
+
+
+def ds_l2_rows_backward(x, r, dy, eps: float = 1e-6, out=None, stream=None):
+    """dx = bf16((dy - s <s,dy>/D^2) / D), the gradient of ds_l2_rows(x, r, eps)
+    with respect to x (and to r when given).  Returns ``out`` (allocated like
+    ``dy`` when not given; may be ``x``, ``r`` or ``dy``)."""
+    return _norm_rows_backward("ds_l2_rows_backward", x, r, dy, eps, out, stream)
 
 
 def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequence,

@@ -348,8 +348,14 @@ const char* ds_status_string(int status) {
   }
 }
 
-int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t rows, int64_t cols,
-               float eps, ds_stream_t stream) {
+namespace {
+
+using ForwardLaunch = hipError_t (*)(Shape, const void*, const void*, void*, int64_t, int, float,
+                                     int, hipStream_t);
+
+// l2_rows and rms_rows: the same checks, shape and grid.
+int norm_rows(ForwardLaunch launch, const uint16_t* x, const uint16_t* r, uint16_t* y,
+              int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
   int st = check_matrix(rows, cols, 8, 2);
   if (st != DS_OK) return st;
   if (!finite_nonneg(eps)) return DS_ERR_ARG;
@@ -365,8 +371,38 @@ int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t rows, 
   if ((st = device_cus(&cus)) != DS_OK) return st;
   const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
   (void)hipGetLastError();   // start from a clean error state
-  return launch_status(dsr::launch_l2_rows(s, x, r, y, rows, (int)(cols / 8), eps,
-                                           grid_for(units, cus), (hipStream_t)stream));
+  return launch_status(launch(s, x, r, y, rows, (int)(cols / 8), eps, grid_for(units, cus),
+                              (hipStream_t)stream));
+}
+
+using BackwardLaunch = hipError_t (*)(Shape, const void*, const void*, const void*, void*,
+                                      int64_t, int, float, int, hipStream_t);
+
+int norm_rows_backward(BackwardLaunch launch, const uint16_t* x, const uint16_t* r,
+                       const uint16_t* dy, uint16_t* dx, int64_t rows, int64_t cols, float eps,
+                       ds_stream_t stream) {
+  int st = check_l2_backward(x, r, dy, dx, rows, cols, eps);
+  if (st != DS_OK || rows == 0) return st;
+  const Shape s = dsr::pick_bf16_shape(cols / 8);
+  if (!s.ok()) return DS_ERR_SHAPE;
+  int cus = 0;
+  if ((st = device_cus(&cus)) != DS_OK) return st;
+  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  (void)hipGetLastError();
+  return launch_status(launch(s, x, r, dy, dx, rows, (int)(cols / 8), eps, grid_for(units, cus),
+                              (hipStream_t)stream));
+}
+
+}  // namespace
+
+int ds_l2_rows(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t rows, int64_t cols,
+               float eps, ds_stream_t stream) {
+  return norm_rows(dsr::launch_l2_rows, x, r, y, rows, cols, eps, stream);
+}
+
+int ds_rms_rows(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t rows, int64_t cols,
+                float eps, ds_stream_t stream) {
+  return norm_rows(dsr::launch_rms_rows, x, r, y, rows, cols, eps, stream);
 }
 
 int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha, uint16_t* h,
@@ -589,16 +625,12 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
 
 int ds_l2_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy, uint16_t* dx,
                         int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
-  int st = check_l2_backward(x, r, dy, dx, rows, cols, eps);
-  if (st != DS_OK || rows == 0) return st;
-  const Shape s = dsr::pick_bf16_shape(cols / 8);
-  if (!s.ok()) return DS_ERR_SHAPE;
-  int cus = 0;
-  if ((st = device_cus(&cus)) != DS_OK) return st;
-  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
-  (void)hipGetLastError();
-  return launch_status(dsr::launch_l2_rows_backward(s, x, r, dy, dx, rows, (int)(cols / 8), eps,
-                                                    grid_for(units, cus), (hipStream_t)stream));
+  return norm_rows_backward(dsr::launch_l2_rows_backward, x, r, dy, dx, rows, cols, eps, stream);
+}
+
+int ds_rms_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy, uint16_t* dx,
+                         int64_t rows, int64_t cols, float eps, ds_stream_t stream) {
+  return norm_rows_backward(dsr::launch_rms_rows_backward, x, r, dy, dx, rows, cols, eps, stream);
 }
 
 int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,

@@ -1,5 +1,6 @@
 """Writes inst_l2.hip, inst_slerp.hip, inst_rownorm.hip, inst_l2_bwd.hip,
-inst_rownorm_bwd.hip, inst_act.hip and inst_rescale.hip: one launcher per op
+inst_rownorm_bwd.hip, inst_act.hip, inst_rescale.hip, inst_rms.hip and
+inst_rms_bwd.hip: one launcher per op
 with a case for every kernel shape (G waves per row, V vectors per lane) that
 launch.hpp's shape policy returns for some width up to DS_MAX_COLS, found by
 evaluating the policy (reproduced below from launch.hpp's constants) at every
@@ -234,7 +235,56 @@ hipError_t launch_rescale_after_step(Shape s, const RescaleArgs& args, int grid,
 
 }  // namespace dsr
 '''
-    for name, text in (("inst_l2.hip", l2), ("inst_slerp.hip", sl), ("inst_rownorm.hip", rn),
+    rms = HEAD.format(what="rms_rows (l2_rows' kernel with the mean)") + '''
+template <int G, int V>
+static hipError_t run(const void* x, const void* r, void* y, int64_t rows, int nvec, float eps,
+                      int grid, hipStream_t stream) {
+  constexpr int T = Geo<G>::THREADS;
+  if (r != nullptr)
+    l2_rows_kernel<G, V, true, true><<<grid, T, 0, stream>>>(
+        (const u32x4_t*)x, (const u32x4_t*)r, (u32x4_t*)y, rows, nvec, eps);
+  else
+    l2_rows_kernel<G, V, false, true><<<grid, T, 0, stream>>>(
+        (const u32x4_t*)x, nullptr, (u32x4_t*)y, rows, nvec, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_rows(Shape s, const void* x, const void* r, void* y, int64_t rows,
+                           int nvec, float eps, int grid, hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(bf16, "return run<{G}, {V}>(x, r, y, rows, nvec, eps, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsr
+'''
+    rmsb = HEAD.format(what="rms_rows gradient (l2_rows' gradient kernel with the mean)") + '''
+template <int G, int V>
+static hipError_t run(const void* x, const void* r, const void* dy, void* dx, int64_t rows,
+                      int nvec, float eps, int grid, hipStream_t stream) {
+  constexpr int T = Geo<G>::THREADS;
+  if (r != nullptr)
+    l2_rows_backward_kernel<G, V, true, true><<<grid, T, 0, stream>>>(
+        (const u32x4_t*)x, (const u32x4_t*)r, (const u32x4_t*)dy, (u32x4_t*)dx, rows, nvec, eps);
+  else
+    l2_rows_backward_kernel<G, V, false, true><<<grid, T, 0, stream>>>(
+        (const u32x4_t*)x, nullptr, (const u32x4_t*)dy, (u32x4_t*)dx, rows, nvec, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_rows_backward(Shape s, const void* x, const void* r, const void* dy,
+                                    void* dx, int64_t rows, int nvec, float eps, int grid,
+                                    hipStream_t stream) {
+  switch (s.G * 100 + s.V) {
+''' + cases(bf16, "return run<{G}, {V}>(x, r, dy, dx, rows, nvec, eps, grid, stream);") + '''
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsr
+'''
+    for name, text in (("inst_l2.hip", l2), ("inst_rms.hip", rms), ("inst_rms_bwd.hip", rmsb), ("inst_slerp.hip", sl), ("inst_rownorm.hip", rn),
                        ("inst_l2_bwd.hip", l2b), ("inst_rownorm_bwd.hip", rnb),
                        ("inst_act.hip", act), ("inst_rescale.hip", rsc)):
         with open(os.path.join(HERE, name), "w") as f:

@@ -62,6 +62,11 @@ inline Shape pick_rownorm_shape(int64_t vectors) { return pick_shape(vectors, kV
 
 hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_t rows,
                           int nvec, float eps, int grid, hipStream_t stream);
+hipError_t launch_rms_rows(Shape s, const void* x, const void* r, void* y, int64_t rows,
+                           int nvec, float eps, int grid, hipStream_t stream);
+hipError_t launch_rms_rows_backward(Shape s, const void* x, const void* r, const void* dy,
+                                    void* dx, int64_t rows, int nvec, float eps, int grid,
+                                    hipStream_t stream);
 hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const float* alpha,
                              void* h, int64_t rows, int nvec, float eps, int grid,
                              hipStream_t stream);

@@ -394,12 +394,14 @@ struct Bf16Row {
 };
 
 // Normalise a packed-bf16 row in place: p <- bf16(p / sqrt(S + eps)), where
-// S is the row's (group-combined) fp32 sum of squares.
-template <int G, int V>
+// S is the row's (group-combined) fp32 sum of squares.  With MEAN the sum is
+// first divided by the row's length n (IEEE division): the RMS norm
+// p <- bf16(p / sqrt(S / n + eps)).
+template <int G, int V, bool MEAN = false>
 __device__ __forceinline__ void l2_in_place(Bf16Row<V>& s, float S, float eps,
                                             GroupScratch<G>& gs, int& slot,
-                                            const Geo<G>& geo) {
-  float T = S + eps;
+                                            const Geo<G>& geo, float n = 1.f) {
+  float T = (MEAN ? S / n : S) + eps;
   bool scaled = false;
   int sh = 0;
   if (T == __builtin_inff() || T < kTiny) {       // uniform over the group
@@ -409,7 +411,7 @@ __device__ __forceinline__ void l2_in_place(Bf16Row<V>& s, float S, float eps,
       sh = rescue_shift(m, eps);
       float t[1] = {wave_sum(s.sumsq_scaled(sh))};
       group_sum<G, 1>(t, gs.next(slot), geo.g, geo.lane);
-      T = t[0] + ldexpf(eps, 2 * sh);
+      T = (MEAN ? t[0] / n : t[0]) + ldexpf(eps, 2 * sh);
       scaled = true;
     }
   }
@@ -420,7 +422,8 @@ __device__ __forceinline__ void l2_in_place(Bf16Row<V>& s, float S, float eps,
 
 // ------------------------------------------------------------------ l2_rows
 
-template <int G, int V, bool RES>
+// MEAN: rms_rows, the same row divided by sqrt(S / n + eps) (n = 8 nvec).
+template <int G, int V, bool RES, bool MEAN = false>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
 l2_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int nvec, float eps) {
   constexpr int R = Geo<G>::R;
@@ -449,7 +452,7 @@ l2_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int
     float S[1] = {wave_sum(s.sumsq())};
     s.fence();
     group_sum<G, 1>(S, gs.next(slot), geo.g, geo.lane);
-    l2_in_place<G, V>(s, S[0], eps, gs, slot, geo);
+    l2_in_place<G, V, MEAN>(s, S[0], eps, gs, slot, geo, (float)(8 * nvec));
     s.store(RowBuf(y + row * nvec, row_bytes), off);
   }
 }
@@ -462,8 +465,10 @@ l2_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int
 // are summed again with s scaled by 2^sa and dy by 2^sb (sa from
 // max(max|s|, sqrt(eps)), sb from max|dy|, bringing each maximum to [1, 2)):
 // the scaled row gives ds * 2^(sb - sa) exactly, undone by one ldexp.
+// MEAN: the rms_rows gradient, with S and P each divided by n = 8 nvec (IEEE
+// division) before inv and k are formed.
 
-template <int G, int V, bool RES>
+template <int G, int V, bool RES, bool MEAN = false>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
 l2_rows_backward_kernel(const u32x4_t* x, const u32x4_t* r, const u32x4_t* dy, u32x4_t* dx,
                         int64_t rows, int nvec, float eps) {
@@ -474,6 +479,7 @@ l2_rows_backward_kernel(const u32x4_t* x, const u32x4_t* r, const u32x4_t* dy, u
   int off[V];
   geo.offsets(off, 16);
   const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  const float n = (float)(8 * nvec);
 
   for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
     const int64_t row = base + geo.rr;
@@ -495,8 +501,8 @@ l2_rows_backward_kernel(const u32x4_t* x, const u32x4_t* r, const u32x4_t* dy, u
     s.fence();
     d.fence();
     group_sum<G, 2>(acc, gs.next(slot), geo.g, geo.lane);
-    float T = acc[0] + eps;
-    float P = acc[1];
+    float T = (MEAN ? acc[0] / n : acc[0]) + eps;
+    float P = MEAN ? acc[1] / n : acc[1];
     bool scaled = false;
     int sa = 0, sb = 0;
     // uniform over the group; NaN sums enter too, and leave with no rescue
@@ -510,8 +516,8 @@ l2_rows_backward_kernel(const u32x4_t* x, const u32x4_t* r, const u32x4_t* dy, u
         sb = (m[1] > 0.f) ? rescue_shift(m[1], 0.f) : 0;
         float t[2] = {wave_sum(s.sumsq_scaled(sa)), wave_sum(s.dot_scaled(d, sa, sb))};
         group_sum<G, 2>(t, gs.next(slot), geo.g, geo.lane);
-        T = t[0] + ldexpf(eps, 2 * sa);
-        P = t[1];
+        T = (MEAN ? t[0] / n : t[0]) + ldexpf(eps, 2 * sa);
+        P = MEAN ? t[1] / n : t[1];
         scaled = true;
       }
     }

@@ -46,6 +46,9 @@ swiglu_l2_rows_8192x7168  g, u ~ N(0,1) bf16; sug, suu ~ U(0.5, 2) fp32 per colu
 rescale_12x4_d768         the 48 linears of rownorm_gain_12x4_d768 as raw rows,
                           W ~ N(0, sd 0.02) fp32, gradients / momenta
                           ~ N(0, sd 1e-3) fp32, radius 1
+rms_rows_bwd_16384x768    RMSNorm rows of the GPT model page's 100m size
+                          (d_model 768) over 8 sequences of 2,048 tokens:
+                          x ~ N(0,1), no residual; upstream dy ~ N(0,1)
 ========================  =======================================================
 
 Upstream gradients (dy, dL/dW_eff) are bf16 values drawn like activations.
@@ -392,6 +395,10 @@ WORKLOADS = {
         "rescale method over 12 pre-norm layers' linears (d 768, d_ff 3072): raw rows "
         "W ~ N(0, sd 0.02) fp32, gradients / momenta ~ N(0, sd 1e-3) fp32, radius 1",
         lambda: rescale_case(transformer_linears(), 1013, name="rescale_12x4_d768")),
+    "rms_rows_bwd_16384x768": (
+        "rms_rows and its gradient, 16384 x 768 bf16 (d_model 768, 8 x 2048 tokens): "
+        "x ~ N(0,1), no residual, dy ~ N(0,1), eps 1e-6",
+        lambda: l2_grad_case(16384, 768, 1014, residual=False, name="rms_rows_bwd_16384x768")),
 }
 
 

@@ -31,13 +31,14 @@ def test_exports_every_declared_function(L):
                           "ds_l2_rows_backward", "ds_weight_rownorm_gain_backward",
                           "ds_gate_l2_rows", "ds_swiglu_l2_rows", "ds_qk_rows_l2",
                           "ds_rescale_project", "ds_rescale_after_step",
+                          "ds_rms_rows", "ds_rms_rows_backward",
                           "ds_status_string", "ds_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10400
+    assert B.ds_version() == 10500
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -49,37 +50,48 @@ Bp = 0x20000000
 C = 0x40000000
 
 
+NORM = ["ds_l2_rows", "ds_rms_rows"]
+NORM_BWD = ["ds_l2_rows_backward", "ds_rms_rows_backward"]
+
+
+@pytest.mark.parametrize("name", NORM)
 @pytest.mark.parametrize("rows,cols,code", [
     (-1, 64, B.DS_ERR_SHAPE), (4, 0, B.DS_ERR_SHAPE), (4, 12, B.DS_ERR_SHAPE),
     (4, 65544, B.DS_ERR_SHAPE), (4, 4, B.DS_ERR_SHAPE), (1 << 60, 64, B.DS_ERR_SHAPE)])
-def test_l2_shape(L, rows, cols, code):
-    assert L.ds_l2_rows(A, None, Bp, rows, cols, 1e-6, None) == code
+def test_l2_shape(L, name, rows, cols, code):
+    assert getattr(L, name)(A, None, Bp, rows, cols, 1e-6, None) == code
 
 
-def test_l2_eps(L):
+@pytest.mark.parametrize("name", NORM)
+def test_l2_eps(L, name):
     for eps in (-1e-6, float("nan"), float("inf")):
-        assert L.ds_l2_rows(A, None, Bp, 4, 64, eps, None) == B.DS_ERR_ARG
+        assert getattr(L, name)(A, None, Bp, 4, 64, eps, None) == B.DS_ERR_ARG
 
 
-def test_l2_pointers(L):
-    assert L.ds_l2_rows(None, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_NULL
-    assert L.ds_l2_rows(A, None, None, 4, 64, 1e-6, None) == B.DS_ERR_NULL
-    assert L.ds_l2_rows(A + 8, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
-    assert L.ds_l2_rows(A, A + 2, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
-    assert L.ds_l2_rows(A, None, Bp + 4, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+@pytest.mark.parametrize("name", NORM)
+def test_l2_pointers(L, name):
+    f = getattr(L, name)
+    assert f(None, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert f(A, None, None, 4, 64, 1e-6, None) == B.DS_ERR_NULL
+    assert f(A + 8, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert f(A, A + 2, Bp, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
+    assert f(A, None, Bp + 4, 4, 64, 1e-6, None) == B.DS_ERR_ALIGN
     # y partly overlapping x or r
-    assert L.ds_l2_rows(A, None, A + 16, 4, 64, 1e-6, None) == B.DS_ERR_ARG
-    assert L.ds_l2_rows(A, C, C + 256, 4, 64, 1e-6, None) == B.DS_ERR_ARG
+    assert f(A, None, A + 16, 4, 64, 1e-6, None) == B.DS_ERR_ARG
+    assert f(A, C, C + 256, 4, 64, 1e-6, None) == B.DS_ERR_ARG
 
 
-def test_l2_zero_rows_is_noop(L):
-    assert L.ds_l2_rows(None, None, None, 0, 64, 1e-6, None) == B.DS_OK
+@pytest.mark.parametrize("name", NORM)
+def test_l2_zero_rows_is_noop(L, name):
+    assert getattr(L, name)(None, None, None, 0, 64, 1e-6, None) == B.DS_OK
 
 
 @pytest.mark.skipif("not no_device()")
-def test_l2_valid_args_reach_device_lookup(L):
-    assert L.ds_l2_rows(A, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE
-    assert L.ds_l2_rows(A, C, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE     # y == x is allowed
+@pytest.mark.parametrize("name", NORM)
+def test_l2_valid_args_reach_device_lookup(L, name):
+    f = getattr(L, name)
+    assert f(A, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE
+    assert f(A, C, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE     # y == x is allowed
     assert L.ds_slerp_rows(A, Bp, C, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE
 
 
@@ -128,8 +140,9 @@ def test_rownorm_valid_args_reach_device_lookup(L):
     assert L.ds_weight_rownorm_gain(_descs(good, shared_w), 2, None) == B.DS_ERR_DEVICE
 
 
-def test_l2_backward_validation(L):
-    f = L.ds_l2_rows_backward
+@pytest.mark.parametrize("name", NORM_BWD)
+def test_l2_backward_validation(L, name):
+    f = getattr(L, name)
     assert f(None, None, C, Bp, 4, 64, 1e-6, None) == B.DS_ERR_NULL
     assert f(A, None, None, Bp, 4, 64, 1e-6, None) == B.DS_ERR_NULL
     assert f(A, None, C, None, 4, 64, 1e-6, None) == B.DS_ERR_NULL
@@ -143,8 +156,9 @@ def test_l2_backward_validation(L):
 
 
 @pytest.mark.skipif("not no_device()")
-def test_l2_backward_valid_args_reach_device_lookup(L):
-    f = L.ds_l2_rows_backward
+@pytest.mark.parametrize("name", NORM_BWD)
+def test_l2_backward_valid_args_reach_device_lookup(L, name):
+    f = getattr(L, name)
     assert f(A, None, C, Bp, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE
     assert f(A, Bp, C, C, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE          # dx == dy
     assert f(A, Bp, C, A, 4, 64, 1e-6, None) == B.DS_ERR_DEVICE          # dx == x

@@ -26,6 +26,8 @@ def test_bf16_launchers_cover_policy():
     assert None not in need
     assert need <= cases("inst_l2.hip")
     assert need <= cases("inst_slerp.hip")
+    assert need <= cases("inst_rms.hip")
+    assert need <= cases("inst_rms_bwd.hip")
 
 
 def test_rownorm_launcher_covers_policy():
@@ -34,6 +36,7 @@ def test_rownorm_launcher_covers_policy():
     assert None not in need
     assert need <= cases("inst_rownorm.hip")
     assert need <= cases("inst_rownorm_bwd.hip")
+    assert need <= cases("inst_rescale.hip")
 
 
 def test_gradient_and_activation_launchers_cover_policy():
