@@ -43,7 +43,9 @@ __all__ = ["eps_as_passed", "l2_rows", "slerp_rows", "slerp_rows_detail",
            "gate_gated_row", "gate_l2_rows", "swiglu_product_row", "swiglu_l2_rows",
            "rope_angles", "qk_rotated_heads", "qk_rows_l2",
            "rescale_project_values", "rescale_project", "rescale_after_step",
-           "rms_rows", "rms_backward_values", "rms_rows_backward"]
+           "rms_rows", "rms_backward_values", "rms_rows_backward",
+           "gains_of", "column_block_rows", "to_column_block", "scalar_gain_gradient",
+           "weight_rownorm_scalar_gain_backward"]
 
 
 def eps_as_passed(eps: float) -> float:
@@ -131,12 +133,13 @@ def weight_rownorm_gain(w: Sequence[np.ndarray], gain: Sequence[np.ndarray],
 
     DragonScale README, "What DragonScale changes".  Returns, per matrix, the
     fp32 row lengths (the float64 length rounded to fp32) and the bf16 bits of
-    W_eff.  A zero-length row scales by 0.
+    W_eff.  A zero-length row scales by 0.  A matrix's gain is [rows], one
+    value for every row (a scalar gain) or None (unit rows: g = 1).
     """
     norms, weffs = [], []
     for wm, gm, rho in zip(w, gain, radius):
         w64 = np.asarray(wm, dtype=np.float64)
-        g64 = np.asarray(gm, dtype=np.float64)
+        g64 = gains_of(gm, w64.shape[0])
         rho64 = float(np.float32(rho))
         n = np.empty(w64.shape[0])
         weff = np.empty_like(w64)
@@ -215,7 +218,8 @@ def weight_rownorm_gain_backward(w: Sequence[np.ndarray], gain: Sequence[np.ndar
     """Per matrix: (dW fp32, dg fp32) from bf16 dL/dW_eff; the float64 values rounded once."""
     dws, dgs = [], []
     for wm, gm, rho, de in zip(w, gain, radius, dweff_bits):
-        dw, dg = rownorm_backward_values(np.asarray(wm, np.float64), np.asarray(gm, np.float64),
+        w64 = np.asarray(wm, np.float64)
+        dw, dg = rownorm_backward_values(w64, gains_of(gm, w64.shape[0]),
                                          float(np.float32(rho)), bf16_value(de))
         with np.errstate(over="ignore"):          # beyond fp32's range: +-inf
             dws.append(dw.astype(np.float32))
@@ -447,3 +451,76 @@ def rms_rows_backward(x_bits: np.ndarray, r_bits: Optional[np.ndarray], dy_bits:
     s = _s_values(x_bits, r_bits)
     dy = bf16_value(np.atleast_2d(dy_bits))
     return bf16_rne(rms_backward_values(s, dy, eps_as_passed(eps))).reshape(np.shape(x_bits))
+
+
+# ---------------------------------------------- gain modes and weight layouts
+#
+# DragonScale README, "Patching options" and "Supported layers": the gain is
+# one per row ("channel") or one for the whole layer ("scalar"), and mode
+# "unit" keeps unit rows with no gain; the patched layers are Linear,
+# Conv1d/2d/3d, ConvTranspose1d/2d/3d, Embedding and GPT-2's Conv1D.
+# Readings:
+# * a scalar gain is one value that every row of the matrix uses; "unit" is
+#   a gain of 1 (W_eff = r W / ||W||);
+# * a scalar gain's gradient is the sum over the rows of what each row's own
+#   gain would receive (the chain rule: every row shares the one value);
+# * a row is everything that feeds one output unit.  Linear, Conv and
+#   Embedding store it contiguously (W[o, ...]); GPT-2's Conv1D stores its
+#   weight as [in, out], so row o is the column W[:, o]; ConvTranspose stores
+#   [in, out / groups, k...], so row o of a group is W[:, o, ...] over the
+#   group's input channels: `in` segments of prod(k) contiguous values, one
+#   per stored row.  Both are "column-block" layouts: a weight stored as
+#   A rows of ld values whose unit u owns the seg values at u * seg of every
+#   stored row (Conv1D: A = in, seg = 1, ld = out; ConvTranspose, one group:
+#   A = in / groups, seg = prod(k), ld = (out / groups) * prod(k)).
+
+def gains_of(gain: Optional[np.ndarray], rows: int) -> np.ndarray:
+    """The per-row gains a gain mode stands for (float64): a [rows] array as
+    given, a one-element array for every row, None for 1 (mode "unit")."""
+    if gain is None:
+        return np.ones(rows)
+    g = np.asarray(gain, dtype=np.float64).reshape(-1)
+    return np.full(rows, g[0]) if g.size == 1 else g
+
+
+def column_block_rows(stored: np.ndarray, units: int, seg: int) -> np.ndarray:
+    """The unit rows [units, A * seg] of a column-block weight stored [A, ld]:
+    row u, element a * seg + b, is stored[a, u * seg + b]."""
+    a = np.asarray(stored)
+    out = np.empty((units, a.shape[0] * seg), dtype=a.dtype)
+    for u in range(units):
+        out[u] = a[:, u * seg:(u + 1) * seg].reshape(-1)
+    return out
+
+
+def to_column_block(rows: np.ndarray, stored_shape, seg: int, fill=0) -> np.ndarray:
+    """Inverse of column_block_rows: an array of stored_shape [A, ld] holding
+    each unit row in its columns, `fill` elsewhere."""
+    units = rows.shape[0]
+    out = np.full(stored_shape, fill, dtype=rows.dtype)
+    for u in range(units):
+        out[:, u * seg:(u + 1) * seg] = rows[u].reshape(stored_shape[0], seg)
+    return out
+
+
+def scalar_gain_gradient(dg_rows64: np.ndarray) -> np.float32:
+    """dL/dg of a scalar gain from the per-row values rho <w, dW_eff> / ||w||
+    (float64): their exact sum, rounded once to fp32."""
+    with np.errstate(over="ignore"):
+        return np.float32(math.fsum(np.asarray(dg_rows64, dtype=np.float64)))
+
+
+def weight_rownorm_scalar_gain_backward(w: np.ndarray, gain: Optional[np.ndarray], radius: float,
+                                        dweff_bits: np.ndarray):
+    """One matrix with a scalar gain (one value) or none: (dW fp32, dL/dg fp32).
+
+    dW is the per-row formula with g_i = g; dL/dg sums rho <w_i, dW_eff_i> /
+    ||w_i|| over the rows (float64, rounded once).  With no gain there is
+    nothing to differentiate and dL/dg is returned as None.
+    """
+    w64 = np.asarray(w, np.float64)
+    dw, dg = rownorm_backward_values(w64, gains_of(gain, w64.shape[0]), float(np.float32(radius)),
+                                     bf16_value(dweff_bits))
+    with np.errstate(over="ignore"):
+        dw32 = dw.astype(np.float32)
+    return dw32, (None if gain is None else scalar_gain_gradient(dg))
