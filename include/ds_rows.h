@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10500          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10600          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -244,10 +244,22 @@ int ds_qk_rows_l2(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk
                   float eps, ds_stream_t stream);
 
 /*
+ * Gain modes of a weight matrix (DragonScale README, "Patching options": a
+ * gain per row, one for the whole layer, or mode "unit" with no gain).
+ */
+enum {
+  DS_GAIN_ROW = 0,      /* gain[i] for row i */
+  DS_GAIN_SCALAR = 1,   /* gain[0] for every row */
+  DS_GAIN_NONE = 2      /* no gain: W_eff = r W / ||W||; gain is ignored */
+};
+
+/*
  * One weight matrix of a ds_weight_rownorm_gain call.
  *
  * w        : [rows, cols] fp32, row-major, contiguous, 16-byte aligned.
- * gain     : [rows] fp32, one learned gain per row; 4-byte aligned.
+ * gain     : per gain_mode: [rows] fp32 (DS_GAIN_ROW), one fp32 value
+ *            (DS_GAIN_SCALAR), or ignored and may be NULL (DS_GAIN_NONE);
+ *            4-byte aligned.
  * radius   : the row radius r: 1 for linears and convs, sqrt(cols) for
  *            embeddings (rows of unit RMS).  Finite.
  * norm_out : [rows] fp32, receives ||W_i|| (fp32 sum of squares, fp32
@@ -266,6 +278,7 @@ typedef struct ds_rownorm_desc {
   uint16_t* w_eff;
   int64_t rows;
   int64_t cols;
+  int32_t gain_mode;    /* DS_GAIN_*; 0 (a gain per row) when left zero */
 } ds_rownorm_desc;
 
 /*
@@ -328,10 +341,17 @@ int ds_rms_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* d
 /*
  * One weight matrix of a ds_weight_rownorm_gain_backward call.
  *
- * w, gain, radius : the forward call's inputs (as in ds_rownorm_desc).
+ * w, gain, radius, gain_mode : the forward call's inputs (as in
+ *                              ds_rownorm_desc).
  * dw_eff   : [rows, cols] bf16 bit patterns, dL/dW_eff; 16-byte aligned.
  * dw       : [rows, cols] fp32, receives dL/dW; 16-byte aligned.
- * dgain    : [rows] fp32, receives dL/dg; may be NULL; 4-byte aligned.
+ * dgain    : [rows] fp32, receives each row's share r <W_i, dW_eff_i> / ||W_i||:
+ *            dL/dg_i with a gain per row; may be NULL; 4-byte aligned.  Must
+ *            be NULL with DS_GAIN_NONE.
+ * dgain_total : one fp32, receives dL/dg of a scalar gain, the sum of the
+ *            rows' shares (added in an order fixed by rows alone); needs
+ *            DS_GAIN_SCALAR and dgain (which then holds the shares); NULL
+ *            otherwise.
  * rows, cols : as in ds_rownorm_desc.
  * dw and dgain must not overlap any input or output of the call.
  */
@@ -344,6 +364,8 @@ typedef struct ds_rownorm_grad_desc {
   float* dgain;
   int64_t rows;
   int64_t cols;
+  int32_t gain_mode;    /* DS_GAIN_*; 0 (a gain per row) when left zero */
+  float* dgain_total;
 } ds_rownorm_grad_desc;
 
 /*
@@ -352,9 +374,11 @@ typedef struct ds_rownorm_grad_desc {
  * (DragonScale README, "What DragonScale changes": the gradient reaching W is
  * tangent to its rows.)
  *
- * Per row i, with n_i = ||W_i|| and P_i = <W_i, dW_eff_i>:
+ * Per row i, with n_i = ||W_i||, P_i = <W_i, dW_eff_i> and g_i the row's
+ * gain under gain_mode (1 with no gain):
  *   dw_i    = (g_i r / n_i) (dW_eff_i - W_i P_i / n_i^2)     fp32
  *   dgain_i = r P_i / n_i                                     fp32
+ *   dgain_total = sum_i dgain_i                 (a scalar gain; fp32 sums)
  * A zero row (n_i = 0, scaled by the constant 0 in the forward) gets zero
  * gradients.
  *

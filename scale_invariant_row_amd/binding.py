@@ -41,6 +41,7 @@ class RownormDesc(ctypes.Structure):
         ("w_eff", ctypes.c_void_p),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
+        ("gain_mode", ctypes.c_int32),
     ]
 
 
@@ -55,6 +56,8 @@ class RownormGradDesc(ctypes.Structure):
         ("dgain", ctypes.c_void_p),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
+        ("gain_mode", ctypes.c_int32),
+        ("dgain_total", ctypes.c_void_p),
     ]
 
 
@@ -233,18 +236,38 @@ def ds_slerp_rows(res, out_rows, alpha, eps: float = 1e-6, h=None, stream=None):
     return h
 
 
+DS_GAIN_ROW, DS_GAIN_SCALAR, DS_GAIN_NONE = 0, 1, 2
+
+
+def _gain_mode(g, rows: int, name: str) -> int:
+    """A gain tensor's mode: None (no gain), a 0-dim or one-element tensor for
+    rows != 1 (one gain for the matrix), or a [rows] tensor (a gain per row)."""
+    torch = _torch()
+    if g is None:
+        return DS_GAIN_NONE
+    if g.dtype != torch.float32 or not g.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous fp32 tensor")
+    if g.dim() == 0 or (g.numel() == 1 and rows != 1):
+        return DS_GAIN_SCALAR
+    if g.shape != (rows,):
+        raise ValueError(f"{name}: expected fp32 [rows], one value, or None")
+    return DS_GAIN_ROW
+
+
 def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Sequence[float]] = None,
                            norm_out: Optional[Sequence] = None, w_eff: Optional[Sequence] = None,
                            stream=None) -> Tuple[list, list]:
     """Per matrix: ||W_i|| (fp32) and bf16(W_i * g_i * radius / ||W_i||), in one call.
 
-    ``ws``: fp32 [rows, cols] tensors; ``gains``: fp32 [rows].  Returns
-    (norms, w_effs); w_effs are bfloat16 tensors unless given.
+    ``ws``: fp32 [rows, cols] tensors; ``gains``: per matrix an fp32 [rows]
+    tensor (a gain per row), a single value (one gain for the matrix) or None
+    (no gain).  Returns (norms, w_effs); w_effs are bfloat16 tensors unless
+    given.
     """
     torch = _torch()
     n = len(ws)
     if len(gains) != n:
-        raise ValueError("one gain vector per matrix")
+        raise ValueError("one gain entry per matrix")
     radius = [1.0] * n if radius is None else list(radius)
     if norm_out is None:
         norm_out = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device) for w in ws]
@@ -255,21 +278,22 @@ def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Seque
     for i, (w, g) in enumerate(zip(ws, gains)):
         if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
             raise ValueError(f"ws[{i}]: expected a contiguous fp32 [rows, cols] tensor")
-        if g.dtype != torch.float32 or g.shape != (w.shape[0],) or not g.is_contiguous():
-            raise ValueError(f"gains[{i}]: expected a contiguous fp32 [rows] tensor")
+        mode = _gain_mode(g, w.shape[0], f"gains[{i}]")
         _bf16_2d(w_eff[i], f"w_eff[{i}]")
         if tuple(w_eff[i].shape) != tuple(w.shape):
             raise ValueError(f"w_eff[{i}]: shape mismatch")
         if norm_out[i] is not None and (norm_out[i].dtype != torch.float32
                                         or norm_out[i].shape != (w.shape[0],)):
             raise ValueError(f"norm_out[{i}]: expected fp32 [rows]")
-        for t in (w, g, w_eff[i]) + ((norm_out[i],) if norm_out[i] is not None else ()):
+        for t in (w, g, w_eff[i], norm_out[i]):
+            if t is None:
+                continue
             if t.device.type != "cuda" or (dev is not None and t.device != dev):
                 raise ValueError("all tensors must be on one HIP device")
             dev = t.device
-        descs[i] = RownormDesc(w.data_ptr(), g.data_ptr(), float(radius[i]),
+        descs[i] = RownormDesc(w.data_ptr(), None if g is None else g.data_ptr(), float(radius[i]),
                                None if norm_out[i] is None else norm_out[i].data_ptr(),
-                               w_eff[i].data_ptr(), w.shape[0], w.shape[1])
+                               w_eff[i].data_ptr(), w.shape[0], w.shape[1], mode)
     if n == 0:
         return [], []
     with torch.cuda.device(dev):
@@ -312,43 +336,53 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
                                     want_dgain: bool = True, stream=None) -> Tuple[list, list]:
     """Per matrix: dL/dW (fp32) and dL/dg (fp32) from dL/dW_eff (bf16), in one call.
 
-    Returns (dws, dgains); a dgain entry is None when ``want_dgain`` is false
-    and none was given.
+    ``gains`` as for ds_weight_rownorm_gain.  Returns (dws, dgains): dL/dg is
+    an fp32 [rows] tensor for a gain per row, a 0-dim fp32 tensor for one gain
+    per matrix (the library sums the rows' shares, kept in a [rows] buffer),
+    and None with no gain or when ``want_dgain`` is false and none was given.
     """
     torch = _torch()
     n = len(ws)
     if len(gains) != n or len(dw_effs) != n:
-        raise ValueError("one gain vector and one dW_eff per matrix")
+        raise ValueError("one gain entry and one dW_eff per matrix")
     radius = [1.0] * n if radius is None else list(radius)
     if dw is None:
         dw = [torch.empty(w.shape, dtype=torch.float32, device=w.device) for w in ws]
+    modes = [_gain_mode(g, w.shape[0], f"gains[{i}]") for i, (w, g) in enumerate(zip(ws, gains))]
     if dgain is None:
-        dgain = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device) if want_dgain
-                 else None for w in ws]
+        dgain = [torch.empty(w.shape[0] if m == DS_GAIN_ROW else (), dtype=torch.float32,
+                             device=w.device) if want_dgain and m != DS_GAIN_NONE else None
+                 for w, m in zip(ws, modes)]
+    shares = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device)
+              if m == DS_GAIN_SCALAR and dgain[i] is not None else None
+              for i, (w, m) in enumerate(zip(ws, modes))]
     descs = (RownormGradDesc * max(n, 1))()
     dev = None
     for i, (w, g, de) in enumerate(zip(ws, gains, dw_effs)):
         if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
             raise ValueError(f"ws[{i}]: expected a contiguous fp32 [rows, cols] tensor")
-        if g.dtype != torch.float32 or g.shape != (w.shape[0],) or not g.is_contiguous():
-            raise ValueError(f"gains[{i}]: expected a contiguous fp32 [rows] tensor")
         _bf16_2d(de, f"dw_effs[{i}]")
         if tuple(de.shape) != tuple(w.shape):
             raise ValueError(f"dw_effs[{i}]: shape mismatch")
         if dw[i].dtype != torch.float32 or tuple(dw[i].shape) != tuple(w.shape) \
                 or not dw[i].is_contiguous():
             raise ValueError(f"dw[{i}]: expected a contiguous fp32 tensor shaped like ws[{i}]")
-        if dgain[i] is not None and (dgain[i].dtype != torch.float32
-                                     or dgain[i].shape != (w.shape[0],)):
-            raise ValueError(f"dgain[{i}]: expected fp32 [rows]")
-        for t in (w, g, de, dw[i]) + ((dgain[i],) if dgain[i] is not None else ()):
+        want = (w.shape[0],) if modes[i] == DS_GAIN_ROW else ()
+        if dgain[i] is not None and (dgain[i].dtype != torch.float32 or dgain[i].shape != want):
+            raise ValueError(f"dgain[{i}]: expected fp32 of shape {want}")
+        for t in (w, g, de, dw[i], dgain[i], shares[i]):
+            if t is None:
+                continue
             if t.device.type != "cuda" or (dev is not None and t.device != dev):
                 raise ValueError("all tensors must be on one HIP device")
             dev = t.device
-        descs[i] = RownormGradDesc(w.data_ptr(), g.data_ptr(), float(radius[i]), de.data_ptr(),
-                                   dw[i].data_ptr(),
-                                   None if dgain[i] is None else dgain[i].data_ptr(),
-                                   w.shape[0], w.shape[1])
+        per_row = dgain[i] if modes[i] == DS_GAIN_ROW else shares[i]
+        total = dgain[i] if modes[i] == DS_GAIN_SCALAR else None
+        descs[i] = RownormGradDesc(w.data_ptr(), None if g is None else g.data_ptr(),
+                                   float(radius[i]), de.data_ptr(), dw[i].data_ptr(),
+                                   None if per_row is None else per_row.data_ptr(),
+                                   w.shape[0], w.shape[1], modes[i],
+                                   None if total is None else total.data_ptr())
     if n == 0:
         return [], []
     with torch.cuda.device(dev):

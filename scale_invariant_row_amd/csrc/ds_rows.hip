@@ -19,6 +19,42 @@
 #include "launch.hpp"
 #include "row_kernels.hpp"
 
+namespace dsr {
+
+// ------------------------------------------------ scalar-gain totals
+//
+// A scalar gain's gradient is the sum of its rows' shares (written by
+// rownorm_backward_kernel).  One workgroup of 256 threads per matrix: thread
+// k adds rows k, k + 256, ... in order, then the 256 partial sums are
+// combined by the wave tree and the four wave totals in order.  The order
+// depends on the row count alone.
+
+struct TotalTask {
+  const float* shares;
+  float* total;
+  int64_t rows;
+};
+constexpr int kTotalTasks = 64;
+struct TotalArgs {
+  int32_t ntasks;
+  TotalTask tasks[kTotalTasks];
+};
+static_assert(sizeof(TotalArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
+__global__ void __launch_bounds__(256) row_total_kernel(const TotalArgs args) {
+  __shared__ float part[4];
+  const TotalTask t = args.tasks[blockIdx.x];
+  float a = 0.f;
+  for (int64_t i = threadIdx.x; i < t.rows; i += 256) a += t.shares[i];
+  a = wave_sum(a);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[wave] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) *t.total = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+}  // namespace dsr
+
 namespace {
 
 using dsr::Shape;
@@ -309,6 +345,14 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
   return result;
 }
 
+bool gain_mode_ok(int32_t m) {
+  return m == DS_GAIN_ROW || m == DS_GAIN_SCALAR || m == DS_GAIN_NONE;
+}
+
+size_t gain_bytes(int32_t mode, int64_t rows) {
+  return mode == DS_GAIN_ROW ? (size_t)rows * 4 : mode == DS_GAIN_SCALAR ? 4 : 0;
+}
+
 // The l2_rows gradient's buffers: dx may be exactly x, r or dy (each row is
 // held in registers before its store), or disjoint from all three.
 int check_l2_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy, uint16_t* dx,
@@ -596,22 +640,25 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     const ds_rownorm_desc& d = descs[i];
     int st = check_matrix(d.rows, d.cols, 4, 4);
     if (st != DS_OK) return st;
-    if (!std::isfinite(d.radius)) return DS_ERR_ARG;
+    if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
     if (d.rows == 0) continue;
-    if (d.w == nullptr || d.gain == nullptr || d.w_eff == nullptr) return DS_ERR_NULL;
-    if (!aligned(d.w, 16) || !aligned(d.w_eff, 16) || !aligned(d.gain, 4) ||
+    const float* gain = d.gain_mode == DS_GAIN_NONE ? nullptr : d.gain;
+    if (d.w == nullptr || d.w_eff == nullptr || (d.gain_mode != DS_GAIN_NONE && gain == nullptr))
+      return DS_ERR_NULL;
+    if (!aligned(d.w, 16) || !aligned(d.w_eff, 16) || !aligned(gain, 4) ||
         (d.norm_out != nullptr && !aligned(d.norm_out, 4)))
       return DS_ERR_ALIGN;
     const size_t nel = (size_t)d.rows * (size_t)d.cols;
     add_range(ins, d.w, nel * 4);
-    add_range(ins, d.gain, (size_t)d.rows * 4);
+    add_range(ins, gain, gain_bytes(d.gain_mode, d.rows));
     add_range(outs, d.w_eff, nel * 2);
     add_range(outs, d.norm_out, (size_t)d.rows * 4);
     const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
     if (!s.ok()) return DS_ERR_SHAPE;
     dsr::RownormTask t{};
     t.w = d.w;
-    t.gain = d.gain;
+    t.gain = gain;
+    t.gain_stride = d.gain_mode == DS_GAIN_ROW ? 1 : 0;
     t.norm_out = d.norm_out;
     t.w_eff = d.w_eff;
     t.rows = d.rows;
@@ -641,28 +688,38 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
 
   std::vector<Range> outs, ins;
   std::vector<std::pair<Shape, dsr::RownormGradTask>> mats;
+  std::vector<dsr::TotalTask> totals;
   for (int32_t i = 0; i < n; ++i) {
     const ds_rownorm_grad_desc& d = descs[i];
     int st = check_matrix(d.rows, d.cols, 4, 4);
     if (st != DS_OK) return st;
-    if (!std::isfinite(d.radius)) return DS_ERR_ARG;
+    if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
+    // a total needs a scalar gain and the per-row shares it sums; no gain, no gradient
+    if (d.dgain_total != nullptr && (d.gain_mode != DS_GAIN_SCALAR || d.dgain == nullptr))
+      return DS_ERR_ARG;
+    if (d.gain_mode == DS_GAIN_NONE && d.dgain != nullptr) return DS_ERR_ARG;
     if (d.rows == 0) continue;
-    if (d.w == nullptr || d.gain == nullptr || d.dw_eff == nullptr || d.dw == nullptr)
+    const float* gain = d.gain_mode == DS_GAIN_NONE ? nullptr : d.gain;
+    if (d.w == nullptr || d.dw_eff == nullptr || d.dw == nullptr ||
+        (d.gain_mode != DS_GAIN_NONE && gain == nullptr))
       return DS_ERR_NULL;
     if (!aligned(d.w, 16) || !aligned(d.dw_eff, 16) || !aligned(d.dw, 16) ||
-        !aligned(d.gain, 4) || (d.dgain != nullptr && !aligned(d.dgain, 4)))
+        !aligned(gain, 4) || !aligned(d.dgain, 4) || !aligned(d.dgain_total, 4))
       return DS_ERR_ALIGN;
     const size_t nel = (size_t)d.rows * (size_t)d.cols;
     add_range(ins, d.w, nel * 4);
-    add_range(ins, d.gain, (size_t)d.rows * 4);
+    add_range(ins, gain, gain_bytes(d.gain_mode, d.rows));
     add_range(ins, d.dw_eff, nel * 2);
     add_range(outs, d.dw, nel * 4);
     add_range(outs, d.dgain, (size_t)d.rows * 4);
+    add_range(outs, d.dgain_total, 4);
+    if (d.dgain_total != nullptr) totals.push_back({d.dgain, d.dgain_total, d.rows});
     const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
     if (!s.ok()) return DS_ERR_SHAPE;
     dsr::RownormGradTask t{};
     t.w = d.w;
-    t.gain = d.gain;
+    t.gain = gain;
+    t.gain_stride = d.gain_mode == DS_GAIN_ROW ? 1 : 0;
     t.dw_eff = d.dw_eff;
     t.dw = d.dw;
     t.dgain = d.dgain;
@@ -672,8 +729,18 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
-  return launch_ragged<dsr::RownormGradTask>(mats, dsr::launch_rownorm_backward,
-                                             (hipStream_t)stream);
+  int st = launch_ragged<dsr::RownormGradTask>(mats, dsr::launch_rownorm_backward,
+                                               (hipStream_t)stream);
+  if (st != DS_OK) return st;
+  // scalar gains: sum each matrix's row shares once the shares are written
+  for (size_t first = 0; first < totals.size(); first += dsr::kTotalTasks) {
+    dsr::TotalArgs args{};
+    args.ntasks = (int32_t)std::min<size_t>(dsr::kTotalTasks, totals.size() - first);
+    for (int k = 0; k < args.ntasks; ++k) args.tasks[k] = totals[first + k];
+    dsr::row_total_kernel<<<args.ntasks, 256, 0, (hipStream_t)stream>>>(args);
+    if (hipGetLastError() != hipSuccess) return DS_ERR_LAUNCH;
+  }
+  return DS_OK;
 }
 
 namespace {

@@ -1029,29 +1029,35 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
 // R rows; matrix m owns items [item_begin, item_begin + ceil(rows / R)).
 struct RownormTask {
   const float* w;
-  const float* gain;
+  const float* gain;    // null: no gain (g = 1)
   float* norm_out;      // may be null
   uint16_t* w_eff;
   int64_t rows;
   int32_t cols;
   float radius;
   int32_t item_begin;
-  int32_t pad_;
+  int32_t gain_stride;  // 1: a gain per row; 0: one gain for the matrix
 };
 
 // One matrix of a ragged gradient call.
 struct RownormGradTask {
   const float* w;
-  const float* gain;
+  const float* gain;    // null: no gain (g = 1)
   const uint16_t* dw_eff;
   float* dw;
-  float* dgain;         // may be null
+  float* dgain;         // may be null; each row's share rho <w, dWe> / ||w||
   int64_t rows;
   int32_t cols;
   float radius;
   int32_t item_begin;
-  int32_t pad_;
+  int32_t gain_stride;  // 1: a gain per row; 0: one gain for the matrix
 };
+
+// The gain of a row: its own, the matrix's one value, or 1 with no gain.
+template <class Task>
+__device__ __forceinline__ float row_gain(const Task& t, int64_t row) {
+  return t.gain != nullptr ? t.gain[row * t.gain_stride] : 1.f;
+}
 
 // The tasks of one launch.  Up to kInlineTasks of them travel inside the
 // kernel arguments (no copy, no device allocation, safe to capture in a
@@ -1106,7 +1112,7 @@ rownorm_kernel(const RownormArgs args) {
     if (G == 1 && row >= t.rows) continue;          // independent waves only
     // the gain is read with the row, ahead of any store (a later read could
     // not move above the norm store, and would add a memory round trip)
-    const float gr = t.gain[row] * t.radius;
+    const float gr = row_gain(t, row) * t.radius;
     const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
     float w[V][4];
 #pragma unroll
@@ -1194,7 +1200,7 @@ rownorm_backward_kernel(const RownormGradArgs args) {
     const RownormGradTask t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
     const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
     if (G == 1 && row >= t.rows) continue;
-    const float gr = t.gain[row] * t.radius;
+    const float gr = row_gain(t, row) * t.radius;
     const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
     const RowBuf eb(t.dw_eff + row * t.cols, (uint32_t)t.cols * 2u);
     float w[V][4];

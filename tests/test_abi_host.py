@@ -38,7 +38,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10500
+    assert B.ds_version() == 10600
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -192,6 +192,44 @@ def test_rownorm_backward_validation(L):
     other = (A + 8192, Bp + 1024, 1.0, C + 8192, A + 2048, None, 16, 64)
     assert f(_gdescs(good, other), 2, None) == B.DS_ERR_ARG
     assert f(_gdescs((None, None, 1.0, None, None, None, 0, 64)), 1, None) == B.DS_OK
+
+
+def test_gain_mode_validation(L):
+    f = L.ds_weight_rownorm_gain
+    # w, gain, radius, norm_out, w_eff, rows, cols, gain_mode
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 64, 3)), 1, None) == B.DS_ERR_ARG
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 64, -1)), 1, None) == B.DS_ERR_ARG
+    assert f(_descs((A, None, 1.0, None, C, 16, 64, B.DS_GAIN_SCALAR)), 1, None) == B.DS_ERR_NULL
+    assert f(_descs((A, Bp + 2, 1.0, None, C, 16, 64, B.DS_GAIN_SCALAR)), 1, None) == B.DS_ERR_ALIGN
+    # a gain per row over W_eff's first bytes
+    assert f(_descs((A, C - 4, 1.0, None, C, 16, 64, B.DS_GAIN_ROW)), 1, None) == B.DS_ERR_ARG
+    g = L.ds_weight_rownorm_gain_backward
+    # w, gain, radius, dw_eff, dw, dgain, rows, cols, gain_mode, dgain_total
+    tot = Bp + 8192
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_ROW, tot)), 1,
+             None) == B.DS_ERR_ARG                       # a total needs a scalar gain
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, None, 16, 64, B.DS_GAIN_SCALAR, tot)), 1,
+             None) == B.DS_ERR_ARG                       # and the shares it sums
+    assert g(_gdescs((A, None, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_NONE)), 1,
+             None) == B.DS_ERR_ARG                       # no gain, no gain gradient
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR, tot + 2)),
+             1, None) == B.DS_ERR_ALIGN
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR,
+                      Bp + 4096 + 60)), 1, None) == B.DS_ERR_ARG   # total over the shares
+
+
+@pytest.mark.skipif("not no_device()")
+def test_gain_modes_reach_device_lookup(L):
+    f = L.ds_weight_rownorm_gain
+    assert f(_descs((A, None, 1.0, None, C, 16, 64, B.DS_GAIN_NONE)), 1, None) == B.DS_ERR_DEVICE
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 64, B.DS_GAIN_SCALAR)), 1, None) == B.DS_ERR_DEVICE
+    # a scalar gain spans 4 bytes: W_eff right after it does not overlap it
+    assert f(_descs((A, C - 4, 1.0, None, C, 16, 64, B.DS_GAIN_SCALAR)), 1, None) == B.DS_ERR_DEVICE
+    g = L.ds_weight_rownorm_gain_backward
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR, Bp + 8192)),
+             1, None) == B.DS_ERR_DEVICE
+    assert g(_gdescs((A, None, 1.0, C, C + 65536, None, 16, 64, B.DS_GAIN_NONE)), 1,
+             None) == B.DS_ERR_DEVICE
 
 
 @pytest.mark.skipif("not no_device()")

@@ -1,0 +1,123 @@
+"""The weight op's gain modes on the GPU against the CPU oracle: one gain for
+the whole matrix, and no gain (mode "unit"), forward and backward, in ragged
+calls that mix them with gains per row.
+
+Forward outputs meet the 1-ulp / 2e-6 contract and the strict interval; dW
+meets the gradient contract and interval; a scalar gain's gradient (the sum
+of the rows' shares) is within 2e-6 relative plus 2^-16 of the sum of the
+shares' magnitudes of the float64 value.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import announce, depth_for, dev_bits, dev_f32, host_bits
+from oracle.bf16 import bf16_value
+from oracle.check import (admissible_rownorm, admissible_rownorm_backward, contract_bf16,
+                          contract_grad, contract_rel, rownorm_grad_terms)
+from oracle.rows import gains_of, weight_rownorm_gain, weight_rownorm_gain_backward, \
+    weight_rownorm_scalar_gain_backward
+from scale_invariant_row_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from scale_invariant_row_amd import binding
+    binding.lib()
+    return binding
+
+
+SHAPES = [(33, 768), (7, 3072), (100, 44), (5, 12288)]
+MODES = ["row", "scalar", "none", "scalar", "none", "row", "scalar", "none"]
+
+
+def _case(seed):
+    shapes = [SHAPES[i % len(SHAPES)] for i in range(len(MODES))]
+    case = inputs.rownorm_grad_case(shapes, seed, radius=1.0)
+    gains = []
+    for m, g in zip(MODES, case.gain):
+        gains.append(g if m == "row" else (g[:1].copy() if m == "scalar" else None))
+    return case, gains
+
+
+def _dev_gain(g, mode):
+    import torch
+    if g is None:
+        return None
+    t = dev_f32(g)
+    return t.reshape(()) if mode == "scalar" else t
+
+
+def test_forward_modes(B):
+    import torch
+    case, gains = _case(1400)
+    announce("rownorm gain modes forward", MODES)
+    ws = [dev_f32(w) for w in case.w]
+    gs = [_dev_gain(g, m) for g, m in zip(gains, MODES)]
+    rho = [1.0, 27.712812921102035] * 4
+    norms, weffs = B.ds_weight_rownorm_gain(ws, gs, rho)
+    torch.cuda.synchronize()
+    for i, (w, g) in enumerate(zip(case.w, gains)):
+        n_ref, e_ref = weight_rownorm_gain([w], [g], [rho[i]])
+        got_n = norms[i].cpu().numpy()
+        got_e = host_bits(weffs[i])
+        assert contract_rel(got_n, n_ref[0]).all(), i
+        assert contract_bf16(got_e, e_ref[0], zero_sign=False).all(), i
+        rn, rw = admissible_rownorm(got_n, got_e, w, gains_of(g, w.shape[0]).astype(np.float32),
+                                    rho[i], depth=depth_for(w.shape[1]))
+        assert rn.ok and rw.ok, f"{i} {MODES[i]}: {rn} / {rw}"
+
+
+def test_backward_modes(B):
+    import torch
+    case, gains = _case(1401)
+    announce("rownorm gain modes backward", MODES)
+    ws = [dev_f32(w) for w in case.w]
+    gs = [_dev_gain(g, m) for g, m in zip(gains, MODES)]
+    des = [dev_bits(d) for d in case.dwe]
+    dws, dgs = B.ds_weight_rownorm_gain_backward(ws, gs, des, case.radius)
+    dws2, dgs2 = B.ds_weight_rownorm_gain_backward(ws, gs, des, case.radius)
+    torch.cuda.synchronize()
+    for i, (w, g, de) in enumerate(zip(case.w, gains, case.dwe)):
+        mode = MODES[i]
+        rho = case.radius[i]
+        g_rows = gains_of(g, w.shape[0]).astype(np.float32)
+        dw = dws[i].cpu().numpy()
+        assert np.array_equal(dw, dws2[i].cpu().numpy())
+        want_dw, want_dg = weight_rownorm_gain_backward([w], [g_rows], [rho], [de])
+        tw, tg = rownorm_grad_terms(w.astype(np.float64), g_rows.astype(np.float64),
+                                    float(np.float32(rho)), bf16_value(de))
+        assert contract_grad(dw, want_dw[0], tw, "f32").all(), f"{i} {mode}: dW"
+        rw, _ = admissible_rownorm_backward(dw, want_dg[0], w, g_rows, rho, de,
+                                            depth=depth_for(w.shape[1]))
+        assert rw.ok, f"{i} {mode}: {rw}"
+        if mode == "none":
+            assert dgs[i] is None
+        elif mode == "row":
+            assert contract_grad(dgs[i].cpu().numpy(), want_dg[0], tg, "f32").all(), i
+        else:
+            got = dgs[i].cpu().numpy()
+            assert got.shape == () and np.array_equal(got, dgs2[i].cpu().numpy())
+            _, total = weight_rownorm_scalar_gain_backward(w, g, rho, de)
+            assert contract_grad(np.array([got]), np.array([total]), np.array([tg.sum()]),
+                                 "f32").all(), f"{i}: scalar gain {got} vs {total}"
+
+
+def test_scalar_gain_on_the_transformer_workload(B):
+    """The 48 linears, each with one gain: dL/dg per matrix on the device."""
+    import torch
+    case = inputs.make("rownorm_gain_bwd_12x4_d768")
+    announce("rownorm scalar gains, 48 linears")
+    ws = [dev_f32(w) for w in case.w]
+    gs = [dev_f32(g[:1]).reshape(()) for g in case.gain]
+    des = [dev_bits(d) for d in case.dwe]
+    _, dgs = B.ds_weight_rownorm_gain_backward(ws, gs, des, case.radius)
+    torch.cuda.synchronize()
+    for i, (w, g, de) in enumerate(zip(case.w, case.gain, case.dwe)):
+        wd, dd = ws[i].double(), des[i].double()
+        n = wd.pow(2).sum(dim=1).sqrt()
+        exact = ((wd * dd).sum(dim=1) / n).sum().item()
+        mag = ((wd * dd).abs().sum(dim=1) / n).sum().item()
+        got = dgs[i].item()
+        assert abs(got - exact) <= 2e-6 * abs(exact) + 2.0 ** -16 * mag, (i, got, exact)
