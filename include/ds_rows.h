@@ -90,6 +90,8 @@ extern "C" {
 
 #define DS_ROWS_VERSION 10600          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
+#define DS_MAX_ELEM_COLS 16384         /* widest fp32 weight row whose width is
+                                          not a multiple of 4 */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
 typedef void* ds_stream_t;
@@ -98,9 +100,10 @@ typedef void* ds_stream_t;
 enum {
   DS_OK = 0,
   DS_ERR_NULL = -1,    /* a required pointer is NULL */
-  DS_ERR_SHAPE = -2,   /* rows < 0, cols not a multiple of 8 (bf16 rows) or 4
-                          (fp32 weight rows), cols below that multiple or above
-                          DS_MAX_COLS, or sizes that overflow */
+  DS_ERR_SHAPE = -2,   /* rows < 0, cols not a multiple of 8 (bf16 rows), cols
+                          below 8 (bf16) or 1 (fp32 weight rows) or above
+                          DS_MAX_COLS (DS_MAX_ELEM_COLS for a weight width
+                          that is not a multiple of 4), or sizes that overflow */
   DS_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned (gain, norm_out and
                           dgain: 4-byte aligned) */
   DS_ERR_ARG = -4,     /* eps negative or not finite, radius not finite,
@@ -256,7 +259,8 @@ enum {
 /*
  * One weight matrix of a ds_weight_rownorm_gain call.
  *
- * w        : [rows, cols] fp32, row-major, contiguous, 16-byte aligned.
+ * w        : [rows, cols] fp32, row-major, contiguous; 16-byte aligned when
+ *            cols is a multiple of 4, else 4-byte aligned.
  * gain     : per gain_mode: [rows] fp32 (DS_GAIN_ROW), one fp32 value
  *            (DS_GAIN_SCALAR), or ignored and may be NULL (DS_GAIN_NONE);
  *            4-byte aligned.
@@ -265,10 +269,15 @@ enum {
  * norm_out : [rows] fp32, receives ||W_i|| (fp32 sum of squares, fp32
  *            square root); may be NULL; 4-byte aligned.
  * w_eff    : [rows, cols] bf16 bit patterns, receives
- *            bf16(W_i * (g_i * radius / ||W_i||)); 16-byte aligned; must not
+ *            bf16(W_i * (g_i * radius / ||W_i||)); 16-byte aligned (2-byte
+ *            when cols is not a multiple of 4); must not
  *            overlap w, gain or norm_out.  A zero row gives a zero row.
  * rows     : >= 0.
- * cols     : multiple of 4, 4 <= cols <= DS_MAX_COLS.
+ * cols     : 1 <= cols <= DS_MAX_COLS.  A multiple of 4 runs on 16-byte
+ *            vectors; any other width (a convolution's in * prod(kernel),
+ *            such as 3 * 7 * 7 = 147) on single elements, up to
+ *            DS_MAX_ELEM_COLS.  A convolution's or an embedding's weight is
+ *            such a row-major matrix of its output units (or vocabulary).
  */
 typedef struct ds_rownorm_desc {
   const float* w;
@@ -343,8 +352,8 @@ int ds_rms_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* d
  *
  * w, gain, radius, gain_mode : the forward call's inputs (as in
  *                              ds_rownorm_desc).
- * dw_eff   : [rows, cols] bf16 bit patterns, dL/dW_eff; 16-byte aligned.
- * dw       : [rows, cols] fp32, receives dL/dW; 16-byte aligned.
+ * dw_eff   : [rows, cols] bf16 bit patterns, dL/dW_eff; aligned as w_eff.
+ * dw       : [rows, cols] fp32, receives dL/dW; aligned as w.
  * dgain    : [rows] fp32, receives each row's share r <W_i, dW_eff_i> / ||W_i||:
  *            dL/dg_i with a gain per row; may be NULL; 4-byte aligned.  Must
  *            be NULL with DS_GAIN_NONE.
@@ -392,14 +401,15 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
 /*
  * One weight matrix of a rescale-method call.
  *
- * w      : [rows, cols] fp32 raw rows, row-major, contiguous, 16-byte aligned.
+ * w      : [rows, cols] fp32 raw rows, row-major, contiguous; aligned as in
+ *          ds_rownorm_desc.
  * v      : [rows, cols] fp32, the gradient (ds_rescale_project) or the
  *          momentum (ds_rescale_after_step: Adam's exp_avg, SGD's or Muon's
- *          momentum buffer; may be NULL there); updated in place; 16-byte
- *          aligned; must not overlap any w or other v of the call.
+ *          momentum buffer; may be NULL there); updated in place; aligned
+ *          as w; must not overlap any w or other v of the call.
  * radius : the row radius after a step (1 for linears and convs, sqrt(cols)
  *          for embeddings); finite.  Unused by ds_rescale_project.
- * rows, cols : rows >= 0; cols a multiple of 4, 4 <= cols <= DS_MAX_COLS.
+ * rows, cols : as in ds_rownorm_desc.
  */
 typedef struct ds_rescale_desc {
   float* w;

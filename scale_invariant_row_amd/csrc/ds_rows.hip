@@ -250,15 +250,14 @@ template <class Task>
 int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLauncher<Task> launch,
                   hipStream_t hs) {
   std::map<int, std::vector<size_t>> classes;     // shape key -> indices into mats
-  for (size_t i = 0; i < mats.size(); ++i)
-    classes[mats[i].first.G * 100 + mats[i].first.V].push_back(i);
+  for (size_t i = 0; i < mats.size(); ++i) classes[mats[i].first.key()].push_back(i);
   if (classes.empty()) return DS_OK;
 
   std::vector<Task> table;
   struct Launch { Shape s; size_t first; int ntasks; int nitems; };
   std::vector<Launch> launches;
   for (auto& kv : classes) {
-    const Shape s{kv.first / 100, kv.first % 100};
+    const Shape s = mats[kv.second.front()].first;
     const int R = s.rows_per_block();
     Launch L{s, table.size(), 0, 0};
     int64_t items = 0;
@@ -343,6 +342,20 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
   }
   if (ring != nullptr) release(*ring, slot, true, hs);   // the copy is in flight either way
   return result;
+}
+
+// An fp32 weight matrix: rows >= 0 and 1 <= cols <= DS_MAX_COLS; a width that
+// is not a multiple of 4 takes the single-element path, up to kMaxElemCols.
+// Returns the kernel shape in *s, and the alignment its fp32 and bf16
+// buffers need (16 bytes on the vector path; 4 and 2 on the element path).
+int check_weight(int64_t rows, int64_t cols, Shape* s, uintptr_t* a32, uintptr_t* a16) {
+  int st = check_matrix(rows, cols, 1, 4);
+  if (st != DS_OK) return st;
+  *s = dsr::pick_weight_shape(cols);
+  if (!s->ok()) return DS_ERR_SHAPE;
+  *a32 = s->NE == 4 ? 16 : 4;
+  *a16 = s->NE == 4 ? 16 : 2;
+  return DS_OK;
 }
 
 bool gain_mode_ok(int32_t m) {
@@ -638,14 +651,16 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
   std::vector<std::pair<Shape, dsr::RownormTask>> mats;
   for (int32_t i = 0; i < n; ++i) {
     const ds_rownorm_desc& d = descs[i];
-    int st = check_matrix(d.rows, d.cols, 4, 4);
+    Shape s;
+    uintptr_t a32 = 16, a16 = 16;
+    int st = check_weight(d.rows, d.cols, &s, &a32, &a16);
     if (st != DS_OK) return st;
     if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
     if (d.rows == 0) continue;
     const float* gain = d.gain_mode == DS_GAIN_NONE ? nullptr : d.gain;
     if (d.w == nullptr || d.w_eff == nullptr || (d.gain_mode != DS_GAIN_NONE && gain == nullptr))
       return DS_ERR_NULL;
-    if (!aligned(d.w, 16) || !aligned(d.w_eff, 16) || !aligned(gain, 4) ||
+    if (!aligned(d.w, a32) || !aligned(d.w_eff, a16) || !aligned(gain, 4) ||
         (d.norm_out != nullptr && !aligned(d.norm_out, 4)))
       return DS_ERR_ALIGN;
     const size_t nel = (size_t)d.rows * (size_t)d.cols;
@@ -653,8 +668,6 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     add_range(ins, gain, gain_bytes(d.gain_mode, d.rows));
     add_range(outs, d.w_eff, nel * 2);
     add_range(outs, d.norm_out, (size_t)d.rows * 4);
-    const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
-    if (!s.ok()) return DS_ERR_SHAPE;
     dsr::RownormTask t{};
     t.w = d.w;
     t.gain = gain;
@@ -691,7 +704,9 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
   std::vector<dsr::TotalTask> totals;
   for (int32_t i = 0; i < n; ++i) {
     const ds_rownorm_grad_desc& d = descs[i];
-    int st = check_matrix(d.rows, d.cols, 4, 4);
+    Shape s;
+    uintptr_t a32 = 16, a16 = 16;
+    int st = check_weight(d.rows, d.cols, &s, &a32, &a16);
     if (st != DS_OK) return st;
     if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
     // a total needs a scalar gain and the per-row shares it sums; no gain, no gradient
@@ -703,7 +718,7 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     if (d.w == nullptr || d.dw_eff == nullptr || d.dw == nullptr ||
         (d.gain_mode != DS_GAIN_NONE && gain == nullptr))
       return DS_ERR_NULL;
-    if (!aligned(d.w, 16) || !aligned(d.dw_eff, 16) || !aligned(d.dw, 16) ||
+    if (!aligned(d.w, a32) || !aligned(d.dw_eff, a16) || !aligned(d.dw, a32) ||
         !aligned(gain, 4) || !aligned(d.dgain, 4) || !aligned(d.dgain_total, 4))
       return DS_ERR_ALIGN;
     const size_t nel = (size_t)d.rows * (size_t)d.cols;
@@ -714,8 +729,6 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     add_range(outs, d.dgain, (size_t)d.rows * 4);
     add_range(outs, d.dgain_total, 4);
     if (d.dgain_total != nullptr) totals.push_back({d.dgain, d.dgain_total, d.rows});
-    const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
-    if (!s.ok()) return DS_ERR_SHAPE;
     dsr::RownormGradTask t{};
     t.w = d.w;
     t.gain = gain;
@@ -755,17 +768,17 @@ int rescale_call(const ds_rescale_desc* descs, int32_t n, bool after_step, ds_st
   std::vector<std::pair<Shape, dsr::RescaleTask>> mats;
   for (int32_t i = 0; i < n; ++i) {
     const ds_rescale_desc& d = descs[i];
-    int st = check_matrix(d.rows, d.cols, 4, 4);
+    Shape s;
+    uintptr_t a32 = 16, a16 = 16;
+    int st = check_weight(d.rows, d.cols, &s, &a32, &a16);
     if (st != DS_OK) return st;
     if (after_step && !std::isfinite(d.radius)) return DS_ERR_ARG;
     if (d.rows == 0) continue;
     if (d.w == nullptr || (!after_step && d.v == nullptr)) return DS_ERR_NULL;
-    if (!aligned(d.w, 16) || (d.v != nullptr && !aligned(d.v, 16))) return DS_ERR_ALIGN;
+    if (!aligned(d.w, a32) || !aligned(d.v, a32)) return DS_ERR_ALIGN;
     const size_t nb = (size_t)d.rows * (size_t)d.cols * 4;
     add_range(after_step ? outs : ins, d.w, nb);
     add_range(outs, d.v, nb);
-    const Shape s = dsr::pick_rownorm_shape(d.cols / 4);
-    if (!s.ok()) return DS_ERR_SHAPE;
     dsr::RescaleTask t{};
     t.w = d.w;
     t.v = d.v;

@@ -16,7 +16,7 @@ def limits():
     text = open(os.path.join(HERE, "launch.hpp")).read()
     get = lambda name: int(re.search(rf"{name}\s*=\s*(\d+)", text).group(1))
     return {k: get(k) for k in ("kBf16SmallVectors", "kVmaxBf16Small", "kVmaxBf16Large",
-                                "kVmaxAct", "kVmaxRownorm", "kVmaxWide")}
+                                "kVmaxAct", "kVmaxRownorm", "kVmaxWide", "kVmaxElem")}
 
 
 def pick_shape(vectors, vmax, wide):
@@ -56,6 +56,29 @@ def rownorm_shapes(lim):
     return sorted({rownorm_shape(n, lim) for n in range(1, MAX_COLS // 4 + 1)})
 
 
+MAX_ELEM_COLS = 16 * 64 * 16
+
+
+def elem_shape(cols, lim):
+    """launch.hpp's pick_elem_shape, in Python."""
+    vmax = lim["kVmaxElem"]
+    v = -(-cols // 64)
+    if v <= vmax:
+        V = 1
+        while V < v:
+            V *= 2
+        return 1, V
+    G = 2
+    while 64 * G * vmax < cols:
+        G *= 2
+    return G, vmax
+
+
+def elem_shapes(lim):
+    """Every shape the single-element fp32 policy returns (rows up to 16,384)."""
+    return sorted({elem_shape(n, lim) for n in range(1, MAX_ELEM_COLS + 1)})
+
+
 HEAD = '''// {what}: one launcher over every kernel shape the shape policy can return.
 // Written by gen_instances.py.
 #include "row_kernels.hpp"
@@ -65,14 +88,17 @@ namespace dsr {{
 '''
 
 
-def cases(lst, call):
-    return "\n".join(f"    case {G * 100 + V}: {call.format(G=G, V=V)}" for G, V in lst)
+def cases(lst, call, ne=None):
+    """Switch cases over shapes; with ne, keys are NE * 10000 + G * 100 + V."""
+    key = (lambda G, V: G * 100 + V) if ne is None else (lambda G, V: ne * 10000 + G * 100 + V)
+    return "\n".join(f"    case {key(G, V)}: {call.format(G=G, V=V, NE=ne)}" for G, V in lst)
 
 
 def main():
     lim = limits()
     bf16 = bf16_shapes(lim)
     rown = rownorm_shapes(lim)
+    elem = elem_shapes(lim)
     actsh = act_shapes(lim)
     l2 = HEAD.format(what="l2_rows") + '''
 template <int G, int V>
@@ -121,16 +147,16 @@ hipError_t launch_slerp_rows(Shape s, const void* res, const void* out, const fl
 }  // namespace dsr
 '''
     rn = HEAD.format(what="weight rownorm+gain") + '''
-template <int G, int V>
+template <int G, int V, int NE>
 static hipError_t run(const RownormArgs& args, int grid, hipStream_t stream) {
   constexpr int T = Geo<G>::THREADS;
-  rownorm_kernel<G, V><<<grid, T, 0, stream>>>(args);
+  rownorm_kernel<G, V, NE><<<grid, T, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_t stream) {
-  switch (s.G * 100 + s.V) {
-''' + cases(rown, "return run<{G}, {V}>(args, grid, stream);") + '''
+  switch (s.key()) {
+''' + cases(rown, "return run<{G}, {V}, {NE}>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;
   }
 }
@@ -163,17 +189,17 @@ hipError_t launch_l2_rows_backward(Shape s, const void* x, const void* r, const 
 }  // namespace dsr
 '''
     rnb = HEAD.format(what="weight rownorm+gain gradient") + '''
-template <int G, int V>
+template <int G, int V, int NE>
 static hipError_t run(const RownormGradArgs& args, int grid, hipStream_t stream) {
   constexpr int T = Geo<G>::THREADS;
-  rownorm_backward_kernel<G, V><<<grid, T, 0, stream>>>(args);
+  rownorm_backward_kernel<G, V, NE><<<grid, T, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_rownorm_backward(Shape s, const RownormGradArgs& args, int grid,
                                    hipStream_t stream) {
-  switch (s.G * 100 + s.V) {
-''' + cases(rown, "return run<{G}, {V}>(args, grid, stream);") + '''
+  switch (s.key()) {
+''' + cases(rown, "return run<{G}, {V}, {NE}>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;
   }
 }
@@ -211,24 +237,24 @@ hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const fl
 }  // namespace dsr
 '''
     rsc = HEAD.format(what="rescale method (projection; rescale after a step)") + '''
-template <int G, int V, bool RESCALE>
+template <int G, int V, int NE, bool RESCALE>
 static hipError_t run(const RescaleArgs& args, int grid, hipStream_t stream) {
   constexpr int T = Geo<G>::THREADS;
-  rescale_kernel<G, V, RESCALE><<<grid, T, 0, stream>>>(args);
+  rescale_kernel<G, V, NE, RESCALE><<<grid, T, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_rescale_project(Shape s, const RescaleArgs& args, int grid, hipStream_t stream) {
-  switch (s.G * 100 + s.V) {
-''' + cases(rown, "return run<{G}, {V}, false>(args, grid, stream);") + '''
+  switch (s.key()) {
+''' + cases(rown, "return run<{G}, {V}, {NE}, false>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}, false>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_rescale_after_step(Shape s, const RescaleArgs& args, int grid,
                                      hipStream_t stream) {
-  switch (s.G * 100 + s.V) {
-''' + cases(rown, "return run<{G}, {V}, true>(args, grid, stream);") + '''
+  switch (s.key()) {
+''' + cases(rown, "return run<{G}, {V}, {NE}, true>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}, true>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;
   }
 }

@@ -5,43 +5,52 @@
 
 namespace dsr {
 
-template <int G, int V>
+template <int G, int V, int NE>
 static hipError_t run(const RownormArgs& args, int grid, hipStream_t stream) {
   constexpr int T = Geo<G>::THREADS;
-  rownorm_kernel<G, V><<<grid, T, 0, stream>>>(args);
+  rownorm_kernel<G, V, NE><<<grid, T, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_t stream) {
-  switch (s.G * 100 + s.V) {
-    case 101: return run<1, 1>(args, grid, stream);
-    case 102: return run<1, 2>(args, grid, stream);
-    case 103: return run<1, 3>(args, grid, stream);
-    case 104: return run<1, 4>(args, grid, stream);
-    case 105: return run<1, 5>(args, grid, stream);
-    case 106: return run<1, 6>(args, grid, stream);
-    case 204: return run<2, 4>(args, grid, stream);
-    case 205: return run<2, 5>(args, grid, stream);
-    case 206: return run<2, 6>(args, grid, stream);
-    case 404: return run<4, 4>(args, grid, stream);
-    case 405: return run<4, 5>(args, grid, stream);
-    case 406: return run<4, 6>(args, grid, stream);
-    case 804: return run<8, 4>(args, grid, stream);
-    case 805: return run<8, 5>(args, grid, stream);
-    case 806: return run<8, 6>(args, grid, stream);
-    case 1604: return run<16, 4>(args, grid, stream);
-    case 1605: return run<16, 5>(args, grid, stream);
-    case 1606: return run<16, 6>(args, grid, stream);
-    case 1607: return run<16, 7>(args, grid, stream);
-    case 1608: return run<16, 8>(args, grid, stream);
-    case 1609: return run<16, 9>(args, grid, stream);
-    case 1610: return run<16, 10>(args, grid, stream);
-    case 1611: return run<16, 11>(args, grid, stream);
-    case 1612: return run<16, 12>(args, grid, stream);
-    case 1613: return run<16, 13>(args, grid, stream);
-    case 1614: return run<16, 14>(args, grid, stream);
-    case 1615: return run<16, 15>(args, grid, stream);
-    case 1616: return run<16, 16>(args, grid, stream);
+  switch (s.key()) {
+    case 40101: return run<1, 1, 4>(args, grid, stream);
+    case 40102: return run<1, 2, 4>(args, grid, stream);
+    case 40103: return run<1, 3, 4>(args, grid, stream);
+    case 40104: return run<1, 4, 4>(args, grid, stream);
+    case 40105: return run<1, 5, 4>(args, grid, stream);
+    case 40106: return run<1, 6, 4>(args, grid, stream);
+    case 40204: return run<2, 4, 4>(args, grid, stream);
+    case 40205: return run<2, 5, 4>(args, grid, stream);
+    case 40206: return run<2, 6, 4>(args, grid, stream);
+    case 40404: return run<4, 4, 4>(args, grid, stream);
+    case 40405: return run<4, 5, 4>(args, grid, stream);
+    case 40406: return run<4, 6, 4>(args, grid, stream);
+    case 40804: return run<8, 4, 4>(args, grid, stream);
+    case 40805: return run<8, 5, 4>(args, grid, stream);
+    case 40806: return run<8, 6, 4>(args, grid, stream);
+    case 41604: return run<16, 4, 4>(args, grid, stream);
+    case 41605: return run<16, 5, 4>(args, grid, stream);
+    case 41606: return run<16, 6, 4>(args, grid, stream);
+    case 41607: return run<16, 7, 4>(args, grid, stream);
+    case 41608: return run<16, 8, 4>(args, grid, stream);
+    case 41609: return run<16, 9, 4>(args, grid, stream);
+    case 41610: return run<16, 10, 4>(args, grid, stream);
+    case 41611: return run<16, 11, 4>(args, grid, stream);
+    case 41612: return run<16, 12, 4>(args, grid, stream);
+    case 41613: return run<16, 13, 4>(args, grid, stream);
+    case 41614: return run<16, 14, 4>(args, grid, stream);
+    case 41615: return run<16, 15, 4>(args, grid, stream);
+    case 41616: return run<16, 16, 4>(args, grid, stream);
+    case 10101: return run<1, 1, 1>(args, grid, stream);
+    case 10102: return run<1, 2, 1>(args, grid, stream);
+    case 10104: return run<1, 4, 1>(args, grid, stream);
+    case 10108: return run<1, 8, 1>(args, grid, stream);
+    case 10116: return run<1, 16, 1>(args, grid, stream);
+    case 10216: return run<2, 16, 1>(args, grid, stream);
+    case 10416: return run<4, 16, 1>(args, grid, stream);
+    case 10816: return run<8, 16, 1>(args, grid, stream);
+    case 11616: return run<16, 16, 1>(args, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

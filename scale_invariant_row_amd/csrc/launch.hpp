@@ -13,13 +13,17 @@ struct RownormGradTask;
 struct QkArgs;
 struct RescaleTask;
 
-// Kernel shape: G waves per row, V 16-byte vectors per lane.
+// Kernel shape: G waves per row, V vectors per lane, NE values per vector
+// (the fp32 weight kernels: 4 for 16-byte vectors, 1 for single elements;
+// every other kernel uses 16-byte vectors).
 struct Shape {
   int G = 0;
   int V = 0;
+  int NE = 4;
   int rows_per_block() const { return G == 1 ? 4 : 1; }
   int threads() const { return 64 * G * rows_per_block(); }
   bool ok() const { return G > 0; }
+  int key() const { return NE * 10000 + G * 100 + V; }
 };
 
 // Shape policy, measured on MI355X (the gradients use the same rules as
@@ -31,6 +35,10 @@ struct Shape {
 //   activation rows (gate, SwiGLU): V <= 2, so the fp32 column scales stay
 //     in VGPRs; these kernels are ALU-bound and gain from more, lighter waves;
 //   fp32 weight rows: V <= 6;
+//   fp32 weight rows of single elements (a width that is not a multiple of
+//     4, rare: a convolution's first layer): one wave with V the next power
+//     of two >= ceil(cols / 64), else the smallest G with V = 16 (rows up to
+//     kMaxElemCols); the buffer range check zeroes the unused vectors;
 //   G = 16 may take V up to 16 (rows up to DS_MAX_COLS).
 // The shape is a function of the width alone.  gen_instances.py evaluates
 // these same rules over every width to list the kernels to instantiate.
@@ -40,6 +48,8 @@ constexpr int kVmaxBf16Large = 4;
 constexpr int kVmaxAct = 2;
 constexpr int kVmaxRownorm = 6;
 constexpr int kVmaxWide = 16;
+constexpr int kVmaxElem = 16;
+constexpr int kMaxElemCols = 16 * 64 * kVmaxElem;   // 16,384
 
 inline Shape pick_shape(int64_t vectors, int vmax) {
   for (int G = 1; G <= 16; G *= 2) {
@@ -59,6 +69,28 @@ inline Shape pick_act_shape(int64_t vectors) { return pick_shape(vectors, kVmaxA
 
 // fp32 weight rows of `vectors` 16-byte vectors (4 columns each)
 inline Shape pick_rownorm_shape(int64_t vectors) { return pick_shape(vectors, kVmaxRownorm); }
+
+// fp32 weight rows of `cols` single elements
+inline Shape pick_elem_shape(int64_t cols) {
+  Shape s{};
+  s.NE = 1;
+  if (cols < 1 || cols > kMaxElemCols) return s;
+  const int64_t v = (cols + 63) / 64;
+  if (v <= kVmaxElem) {
+    s.G = 1;
+    for (s.V = 1; s.V < v; s.V *= 2) {}
+  } else {
+    for (s.G = 2; (int64_t)64 * s.G * kVmaxElem < cols; s.G *= 2) {}
+    s.V = kVmaxElem;
+  }
+  return s;
+}
+
+// The shape of an fp32 weight row of `cols` values: 16-byte vectors when cols
+// is a multiple of 4, single elements otherwise.
+inline Shape pick_weight_shape(int64_t cols) {
+  return cols % 4 == 0 ? pick_rownorm_shape(cols / 4) : pick_elem_shape(cols);
+}
 
 hipError_t launch_l2_rows(Shape s, const void* x, const void* r, void* y, int64_t rows,
                           int nvec, float eps, int grid, hipStream_t stream);

@@ -95,6 +95,19 @@ struct RowBuf {
   __device__ __forceinline__ void st8(u32x2_t v, int off) const {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolSt);
   }
+  // single elements (rows whose width is not a multiple of the vector)
+  __device__ __forceinline__ float ld4f(int off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCpolLd));
+  }
+  __device__ __forceinline__ uint32_t ld2(int off) const {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kCpolLd);
+  }
+  __device__ __forceinline__ void st4(float v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kCpolSt);
+  }
+  __device__ __forceinline__ void st2(uint32_t v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, off, 0, kCpolSt);
+  }
 };
 
 // ---------------------------------------------------------------- bf16 pack
@@ -1024,6 +1037,67 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
 }
 
 // ------------------------------------------------------- weight rownorm+gain
+//
+// The fp32 weight kernels take NE values per lane-vector: NE = 4 (16-byte
+// accesses) for rows whose width is a multiple of 4, NE = 1 (single
+// elements) for the others, such as a convolution's 3 x 7 x 7 = 147.  A
+// lane's values at vector v are elements NE * vec_index(v) + k of the row.
+
+template <int NE>
+struct F32Vec {
+  static_assert(NE == 4 || NE == 1, "4 or 1 values per lane-vector");
+  __device__ __forceinline__ static void load(const RowBuf& b, int off, float (&d)[NE]) {
+    if constexpr (NE == 4) {
+      const f32x4_t q = b.ld16f(off);
+      d[0] = q.x; d[1] = q.y; d[2] = q.z; d[3] = q.w;
+    } else {
+      d[0] = b.ld4f(off);
+    }
+  }
+  __device__ __forceinline__ static void store(const RowBuf& b, int off, const float (&v)[NE]) {
+    if constexpr (NE == 4) {
+      const f32x4_t o = {v[0], v[1], v[2], v[3]};
+      b.st16(__builtin_bit_cast(u32x4_t, o), off);
+    } else {
+      b.st4(v[0], off);
+    }
+  }
+};
+
+// NE bf16 values, packed two to a register (one, in the low half, for NE = 1).
+template <int NE>
+struct Bf16Vec {
+  static constexpr int P = (NE + 1) / 2;
+  uint32_t p[P];
+  __device__ __forceinline__ void load(const RowBuf& b, int off) {
+    if constexpr (NE == 4) {
+      const u32x2_t q = b.ld8(off);
+      p[0] = q.x; p[1] = q.y;
+    } else {
+      p[0] = b.ld2(off);
+    }
+  }
+  __device__ __forceinline__ float get(int k) const { return (k & 1) ? bf_hi(p[k / 2]) : bf_lo(p[k / 2]); }
+  // |max| over the packed values, on the bits (a bf16 pattern with the sign
+  // cleared orders like its magnitude)
+  __device__ __forceinline__ u16x2_t absmax(u16x2_t mx) const {
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, p[i] & 0x7fff7fffu));
+    return mx;
+  }
+};
+
+// Store NE values as bf16 (round to nearest even).
+template <int NE>
+__device__ __forceinline__ void store_bf16(const RowBuf& b, int off, const float (&v)[NE]) {
+  if constexpr (NE == 4) {
+    const u32x2_t o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    b.st8(o, off);
+  } else {
+    b.st2(pack_bf16(v[0], 0.f), off);
+  }
+}
 
 // One matrix of a ragged call, as the kernel reads it.  Items are groups of
 // R rows; matrix m owns items [item_begin, item_begin + ceil(rows / R)).
@@ -1094,7 +1168,7 @@ __device__ __forceinline__ int owning_task(const TaskArgs<Task>& a, int item, in
   return count - 1;
 }
 
-template <int G, int V>
+template <int G, int V, int NE>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
 rownorm_kernel(const RownormArgs args) {
   constexpr int R = Geo<G>::R;
@@ -1102,7 +1176,7 @@ rownorm_kernel(const RownormArgs args) {
   __shared__ GroupScratch<G> gs;
   int slot = 0;
   int off[V];
-  geo.offsets(off, 16);
+  geo.offsets(off, 4 * NE);
   const int nitems = args.nitems;
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
@@ -1114,21 +1188,16 @@ rownorm_kernel(const RownormArgs args) {
     // not move above the norm store, and would add a memory round trip)
     const float gr = row_gain(t, row) * t.radius;
     const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
-    float w[V][4];
+    float w[V][NE];
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const f32x4_t q = wb.ld16f(off[v]);
-      w[v][0] = q.x; w[v][1] = q.y; w[v][2] = q.z; w[v][3] = q.w;
-    }
-    float a0 = 0.f, a1 = 0.f;
+    for (int v = 0; v < V; ++v) F32Vec<NE>::load(wb, off[v], w[v]);
+    // two fma chains, alternating over the row's elements
+    float a[2] = {0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      a0 = __builtin_fmaf(w[v][0], w[v][0], a0);
-      a1 = __builtin_fmaf(w[v][1], w[v][1], a1);
-      a0 = __builtin_fmaf(w[v][2], w[v][2], a0);
-      a1 = __builtin_fmaf(w[v][3], w[v][3], a1);
-    }
-    float S[1] = {wave_sum(a0 + a1)};
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < NE; ++k) a[(v * NE + k) & 1] = __builtin_fmaf(w[v][k], w[v][k], a[(v * NE + k) & 1]);
+    float S[1] = {wave_sum(a[0] + a[1])};
     group_sum<G, 1>(S, gs.next(slot), geo.g, geo.lane);
     float T = S[0];
     bool scaled = false;
@@ -1138,21 +1207,19 @@ rownorm_kernel(const RownormArgs args) {
 #pragma unroll
       for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(w[v][k]));
+        for (int k = 0; k < NE; ++k) m = fmaxf(m, fabsf(w[v][k]));
       m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
       if (m > 0.f && m < __builtin_inff()) {
         sh = rescue_shift(m, 0.f);
-        float c0 = 0.f, c1 = 0.f;
+        float c[2] = {0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          float q0 = ldexpf(w[v][0], sh), q1 = ldexpf(w[v][1], sh);
-          float q2 = ldexpf(w[v][2], sh), q3 = ldexpf(w[v][3], sh);
-          c0 = __builtin_fmaf(q0, q0, c0);
-          c1 = __builtin_fmaf(q1, q1, c1);
-          c0 = __builtin_fmaf(q2, q2, c0);
-          c1 = __builtin_fmaf(q3, q3, c1);
-        }
-        float tt[1] = {wave_sum(c0 + c1)};
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < NE; ++k) {
+            const float q = ldexpf(w[v][k], sh);
+            c[(v * NE + k) & 1] = __builtin_fmaf(q, q, c[(v * NE + k) & 1]);
+          }
+        float tt[1] = {wave_sum(c[0] + c[1])};
         group_sum<G, 1>(tt, gs.next(slot), geo.g, geo.lane);
         T = tt[0];
         scaled = true;
@@ -1165,13 +1232,10 @@ rownorm_kernel(const RownormArgs args) {
     const RowBuf eb(t.w_eff + row * t.cols, (uint32_t)t.cols * 2u);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      float q[4] = {w[v][0], w[v][1], w[v][2], w[v][3]};
-      if (scaled) {
+      float q[NE];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) q[k] = ldexpf(q[k], sh);
-      }
-      u32x2_t o = {pack_bf16(q[0] * c, q[1] * c), pack_bf16(q[2] * c, q[3] * c)};
-      eb.st8(o, off[v] / 2);
+      for (int k = 0; k < NE; ++k) q[k] = (scaled ? ldexpf(w[v][k], sh) : w[v][k]) * c;
+      store_bf16<NE>(eb, off[v] / 2, q);
     }
   }
 }
@@ -1184,7 +1248,7 @@ rownorm_kernel(const RownormArgs args) {
 // by 2^sa and dWe by 2^sb (as for l2_rows' gradient; no eps here).  A zero
 // row gets exact zeros: the forward scales it by the constant 0.
 
-template <int G, int V>
+template <int G, int V, int NE>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
 rownorm_backward_kernel(const RownormGradArgs args) {
   constexpr int R = Geo<G>::R;
@@ -1192,7 +1256,7 @@ rownorm_backward_kernel(const RownormGradArgs args) {
   __shared__ GroupScratch<G> gs;
   int slot = 0;
   int off[V];
-  geo.offsets(off, 16);
+  geo.offsets(off, 4 * NE);
   const int nitems = args.nitems;
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
@@ -1203,28 +1267,23 @@ rownorm_backward_kernel(const RownormGradArgs args) {
     const float gr = row_gain(t, row) * t.radius;
     const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
     const RowBuf eb(t.dw_eff + row * t.cols, (uint32_t)t.cols * 2u);
-    float w[V][4];
-    uint32_t e[V][2];
+    float w[V][NE];
+    Bf16Vec<NE> e[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const f32x4_t q = wb.ld16f(off[v]);
-      w[v][0] = q.x; w[v][1] = q.y; w[v][2] = q.z; w[v][3] = q.w;
-      const u32x2_t b = eb.ld8(off[v] / 2);
-      e[v][0] = b.x; e[v][1] = b.y;
+      F32Vec<NE>::load(wb, off[v], w[v]);
+      e[v].load(eb, off[v] / 2);
     }
-    float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+    float a[2] = {0.f, 0.f}, p[2] = {0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      a0 = __builtin_fmaf(w[v][0], w[v][0], a0);
-      a1 = __builtin_fmaf(w[v][1], w[v][1], a1);
-      a0 = __builtin_fmaf(w[v][2], w[v][2], a0);
-      a1 = __builtin_fmaf(w[v][3], w[v][3], a1);
-      p0 = __builtin_fmaf(w[v][0], bf_lo(e[v][0]), p0);
-      p1 = __builtin_fmaf(w[v][1], bf_hi(e[v][0]), p1);
-      p0 = __builtin_fmaf(w[v][2], bf_lo(e[v][1]), p0);
-      p1 = __builtin_fmaf(w[v][3], bf_hi(e[v][1]), p1);
-    }
-    float acc[2] = {wave_sum(a0 + a1), wave_sum(p0 + p1)};
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const int ch = (v * NE + k) & 1;
+        a[ch] = __builtin_fmaf(w[v][k], w[v][k], a[ch]);
+        p[ch] = __builtin_fmaf(w[v][k], e[v].get(k), p[ch]);
+      }
+    float acc[2] = {wave_sum(a[0] + a[1]), wave_sum(p[0] + p[1])};
     group_sum<G, 2>(acc, gs.next(slot), geo.g, geo.lane);
     float T = acc[0];
     float P = acc[1];
@@ -1236,9 +1295,8 @@ rownorm_backward_kernel(const RownormGradArgs args) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m[0] = fmaxf(m[0], fabsf(w[v][k]));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, e[v][0] & 0x7fff7fffu));
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, e[v][1] & 0x7fff7fffu));
+        for (int k = 0; k < NE; ++k) m[0] = fmaxf(m[0], fabsf(w[v][k]));
+        mx = e[v].absmax(mx);
       }
       m[1] = __uint_as_float((uint32_t)(mx.x > mx.y ? mx.x : mx.y) << 16);
       m[0] = wave_max(m[0]);
@@ -1247,21 +1305,17 @@ rownorm_backward_kernel(const RownormGradArgs args) {
       if (m[0] > 0.f && m[0] < __builtin_inff() && m[1] < __builtin_inff()) {
         sa = rescue_shift(m[0], 0.f);
         sb = (m[1] > 0.f) ? rescue_shift(m[1], 0.f) : 0;
-        float c0 = 0.f, c1 = 0.f, q0 = 0.f, q1 = 0.f;
+        float c[2] = {0.f, 0.f}, q[2] = {0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const float w0 = ldexpf(w[v][0], sa), w1 = ldexpf(w[v][1], sa);
-          const float w2 = ldexpf(w[v][2], sa), w3 = ldexpf(w[v][3], sa);
-          c0 = __builtin_fmaf(w0, w0, c0);
-          c1 = __builtin_fmaf(w1, w1, c1);
-          c0 = __builtin_fmaf(w2, w2, c0);
-          c1 = __builtin_fmaf(w3, w3, c1);
-          q0 = __builtin_fmaf(w0, ldexpf(bf_lo(e[v][0]), sb), q0);
-          q1 = __builtin_fmaf(w1, ldexpf(bf_hi(e[v][0]), sb), q1);
-          q0 = __builtin_fmaf(w2, ldexpf(bf_lo(e[v][1]), sb), q0);
-          q1 = __builtin_fmaf(w3, ldexpf(bf_hi(e[v][1]), sb), q1);
-        }
-        float tt[2] = {wave_sum(c0 + c1), wave_sum(q0 + q1)};
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < NE; ++k) {
+            const int ch = (v * NE + k) & 1;
+            const float x = ldexpf(w[v][k], sa);
+            c[ch] = __builtin_fmaf(x, x, c[ch]);
+            q[ch] = __builtin_fmaf(x, ldexpf(e[v].get(k), sb), q[ch]);
+          }
+        float tt[2] = {wave_sum(c[0] + c[1]), wave_sum(q[0] + q[1])};
         group_sum<G, 2>(tt, gs.next(slot), geo.g, geo.lane);
         T = tt[0];
         P = tt[1];
@@ -1279,21 +1333,19 @@ rownorm_backward_kernel(const RownormGradArgs args) {
     const int sh = sa - sb;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      float wv[4] = {w[v][0], w[v][1], w[v][2], w[v][3]};
-      float ev[4] = {bf_lo(e[v][0]), bf_hi(e[v][0]), bf_lo(e[v][1]), bf_hi(e[v][1])};
-      float o[4];
+      float o[NE];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < NE; ++k) {
+        float wv = w[v][k], ev = e[v].get(k);
         if (scaled) {
-          wv[k] = ldexpf(wv[k], sa);
-          ev[k] = ldexpf(ev[k], sb);
+          wv = ldexpf(wv, sa);
+          ev = ldexpf(ev, sb);
         }
-        o[k] = c * __builtin_fmaf(-wv[k], kk, ev[k]);
+        o[k] = c * __builtin_fmaf(-wv, kk, ev);
         if (scaled) o[k] = ldexpf(o[k], sh);
         if (zero) o[k] = 0.f;
       }
-      const f32x4_t ov = {o[0], o[1], o[2], o[3]};
-      ob.st16(__builtin_bit_cast(u32x4_t, ov), off[v]);
+      F32Vec<NE>::store(ob, off[v], o);
     }
   }
 }
@@ -1322,7 +1374,7 @@ struct RescaleTask {
 using RescaleArgs = TaskArgs<RescaleTask>;
 static_assert(sizeof(RescaleArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
-template <int G, int V, bool RESCALE>
+template <int G, int V, int NE, bool RESCALE>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
 rescale_kernel(const RescaleArgs args) {
   constexpr int R = Geo<G>::R;
@@ -1330,7 +1382,7 @@ rescale_kernel(const RescaleArgs args) {
   __shared__ GroupScratch<G> gs;
   int slot = 0;
   int off[V];
-  geo.offsets(off, 16);
+  geo.offsets(off, 4 * NE);
   const int nitems = args.nitems;
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
@@ -1342,27 +1394,22 @@ rescale_kernel(const RescaleArgs args) {
     const uint32_t bytes = (uint32_t)t.cols * 4u;
     const RowBuf wb(t.w + row * t.cols, bytes);
     const RowBuf vb(has_v ? t.v + row * t.cols : t.w, has_v ? bytes : 0u);
-    float w[V][4], v[V][4];
+    float w[V][NE], v[V][NE];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      const f32x4_t a = wb.ld16f(off[k]);
-      w[k][0] = a.x; w[k][1] = a.y; w[k][2] = a.z; w[k][3] = a.w;
-      const f32x4_t b = vb.ld16f(off[k]);          // zeros when there is no v
-      v[k][0] = b.x; v[k][1] = b.y; v[k][2] = b.z; v[k][3] = b.w;
+      F32Vec<NE>::load(wb, off[k], w[k]);
+      F32Vec<NE>::load(vb, off[k], v[k]);          // zeros when there is no v
     }
-    float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+    float a[2] = {0.f, 0.f}, p[2] = {0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      a0 = __builtin_fmaf(w[k][0], w[k][0], a0);
-      a1 = __builtin_fmaf(w[k][1], w[k][1], a1);
-      a0 = __builtin_fmaf(w[k][2], w[k][2], a0);
-      a1 = __builtin_fmaf(w[k][3], w[k][3], a1);
-      p0 = __builtin_fmaf(w[k][0], v[k][0], p0);
-      p1 = __builtin_fmaf(w[k][1], v[k][1], p1);
-      p0 = __builtin_fmaf(w[k][2], v[k][2], p0);
-      p1 = __builtin_fmaf(w[k][3], v[k][3], p1);
-    }
-    float acc[2] = {wave_sum(a0 + a1), wave_sum(p0 + p1)};
+    for (int k = 0; k < V; ++k)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int ch = (k * NE + j) & 1;
+        a[ch] = __builtin_fmaf(w[k][j], w[k][j], a[ch]);
+        p[ch] = __builtin_fmaf(w[k][j], v[k][j], p[ch]);
+      }
+    float acc[2] = {wave_sum(a[0] + a[1]), wave_sum(p[0] + p[1])};
     group_sum<G, 2>(acc, gs.next(slot), geo.g, geo.lane);
     float T = acc[0];
     float P = acc[1];
@@ -1373,7 +1420,7 @@ rescale_kernel(const RescaleArgs args) {
 #pragma unroll
       for (int k = 0; k < V; ++k)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NE; ++j) {
           m[0] = fmaxf(m[0], fabsf(w[k][j]));
           m[1] = fmaxf(m[1], fabsf(v[k][j]));
         }
@@ -1383,19 +1430,17 @@ rescale_kernel(const RescaleArgs args) {
       if (m[0] > 0.f && m[0] < __builtin_inff() && m[1] < __builtin_inff()) {
         sa = rescue_shift(m[0], 0.f);
         sb = (m[1] > 0.f) ? rescue_shift(m[1], 0.f) : 0;
-        float c0 = 0.f, c1 = 0.f, q0 = 0.f, q1 = 0.f;
+        float c[2] = {0.f, 0.f}, q[2] = {0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
+        for (int k = 0; k < V; ++k)
 #pragma unroll
-          for (int j = 0; j < 4; j += 2) {
-            const float x0 = ldexpf(w[k][j], sa), x1 = ldexpf(w[k][j + 1], sa);
-            c0 = __builtin_fmaf(x0, x0, c0);
-            c1 = __builtin_fmaf(x1, x1, c1);
-            q0 = __builtin_fmaf(x0, ldexpf(v[k][j], sb), q0);
-            q1 = __builtin_fmaf(x1, ldexpf(v[k][j + 1], sb), q1);
+          for (int j = 0; j < NE; ++j) {
+            const int ch = (k * NE + j) & 1;
+            const float x = ldexpf(w[k][j], sa);
+            c[ch] = __builtin_fmaf(x, x, c[ch]);
+            q[ch] = __builtin_fmaf(x, ldexpf(v[k][j], sb), q[ch]);
           }
-        }
-        float tt[2] = {wave_sum(c0 + c1), wave_sum(q0 + q1)};
+        float tt[2] = {wave_sum(c[0] + c[1]), wave_sum(q[0] + q[1])};
         group_sum<G, 2>(tt, gs.next(slot), geo.g, geo.lane);
         T = tt[0];
         P = tt[1];
@@ -1408,23 +1453,17 @@ rescale_kernel(const RescaleArgs args) {
     const float c = t.radius * inv;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      float ov[4], ow[4];
+      float ov[NE], ow[NE];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NE; ++j) {
         const float wj = scaled ? ldexpf(w[k][j], sa) : w[k][j];
         const float vj = scaled ? ldexpf(v[k][j], sb) : v[k][j];
         const float r = __builtin_fmaf(-wj, kk, vj);
         ov[j] = scaled ? ldexpf(r, -sb) : r;
         ow[j] = wj * c;
       }
-      if (has_v) {
-        const f32x4_t o = {ov[0], ov[1], ov[2], ov[3]};
-        vb.st16(__builtin_bit_cast(u32x4_t, o), off[k]);
-      }
-      if constexpr (RESCALE) {
-        const f32x4_t o = {ow[0], ow[1], ow[2], ow[3]};
-        wb.st16(__builtin_bit_cast(u32x4_t, o), off[k]);
-      }
+      if (has_v) F32Vec<NE>::store(vb, off[k], ov);
+      if constexpr (RESCALE) F32Vec<NE>::store(wb, off[k], ow);
     }
   }
 }

@@ -46,6 +46,12 @@ swiglu_l2_rows_8192x7168  g, u ~ N(0,1) bf16; sug, suu ~ U(0.5, 2) fp32 per colu
 rescale_12x4_d768         the 48 linears of rownorm_gain_12x4_d768 as raw rows,
                           W ~ N(0, sd 0.02) fp32, gradients / momenta
                           ~ N(0, sd 1e-3) fp32, radius 1
+rownorm_gain_resnet50     ResNet-50's 53 convolutions and classifier as unit rows
+                          (out channels x in * kh * kw; the stem's 147 is not
+                          a multiple of 4); W ~ N(0, sd 0.02); g ~ U(0.5, 2)
+rownorm_gain_bwd_resnet50 the same matrices; dL/dW_eff ~ N(0,1)
+rownorm_gain_embedding    a 50304 x 768 vocabulary embedding, radius sqrt(768)
+_50304x768                (the DragonScale README's radius for embeddings)
 rms_rows_bwd_16384x768    RMSNorm rows of the GPT model page's 100m size
                           (d_model 768) over 8 sequences of 2,048 tokens:
                           x ~ N(0,1), no residual; upstream dy ~ N(0,1)
@@ -68,7 +74,7 @@ __all__ = [
     "transformer_linears", "stress_l2_case", "WORKLOADS", "make",
     "L2GradCase", "RownormGradCase", "grad_bits", "l2_grad_case", "rownorm_grad_case",
     "ActCase", "gate_case", "swiglu_case", "QkCase", "qk_case", "rope_inv_freq",
-    "RescaleCase", "rescale_case",
+    "RescaleCase", "rescale_case", "resnet50_convs",
 ]
 
 
@@ -226,6 +232,23 @@ def transformer_linears(layers: int = 12, d: int = 768, d_ff: int = 3072):
     shapes = []
     for _ in range(layers):
         shapes += [(3 * d, d), (d, d), (d_ff, d), (d, d_ff)]
+    return shapes
+
+
+def resnet50_convs():
+    """(out channels, in * kh * kw) of ResNet-50's 53 convolutions, then its
+    1000 x 2048 classifier: the rows of a convolutional network's weights
+    (the stem's 3 x 7 x 7 = 147 is a width that is not a multiple of 4)."""
+    shapes = [(64, 3 * 49)]
+    cin = 64
+    for blocks, width in ((3, 64), (4, 128), (6, 256), (3, 512)):
+        out = 4 * width
+        for b in range(blocks):
+            shapes += [(width, cin), (width, width * 9), (out, width)]
+            if b == 0:
+                shapes.append((out, cin))                 # the projection shortcut
+            cin = out
+    shapes.append((1000, 2048))
     return shapes
 
 
@@ -395,6 +418,19 @@ WORKLOADS = {
         "rescale method over 12 pre-norm layers' linears (d 768, d_ff 3072): raw rows "
         "W ~ N(0, sd 0.02) fp32, gradients / momenta ~ N(0, sd 1e-3) fp32, radius 1",
         lambda: rescale_case(transformer_linears(), 1013, name="rescale_12x4_d768")),
+    "rownorm_gain_resnet50": (
+        "weight rownorm + gain over ResNet-50's 53 convolutions (rows = output channels, "
+        "in * kh * kw values each; the stem's 147 takes single elements) and classifier: "
+        "W ~ N(0, sd 0.02) fp32, g ~ U(0.5, 2), rho 1",
+        lambda: rownorm_case(resnet50_convs(), 1015, name="rownorm_gain_resnet50")),
+    "rownorm_gain_bwd_resnet50": (
+        "the gradient of rownorm_gain_resnet50: dL/dW_eff ~ N(0,1) bf16",
+        lambda: rownorm_grad_case(resnet50_convs(), 1016, name="rownorm_gain_bwd_resnet50")),
+    "rownorm_gain_embedding_50304x768": (
+        "a GPT vocabulary embedding, 50304 x 768 fp32, radius sqrt(768) (rows of unit RMS): "
+        "W ~ N(0, sd 0.02), g ~ U(0.5, 2)",
+        lambda: rownorm_case([(50304, 768)], 1017, radius=float(np.sqrt(np.float32(768))),
+                             name="rownorm_gain_embedding_50304x768")),
     "rms_rows_bwd_16384x768": (
         "rms_rows and its gradient, 16384 x 768 bf16 (d_model 768, 8 x 2048 tokens): "
         "x ~ N(0,1), no residual, dy ~ N(0,1), eps 1e-6",

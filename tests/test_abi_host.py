@@ -119,7 +119,13 @@ def test_rownorm_validation(L):
     assert f(_descs(good), -1, None) == B.DS_ERR_ARG
     assert f(None, 0, None) == B.DS_OK
     assert f(None, 2, None) == B.DS_ERR_NULL
-    assert f(_descs((A, Bp, 1.0, None, C, 16, 6)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 0)), 1, None) == B.DS_ERR_SHAPE
+    # a width that is not a multiple of 4 takes single elements, up to 16,384
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 16387)), 1, None) == B.DS_ERR_SHAPE
+    # ... with 4-byte fp32 and 2-byte bf16 alignment (16 on the vector path)
+    assert f(_descs((A + 2, Bp, 1.0, None, C, 16, 147)), 1, None) == B.DS_ERR_ALIGN
+    assert f(_descs((A + 4, Bp, 1.0, None, C + 1, 16, 147)), 1, None) == B.DS_ERR_ALIGN
+    assert f(_descs((A + 4, Bp, 1.0, None, C, 16, 148)), 1, None) == B.DS_ERR_ALIGN
     assert f(_descs((A, Bp, float("inf"), None, C, 16, 64)), 1, None) == B.DS_ERR_ARG
     assert f(_descs((A, None, 1.0, None, C, 16, 64)), 1, None) == B.DS_ERR_NULL
     assert f(_descs((A + 4, Bp, 1.0, None, C, 16, 64)), 1, None) == B.DS_ERR_ALIGN
@@ -178,7 +184,9 @@ def test_rownorm_backward_validation(L):
     assert f(_gdescs(good), -1, None) == B.DS_ERR_ARG
     assert f(None, 0, None) == B.DS_OK
     assert f(None, 1, None) == B.DS_ERR_NULL
-    assert f(_gdescs((A, Bp, 1.0, C, C + 65536, None, 16, 6)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_gdescs((A, Bp, 1.0, C, C + 65536, None, 16, 0)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_gdescs((A, Bp, 1.0, C, C + 65536, None, 16, 65537)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_gdescs((A, Bp, 1.0, C + 1, C + 65536, None, 16, 147)), 1, None) == B.DS_ERR_ALIGN
     assert f(_gdescs((A, Bp, float("nan"), C, C + 65536, None, 16, 64)), 1, None) == B.DS_ERR_ARG
     assert f(_gdescs((A, Bp, 1.0, None, C + 65536, None, 16, 64)), 1, None) == B.DS_ERR_NULL
     assert f(_gdescs((A, Bp, 1.0, C, None, None, 16, 64)), 1, None) == B.DS_ERR_NULL
@@ -216,6 +224,15 @@ def test_gain_mode_validation(L):
              1, None) == B.DS_ERR_ALIGN
     assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR,
                       Bp + 4096 + 60)), 1, None) == B.DS_ERR_ARG   # total over the shares
+
+
+@pytest.mark.skipif("not no_device()")
+def test_odd_widths_reach_device_lookup(L):
+    assert L.ds_weight_rownorm_gain(_descs((A + 4, Bp, 1.0, None, C + 2, 16, 147)), 1,
+                                    None) == B.DS_ERR_DEVICE
+    assert L.ds_weight_rownorm_gain_backward(
+        _gdescs((A + 4, Bp, 1.0, C + 2, C + 65540, None, 16, 27)), 1, None) == B.DS_ERR_DEVICE
+    assert L.ds_rescale_project(_rdescs((A + 4, C + 4, 1.0, 16, 16383)), 1, None) == B.DS_ERR_DEVICE
 
 
 @pytest.mark.skipif("not no_device()")
@@ -322,7 +339,9 @@ def test_rescale_validation(L):
     assert pr(None, 0, None) == B.DS_OK and af(None, 0, None) == B.DS_OK
     assert pr(None, 1, None) == B.DS_ERR_NULL
     assert pr(_rdescs((A, None, 1.0, 16, 64)), 1, None) == B.DS_ERR_NULL      # project needs v
-    assert pr(_rdescs((A, C, 1.0, 16, 6)), 1, None) == B.DS_ERR_SHAPE
+    assert pr(_rdescs((A, C, 1.0, 16, 0)), 1, None) == B.DS_ERR_SHAPE
+    assert pr(_rdescs((A, C, 1.0, 16, 20001)), 1, None) == B.DS_ERR_SHAPE
+    assert pr(_rdescs((A, C + 2, 1.0, 16, 147)), 1, None) == B.DS_ERR_ALIGN
     assert pr(_rdescs((A + 8, C, 1.0, 16, 64)), 1, None) == B.DS_ERR_ALIGN
     assert pr(_rdescs((A, A + 1024, 1.0, 16, 64)), 1, None) == B.DS_ERR_ARG   # v over w
     assert af(_rdescs((A, C, float("inf"), 16, 64)), 1, None) == B.DS_ERR_ARG

@@ -1,6 +1,9 @@
-"""The weight op's gain modes on the GPU against the CPU oracle: one gain for
-the whole matrix, and no gain (mode "unit"), forward and backward, in ragged
-calls that mix them with gains per row.
+"""The weight ops' gain modes and widths on the GPU against the CPU oracle:
+one gain for the whole matrix and no gain (mode "unit"), forward and
+backward, in ragged calls that mix them with gains per row; rows whose width
+is not a multiple of 4 (a convolution's 3 x 7 x 7) in the forward, gradient
+and rescale calls; ResNet-50's convolutions and a vocabulary embedding at
+radius sqrt(768).
 
 Forward outputs meet the 1-ulp / 2e-6 contract and the strict interval; dW
 meets the gradient contract and interval; a scalar gain's gradient (the sum
@@ -121,3 +124,76 @@ def test_scalar_gain_on_the_transformer_workload(B):
         mag = ((wd * dd).abs().sum(dim=1) / n).sum().item()
         got = dgs[i].item()
         assert abs(got - exact) <= 2e-6 * abs(exact) + 2.0 ** -16 * mag, (i, got, exact)
+
+
+# ------------------------------------------------ widths not a multiple of 4
+
+from test_gpu_backward import check_rn, run_rn                       # noqa: E402
+from test_gpu_rescale import check as check_rescale, run as run_rescale  # noqa: E402
+from test_gpu_rownorm import check_matrix, run as run_fwd           # noqa: E402
+
+ODD = [1, 3, 27, 75, 147, 1001, 1025, 4097, 16383]
+
+
+@pytest.mark.parametrize("cols", ODD)
+def test_odd_widths(B, cols):
+    rows = 37 if cols <= 4097 else 5
+    announce("weights, single-element rows", rows, cols)
+    fc = inputs.rownorm_case([(rows, cols)], 1500 + cols % 71)
+    n, w = run_fwd(B, fc)
+    check_matrix(n[0], w[0], fc.w[0], fc.gain[0], 1.0, np.arange(rows), f"fwd {rows}x{cols}")
+    gc_ = inputs.rownorm_grad_case([(rows, cols)], 1600 + cols % 71)
+    dw, dg = run_rn(B, gc_)
+    check_rn(dw[0], dg[0], gc_.w[0], gc_.gain[0], 1.0, gc_.dwe[0], np.arange(rows),
+             f"bwd {rows}x{cols}")
+    rc = inputs.rescale_case([(rows, cols)], 1700 + cols % 71, radius=2.0)
+    for after in (False, True):
+        gw, gv = run_rescale(B, rc, after)
+        check_rescale(gw[0], gv[0], rc.w[0], rc.v[0], 2.0, after, np.arange(rows),
+                      f"rescale {'after' if after else 'project'} {rows}x{cols}")
+
+
+def test_mixed_widths_ragged_equals_single(B):
+    """Element-path and vector-path matrices in one call: each matrix's bits
+    are those of a call holding it alone."""
+    shapes = [(40, 147), (33, 768), (9, 27), (64, 4096), (5, 1001)]
+    case = inputs.rownorm_case(shapes, 1501)
+    announce("weights, mixed widths ragged")
+    n_all, w_all = run_fwd(B, case)
+    for i in range(len(shapes)):
+        one = inputs.RownormCase("one", [case.w[i]], [case.gain[i]], [case.radius[i]])
+        n1, w1 = run_fwd(B, one)
+        assert np.array_equal(n1[0], n_all[i]) and np.array_equal(w1[0], w_all[i]), shapes[i]
+
+
+def test_resnet50_workload(B):
+    """ResNet-50's convolutions and classifier, forward and backward, sampled rows."""
+    case = inputs.make("rownorm_gain_resnet50")
+    announce("weights", case.name, len(case.w))
+    n, w = run_fwd(B, case)
+    for i, (wm, gm) in enumerate(zip(case.w, case.gain)):
+        exact = np.sqrt((wm.astype(np.float64) ** 2).sum(axis=1))
+        assert contract_rel(n[i], exact).all(), f"matrix {i}"
+        rows = np.unique(np.r_[0, wm.shape[0] - 1, np.arange(0, wm.shape[0], 97)])
+        check_matrix(n[i], w[i], wm, gm, 1.0, rows, f"conv {i} {wm.shape}")
+    gcase = inputs.make("rownorm_gain_bwd_resnet50")
+    dw, dg = run_rn(B, gcase)
+    for i, (wm, gm, de) in enumerate(zip(gcase.w, gcase.gain, gcase.dwe)):
+        rows = np.unique(np.r_[0, wm.shape[0] - 1, np.arange(0, wm.shape[0], 131)])
+        check_rn(dw[i], dg[i], wm, gm, 1.0, de, rows, f"conv {i} {wm.shape}")
+
+
+def test_embedding_workload(B):
+    """A 50304 x 768 vocabulary embedding at radius sqrt(768)."""
+    case = inputs.make("rownorm_gain_embedding_50304x768")
+    announce("weights", case.name)
+    n, w = run_fwd(B, case)
+    wm, gm, rho = case.w[0], case.gain[0], case.radius[0]
+    exact = np.sqrt((wm.astype(np.float64) ** 2).sum(axis=1))
+    assert contract_rel(n[0], exact).all()
+    rows = np.unique(np.r_[0, wm.shape[0] - 1, np.arange(0, wm.shape[0], 509)])
+    check_matrix(n[0], w[0], wm, gm, rho, rows, case.name)
+    # every row: |W_eff_i| = g_i rho within bf16 rounding
+    le = np.sqrt((bf16_value(w[0]) ** 2).sum(axis=1))
+    assert np.all(np.abs(le - np.abs(gm.astype(np.float64)) * rho) <=
+                  2.0 ** -8 * np.abs(gm) * rho)

@@ -16,8 +16,12 @@ import gen_instances as gen  # noqa: E402
 
 
 def cases(name):
+    """(G, V) of each case; (NE, G, V) where keys carry NE * 10000."""
     text = open(os.path.join(CSRC, name)).read()
-    return {(int(c) // 100, int(c) % 100) for c in re.findall(r"case (\d+):", text)}
+    out = set()
+    for c in map(int, re.findall(r"case (\d+):", text)):
+        out.add((c // 10000, c // 100 % 100, c % 100) if c >= 10000 else (c // 100, c % 100))
+    return out
 
 
 def test_bf16_launchers_cover_policy():
@@ -32,7 +36,8 @@ def test_bf16_launchers_cover_policy():
 
 def test_rownorm_launcher_covers_policy():
     lim = gen.limits()
-    need = {gen.rownorm_shape(n, lim) for n in range(1, 65536 // 4 + 1)}
+    need = {(4,) + gen.rownorm_shape(n, lim) for n in range(1, 65536 // 4 + 1)}
+    need |= {(1,) + gen.elem_shape(n, lim) for n in range(1, gen.MAX_ELEM_COLS + 1)}
     assert None not in need
     assert need <= cases("inst_rownorm.hip")
     assert need <= cases("inst_rownorm_bwd.hip")
