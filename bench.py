@@ -39,7 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
                   "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip",
                   "inst_qk.hip", "inst_rescale.hip", "inst_rms.hip", "inst_rms_bwd.hip",
-                  "ds_rows.hip"]
+                  "colblock_kernels.hpp", "inst_colblock.hip", "ds_rows.hip"]
 
 
 def kernel_hash() -> str:

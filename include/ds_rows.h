@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10600          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10700          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 #define DS_MAX_ELEM_COLS 16384         /* widest fp32 weight row whose width is
                                           not a multiple of 4 */
@@ -278,6 +278,19 @@ enum {
  *            such as 3 * 7 * 7 = 147) on single elements, up to
  *            DS_MAX_ELEM_COLS.  A convolution's or an embedding's weight is
  *            such a row-major matrix of its output units (or vocabulary).
+ * seg, ld  : the layout.  seg = 0: contiguous rows as above.  seg > 0: a
+ *            column block, for layers whose output unit is not a stored row
+ *            (DragonScale README, "Supported layers": GPT-2's Conv1D stores
+ *            [in, out], a ConvTranspose [in, out / groups, k...]).  The
+ *            weight is A = cols / seg stored rows, ld elements apart, and
+ *            row i (an output unit) is the seg values at i * seg of each
+ *            stored row: element (i, a * seg + b) sits at a * ld + i * seg + b.
+ *            Conv1D: seg = 1, ld = out, cols = in.  ConvTranspose, one group
+ *            per descriptor: seg = prod(k), ld = (out / groups) * seg,
+ *            cols = (in / groups) * seg.  Needs 1 <= seg <= 64, cols a
+ *            multiple of seg, ld >= rows * seg; w_eff (and every other
+ *            per-element buffer of the call) has the same layout; fp32
+ *            buffers 4-byte aligned, bf16 ones 2-byte aligned.
  */
 typedef struct ds_rownorm_desc {
   const float* w;
@@ -288,6 +301,8 @@ typedef struct ds_rownorm_desc {
   int64_t rows;
   int64_t cols;
   int32_t gain_mode;    /* DS_GAIN_*; 0 (a gain per row) when left zero */
+  int32_t seg;          /* 0: contiguous rows; else a column block (below) */
+  int64_t ld;           /* column blocks: elements between stored rows */
 } ds_rownorm_desc;
 
 /*
@@ -375,6 +390,8 @@ typedef struct ds_rownorm_grad_desc {
   int64_t cols;
   int32_t gain_mode;    /* DS_GAIN_*; 0 (a gain per row) when left zero */
   float* dgain_total;
+  int32_t seg;          /* as in ds_rownorm_desc */
+  int64_t ld;
 } ds_rownorm_grad_desc;
 
 /*
@@ -417,6 +434,8 @@ typedef struct ds_rescale_desc {
   float radius;
   int64_t rows;
   int64_t cols;
+  int32_t seg;          /* as in ds_rownorm_desc */
+  int64_t ld;
 } ds_rescale_desc;
 
 /*

@@ -42,6 +42,8 @@ class RownormDesc(ctypes.Structure):
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
         ("gain_mode", ctypes.c_int32),
+        ("seg", ctypes.c_int32),
+        ("ld", ctypes.c_int64),
     ]
 
 
@@ -58,6 +60,8 @@ class RownormGradDesc(ctypes.Structure):
         ("cols", ctypes.c_int64),
         ("gain_mode", ctypes.c_int32),
         ("dgain_total", ctypes.c_void_p),
+        ("seg", ctypes.c_int32),
+        ("ld", ctypes.c_int64),
     ]
 
 
@@ -69,6 +73,8 @@ class RescaleDesc(ctypes.Structure):
         ("radius", ctypes.c_float),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
+        ("seg", ctypes.c_int32),
+        ("ld", ctypes.c_int64),
     ]
 
 
@@ -239,6 +245,18 @@ def ds_slerp_rows(res, out_rows, alpha, eps: float = 1e-6, h=None, stream=None):
 DS_GAIN_ROW, DS_GAIN_SCALAR, DS_GAIN_NONE = 0, 1, 2
 
 
+def _layout(w, seg):
+    """(rows, cols, seg, ld) of a stored 2-D weight.  seg None or 0: its rows
+    are the unit rows.  seg > 0: a column block (GPT-2's Conv1D [in, out] with
+    seg 1; one ConvTranspose group [in, out * k] with seg k): unit u owns the
+    seg values at u * seg of every stored row."""
+    if not seg:
+        return w.shape[0], w.shape[1], 0, 0
+    if w.shape[1] % seg != 0:
+        raise ValueError(f"a column block of seg {seg} needs a multiple of {seg} stored columns")
+    return w.shape[1] // seg, w.shape[0] * seg, int(seg), w.shape[1]
+
+
 def _gain_mode(g, rows: int, name: str) -> int:
     """A gain tensor's mode: None (no gain), a 0-dim or one-element tensor for
     rows != 1 (one gain for the matrix), or a [rows] tensor (a gain per row)."""
@@ -256,21 +274,24 @@ def _gain_mode(g, rows: int, name: str) -> int:
 
 def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Sequence[float]] = None,
                            norm_out: Optional[Sequence] = None, w_eff: Optional[Sequence] = None,
-                           stream=None) -> Tuple[list, list]:
+                           stream=None, segs: Optional[Sequence] = None) -> Tuple[list, list]:
     """Per matrix: ||W_i|| (fp32) and bf16(W_i * g_i * radius / ||W_i||), in one call.
 
-    ``ws``: fp32 [rows, cols] tensors; ``gains``: per matrix an fp32 [rows]
-    tensor (a gain per row), a single value (one gain for the matrix) or None
-    (no gain).  Returns (norms, w_effs); w_effs are bfloat16 tensors unless
-    given.
+    ``ws``: fp32 2-D tensors; ``gains``: per matrix an fp32 [rows] tensor (a
+    gain per row), a single value (one gain for the matrix) or None (no gain);
+    ``segs``: per matrix None (the stored rows are the unit rows) or the seg
+    of a column block (see ``_layout``).  Returns (norms, w_effs); w_effs are
+    bfloat16 tensors shaped like ws unless given.
     """
     torch = _torch()
     n = len(ws)
     if len(gains) != n:
         raise ValueError("one gain entry per matrix")
     radius = [1.0] * n if radius is None else list(radius)
+    lay = [_layout(w, None if segs is None else segs[i]) for i, w in enumerate(ws)]
     if norm_out is None:
-        norm_out = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device) for w in ws]
+        norm_out = [torch.empty(lay[i][0], dtype=torch.float32, device=w.device)
+                    for i, w in enumerate(ws)]
     if w_eff is None:
         w_eff = [torch.empty(w.shape, dtype=torch.bfloat16, device=w.device) for w in ws]
     descs = (RownormDesc * max(n, 1))()
@@ -278,12 +299,13 @@ def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Seque
     for i, (w, g) in enumerate(zip(ws, gains)):
         if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
             raise ValueError(f"ws[{i}]: expected a contiguous fp32 [rows, cols] tensor")
-        mode = _gain_mode(g, w.shape[0], f"gains[{i}]")
+        rows, cols, seg, ld = lay[i]
+        mode = _gain_mode(g, rows, f"gains[{i}]")
         _bf16_2d(w_eff[i], f"w_eff[{i}]")
         if tuple(w_eff[i].shape) != tuple(w.shape):
             raise ValueError(f"w_eff[{i}]: shape mismatch")
         if norm_out[i] is not None and (norm_out[i].dtype != torch.float32
-                                        or norm_out[i].shape != (w.shape[0],)):
+                                        or norm_out[i].shape != (rows,)):
             raise ValueError(f"norm_out[{i}]: expected fp32 [rows]")
         for t in (w, g, w_eff[i], norm_out[i]):
             if t is None:
@@ -293,7 +315,7 @@ def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Seque
             dev = t.device
         descs[i] = RownormDesc(w.data_ptr(), None if g is None else g.data_ptr(), float(radius[i]),
                                None if norm_out[i] is None else norm_out[i].data_ptr(),
-                               w_eff[i].data_ptr(), w.shape[0], w.shape[1], mode)
+                               w_eff[i].data_ptr(), rows, cols, mode, seg, ld)
     if n == 0:
         return [], []
     with torch.cuda.device(dev):
@@ -333,10 +355,11 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
                                     radius: Optional[Sequence[float]] = None,
                                     dw: Optional[Sequence] = None,
                                     dgain: Optional[Sequence] = None,
-                                    want_dgain: bool = True, stream=None) -> Tuple[list, list]:
+                                    want_dgain: bool = True, stream=None,
+                                    segs: Optional[Sequence] = None) -> Tuple[list, list]:
     """Per matrix: dL/dW (fp32) and dL/dg (fp32) from dL/dW_eff (bf16), in one call.
 
-    ``gains`` as for ds_weight_rownorm_gain.  Returns (dws, dgains): dL/dg is
+    ``gains`` and ``segs`` as for ds_weight_rownorm_gain.  Returns (dws, dgains): dL/dg is
     an fp32 [rows] tensor for a gain per row, a 0-dim fp32 tensor for one gain
     per matrix (the library sums the rows' shares, kept in a [rows] buffer),
     and None with no gain or when ``want_dgain`` is false and none was given.
@@ -348,12 +371,13 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
     radius = [1.0] * n if radius is None else list(radius)
     if dw is None:
         dw = [torch.empty(w.shape, dtype=torch.float32, device=w.device) for w in ws]
-    modes = [_gain_mode(g, w.shape[0], f"gains[{i}]") for i, (w, g) in enumerate(zip(ws, gains))]
+    lay = [_layout(w, None if segs is None else segs[i]) for i, w in enumerate(ws)]
+    modes = [_gain_mode(g, lay[i][0], f"gains[{i}]") for i, g in enumerate(gains)]
     if dgain is None:
-        dgain = [torch.empty(w.shape[0] if m == DS_GAIN_ROW else (), dtype=torch.float32,
+        dgain = [torch.empty(lay[i][0] if m == DS_GAIN_ROW else (), dtype=torch.float32,
                              device=w.device) if want_dgain and m != DS_GAIN_NONE else None
-                 for w, m in zip(ws, modes)]
-    shares = [torch.empty(w.shape[0], dtype=torch.float32, device=w.device)
+                 for i, (w, m) in enumerate(zip(ws, modes))]
+    shares = [torch.empty(lay[i][0], dtype=torch.float32, device=w.device)
               if m == DS_GAIN_SCALAR and dgain[i] is not None else None
               for i, (w, m) in enumerate(zip(ws, modes))]
     descs = (RownormGradDesc * max(n, 1))()
@@ -367,7 +391,8 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
         if dw[i].dtype != torch.float32 or tuple(dw[i].shape) != tuple(w.shape) \
                 or not dw[i].is_contiguous():
             raise ValueError(f"dw[{i}]: expected a contiguous fp32 tensor shaped like ws[{i}]")
-        want = (w.shape[0],) if modes[i] == DS_GAIN_ROW else ()
+        rows, cols, seg, ld = lay[i]
+        want = (rows,) if modes[i] == DS_GAIN_ROW else ()
         if dgain[i] is not None and (dgain[i].dtype != torch.float32 or dgain[i].shape != want):
             raise ValueError(f"dgain[{i}]: expected fp32 of shape {want}")
         for t in (w, g, de, dw[i], dgain[i], shares[i]):
@@ -381,8 +406,8 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
         descs[i] = RownormGradDesc(w.data_ptr(), None if g is None else g.data_ptr(),
                                    float(radius[i]), de.data_ptr(), dw[i].data_ptr(),
                                    None if per_row is None else per_row.data_ptr(),
-                                   w.shape[0], w.shape[1], modes[i],
-                                   None if total is None else total.data_ptr())
+                                   rows, cols, modes[i],
+                                   None if total is None else total.data_ptr(), seg, ld)
     if n == 0:
         return [], []
     with torch.cuda.device(dev):
@@ -475,7 +500,7 @@ def ds_qk_rows_l2(q, k, positions, inv_freq, q_scale, head_dim: int, eps: float 
     return q_out, k_out
 
 
-def _rescale(ws, vs, radius, after_step, stream):
+def _rescale(ws, vs, radius, after_step, stream, segs=None):
     torch = _torch()
     n = len(ws)
     vs = [None] * n if vs is None else list(vs)
@@ -491,8 +516,9 @@ def _rescale(ws, vs, radius, after_step, stream):
                     or (dev is not None and t.device != dev):
                 raise ValueError(f"{name}[{i}]: expected a contiguous fp32 HIP tensor shaped like w")
             dev = t.device
+        rows, cols, seg, ld = _layout(w, None if segs is None else segs[i])
         descs[i] = RescaleDesc(w.data_ptr(), None if vs[i] is None else vs[i].data_ptr(),
-                               float(radius[i]), w.shape[0], w.shape[1])
+                               float(radius[i]), rows, cols, seg, ld)
     if n == 0:
         return
     with torch.cuda.device(dev):
@@ -501,14 +527,17 @@ def _rescale(ws, vs, radius, after_step, stream):
     _check(st, "ds_rescale_after_step" if after_step else "ds_rescale_project")
 
 
-def ds_rescale_project(ws: Sequence, grads: Sequence, stream=None) -> None:
-    """In place, per matrix: grad <- grad - w <w, grad> / ||w||^2 per row."""
+def ds_rescale_project(ws: Sequence, grads: Sequence, stream=None,
+                       segs: Optional[Sequence] = None) -> None:
+    """In place, per matrix: grad <- grad - w <w, grad> / ||w||^2 per unit row
+    (``segs`` as for ds_weight_rownorm_gain)."""
     if len(grads) != len(ws):
         raise ValueError("one gradient per matrix")
-    _rescale(ws, grads, None, False, stream)
+    _rescale(ws, grads, None, False, stream, segs)
 
 
 def ds_rescale_after_step(ws: Sequence, moms: Optional[Sequence] = None,
-                          radius: Optional[Sequence[float]] = None, stream=None) -> None:
+                          radius: Optional[Sequence[float]] = None, stream=None,
+                          segs: Optional[Sequence] = None) -> None:
     """In place, per matrix: project the momentum (if given), then w <- radius w/||w||."""
-    _rescale(ws, moms, radius, True, stream)
+    _rescale(ws, moms, radius, True, stream, segs)

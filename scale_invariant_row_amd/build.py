@@ -22,7 +22,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libdsrows.so")
 SOURCES = ["ds_rows.hip", "inst_l2.hip", "inst_slerp.hip", "inst_rownorm.hip",
            "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip", "inst_qk.hip",
-           "inst_rescale.hip", "inst_rms.hip", "inst_rms_bwd.hip"]
+           "inst_rescale.hip", "inst_rms.hip", "inst_rms_bwd.hip", "inst_colblock.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: only explicit fmaf fuses (the slerp lerp is three

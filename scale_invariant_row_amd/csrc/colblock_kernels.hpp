@@ -1,0 +1,238 @@
+// Weight rows stored as column blocks: the fp32 weight ops on layers whose
+// output unit is not a stored row.
+//
+// DragonScale README, "Supported layers": GPT-2's Conv1D stores its weight
+// as [in, out] and a ConvTranspose as [in, out / groups, k...], so the
+// values feeding output unit u (the unit row the method normalises) are
+// spread over the stored rows: seg contiguous values at u * seg in each of
+// the A = cols / seg stored rows, ld elements apart (Conv1D: seg = 1,
+// ld = out; ConvTranspose, one group: seg = prod(k), ld = (out / groups)
+// * prod(k)).  The arithmetic per unit is the row kernels' (sums of squares
+// and products in fp32, the same rescue for sums out of range); only the
+// order of the sums differs, fixed by the layout alone.
+//
+// One workgroup of 256 threads (4 waves) takes a tile of TU = 64 / seg
+// adjacent units: 64 / seg * seg <= 64 adjacent columns, lane c holding
+// column c of every stored row.  Wave w reads stored rows w, w + 4, ...,
+// eight of them in flight, accumulating into eight chains (stored row
+// w + 4 (8 i + j) into chain j).  A column's total is then a fixed tree: the
+// eight chains pairwise, the four waves pairwise, and a unit's seg columns
+// pairwise (through LDS).  A second pass over the tile applies each unit's
+// coefficients and writes the outputs; the tile is read twice, the second
+// time mostly from the caches.
+#pragma once
+
+#include "row_kernels.hpp"
+
+namespace dsr {
+
+enum class ColOp { kFwd, kBwd, kProject, kAfterStep };
+
+constexpr int kColChains = 8;
+
+template <ColOp OP>
+struct ColTaskOf { using T = RescaleTask; };
+template <>
+struct ColTaskOf<ColOp::kFwd> { using T = RownormTask; };
+template <>
+struct ColTaskOf<ColOp::kBwd> { using T = RownormGradTask; };
+
+// The second input of a unit's sums: dL/dW_eff (bf16), the gradient or
+// momentum v (fp32, may be absent after a step), or none (forward).
+template <ColOp OP>
+__device__ __forceinline__ float second_in(const typename ColTaskOf<OP>::T& t, int64_t off) {
+  if constexpr (OP == ColOp::kBwd) {
+    return bf_lo((uint32_t)t.dw_eff[off]);
+  } else if constexpr (OP == ColOp::kFwd) {
+    return 0.f;
+  } else {
+    return t.v != nullptr ? t.v[off] : 0.f;
+  }
+}
+
+// Pairwise sum of the chains: ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)).
+__device__ __forceinline__ float chain_total(const float (&c)[kColChains]) {
+  return ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
+}
+
+struct ColScratch {
+  float part[2][4][64];     // per wave: the lane's S and P totals
+  float pmax[2][4][64];     // per wave: the lane's max |x| and max |y|
+  float col[2][64];         // per column: S, P (then unit trees in place)
+  float mx[2][64];          // per column: max |x|, max |y| (rescue)
+  float coef[4][64];        // per unit: the output coefficients
+  int shift[2][64];         // per unit: rescue exponents for x and y
+  int any_rescue;
+};
+
+template <ColOp OP>
+__global__ void __launch_bounds__(256) colblock_kernel(const TaskArgs<typename ColTaskOf<OP>::T> args) {
+  using Task = typename ColTaskOf<OP>::T;
+  constexpr bool kTwo = OP != ColOp::kFwd;          // a second input, and P
+  __shared__ ColScratch sc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nitems = args.nitems;
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int lo = __builtin_amdgcn_readfirstlane(owning_task(args, item, lane));
+    const Task t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
+    const int seg = t.seg;
+    const int TU = 64 / seg;
+    const int64_t u0 = (int64_t)(item - t.item_begin) * TU;
+    const int tu = (int)min<int64_t>(TU, t.rows - u0);
+    const int tw = tu * seg;
+    const int A = t.cols / seg;
+    const bool active = lane < tw;
+    const int uo = lane / seg;                        // this column's unit in the tile
+    const int64_t base = u0 * seg + lane;             // column offset in a stored row
+
+    // ---- pass 1: column sums (scaled by the unit's shifts on a rescue)
+    auto column_sums = [&](bool scaled) {
+      const int sa = scaled && active ? sc.shift[0][uo] : 0;
+      const int sb = scaled && active ? sc.shift[1][uo] : 0;
+      float cs[kColChains], cp[kColChains];
+      float mx = 0.f, my = 0.f;
+#pragma unroll
+      for (int j = 0; j < kColChains; ++j) cs[j] = cp[j] = 0.f;
+      for (int a0 = wave; a0 < A; a0 += 4 * kColChains) {
+        float x[kColChains], y[kColChains];
+#pragma unroll
+        for (int j = 0; j < kColChains; ++j) {
+          const int a = a0 + 4 * j;
+          const bool in = active && a < A;
+          const int64_t off = (int64_t)a * t.ld + base;
+          x[j] = in ? t.w[off] : 0.f;
+          y[j] = (kTwo && in) ? second_in<OP>(t, off) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kColChains; ++j) {
+          if (!scaled) {
+            mx = fmaxf(mx, fabsf(x[j]));
+            if constexpr (kTwo) my = fmaxf(my, fabsf(y[j]));
+          }
+          const float xs = scaled ? ldexpf(x[j], sa) : x[j];
+          cs[j] = __builtin_fmaf(xs, xs, cs[j]);
+          if constexpr (kTwo) cp[j] = __builtin_fmaf(xs, scaled ? ldexpf(y[j], sb) : y[j], cp[j]);
+        }
+      }
+      sc.part[0][wave][lane] = chain_total(cs);
+      if constexpr (kTwo) sc.part[1][wave][lane] = chain_total(cp);
+      sc.pmax[0][wave][lane] = mx;
+      sc.pmax[1][wave][lane] = my;
+      __syncthreads();
+      if (wave == 0) {
+        sc.col[0][lane] = (sc.part[0][0][lane] + sc.part[0][1][lane]) +
+                          (sc.part[0][2][lane] + sc.part[0][3][lane]);
+        if constexpr (kTwo)
+          sc.col[1][lane] = (sc.part[1][0][lane] + sc.part[1][1][lane]) +
+                            (sc.part[1][2][lane] + sc.part[1][3][lane]);
+        if (!scaled) {
+          sc.mx[0][lane] = fmaxf(fmaxf(sc.pmax[0][0][lane], sc.pmax[0][1][lane]),
+                                 fmaxf(sc.pmax[0][2][lane], sc.pmax[0][3][lane]));
+          sc.mx[1][lane] = fmaxf(fmaxf(sc.pmax[1][0][lane], sc.pmax[1][1][lane]),
+                                 fmaxf(sc.pmax[1][2][lane], sc.pmax[1][3][lane]));
+        }
+      }
+      __syncthreads();
+      // a unit's seg columns, pairwise: column c adds column c + s when c's
+      // offset in its unit is a multiple of 2s and the partner is in the unit
+      for (int s = 1; s < seg; s *= 2) {
+        if (wave == 0 && active) {
+          const int b = lane - uo * seg;
+          if ((b % (2 * s)) == 0 && b + s < seg) {
+            sc.col[0][lane] += sc.col[0][lane + s];
+            if constexpr (kTwo) sc.col[1][lane] += sc.col[1][lane + s];
+            if (!scaled) {
+              sc.mx[0][lane] = fmaxf(sc.mx[0][lane], sc.mx[0][lane + s]);
+              if constexpr (kTwo) sc.mx[1][lane] = fmaxf(sc.mx[1][lane], sc.mx[1][lane + s]);
+            }
+          }
+        }
+        __syncthreads();
+      }
+    };
+
+    if (threadIdx.x == 0) sc.any_rescue = 0;
+    column_sums(false);
+    // ---- per unit: decide on a rescue (uniform over the tile)
+    if (wave == 0 && lane < tu) {
+      const float T = sc.col[0][lane * seg];
+      const float P = kTwo ? sc.col[1][lane * seg] : 0.f;
+      const float m0 = sc.mx[0][lane * seg];
+      const float m1 = kTwo ? sc.mx[1][lane * seg] : 0.f;
+      const bool out = !(T >= kTiny && T < __builtin_inff() && fabsf(P) < __builtin_inff());
+      const bool fix = out && m0 > 0.f && m0 < __builtin_inff() && m1 < __builtin_inff();
+      sc.shift[0][lane] = fix ? rescue_shift(m0, 0.f) : 0;
+      sc.shift[1][lane] = (fix && m1 > 0.f) ? rescue_shift(m1, 0.f) : 0;
+      sc.coef[3][lane] = fix ? 1.f : 0.f;            // the unit was rescued
+      if (fix) sc.any_rescue = 1;
+    }
+    __syncthreads();
+    if (sc.any_rescue) column_sums(true);           // uniform: LDS read after a barrier
+
+    // ---- per unit: the output coefficients
+    if (wave == 0 && lane < tu) {
+      const int64_t u = u0 + lane;
+      const bool scaled = sc.coef[3][lane] != 0.f;
+      const float T = sc.col[0][lane * seg];
+      const float P = kTwo ? sc.col[1][lane * seg] : 0.f;
+      const int sa = sc.shift[0][lane], sb = sc.shift[1][lane];
+      if constexpr (OP == ColOp::kFwd) {
+        const float rn = sqrtf(T);
+        if (t.norm_out != nullptr) t.norm_out[u] = scaled ? ldexpf(rn, -sa) : rn;
+        const float gr = row_gain(t, u) * t.radius;
+        sc.coef[0][lane] = (rn == 0.f) ? 0.f : gr / rn;
+      } else if constexpr (OP == ColOp::kBwd) {
+        const bool zero = T == 0.f;
+        const float inv = inv_sqrt(T);
+        float dg = (t.radius * P) * inv;
+        if (scaled) dg = ldexpf(dg, -sb);
+        if (t.dgain != nullptr) t.dgain[u] = zero ? 0.f : dg;
+        sc.coef[0][lane] = zero ? 0.f : row_gain(t, u) * t.radius * inv;   // c
+        sc.coef[1][lane] = zero ? 0.f : (P * inv) * inv;                    // k
+        sc.coef[2][lane] = zero ? 1.f : 0.f;
+      } else {
+        const float inv = inv_sqrt(T);
+        sc.coef[0][lane] = t.radius * inv;                                  // c
+        sc.coef[1][lane] = (P * inv) * inv;                                 // k
+        sc.coef[2][lane] = T == 0.f ? 1.f : 0.f;                           // untouched
+      }
+    }
+    __syncthreads();
+
+    // ---- pass 2: outputs
+    if (active) {
+      const bool scaled = sc.coef[3][uo] != 0.f;
+      const int sa = sc.shift[0][uo], sb = sc.shift[1][uo];
+      const float c0 = sc.coef[0][uo], c1 = sc.coef[1][uo];
+      const bool skip = OP != ColOp::kFwd && sc.coef[2][uo] != 0.f;
+      for (int a = wave; a < A; a += 4) {
+        const int64_t off = (int64_t)a * t.ld + base;
+        const float xr = t.w[off];
+        const float x = scaled ? ldexpf(xr, sa) : xr;
+        if constexpr (OP == ColOp::kFwd) {
+          t.w_eff[off] = (uint16_t)pack_bf16(x * c0, 0.f);
+        } else if constexpr (OP == ColOp::kBwd) {
+          const float yr = second_in<OP>(t, off);
+          const float y = scaled ? ldexpf(yr, sb) : yr;
+          float o = c0 * __builtin_fmaf(-x, c1, y);
+          if (scaled) o = ldexpf(o, sa - sb);
+          t.dw[off] = skip ? 0.f : o;
+        } else {
+          if (skip) continue;                       // a zero unit is left as it is
+          if (t.v != nullptr) {
+            const float yr = t.v[off];
+            const float y = scaled ? ldexpf(yr, sb) : yr;
+            const float r = __builtin_fmaf(-x, c1, y);
+            t.v[off] = scaled ? ldexpf(r, -sb) : r;
+          }
+          if constexpr (OP == ColOp::kAfterStep) t.w[off] = x * c0;
+        }
+      }
+    }
+    __syncthreads();                                // LDS is reused by the next tile
+  }
+}
+
+}  // namespace dsr

@@ -344,6 +344,31 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
   return result;
 }
 
+// The weight launchers: row kernels, or the column-block kernel for a
+// column-block shape class.
+hipError_t launch_rownorm_any(Shape s, const dsr::TaskArgs<dsr::RownormTask>& a, int grid,
+                              hipStream_t hs) {
+  return s.units > 0 ? dsr::launch_colblock_rownorm(a, grid, hs) : dsr::launch_rownorm(s, a, grid, hs);
+}
+
+hipError_t launch_rownorm_backward_any(Shape s, const dsr::TaskArgs<dsr::RownormGradTask>& a,
+                                       int grid, hipStream_t hs) {
+  return s.units > 0 ? dsr::launch_colblock_rownorm_backward(a, grid, hs)
+                     : dsr::launch_rownorm_backward(s, a, grid, hs);
+}
+
+hipError_t launch_project_any(Shape s, const dsr::TaskArgs<dsr::RescaleTask>& a, int grid,
+                              hipStream_t hs) {
+  return s.units > 0 ? dsr::launch_colblock_rescale(false, a, grid, hs)
+                     : dsr::launch_rescale_project(s, a, grid, hs);
+}
+
+hipError_t launch_after_step_any(Shape s, const dsr::TaskArgs<dsr::RescaleTask>& a, int grid,
+                                 hipStream_t hs) {
+  return s.units > 0 ? dsr::launch_colblock_rescale(true, a, grid, hs)
+                     : dsr::launch_rescale_after_step(s, a, grid, hs);
+}
+
 // An fp32 weight matrix: rows >= 0 and 1 <= cols <= DS_MAX_COLS; a width that
 // is not a multiple of 4 takes the single-element path, up to kMaxElemCols.
 // Returns the kernel shape in *s, and the alignment its fp32 and bf16
@@ -355,6 +380,30 @@ int check_weight(int64_t rows, int64_t cols, Shape* s, uintptr_t* a32, uintptr_t
   if (!s->ok()) return DS_ERR_SHAPE;
   *a32 = s->NE == 4 ? 16 : 4;
   *a16 = s->NE == 4 ? 16 : 2;
+  return DS_OK;
+}
+
+// A weight's layout: contiguous rows (seg == 0; check_weight), or a column
+// block: `rows` units of cols = A * seg values, unit u owning the seg values
+// at u * seg of each of the A stored rows, ld elements apart.  Returns the
+// shape, the alignments (4-byte fp32, 2-byte bf16 for column blocks) and the
+// span, in elements, from the first value to one past the last.
+int check_layout(int64_t rows, int64_t cols, int32_t seg, int64_t ld, Shape* s,
+                 uintptr_t* a32, uintptr_t* a16, int64_t* span) {
+  if (seg == 0) {
+    int st = check_weight(rows, cols, s, a32, a16);
+    *span = rows * cols;
+    return st;
+  }
+  int st = check_matrix(rows, cols, 1, 4);
+  if (st != DS_OK) return st;
+  if (seg < 0 || seg > dsr::kMaxSeg || cols % seg != 0) return DS_ERR_SHAPE;
+  const int64_t A = cols / seg;
+  if (ld < rows * seg || (A > 1 && ld > (INT64_MAX / 8) / (A - 1))) return DS_ERR_SHAPE;
+  *span = (A - 1) * ld + rows * seg;
+  *s = dsr::colblock_shape(seg);
+  *a32 = 4;
+  *a16 = 2;
   return DS_OK;
 }
 
@@ -653,7 +702,8 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     const ds_rownorm_desc& d = descs[i];
     Shape s;
     uintptr_t a32 = 16, a16 = 16;
-    int st = check_weight(d.rows, d.cols, &s, &a32, &a16);
+    int64_t span = 0;
+    int st = check_layout(d.rows, d.cols, d.seg, d.ld, &s, &a32, &a16, &span);
     if (st != DS_OK) return st;
     if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
     if (d.rows == 0) continue;
@@ -663,7 +713,7 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     if (!aligned(d.w, a32) || !aligned(d.w_eff, a16) || !aligned(gain, 4) ||
         (d.norm_out != nullptr && !aligned(d.norm_out, 4)))
       return DS_ERR_ALIGN;
-    const size_t nel = (size_t)d.rows * (size_t)d.cols;
+    const size_t nel = (size_t)span;
     add_range(ins, d.w, nel * 4);
     add_range(ins, gain, gain_bytes(d.gain_mode, d.rows));
     add_range(outs, d.w_eff, nel * 2);
@@ -677,10 +727,12 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     t.rows = d.rows;
     t.cols = (int32_t)d.cols;
     t.radius = d.radius;
+    t.seg = d.seg;
+    t.ld = d.ld;
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
-  return launch_ragged<dsr::RownormTask>(mats, dsr::launch_rownorm, (hipStream_t)stream);
+  return launch_ragged<dsr::RownormTask>(mats, launch_rownorm_any, (hipStream_t)stream);
 }
 
 int ds_l2_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* dy, uint16_t* dx,
@@ -706,7 +758,8 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     const ds_rownorm_grad_desc& d = descs[i];
     Shape s;
     uintptr_t a32 = 16, a16 = 16;
-    int st = check_weight(d.rows, d.cols, &s, &a32, &a16);
+    int64_t span = 0;
+    int st = check_layout(d.rows, d.cols, d.seg, d.ld, &s, &a32, &a16, &span);
     if (st != DS_OK) return st;
     if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
     // a total needs a scalar gain and the per-row shares it sums; no gain, no gradient
@@ -721,7 +774,7 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     if (!aligned(d.w, a32) || !aligned(d.dw_eff, a16) || !aligned(d.dw, a32) ||
         !aligned(gain, 4) || !aligned(d.dgain, 4) || !aligned(d.dgain_total, 4))
       return DS_ERR_ALIGN;
-    const size_t nel = (size_t)d.rows * (size_t)d.cols;
+    const size_t nel = (size_t)span;
     add_range(ins, d.w, nel * 4);
     add_range(ins, gain, gain_bytes(d.gain_mode, d.rows));
     add_range(ins, d.dw_eff, nel * 2);
@@ -739,10 +792,12 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     t.rows = d.rows;
     t.cols = (int32_t)d.cols;
     t.radius = d.radius;
+    t.seg = d.seg;
+    t.ld = d.ld;
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
-  int st = launch_ragged<dsr::RownormGradTask>(mats, dsr::launch_rownorm_backward,
+  int st = launch_ragged<dsr::RownormGradTask>(mats, launch_rownorm_backward_any,
                                                (hipStream_t)stream);
   if (st != DS_OK) return st;
   // scalar gains: sum each matrix's row shares once the shares are written
@@ -770,13 +825,14 @@ int rescale_call(const ds_rescale_desc* descs, int32_t n, bool after_step, ds_st
     const ds_rescale_desc& d = descs[i];
     Shape s;
     uintptr_t a32 = 16, a16 = 16;
-    int st = check_weight(d.rows, d.cols, &s, &a32, &a16);
+    int64_t span = 0;
+    int st = check_layout(d.rows, d.cols, d.seg, d.ld, &s, &a32, &a16, &span);
     if (st != DS_OK) return st;
     if (after_step && !std::isfinite(d.radius)) return DS_ERR_ARG;
     if (d.rows == 0) continue;
     if (d.w == nullptr || (!after_step && d.v == nullptr)) return DS_ERR_NULL;
     if (!aligned(d.w, a32) || !aligned(d.v, a32)) return DS_ERR_ALIGN;
-    const size_t nb = (size_t)d.rows * (size_t)d.cols * 4;
+    const size_t nb = (size_t)span * 4;
     add_range(after_step ? outs : ins, d.w, nb);
     add_range(outs, d.v, nb);
     dsr::RescaleTask t{};
@@ -785,12 +841,13 @@ int rescale_call(const ds_rescale_desc* descs, int32_t n, bool after_step, ds_st
     t.rows = d.rows;
     t.cols = (int32_t)d.cols;
     t.radius = d.radius;
+    t.seg = d.seg;
+    t.ld = d.ld;
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
   return launch_ragged<dsr::RescaleTask>(
-      mats, after_step ? dsr::launch_rescale_after_step : dsr::launch_rescale_project,
-      (hipStream_t)stream);
+      mats, after_step ? launch_after_step_any : launch_project_any, (hipStream_t)stream);
 }
 
 }  // namespace

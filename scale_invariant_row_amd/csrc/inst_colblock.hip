@@ -1,0 +1,28 @@
+// Launchers of the column-block weight kernels (one instance per op).
+#include "colblock_kernels.hpp"
+#include "launch.hpp"
+
+namespace dsr {
+
+hipError_t launch_colblock_rownorm(const TaskArgs<RownormTask>& args, int grid,
+                                   hipStream_t stream) {
+  colblock_kernel<ColOp::kFwd><<<grid, 256, 0, stream>>>(args);
+  return hipGetLastError();
+}
+
+hipError_t launch_colblock_rownorm_backward(const TaskArgs<RownormGradTask>& args, int grid,
+                                            hipStream_t stream) {
+  colblock_kernel<ColOp::kBwd><<<grid, 256, 0, stream>>>(args);
+  return hipGetLastError();
+}
+
+hipError_t launch_colblock_rescale(bool after_step, const TaskArgs<RescaleTask>& args, int grid,
+                                   hipStream_t stream) {
+  if (after_step)
+    colblock_kernel<ColOp::kAfterStep><<<grid, 256, 0, stream>>>(args);
+  else
+    colblock_kernel<ColOp::kProject><<<grid, 256, 0, stream>>>(args);
+  return hipGetLastError();
+}
+
+}  // namespace dsr

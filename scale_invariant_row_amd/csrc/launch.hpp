@@ -16,15 +16,26 @@ struct RescaleTask;
 // Kernel shape: G waves per row, V vectors per lane, NE values per vector
 // (the fp32 weight kernels: 4 for 16-byte vectors, 1 for single elements;
 // every other kernel uses 16-byte vectors).
+// A column-block weight (its rows spread over the stored rows) instead runs
+// one 256-thread workgroup per tile of `units` adjacent rows.
 struct Shape {
   int G = 0;
   int V = 0;
   int NE = 4;
-  int rows_per_block() const { return G == 1 ? 4 : 1; }
-  int threads() const { return 64 * G * rows_per_block(); }
-  bool ok() const { return G > 0; }
-  int key() const { return NE * 10000 + G * 100 + V; }
+  int units = 0;
+  int rows_per_block() const { return units > 0 ? units : (G == 1 ? 4 : 1); }
+  int threads() const { return units > 0 ? 256 : 64 * G * rows_per_block(); }
+  bool ok() const { return G > 0 || units > 0; }
+  int key() const { return units > 0 ? 1000000 + units : NE * 10000 + G * 100 + V; }
 };
+
+// Column-block tiles: 64 / seg rows of seg values per stored row.
+constexpr int kMaxSeg = 64;
+inline Shape colblock_shape(int64_t seg) {
+  Shape s{};
+  if (seg >= 1 && seg <= kMaxSeg) s.units = (int)(64 / seg);
+  return s;
+}
 
 // Shape policy, measured on MI355X (the gradients use the same rules as
 // their forward ops).  A row is spread over the smallest wave
@@ -118,6 +129,12 @@ hipError_t launch_l2_rows_backward(Shape s, const void* x, const void* r, const 
                                    void* dx, int64_t rows, int nvec, float eps, int grid,
                                    hipStream_t stream);
 hipError_t launch_rownorm_backward(Shape s, const TaskArgs<RownormGradTask>& args, int grid,
+                                   hipStream_t stream);
+hipError_t launch_colblock_rownorm(const TaskArgs<RownormTask>& args, int grid,
+                                   hipStream_t stream);
+hipError_t launch_colblock_rownorm_backward(const TaskArgs<RownormGradTask>& args, int grid,
+                                            hipStream_t stream);
+hipError_t launch_colblock_rescale(bool after_step, const TaskArgs<RescaleTask>& args, int grid,
                                    hipStream_t stream);
 
 }  // namespace dsr

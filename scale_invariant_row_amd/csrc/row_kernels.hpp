@@ -1111,6 +1111,8 @@ struct RownormTask {
   float radius;
   int32_t item_begin;
   int32_t gain_stride;  // 1: a gain per row; 0: one gain for the matrix
+  int32_t seg;          // column-block layouts: values per stored row (0: rows)
+  int64_t ld;           // column-block layouts: elements between stored rows
 };
 
 // One matrix of a ragged gradient call.
@@ -1125,6 +1127,8 @@ struct RownormGradTask {
   float radius;
   int32_t item_begin;
   int32_t gain_stride;  // 1: a gain per row; 0: one gain for the matrix
+  int32_t seg;          // column-block layouts (as in RownormTask)
+  int64_t ld;
 };
 
 // The gain of a row: its own, the matrix's one value, or 1 with no gain.
@@ -1369,7 +1373,8 @@ struct RescaleTask {
   int32_t cols;
   float radius;
   int32_t item_begin;
-  int32_t pad_;
+  int32_t seg;          // column-block layouts (as in RownormTask)
+  int64_t ld;
 };
 using RescaleArgs = TaskArgs<RescaleTask>;
 static_assert(sizeof(RescaleArgs) <= 4096, "kernel arguments are limited to 4 KiB");

@@ -52,6 +52,10 @@ rownorm_gain_resnet50     ResNet-50's 53 convolutions and classifier as unit row
 rownorm_gain_bwd_resnet50 the same matrices; dL/dW_eff ~ N(0,1)
 rownorm_gain_embedding    a 50304 x 768 vocabulary embedding, radius sqrt(768)
 _50304x768                (the DragonScale README's radius for embeddings)
+rownorm_gain_gpt2_conv1d  GPT-2 small's 48 Conv1D weights stored [in, out]
+                          (c_attn 768x2304, c_proj 768x768, c_fc 768x3072,
+                          mlp c_proj 3072x768), units = columns; W ~ N(0, sd
+                          0.02), g ~ U(0.5, 2) per unit, dL/dW_eff ~ N(0,1)
 rms_rows_bwd_16384x768    RMSNorm rows of the GPT model page's 100m size
                           (d_model 768) over 8 sequences of 2,048 tokens:
                           x ~ N(0,1), no residual; upstream dy ~ N(0,1)
@@ -74,7 +78,7 @@ __all__ = [
     "transformer_linears", "stress_l2_case", "WORKLOADS", "make",
     "L2GradCase", "RownormGradCase", "grad_bits", "l2_grad_case", "rownorm_grad_case",
     "ActCase", "gate_case", "swiglu_case", "QkCase", "qk_case", "rope_inv_freq",
-    "RescaleCase", "rescale_case", "resnet50_convs",
+    "RescaleCase", "rescale_case", "resnet50_convs", "gpt2_conv1d", "colblock_grad_case",
 ]
 
 
@@ -250,6 +254,30 @@ def resnet50_convs():
             cin = out
     shapes.append((1000, 2048))
     return shapes
+
+
+def gpt2_conv1d(layers: int = 12, d: int = 768):
+    """Stored shapes [in, out] of GPT-2's Conv1D weights, layer-major: c_attn,
+    attn c_proj, mlp c_fc, mlp c_proj.  Each output unit is a column."""
+    shapes = []
+    for _ in range(layers):
+        shapes += [(d, 3 * d), (d, d), (d, 4 * d), (4 * d, d)]
+    return shapes
+
+
+def colblock_grad_case(stored_shapes, seg: int, seed: int, w_sd: float = 0.02,
+                       g_lo: float = 0.5, g_hi: float = 2.0, radius: float = 1.0,
+                       name: Optional[str] = None) -> "RownormGradCase":
+    """Weights stored as column blocks ([A, ld], units = ld // seg): fp32 W, one
+    gain per unit, a bf16 dL/dW_eff of the stored shape."""
+    gens = _streams(seed, 3 * len(stored_shapes))
+    ws, gs, des = [], [], []
+    for i, (a, ld) in enumerate(stored_shapes):
+        ws.append((w_sd * gens[3 * i].standard_normal((a, ld))).astype(np.float32))
+        gs.append(gens[3 * i + 1].uniform(g_lo, g_hi, ld // seg).astype(np.float32))
+        des.append(to_bf16_bits(gens[3 * i + 2].standard_normal((a, ld))))
+    return RownormGradCase(name or f"colblock_{len(stored_shapes)}", ws, gs,
+                           [float(radius)] * len(stored_shapes), des)
 
 
 def rownorm_case(shapes, seed: int, w_sd: float = 0.02, g_lo: float = 0.5,
@@ -431,6 +459,11 @@ WORKLOADS = {
         "W ~ N(0, sd 0.02), g ~ U(0.5, 2)",
         lambda: rownorm_case([(50304, 768)], 1017, radius=float(np.sqrt(np.float32(768))),
                              name="rownorm_gain_embedding_50304x768")),
+    "rownorm_gain_gpt2_conv1d": (
+        "weight rownorm + gain over GPT-2 small's 48 Conv1D weights, stored [in, out] (each "
+        "output unit a column): W ~ N(0, sd 0.02) fp32, g ~ U(0.5, 2) per unit, "
+        "dL/dW_eff ~ N(0,1) bf16 (same layout)",
+        lambda: colblock_grad_case(gpt2_conv1d(), 1, 1018, name="rownorm_gain_gpt2_conv1d")),
     "rms_rows_bwd_16384x768": (
         "rms_rows and its gradient, 16384 x 768 bf16 (d_model 768, 8 x 2048 tokens): "
         "x ~ N(0,1), no residual, dy ~ N(0,1), eps 1e-6",

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10600
+    assert B.ds_version() == 10700
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -224,6 +224,34 @@ def test_gain_mode_validation(L):
              1, None) == B.DS_ERR_ALIGN
     assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR,
                       Bp + 4096 + 60)), 1, None) == B.DS_ERR_ARG   # total over the shares
+
+
+def test_column_block_validation(L):
+    f = L.ds_weight_rownorm_gain
+    # w, gain, radius, norm_out, w_eff, rows (units), cols (A * seg), gain_mode, seg, ld
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 130, 0, 65, 2000)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 10, 0, 3, 2000)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 12, 0, 3, 47)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_descs((A, Bp, 1.0, None, C, 16, 12, 0, -3, 48)), 1, None) == B.DS_ERR_SHAPE
+    assert f(_descs((A + 2, Bp, 1.0, None, C, 16, 12, 0, 3, 48)), 1, None) == B.DS_ERR_ALIGN
+    assert f(_descs((A, Bp, 1.0, None, C + 1, 16, 12, 0, 3, 48)), 1, None) == B.DS_ERR_ALIGN
+    # W_eff over the last stored row of w: the span is (A - 1) * ld + rows * seg values
+    assert f(_descs((A, Bp, 1.0, None, A + 4 * (3 * 48 + 40), 16, 12, 0, 3, 48)), 1,
+             None) == B.DS_ERR_ARG
+    g = L.ds_weight_rownorm_gain_backward
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, None, 16, 12, 0, None, 70, 48)), 1,
+             None) == B.DS_ERR_SHAPE
+    r = L.ds_rescale_project
+    assert r(_rdescs((A, C, 1.0, 16, 12, 4, 40)), 1, None) == B.DS_ERR_SHAPE    # ld < rows * seg
+
+
+@pytest.mark.skipif("not no_device()")
+def test_column_blocks_reach_device_lookup(L):
+    f = L.ds_weight_rownorm_gain
+    assert f(_descs((A + 4, Bp, 1.0, None, C + 2, 16, 12, 0, 3, 48)), 1, None) == B.DS_ERR_DEVICE
+    assert f(_descs((A, Bp, 1.0, None, C, 2304, 768, 0, 1, 2304)), 1, None) == B.DS_ERR_DEVICE
+    assert L.ds_rescale_after_step(_rdescs((A, None, 1.0, 16, 12, 3, 48)), 1,
+                                   None) == B.DS_ERR_DEVICE
 
 
 @pytest.mark.skipif("not no_device()")
