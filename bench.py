@@ -289,25 +289,31 @@ def main():
     # N(0, 0.02), gains U(0.5, 2), bf16 upstream gradients N(0, 1))
     gen = torch.Generator(device=dev).manual_seed(4242)
 
-    def weight_sets(shapes, nsets):
+    def weight_sets(shapes, nsets, seg=0, rho=1.0):
+        """Descriptor sets over stored fp32 weights; seg > 0: column blocks
+        (units = stored columns / seg)."""
         out = []
         for _ in range(nsets):
             ws = [0.02 * torch.randn(sh, device=dev, generator=gen) for sh in shapes]
-            gs = [0.5 + 1.5 * torch.rand(sh[0], device=dev, generator=gen) for sh in shapes]
+            lay = [(sh[0], sh[1], 0, 0) if not seg else (sh[1] // seg, sh[0] * seg, seg, sh[1])
+                   for sh in shapes]
+            gs = [0.5 + 1.5 * torch.rand(ly[0], device=dev, generator=gen) for ly in lay]
             de = [torch.randn(sh, device=dev, generator=gen).to(torch.bfloat16) for sh in shapes]
             fw = (B.RownormDesc * len(ws))()
             bw = (B.RownormGradDesc * len(ws))()
             keep = [ws, gs, de]
             for i, w in enumerate(ws):
-                n_out = torch.empty(w.shape[0], device=dev)
+                units, cols, sg, ld = lay[i]
+                n_out = torch.empty(units, device=dev)
                 e_out = torch.empty(w.shape, dtype=torch.int16, device=dev)
                 dw = torch.empty_like(w)
-                dg = torch.empty(w.shape[0], device=dev)
+                dg = torch.empty(units, device=dev)
                 keep += [n_out, e_out, dw, dg]
-                fw[i] = B.RownormDesc(w.data_ptr(), gs[i].data_ptr(), 1.0, n_out.data_ptr(),
-                                      e_out.data_ptr(), w.shape[0], w.shape[1])
-                bw[i] = B.RownormGradDesc(w.data_ptr(), gs[i].data_ptr(), 1.0, de[i].data_ptr(),
-                                          dw.data_ptr(), dg.data_ptr(), w.shape[0], w.shape[1])
+                fw[i] = B.RownormDesc(w.data_ptr(), gs[i].data_ptr(), rho, n_out.data_ptr(),
+                                      e_out.data_ptr(), units, cols, 0, sg, ld)
+                bw[i] = B.RownormGradDesc(w.data_ptr(), gs[i].data_ptr(), rho, de[i].data_ptr(),
+                                          dw.data_ptr(), dg.data_ptr(), units, cols, 0, None,
+                                          sg, ld)
             out.append((fw, bw, len(ws), keep))
         torch.cuda.synchronize()
         return out
@@ -332,6 +338,23 @@ def main():
     rnb_us = ragged_us(wsets, 1, 60)
     ops["weight_rownorm_gain_bwd_12x4_d768"] = op(rnb_us, n_el * 10 + n_rows * 8, n_rows)
     del wsets
+
+    # ---- other layers' weights, forward and backward: ResNet-50's convolutions
+    # (rows = output channels; the stem's 147-wide rows on single elements),
+    # GPT-2 small's 48 Conv1D weights (column blocks: each output unit a column
+    # of the stored [in, out]), and a 50304 x 768 embedding at radius sqrt(768)
+    for name, shapes, seg, rho in (
+            ("resnet50", inputs.resnet50_convs(), 0, 1.0),
+            ("gpt2_conv1d", inputs.gpt2_conv1d(), 1, 1.0),
+            ("embedding_50304x768", [(50304, 768)], 0, float(np.sqrt(np.float32(768))))):
+        sets = weight_sets(shapes, 3, seg, rho)
+        el = sum(a * b for a, b in shapes)
+        units = sum((b // seg) if seg else a for a, b in shapes)
+        ops[f"weight_rownorm_gain_{name}"] = op(ragged_us(sets, 0, 40), el * 6 + units * 8, units)
+        ops[f"weight_rownorm_gain_bwd_{name}"] = op(ragged_us(sets, 1, 40), el * 10 + units * 8,
+                                                    units)
+        del sets
+        torch.cuda.empty_cache()
     # ---- the rescale method on the 48 linears: project (W, G read; G written) and
     # after a step (W, M read and written)
     rs_sets = []

@@ -11,15 +11,16 @@
 // and products in fp32, the same rescue for sums out of range); only the
 // order of the sums differs, fixed by the layout alone.
 //
-// One workgroup of 256 threads (4 waves) takes a tile of TU = 64 / seg
+// One workgroup of 1024 threads (16 waves) takes a tile of TU = 64 / seg
 // adjacent units: 64 / seg * seg <= 64 adjacent columns, lane c holding
-// column c of every stored row.  Wave w reads stored rows w, w + 4, ...,
+// column c of every stored row.  Wave w reads stored rows w, w + 16, ...,
 // eight of them in flight, accumulating into eight chains (stored row
-// w + 4 (8 i + j) into chain j).  A column's total is then a fixed tree: the
-// eight chains pairwise, the four waves pairwise, and a unit's seg columns
-// pairwise (through LDS).  A second pass over the tile applies each unit's
-// coefficients and writes the outputs; the tile is read twice, the second
-// time mostly from the caches.
+// w + 16 (8 i + j) into chain j); sixteen waves keep each wave's walk down a
+// tall matrix (GPT-2's 3072-row MLP projection) short.  A column's total is
+// then a fixed tree: the eight chains pairwise, the sixteen waves pairwise,
+// and a unit's seg columns pairwise (through LDS).  A second pass over the
+// tile applies each unit's coefficients and writes the outputs; the tile is
+// read twice, the second time mostly from the caches.
 #pragma once
 
 #include "row_kernels.hpp"
@@ -29,6 +30,11 @@ namespace dsr {
 enum class ColOp { kFwd, kBwd, kProject, kAfterStep };
 
 constexpr int kColChains = 8;
+#ifndef DSR_COL_WAVES
+#define DSR_COL_WAVES 16      // waves per tile (tuning knob: 4, 8 or 16)
+#endif
+constexpr int kColWaves = DSR_COL_WAVES;
+constexpr int kColThreads = 64 * kColWaves;
 
 template <ColOp OP>
 struct ColTaskOf { using T = RescaleTask; };
@@ -55,9 +61,21 @@ __device__ __forceinline__ float chain_total(const float (&c)[kColChains]) {
   return ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
 }
 
+// Pairwise sum of the waves' values of one column.
+__device__ __forceinline__ float waves_total(const float (&p)[kColWaves][64], int lane) {
+  float q[kColWaves];
+#pragma unroll
+  for (int i = 0; i < kColWaves; ++i) q[i] = p[i][lane];
+#pragma unroll
+  for (int n = kColWaves; n > 1; n /= 2)
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) q[i] = q[2 * i] + q[2 * i + 1];
+  return q[0];
+}
+
 struct ColScratch {
-  float part[2][4][64];     // per wave: the lane's S and P totals
-  float pmax[2][4][64];     // per wave: the lane's max |x| and max |y|
+  float part[2][kColWaves][64];   // per wave: the lane's S and P totals
+  float pmax[2][kColWaves][64];   // per wave: the lane's max |x| and max |y|
   float col[2][64];         // per column: S, P (then unit trees in place)
   float mx[2][64];          // per column: max |x|, max |y| (rescue)
   float coef[4][64];        // per unit: the output coefficients
@@ -66,7 +84,7 @@ struct ColScratch {
 };
 
 template <ColOp OP>
-__global__ void __launch_bounds__(256) colblock_kernel(const TaskArgs<typename ColTaskOf<OP>::T> args) {
+__global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<typename ColTaskOf<OP>::T> args) {
   using Task = typename ColTaskOf<OP>::T;
   constexpr bool kTwo = OP != ColOp::kFwd;          // a second input, and P
   __shared__ ColScratch sc;
@@ -95,11 +113,11 @@ __global__ void __launch_bounds__(256) colblock_kernel(const TaskArgs<typename C
       float mx = 0.f, my = 0.f;
 #pragma unroll
       for (int j = 0; j < kColChains; ++j) cs[j] = cp[j] = 0.f;
-      for (int a0 = wave; a0 < A; a0 += 4 * kColChains) {
+      for (int a0 = wave; a0 < A; a0 += kColWaves * kColChains) {
         float x[kColChains], y[kColChains];
 #pragma unroll
         for (int j = 0; j < kColChains; ++j) {
-          const int a = a0 + 4 * j;
+          const int a = a0 + kColWaves * j;
           const bool in = active && a < A;
           const int64_t off = (int64_t)a * t.ld + base;
           x[j] = in ? t.w[off] : 0.f;
@@ -122,16 +140,17 @@ __global__ void __launch_bounds__(256) colblock_kernel(const TaskArgs<typename C
       sc.pmax[1][wave][lane] = my;
       __syncthreads();
       if (wave == 0) {
-        sc.col[0][lane] = (sc.part[0][0][lane] + sc.part[0][1][lane]) +
-                          (sc.part[0][2][lane] + sc.part[0][3][lane]);
-        if constexpr (kTwo)
-          sc.col[1][lane] = (sc.part[1][0][lane] + sc.part[1][1][lane]) +
-                            (sc.part[1][2][lane] + sc.part[1][3][lane]);
+        sc.col[0][lane] = waves_total(sc.part[0], lane);
+        if constexpr (kTwo) sc.col[1][lane] = waves_total(sc.part[1], lane);
         if (!scaled) {
-          sc.mx[0][lane] = fmaxf(fmaxf(sc.pmax[0][0][lane], sc.pmax[0][1][lane]),
-                                 fmaxf(sc.pmax[0][2][lane], sc.pmax[0][3][lane]));
-          sc.mx[1][lane] = fmaxf(fmaxf(sc.pmax[1][0][lane], sc.pmax[1][1][lane]),
-                                 fmaxf(sc.pmax[1][2][lane], sc.pmax[1][3][lane]));
+          float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < kColWaves; ++i) {
+            m0 = fmaxf(m0, sc.pmax[0][i][lane]);
+            m1 = fmaxf(m1, sc.pmax[1][i][lane]);
+          }
+          sc.mx[0][lane] = m0;
+          sc.mx[1][lane] = m1;
         }
       }
       __syncthreads();
@@ -201,33 +220,44 @@ __global__ void __launch_bounds__(256) colblock_kernel(const TaskArgs<typename C
     }
     __syncthreads();
 
-    // ---- pass 2: outputs
+    // ---- pass 2: outputs, eight stored rows in flight per wave
     if (active) {
       const bool scaled = sc.coef[3][uo] != 0.f;
       const int sa = sc.shift[0][uo], sb = sc.shift[1][uo];
       const float c0 = sc.coef[0][uo], c1 = sc.coef[1][uo];
       const bool skip = OP != ColOp::kFwd && sc.coef[2][uo] != 0.f;
-      for (int a = wave; a < A; a += 4) {
-        const int64_t off = (int64_t)a * t.ld + base;
-        const float xr = t.w[off];
-        const float x = scaled ? ldexpf(xr, sa) : xr;
-        if constexpr (OP == ColOp::kFwd) {
-          t.w_eff[off] = (uint16_t)pack_bf16(x * c0, 0.f);
-        } else if constexpr (OP == ColOp::kBwd) {
-          const float yr = second_in<OP>(t, off);
-          const float y = scaled ? ldexpf(yr, sb) : yr;
-          float o = c0 * __builtin_fmaf(-x, c1, y);
-          if (scaled) o = ldexpf(o, sa - sb);
-          t.dw[off] = skip ? 0.f : o;
-        } else {
-          if (skip) continue;                       // a zero unit is left as it is
-          if (t.v != nullptr) {
-            const float yr = t.v[off];
-            const float y = scaled ? ldexpf(yr, sb) : yr;
-            const float r = __builtin_fmaf(-x, c1, y);
-            t.v[off] = scaled ? ldexpf(r, -sb) : r;
+      // a zero unit of the rescale calls is left as it is
+      const bool work = !(skip && (OP == ColOp::kProject || OP == ColOp::kAfterStep));
+      for (int a0 = wave; work && a0 < A; a0 += kColWaves * kColChains) {
+        float xr[kColChains], yr[kColChains];
+#pragma unroll
+        for (int j = 0; j < kColChains; ++j) {
+          const int a = a0 + kColWaves * j;
+          const int64_t off = (int64_t)a * t.ld + base;
+          xr[j] = a < A ? t.w[off] : 0.f;
+          yr[j] = (kTwo && a < A) ? second_in<OP>(t, off) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kColChains; ++j) {
+          const int a = a0 + kColWaves * j;
+          if (a >= A) break;
+          const int64_t off = (int64_t)a * t.ld + base;
+          const float x = scaled ? ldexpf(xr[j], sa) : xr[j];
+          if constexpr (OP == ColOp::kFwd) {
+            t.w_eff[off] = (uint16_t)pack_bf16(x * c0, 0.f);
+          } else if constexpr (OP == ColOp::kBwd) {
+            const float y = scaled ? ldexpf(yr[j], sb) : yr[j];
+            float o = c0 * __builtin_fmaf(-x, c1, y);
+            if (scaled) o = ldexpf(o, sa - sb);
+            t.dw[off] = skip ? 0.f : o;
+          } else {
+            if (t.v != nullptr) {
+              const float y = scaled ? ldexpf(yr[j], sb) : yr[j];
+              const float r = __builtin_fmaf(-x, c1, y);
+              t.v[off] = scaled ? ldexpf(r, -sb) : r;
+            }
+            if constexpr (OP == ColOp::kAfterStep) t.w[off] = x * c0;
           }
-          if constexpr (OP == ColOp::kAfterStep) t.w[off] = x * c0;
         }
       }
     }

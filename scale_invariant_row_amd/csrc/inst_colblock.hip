@@ -6,22 +6,22 @@ namespace dsr {
 
 hipError_t launch_colblock_rownorm(const TaskArgs<RownormTask>& args, int grid,
                                    hipStream_t stream) {
-  colblock_kernel<ColOp::kFwd><<<grid, 256, 0, stream>>>(args);
+  colblock_kernel<ColOp::kFwd><<<grid, kColThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_colblock_rownorm_backward(const TaskArgs<RownormGradTask>& args, int grid,
                                             hipStream_t stream) {
-  colblock_kernel<ColOp::kBwd><<<grid, 256, 0, stream>>>(args);
+  colblock_kernel<ColOp::kBwd><<<grid, kColThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 
 hipError_t launch_colblock_rescale(bool after_step, const TaskArgs<RescaleTask>& args, int grid,
                                    hipStream_t stream) {
   if (after_step)
-    colblock_kernel<ColOp::kAfterStep><<<grid, 256, 0, stream>>>(args);
+    colblock_kernel<ColOp::kAfterStep><<<grid, kColThreads, 0, stream>>>(args);
   else
-    colblock_kernel<ColOp::kProject><<<grid, 256, 0, stream>>>(args);
+    colblock_kernel<ColOp::kProject><<<grid, kColThreads, 0, stream>>>(args);
   return hipGetLastError();
 }
 

@@ -17,14 +17,14 @@ struct RescaleTask;
 // (the fp32 weight kernels: 4 for 16-byte vectors, 1 for single elements;
 // every other kernel uses 16-byte vectors).
 // A column-block weight (its rows spread over the stored rows) instead runs
-// one 256-thread workgroup per tile of `units` adjacent rows.
+// one 1024-thread workgroup per tile of `units` adjacent rows.
 struct Shape {
   int G = 0;
   int V = 0;
   int NE = 4;
   int units = 0;
   int rows_per_block() const { return units > 0 ? units : (G == 1 ? 4 : 1); }
-  int threads() const { return units > 0 ? 256 : 64 * G * rows_per_block(); }
+  int threads() const { return units > 0 ? 1024 : 64 * G * rows_per_block(); }
   bool ok() const { return G > 0 || units > 0; }
   int key() const { return units > 0 ? 1000000 + units : NE * 10000 + G * 100 + V; }
 };

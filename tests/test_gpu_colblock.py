@@ -33,10 +33,9 @@ def B():
 
 def depth_col(stored_rows, seg):
     """Additions along any path of the column-block sum tree: a chain of
-    ceil(A / 32) terms, the eight chains and four waves pairwise, a unit's seg
-    columns pairwise (plus one for the chain's first addition)."""
-    return -(-stored_rows // 32) + 1 + 3 + 2 + math.ceil(math.log2(seg)) if seg > 1 else \
-        -(-stored_rows // 32) + 1 + 3 + 2
+    ceil(A / 128) terms, the eight chains and sixteen waves pairwise, a unit's
+    seg columns pairwise (plus one for the chain's first addition)."""
+    return -(-stored_rows // 128) + 1 + 3 + 4 + (math.ceil(math.log2(seg)) if seg > 1 else 0)
 
 
 def rows_of(stored, seg):
