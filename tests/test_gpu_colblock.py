@@ -215,3 +215,64 @@ def test_gpt2_conv1d_workload(B):
         sample = np.unique(np.r_[0, w.shape[1] - 1, np.arange(0, w.shape[1], 61)])
         check_forward(n[i], e[i], w, g, 1.0, 1, f"matrix {i}", sample)
         check_backward(dw[i], dg[i], w, g, 1.0, de, 1, f"matrix {i}", sample)
+
+
+def test_graph_replays_match_eager(B):
+    """RMS rows and their gradient, a scalar-gain gradient (its row-share total
+    kernel), single-element rows and column blocks, captured in one graph:
+    each replay, with inputs rewritten eagerly between replays, equals eager
+    calls bit for bit."""
+    import torch
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev).manual_seed(1900)
+    x = torch.randn(512, 768, device=dev, generator=gen).to(torch.bfloat16)
+    dy = torch.randn(512, 768, device=dev, generator=gen).to(torch.bfloat16)
+    cb = inputs.colblock_grad_case([(96, 320), (12, 90)], 1, 1901)
+    el = inputs.rownorm_grad_case([(40, 147)], 1902)
+    ws = [torch.from_numpy(m).to(dev) for m in cb.w + el.w]
+    gs = [torch.from_numpy(cb.gain[0]).to(dev), torch.from_numpy(cb.gain[1][:1]).to(dev).reshape(()),
+          torch.from_numpy(el.gain[0]).to(dev)]
+    des = [dev_bits(d) for d in cb.dwe + el.dwe]
+    segs = [1, 1, None]
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    weff = [torch.empty(m.shape, dtype=torch.bfloat16, device=dev) for m in ws]
+    norms = [torch.empty(m.shape[1] if s else m.shape[0], device=dev) for m, s in zip(ws, segs)]
+    dws = [torch.empty_like(m) for m in ws]
+    dgs = [torch.empty(ws[0].shape[1], device=dev), torch.empty((), device=dev),
+           torch.empty(ws[2].shape[0], device=dev)]
+
+    def step():
+        B.ds_rms_rows(x, None, 1e-6, out=y)
+        B.ds_rms_rows_backward(x, None, dy, 1e-6, out=dx)
+        B.ds_weight_rownorm_gain(ws, gs, None, norm_out=norms, w_eff=weff, segs=segs)
+        B.ds_weight_rownorm_gain_backward(ws, gs, des, dw=dws, dgain=dgs, segs=segs)
+
+    announce("graph capture: rms, scalar gain, element rows, column blocks")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        g2 = torch.Generator(device=dev).manual_seed(1950 + rep)
+        x.copy_(torch.randn(512, 768, device=dev, generator=g2).to(torch.bfloat16))
+        for m in ws:
+            m.mul_(0.5 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ye = B.ds_rms_rows(x, None, 1e-6)
+        dxe = B.ds_rms_rows_backward(x, None, dy, 1e-6)
+        ne, ee = B.ds_weight_rownorm_gain(ws, gs, None, segs=segs)
+        dwe, dge = B.ds_weight_rownorm_gain_backward(ws, gs, des, segs=segs)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), rep
+        assert torch.equal(dx.view(torch.int16), dxe.view(torch.int16)), rep
+        for i in range(3):
+            assert torch.equal(norms[i], ne[i]) and torch.equal(weff[i].view(torch.int16),
+                                                                ee[i].view(torch.int16)), (rep, i)
+            assert torch.equal(dws[i], dwe[i]) and torch.equal(dgs[i], dge[i]), (rep, i)
