@@ -43,16 +43,48 @@ struct ColTaskOf<ColOp::kFwd> { using T = RownormTask; };
 template <>
 struct ColTaskOf<ColOp::kBwd> { using T = RownormGradTask; };
 
+// Global-memory view of a task pointer: plain loads through it compile to
+// global (not flat) accesses, counted only against the vector-memory counter.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem_out(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // The second input of a unit's sums: dL/dW_eff (bf16), the gradient or
-// momentum v (fp32, may be absent after a step), or none (forward).
+// momentum v (fp32, may be absent after a step), or none (forward).  It is
+// loaded as raw bits and converted once every load of a batch is in flight.
 template <ColOp OP>
-__device__ __forceinline__ float second_in(const typename ColTaskOf<OP>::T& t, int64_t off) {
+__device__ __forceinline__ bool has_second(const typename ColTaskOf<OP>::T& t) {
   if constexpr (OP == ColOp::kBwd) {
-    return bf_lo((uint32_t)t.dw_eff[off]);
+    return true;
   } else if constexpr (OP == ColOp::kFwd) {
-    return 0.f;
+    return false;
   } else {
-    return t.v != nullptr ? t.v[off] : 0.f;
+    return t.v != nullptr;
+  }
+}
+
+template <ColOp OP>
+__device__ __forceinline__ uint32_t second_bits(const typename ColTaskOf<OP>::T& t, int64_t off) {
+  if constexpr (OP == ColOp::kBwd) {
+    return (uint32_t)gmem(t.dw_eff)[off];
+  } else if constexpr (OP == ColOp::kFwd) {
+    return 0u;
+  } else {
+    return __float_as_uint(gmem((const float*)t.v)[off]);
+  }
+}
+
+template <ColOp OP>
+__device__ __forceinline__ float second_value(uint32_t bits) {
+  if constexpr (OP == ColOp::kBwd) {
+    return bf_lo(bits);
+  } else {
+    return __uint_as_float(bits);
   }
 }
 
@@ -104,6 +136,8 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
     const bool active = lane < tw;
     const int uo = lane / seg;                        // this column's unit in the tile
     const int64_t base = u0 * seg + lane;             // column offset in a stored row
+    const int64_t first = u0 * seg;                   // the tile's first value
+    const bool two = kTwo && has_second<OP>(t);        // uniform over the workgroup
 
     // ---- pass 1: column sums (scaled by the unit's shifts on a rescue)
     auto column_sums = [&](bool scaled) {
@@ -114,24 +148,38 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
 #pragma unroll
       for (int j = 0; j < kColChains; ++j) cs[j] = cp[j] = 0.f;
       for (int a0 = wave; a0 < A; a0 += kColWaves * kColChains) {
-        float x[kColChains], y[kColChains];
+        // every load of the batch is issued before any is used.  With a
+        // second input a lane past the tile, or a stored row past the matrix,
+        // reads the tile's first value (always present) and drops it: a
+        // predicated load whose value is converted inside its branch would
+        // wait there for every load in flight.  The forward's single input
+        // needs no conversion, and its predicated loads measured as fast.
+        float xr[kColChains];
+        uint32_t yr[kColChains];
 #pragma unroll
         for (int j = 0; j < kColChains; ++j) {
           const int a = a0 + kColWaves * j;
           const bool in = active && a < A;
-          const int64_t off = (int64_t)a * t.ld + base;
-          x[j] = in ? t.w[off] : 0.f;
-          y[j] = (kTwo && in) ? second_in<OP>(t, off) : 0.f;
+          if constexpr (OP == ColOp::kFwd) {
+            xr[j] = in ? gmem(t.w)[(int64_t)a * t.ld + base] : 0.f;
+          } else {
+            const int64_t off = in ? (int64_t)a * t.ld + base : first;
+            xr[j] = gmem(t.w)[off];
+            yr[j] = two ? second_bits<OP>(t, off) : 0u;
+          }
         }
 #pragma unroll
         for (int j = 0; j < kColChains; ++j) {
+          const bool in = active && a0 + kColWaves * j < A;
+          const float x = in ? xr[j] : 0.f;
+          const float y = (two && in) ? second_value<OP>(yr[j]) : 0.f;
           if (!scaled) {
-            mx = fmaxf(mx, fabsf(x[j]));
-            if constexpr (kTwo) my = fmaxf(my, fabsf(y[j]));
+            mx = fmaxf(mx, fabsf(x));
+            if constexpr (kTwo) my = fmaxf(my, fabsf(y));
           }
-          const float xs = scaled ? ldexpf(x[j], sa) : x[j];
+          const float xs = scaled ? ldexpf(x, sa) : x;
           cs[j] = __builtin_fmaf(xs, xs, cs[j]);
-          if constexpr (kTwo) cp[j] = __builtin_fmaf(xs, scaled ? ldexpf(y[j], sb) : y[j], cp[j]);
+          if constexpr (kTwo) cp[j] = __builtin_fmaf(xs, scaled ? ldexpf(y, sb) : y, cp[j]);
         }
       }
       sc.part[0][wave][lane] = chain_total(cs);
@@ -229,13 +277,18 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
       // a zero unit of the rescale calls is left as it is
       const bool work = !(skip && (OP == ColOp::kProject || OP == ColOp::kAfterStep));
       for (int a0 = wave; work && a0 < A; a0 += kColWaves * kColChains) {
-        float xr[kColChains], yr[kColChains];
+        float xr[kColChains];
+        uint32_t yr[kColChains];
 #pragma unroll
         for (int j = 0; j < kColChains; ++j) {
           const int a = a0 + kColWaves * j;
-          const int64_t off = (int64_t)a * t.ld + base;
-          xr[j] = a < A ? t.w[off] : 0.f;
-          yr[j] = (kTwo && a < A) ? second_in<OP>(t, off) : 0.f;
+          if constexpr (OP == ColOp::kFwd) {
+            xr[j] = a < A ? gmem(t.w)[(int64_t)a * t.ld + base] : 0.f;
+          } else {
+            const int64_t off = a < A ? (int64_t)a * t.ld + base : base;
+            xr[j] = gmem(t.w)[off];
+            yr[j] = two ? second_bits<OP>(t, off) : 0u;
+          }
         }
 #pragma unroll
         for (int j = 0; j < kColChains; ++j) {
@@ -244,19 +297,21 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
           const int64_t off = (int64_t)a * t.ld + base;
           const float x = scaled ? ldexpf(xr[j], sa) : xr[j];
           if constexpr (OP == ColOp::kFwd) {
-            t.w_eff[off] = (uint16_t)pack_bf16(x * c0, 0.f);
+            gmem_out(t.w_eff)[off] = (uint16_t)pack_bf16(x * c0, 0.f);
           } else if constexpr (OP == ColOp::kBwd) {
-            const float y = scaled ? ldexpf(yr[j], sb) : yr[j];
+            const float yv = second_value<OP>(yr[j]);
+            const float y = scaled ? ldexpf(yv, sb) : yv;
             float o = c0 * __builtin_fmaf(-x, c1, y);
             if (scaled) o = ldexpf(o, sa - sb);
-            t.dw[off] = skip ? 0.f : o;
+            gmem_out(t.dw)[off] = skip ? 0.f : o;
           } else {
-            if (t.v != nullptr) {
-              const float y = scaled ? ldexpf(yr[j], sb) : yr[j];
+            if (two) {
+              const float yv = second_value<OP>(yr[j]);
+              const float y = scaled ? ldexpf(yv, sb) : yv;
               const float r = __builtin_fmaf(-x, c1, y);
-              t.v[off] = scaled ? ldexpf(r, -sb) : r;
+              gmem_out(t.v)[off] = scaled ? ldexpf(r, -sb) : r;
             }
-            if constexpr (OP == ColOp::kAfterStep) t.w[off] = x * c0;
+            if constexpr (OP == ColOp::kAfterStep) gmem_out(t.w)[off] = x * c0;
           }
         }
       }

@@ -126,6 +126,27 @@ def test_shapes(B, A, units, seg):
     assert rw.ok and rv.ok, f"after step: {rw} / {rv}"
 
 
+@pytest.mark.parametrize("A,units,seg", [(768, 96, 1), (33, 70, 5), (3, 4, 64)])
+def test_after_step_without_momentum(B, A, units, seg):
+    """After a step with no momentum only the weight is rescaled; a zero unit
+    is left as it is."""
+    import torch
+    announce("colblock after_step, no momentum", A, units, seg)
+    rng = np.random.default_rng(1806 + A + seg)
+    w = rng.standard_normal((A, units * seg)).astype(np.float32)
+    w[:, seg:2 * seg] = 0.0                            # unit 1 is zero
+    wd = dev_f32(w)
+    B.ds_rescale_after_step([wd], None, [1.5], segs=[seg])
+    torch.cuda.synchronize()
+    rows = rows_of(w, seg)
+    got = rows_of(wd.cpu().numpy(), seg)
+    want, _ = rescale_after_step([rows], [None], [1.5])
+    assert contract_rel(got, want[0]).all(), "after step: w"
+    assert np.array_equal(got[1], rows[1]), "zero unit"
+    rw, _ = admissible_rescale(got, None, rows, None, 1.5, True, depth=depth_col(A, seg))
+    assert rw.ok, f"after step: {rw}"
+
+
 def test_outputs_keep_the_layout(B):
     """Values outside the units' columns (ld > units * seg) are not touched, and
     W_eff lands where each unit's values sit."""
