@@ -242,40 +242,65 @@ bool outputs_disjoint(std::vector<Range>& outs, std::vector<Range>& ins) {
 template <class Task>
 using RaggedLauncher = hipError_t (*)(Shape, const dsr::TaskArgs<Task>&, int, hipStream_t);
 
-// One launch per kernel shape class over the matrices' tasks.  A class of at
+// The launches over the matrices' tasks.  Matrices of one kernel shape form
+// a class.  Small classes of contiguous rows that share a workgroup size (up
+// to kMaxMixedThreads) run in one mixed-shape launch, each task carrying its
+// shape key; every other class (a large one, 1,024-thread rows, a
+// column-block tile width) runs in its shape's own kernel.  A launch of at
 // most kInlineTasks matrices carries its table inside the kernel arguments;
-// larger classes share one table (tasks, then their first items as a compact
-// int32 array) staged through the ring and copied on the stream first.
+// larger launches share one table (tasks, then their first items as a
+// compact int32 array) staged through the ring and copied on the stream
+// first.
 template <class Task>
 int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLauncher<Task> launch,
                   hipStream_t hs) {
+  if (mats.empty()) return DS_OK;
   std::map<int, std::vector<size_t>> classes;     // shape key -> indices into mats
-  for (size_t i = 0; i < mats.size(); ++i) classes[mats[i].first.key()].push_back(i);
-  if (classes.empty()) return DS_OK;
+  std::map<int, int64_t> class_items;
+  for (size_t i = 0; i < mats.size(); ++i) {
+    const Shape& s = mats[i].first;
+    classes[s.key()].push_back(i);
+    int64_t& n = class_items[s.key()];
+    n += (mats[i].second.rows + s.rows_per_block() - 1) / s.rows_per_block();
+    if (n > INT32_MAX) return DS_ERR_SHAPE;
+  }
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st != DS_OK) return st;
+  // launch group (-workgroup size for a mixed launch, else the shape key)
+  // -> shape key -> indices into mats
+  std::map<int, std::map<int, std::vector<size_t>>> groups;
+  for (auto& kv : classes) {
+    const Shape& s = mats[kv.second.front()].first;
+    const bool small = class_items[kv.first] < (int64_t)dsr::kMixedItemsPerCu * cus;
+    const bool mixable = s.units == 0 && s.threads() <= dsr::kMaxMixedThreads && small;
+    groups[mixable ? -s.threads() : kv.first][kv.first] = kv.second;
+  }
 
   std::vector<Task> table;
   struct Launch { Shape s; size_t first; int ntasks; int nitems; };
   std::vector<Launch> launches;
-  for (auto& kv : classes) {
-    const Shape s = mats[kv.second.front()].first;
-    const int R = s.rows_per_block();
-    Launch L{s, table.size(), 0, 0};
+  for (auto& grp : groups) {
+    Shape ls = mats[grp.second.begin()->second.front()].first;
+    if (grp.second.size() > 1) ls.mixed = ls.threads();
+    Launch L{ls, table.size(), 0, 0};
     int64_t items = 0;
-    for (size_t i : kv.second) {
-      Task t = mats[i].second;
-      t.item_begin = (int32_t)items;
-      items += (t.rows + R - 1) / R;
-      if (items > INT32_MAX) return DS_ERR_SHAPE;
-      table.push_back(t);
+    for (auto& cls : grp.second) {
+      for (size_t i : cls.second) {
+        const int R = mats[i].first.rows_per_block();
+        Task t = mats[i].second;
+        t.item_begin = (int32_t)items;
+        t.shape = mats[i].first.key();
+        items += (t.rows + R - 1) / R;
+        if (items > INT32_MAX) return DS_ERR_SHAPE;
+        table.push_back(t);
+        ++L.ntasks;
+      }
     }
-    L.ntasks = (int)kv.second.size();
     L.nitems = (int)items;
     launches.push_back(L);
   }
 
-  int cus = 0;
-  int st = device_cus(&cus);
-  if (st != DS_OK) return st;
   size_t staged_tasks = 0;
   for (const Launch& L : launches)
     if (L.ntasks > dsr::kInlineTasks) staged_tasks += (size_t)L.ntasks;

@@ -4,7 +4,9 @@ inst_rms_bwd.hip: one launcher per op
 with a case for every kernel shape (G waves per row, V vectors per lane) that
 launch.hpp's shape policy returns for some width up to DS_MAX_COLS, found by
 evaluating the policy (reproduced below from launch.hpp's constants) at every
-width.  Run it after a change of the policy."""
+width.  The fp32 weight ops also get mixed-shape kernels, one per workgroup
+size, that switch on each task's shape key.  Run it after a change of the
+policy."""
 import os
 import re
 
@@ -94,6 +96,71 @@ def cases(lst, call, ne=None):
     return "\n".join(f"    case {key(G, V)}: {call.format(G=G, V=V, NE=ne)}" for G, V in lst)
 
 
+def threads_of(G):
+    """Workgroup size of a row shape: four one-wave rows, or one row of G waves."""
+    return 256 if G == 1 else 64 * G
+
+
+# Workgroup sizes with a mixed-shape kernel (launch.hpp's kMaxMixedThreads):
+# at 1,024 threads the union of the bodies no longer fits the registers.
+MIXED_THREADS = (128, 256, 512)
+# Waves per SIMD the 256-thread mixed kernels are compiled for (a register
+# cap of 128): measured faster than the compiler's own choice for the
+# gradient (ResNet-50's weights, 54.3 against 58.1 us).
+MIXED_WAVES_256 = 4
+
+
+def mixed(name, item, args, task, lists, rescale=False):
+    """Mixed-shape kernels: one per workgroup size in MIXED_THREADS, each
+    switching on its task's shape key to the matching item body, and their
+    launcher run_mixed(threads, ...).  With rescale, both are templates on
+    RESCALE."""
+    by_threads = {}
+    for ne, lst in lists:
+        for G, V in lst:
+            if threads_of(G) in MIXED_THREADS:
+                by_threads.setdefault(threads_of(G), []).append((ne, G, V))
+    tmpl = "template <bool RESCALE>\n" if rescale else ""
+    extra = ", RESCALE" if rescale else ""
+    inst = "<RESCALE>" if rescale else ""
+    out = []
+    for T in sorted(by_threads):
+        shapes = by_threads[T]
+        decl = "\n".join(f"  __shared__ GroupScratch<{G}> gs{G};"
+                         for G in sorted({G for _, G, _ in shapes}))
+        waves = f", {MIXED_WAVES_256}" if T == 256 else ""
+        body = "\n".join(
+            f"      case {ne * 10000 + G * 100 + V}: "
+            f"{item}<{G}, {V}, {ne}{extra}>(t, item, Geo<{G}>(), gs{G}, slot); break;"
+            for ne, G, V in shapes)
+        out.append(f"""
+{tmpl}__global__ void __launch_bounds__({T}{waves}) {name}_mixed_{T}(const {args} args) {{
+{decl}
+  int slot = 0;
+  for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {{
+    const {task} t = task_of(args, item, (int)(threadIdx.x & 63));
+    switch (t.shape) {{
+{body}
+      default: break;
+    }}
+  }}
+}}
+""")
+    launch = "\n".join(f"    case {T}: {name}_mixed_{T}{inst}<<<grid, {T}, 0, stream>>>(args); break;"
+                        for T in sorted(by_threads))
+    out.append(f"""
+// The classes of a ragged call that share a workgroup size, in one launch.
+{tmpl}static hipError_t run_mixed(int threads, const {args}& args, int grid, hipStream_t stream) {{
+  switch (threads) {{
+{launch}
+    default: return hipErrorInvalidValue;
+  }}
+  return hipGetLastError();
+}}
+""")
+    return "".join(out)
+
+
 def main():
     lim = limits()
     bf16 = bf16_shapes(lim)
@@ -154,7 +221,9 @@ static hipError_t run(const RownormArgs& args, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+''' + mixed("rownorm", "rownorm_item", "RownormArgs", "RownormTask", ((4, rown), (1, elem))) + '''
 hipError_t launch_rownorm(Shape s, const RownormArgs& args, int grid, hipStream_t stream) {
+  if (s.mixed > 0) return run_mixed(s.mixed, args, grid, stream);
   switch (s.key()) {
 ''' + cases(rown, "return run<{G}, {V}, {NE}>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;
@@ -196,8 +265,11 @@ static hipError_t run(const RownormGradArgs& args, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
+''' + mixed("rownorm_backward", "rownorm_backward_item", "RownormGradArgs", "RownormGradTask",
+             ((4, rown), (1, elem))) + '''
 hipError_t launch_rownorm_backward(Shape s, const RownormGradArgs& args, int grid,
                                    hipStream_t stream) {
+  if (s.mixed > 0) return run_mixed(s.mixed, args, grid, stream);
   switch (s.key()) {
 ''' + cases(rown, "return run<{G}, {V}, {NE}>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;
@@ -244,7 +316,9 @@ static hipError_t run(const RescaleArgs& args, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+''' + mixed("rescale", "rescale_item", "RescaleArgs", "RescaleTask", ((4, rown), (1, elem)), True) + '''
 hipError_t launch_rescale_project(Shape s, const RescaleArgs& args, int grid, hipStream_t stream) {
+  if (s.mixed > 0) return run_mixed<false>(s.mixed, args, grid, stream);
   switch (s.key()) {
 ''' + cases(rown, "return run<{G}, {V}, {NE}, false>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}, false>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;
@@ -253,6 +327,7 @@ hipError_t launch_rescale_project(Shape s, const RescaleArgs& args, int grid, hi
 
 hipError_t launch_rescale_after_step(Shape s, const RescaleArgs& args, int grid,
                                      hipStream_t stream) {
+  if (s.mixed > 0) return run_mixed<true>(s.mixed, args, grid, stream);
   switch (s.key()) {
 ''' + cases(rown, "return run<{G}, {V}, {NE}, true>(args, grid, stream);", 4) + "\n" + cases(elem, "return run<{G}, {V}, {NE}, true>(args, grid, stream);", 1) + '''
     default: return hipErrorInvalidValue;

@@ -12,7 +12,81 @@ static hipError_t run(const RescaleArgs& args, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
+template <bool RESCALE>
+__global__ void __launch_bounds__(128) rescale_mixed_128(const RescaleArgs args) {
+  __shared__ GroupScratch<2> gs2;
+  int slot = 0;
+  for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
+    const RescaleTask t = task_of(args, item, (int)(threadIdx.x & 63));
+    switch (t.shape) {
+      case 40204: rescale_item<2, 4, 4, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
+      case 40205: rescale_item<2, 5, 4, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
+      case 40206: rescale_item<2, 6, 4, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
+      case 10216: rescale_item<2, 16, 1, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
+      default: break;
+    }
+  }
+}
+
+template <bool RESCALE>
+__global__ void __launch_bounds__(256, 4) rescale_mixed_256(const RescaleArgs args) {
+  __shared__ GroupScratch<1> gs1;
+  __shared__ GroupScratch<4> gs4;
+  int slot = 0;
+  for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
+    const RescaleTask t = task_of(args, item, (int)(threadIdx.x & 63));
+    switch (t.shape) {
+      case 40101: rescale_item<1, 1, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 40102: rescale_item<1, 2, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 40103: rescale_item<1, 3, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 40104: rescale_item<1, 4, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 40105: rescale_item<1, 5, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 40106: rescale_item<1, 6, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 40404: rescale_item<4, 4, 4, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
+      case 40405: rescale_item<4, 5, 4, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
+      case 40406: rescale_item<4, 6, 4, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
+      case 10101: rescale_item<1, 1, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 10102: rescale_item<1, 2, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 10104: rescale_item<1, 4, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 10108: rescale_item<1, 8, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 10116: rescale_item<1, 16, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
+      case 10416: rescale_item<4, 16, 1, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
+      default: break;
+    }
+  }
+}
+
+template <bool RESCALE>
+__global__ void __launch_bounds__(512) rescale_mixed_512(const RescaleArgs args) {
+  __shared__ GroupScratch<8> gs8;
+  int slot = 0;
+  for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
+    const RescaleTask t = task_of(args, item, (int)(threadIdx.x & 63));
+    switch (t.shape) {
+      case 40804: rescale_item<8, 4, 4, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
+      case 40805: rescale_item<8, 5, 4, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
+      case 40806: rescale_item<8, 6, 4, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
+      case 10816: rescale_item<8, 16, 1, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
+      default: break;
+    }
+  }
+}
+
+// The classes of a ragged call that share a workgroup size, in one launch.
+template <bool RESCALE>
+static hipError_t run_mixed(int threads, const RescaleArgs& args, int grid, hipStream_t stream) {
+  switch (threads) {
+    case 128: rescale_mixed_128<RESCALE><<<grid, 128, 0, stream>>>(args); break;
+    case 256: rescale_mixed_256<RESCALE><<<grid, 256, 0, stream>>>(args); break;
+    case 512: rescale_mixed_512<RESCALE><<<grid, 512, 0, stream>>>(args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_rescale_project(Shape s, const RescaleArgs& args, int grid, hipStream_t stream) {
+  if (s.mixed > 0) return run_mixed<false>(s.mixed, args, grid, stream);
   switch (s.key()) {
     case 40101: return run<1, 1, 4, false>(args, grid, stream);
     case 40102: return run<1, 2, 4, false>(args, grid, stream);
@@ -57,6 +131,7 @@ hipError_t launch_rescale_project(Shape s, const RescaleArgs& args, int grid, hi
 
 hipError_t launch_rescale_after_step(Shape s, const RescaleArgs& args, int grid,
                                      hipStream_t stream) {
+  if (s.mixed > 0) return run_mixed<true>(s.mixed, args, grid, stream);
   switch (s.key()) {
     case 40101: return run<1, 1, 4, true>(args, grid, stream);
     case 40102: return run<1, 2, 4, true>(args, grid, stream);

@@ -17,17 +17,30 @@ struct RescaleTask;
 // (the fp32 weight kernels: 4 for 16-byte vectors, 1 for single elements;
 // every other kernel uses 16-byte vectors).
 // A column-block weight (its rows spread over the stored rows) instead runs
-// one 1024-thread workgroup per tile of `units` adjacent rows.
+// one 1024-thread workgroup per tile of `units` adjacent rows.  A launch
+// with `mixed` > 0 runs the ragged weight kernels' mixed-shape kernel of
+// that workgroup size: each task carries its own row shape.
 struct Shape {
   int G = 0;
   int V = 0;
   int NE = 4;
   int units = 0;
+  int mixed = 0;
   int rows_per_block() const { return units > 0 ? units : (G == 1 ? 4 : 1); }
-  int threads() const { return units > 0 ? 1024 : 64 * G * rows_per_block(); }
+  int threads() const { return mixed > 0 ? mixed : units > 0 ? 1024 : 64 * G * rows_per_block(); }
   bool ok() const { return G > 0 || units > 0; }
   int key() const { return units > 0 ? 1000000 + units : NE * 10000 + G * 100 + V; }
 };
+
+// Mixed-shape launches of the ragged weight calls (measured on MI355X): the
+// small classes of contiguous rows that share a workgroup size of at most
+// kMaxMixedThreads run in one launch, so their short kernels' fixed
+// latencies overlap (ResNet-50's 54 weights: 36 instead of 60 us forward);
+// a class of at least kMixedItemsPerCu items per compute unit streams at its
+// own kernel's speed and keeps its own launch (GPT-2's 48 linears lost 8% in
+// the gradient when their two classes shared one).
+constexpr int kMaxMixedThreads = 512;
+constexpr int kMixedItemsPerCu = 32;
 
 // Column-block tiles: 64 / seg rows of seg values per stored row.
 constexpr int kMaxSeg = 64;

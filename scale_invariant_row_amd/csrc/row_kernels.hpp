@@ -226,6 +226,13 @@ struct GroupScratch {
   float buf[2][2 * G];
   __device__ __forceinline__ float* next(int& k) { float* p = buf[k]; k ^= 1; return p; }
 };
+// One wave per row combines nothing, and leaves the slot index alone: a
+// mixed-shape kernel interleaves such rows with its multi-wave rows, whose
+// consecutive combines must still alternate slots.
+template <>
+struct GroupScratch<1> {
+  __device__ __forceinline__ float* next(int&) { return nullptr; }
+};
 
 // Geometry of one launch: which row this wave works on, and its lane/wave.
 template <int G>
@@ -1112,6 +1119,7 @@ struct RownormTask {
   int32_t item_begin;
   int32_t gain_stride;  // 1: a gain per row; 0: one gain for the matrix
   int32_t seg;          // column-block layouts: values per stored row (0: rows)
+  int32_t shape;        // row kernel shape key, NE * 10000 + G * 100 + V
   int64_t ld;           // column-block layouts: elements between stored rows
 };
 
@@ -1128,6 +1136,7 @@ struct RownormGradTask {
   int32_t item_begin;
   int32_t gain_stride;  // 1: a gain per row; 0: one gain for the matrix
   int32_t seg;          // column-block layouts (as in RownormTask)
+  int32_t shape;        // as in RownormTask
   int64_t ld;
 };
 
@@ -1172,22 +1181,24 @@ __device__ __forceinline__ int owning_task(const TaskArgs<Task>& a, int item, in
   return count - 1;
 }
 
+// The task owning `item` (its index is uniform over the workgroup).
+template <class Task>
+__device__ __forceinline__ Task task_of(const TaskArgs<Task>& a, int item, int lane) {
+  const int lo = __builtin_amdgcn_readfirstlane(owning_task(a, item, lane));
+  return a.tasks != nullptr ? a.tasks[lo] : a.inline_tasks[lo];
+}
+
+// One item (R rows) of a task.  Shared by the one-shape kernel below and the
+// mixed-shape kernels of a ragged call (one launch per workgroup size).
 template <int G, int V, int NE>
-__global__ void __launch_bounds__(Geo<G>::THREADS)
-rownorm_kernel(const RownormArgs args) {
+__device__ __forceinline__ void rownorm_item(const RownormTask& t, int item, const Geo<G>& geo,
+                                             GroupScratch<G>& gs, int& slot) {
   constexpr int R = Geo<G>::R;
-  const Geo<G> geo;
-  __shared__ GroupScratch<G> gs;
-  int slot = 0;
   int off[V];
   geo.offsets(off, 4 * NE);
-  const int nitems = args.nitems;
-
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int lo = __builtin_amdgcn_readfirstlane(owning_task(args, item, geo.lane));
-    const RownormTask t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
+  {
     const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
-    if (G == 1 && row >= t.rows) continue;          // independent waves only
+    if (G == 1 && row >= t.rows) return;            // independent waves only
     // the gain is read with the row, ahead of any store (a later read could
     // not move above the norm store, and would add a memory round trip)
     const float gr = row_gain(t, row) * t.radius;
@@ -1244,6 +1255,16 @@ rownorm_kernel(const RownormArgs args) {
   }
 }
 
+template <int G, int V, int NE>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+rownorm_kernel(const RownormArgs args) {
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  for (int item = blockIdx.x; item < args.nitems; item += gridDim.x)
+    rownorm_item<G, V, NE>(task_of(args, item, geo.lane), item, geo, gs, slot);
+}
+
 // ------------------------------------------------ weight rownorm gradient
 //
 // Per row: S = sum w^2 and P = <w, dWe> in one pass (w fp32, dWe bf16), then
@@ -1253,21 +1274,15 @@ rownorm_kernel(const RownormArgs args) {
 // row gets exact zeros: the forward scales it by the constant 0.
 
 template <int G, int V, int NE>
-__global__ void __launch_bounds__(Geo<G>::THREADS)
-rownorm_backward_kernel(const RownormGradArgs args) {
+__device__ __forceinline__ void rownorm_backward_item(const RownormGradTask& t, int item,
+                                                      const Geo<G>& geo, GroupScratch<G>& gs,
+                                                      int& slot) {
   constexpr int R = Geo<G>::R;
-  const Geo<G> geo;
-  __shared__ GroupScratch<G> gs;
-  int slot = 0;
   int off[V];
   geo.offsets(off, 4 * NE);
-  const int nitems = args.nitems;
-
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int lo = __builtin_amdgcn_readfirstlane(owning_task(args, item, geo.lane));
-    const RownormGradTask t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
+  {
     const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
-    if (G == 1 && row >= t.rows) continue;
+    if (G == 1 && row >= t.rows) return;
     const float gr = row_gain(t, row) * t.radius;
     const RowBuf wb(t.w + row * t.cols, (uint32_t)t.cols * 4u);
     const RowBuf eb(t.dw_eff + row * t.cols, (uint32_t)t.cols * 2u);
@@ -1354,6 +1369,16 @@ rownorm_backward_kernel(const RownormGradArgs args) {
   }
 }
 
+template <int G, int V, int NE>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+rownorm_backward_kernel(const RownormGradArgs args) {
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  for (int item = blockIdx.x; item < args.nitems; item += gridDim.x)
+    rownorm_backward_item<G, V, NE>(task_of(args, item, geo.lane), item, geo, gs, slot);
+}
+
 // ------------------------------------------------------------ rescale method
 //
 // DragonScale README, "Optimizer": with raw rows (method "rescale"), the
@@ -1374,27 +1399,21 @@ struct RescaleTask {
   float radius;
   int32_t item_begin;
   int32_t seg;          // column-block layouts (as in RownormTask)
+  int32_t shape;        // as in RownormTask
   int64_t ld;
 };
 using RescaleArgs = TaskArgs<RescaleTask>;
 static_assert(sizeof(RescaleArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 template <int G, int V, int NE, bool RESCALE>
-__global__ void __launch_bounds__(Geo<G>::THREADS)
-rescale_kernel(const RescaleArgs args) {
+__device__ __forceinline__ void rescale_item(const RescaleTask& t, int item, const Geo<G>& geo,
+                                             GroupScratch<G>& gs, int& slot) {
   constexpr int R = Geo<G>::R;
-  const Geo<G> geo;
-  __shared__ GroupScratch<G> gs;
-  int slot = 0;
   int off[V];
   geo.offsets(off, 4 * NE);
-  const int nitems = args.nitems;
-
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int lo = __builtin_amdgcn_readfirstlane(owning_task(args, item, geo.lane));
-    const RescaleTask t = args.tasks != nullptr ? args.tasks[lo] : args.inline_tasks[lo];
+  {
     const int64_t row = (int64_t)(item - t.item_begin) * R + geo.rr;
-    if (G == 1 && row >= t.rows) continue;
+    if (G == 1 && row >= t.rows) return;
     const bool has_v = t.v != nullptr;             // uniform
     const uint32_t bytes = (uint32_t)t.cols * 4u;
     const RowBuf wb(t.w + row * t.cols, bytes);
@@ -1452,7 +1471,7 @@ rescale_kernel(const RescaleArgs args) {
         scaled = true;
       }
     }
-    if (T == 0.f) continue;                        // a zero row: nothing to do (uniform)
+    if (T == 0.f) return;                          // a zero row: nothing to do (uniform)
     const float inv = inv_sqrt(T);
     const float kk = (P * inv) * inv;
     const float c = t.radius * inv;
@@ -1471,6 +1490,16 @@ rescale_kernel(const RescaleArgs args) {
       if constexpr (RESCALE) F32Vec<NE>::store(wb, off[k], ow);
     }
   }
+}
+
+template <int G, int V, int NE, bool RESCALE>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+rescale_kernel(const RescaleArgs args) {
+  const Geo<G> geo;
+  __shared__ GroupScratch<G> gs;
+  int slot = 0;
+  for (int item = blockIdx.x; item < args.nitems; item += gridDim.x)
+    rescale_item<G, V, NE, RESCALE>(task_of(args, item, geo.lane), item, geo, gs, slot);
 }
 
 }  // namespace dsr

@@ -75,3 +75,35 @@ def test_reduction_depth_bound():
         assert 2 * V + 1 + 6 + (G - 1) <= 64
     for G, V in gen.act_shapes(lim):
         assert 4 * V + 1 + 6 + (G - 1) <= 64
+
+
+def mixed_cases(name):
+    """{workgroup size: {(NE, G, V)}} of the mixed-shape kernels' switches."""
+    text = open(os.path.join(CSRC, name)).read()
+    out = {}
+    for m in re.finditer(r"__global__ void __launch_bounds__\((\d+)[^)]*\) \w+_mixed_(\d+)\(", text):
+        assert m.group(1) == m.group(2)
+        body = text[m.end():text.find("\n}\n", m.end())]
+        keys = set()
+        for c in map(int, re.findall(r"case (\d+):", body)):
+            keys.add((c // 10000, c // 100 % 100, c % 100))
+        out.setdefault(int(m.group(1)), set()).update(keys)
+    return out
+
+
+def test_mixed_kernels_cover_policy():
+    """Each mixed-shape kernel holds every weight shape of its workgroup size
+    (one row of G waves, or four one-wave rows), for the sizes launch.hpp
+    allows to mix."""
+    lim = gen.limits()
+    need = {(4,) + gen.rownorm_shape(n, lim) for n in range(1, 65536 // 4 + 1)}
+    need |= {(1,) + gen.elem_shape(n, lim) for n in range(1, gen.MAX_ELEM_COLS + 1)}
+    text = open(os.path.join(CSRC, "launch.hpp")).read()
+    max_mixed = int(re.search(r"kMaxMixedThreads\s*=\s*(\d+)", text).group(1))
+    sizes = {gen.threads_of(G) for _, G, _ in need if gen.threads_of(G) <= max_mixed}
+    assert sizes == set(gen.MIXED_THREADS)
+    for name in ("inst_rownorm.hip", "inst_rownorm_bwd.hip", "inst_rescale.hip"):
+        got = mixed_cases(name)
+        assert set(got) == sizes, name
+        for T in sizes:
+            assert got[T] == {s for s in need if gen.threads_of(s[1]) == T}, (name, T)
