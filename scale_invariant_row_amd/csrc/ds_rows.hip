@@ -283,19 +283,29 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
   for (auto& grp : groups) {
     Shape ls = mats[grp.second.begin()->second.front()].first;
     if (grp.second.size() > 1) ls.mixed = ls.threads();
+    std::vector<size_t> order;
+    for (auto& cls : grp.second) order.insert(order.end(), cls.second.begin(), cls.second.end());
+    // Column blocks: tallest matrices first.  Workgroups start in item order
+    // and a tile's time grows with its stored rows, so the tall tiles (GPT-2's
+    // 3,072-row MLP projections) start early instead of running alone at the
+    // end: 146 instead of 172 us forward on GPT-2's Conv1D set.  (Row items
+    // are short; their call order measured as fast.)  The order of the tasks
+    // changes no result.
+    if (ls.units > 0)
+      std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) {
+        return mats[x].second.cols / mats[x].second.seg > mats[y].second.cols / mats[y].second.seg;
+      });
     Launch L{ls, table.size(), 0, 0};
     int64_t items = 0;
-    for (auto& cls : grp.second) {
-      for (size_t i : cls.second) {
-        const int R = mats[i].first.rows_per_block();
-        Task t = mats[i].second;
-        t.item_begin = (int32_t)items;
-        t.shape = mats[i].first.key();
-        items += (t.rows + R - 1) / R;
-        if (items > INT32_MAX) return DS_ERR_SHAPE;
-        table.push_back(t);
-        ++L.ntasks;
-      }
+    for (size_t i : order) {
+      const int R = mats[i].first.rows_per_block();
+      Task t = mats[i].second;
+      t.item_begin = (int32_t)items;
+      t.shape = mats[i].first.key();
+      items += (t.rows + R - 1) / R;
+      if (items > INT32_MAX) return DS_ERR_SHAPE;
+      table.push_back(t);
+      ++L.ntasks;
     }
     L.nitems = (int)items;
     launches.push_back(L);
