@@ -105,6 +105,75 @@ __device__ __forceinline__ float waves_total(const float (&p)[kColWaves][64], in
   return q[0];
 }
 
+// Per unit, after its first pass: whether the sums are out of fp32's range
+// and can be rescued, with the power-of-two exponents for x and y.
+template <ColOp OP>
+__device__ __forceinline__ bool unit_rescue(float T, float P, float m0, float m1, int& sa,
+                                            int& sb) {
+  constexpr bool kTwo = OP != ColOp::kFwd;
+  if constexpr (!kTwo) {
+    P = 0.f;
+    m1 = 0.f;
+  }
+  const bool out = !(T >= kTiny && T < __builtin_inff() && fabsf(P) < __builtin_inff());
+  const bool fix = out && m0 > 0.f && m0 < __builtin_inff() && m1 < __builtin_inff();
+  sa = fix ? rescue_shift(m0, 0.f) : 0;
+  sb = (fix && m1 > 0.f) ? rescue_shift(m1, 0.f) : 0;
+  return fix;
+}
+
+// Per unit: the output coefficients c[0], c[1] and the flag c[2] (a zero unit,
+// which the gradient zeroes and the rescale calls leave as it is); writes the
+// unit's length (forward) or gain gradient (gradient).
+template <ColOp OP, class Task>
+__device__ __forceinline__ void unit_coefficients(const Task& t, int64_t u, float T, float P,
+                                                  bool scaled, int sa, int sb, float (&c)[3]) {
+  c[0] = c[1] = c[2] = 0.f;
+  if constexpr (OP == ColOp::kFwd) {
+    const float rn = sqrtf(T);
+    if (t.norm_out != nullptr) t.norm_out[u] = scaled ? ldexpf(rn, -sa) : rn;
+    const float gr = row_gain(t, u) * t.radius;
+    c[0] = (rn == 0.f) ? 0.f : gr / rn;
+  } else if constexpr (OP == ColOp::kBwd) {
+    const bool zero = T == 0.f;
+    const float inv = inv_sqrt(T);
+    float dg = (t.radius * P) * inv;
+    if (scaled) dg = ldexpf(dg, -sb);
+    if (t.dgain != nullptr) t.dgain[u] = zero ? 0.f : dg;
+    c[0] = zero ? 0.f : row_gain(t, u) * t.radius * inv;   // c
+    c[1] = zero ? 0.f : (P * inv) * inv;                    // k
+    c[2] = zero ? 1.f : 0.f;
+  } else {
+    const float inv = inv_sqrt(T);
+    c[0] = t.radius * inv;                                  // c
+    c[1] = (P * inv) * inv;                                 // k
+    c[2] = T == 0.f ? 1.f : 0.f;                           // untouched
+  }
+}
+
+// One value's outputs from its unit's coefficients: o0 is the forward's
+// W_eff value (before its bf16 rounding), the gradient's dW, or the rescale
+// calls' new v; o1 is the new w after a step.
+template <ColOp OP>
+__device__ __forceinline__ void col_values(float xr, float yv, bool scaled, int sa, int sb,
+                                           float c0, float c1, bool skip, float& o0, float& o1) {
+  const float x = scaled ? ldexpf(xr, sa) : xr;
+  o1 = 0.f;
+  if constexpr (OP == ColOp::kFwd) {
+    o0 = x * c0;
+  } else if constexpr (OP == ColOp::kBwd) {
+    const float y = scaled ? ldexpf(yv, sb) : yv;
+    float o = c0 * __builtin_fmaf(-x, c1, y);
+    if (scaled) o = ldexpf(o, sa - sb);
+    o0 = skip ? 0.f : o;
+  } else {
+    const float y = scaled ? ldexpf(yv, sb) : yv;
+    const float r = __builtin_fmaf(-x, c1, y);
+    o0 = scaled ? ldexpf(r, -sb) : r;
+    o1 = x * c0;
+  }
+}
+
 struct ColScratch {
   float part[2][kColWaves][64];   // per wave: the lane's S and P totals
   float pmax[2][kColWaves][64];   // per wave: the lane's max |x| and max |y|
@@ -224,14 +293,11 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
     column_sums(false);
     // ---- per unit: decide on a rescue (uniform over the tile)
     if (wave == 0 && lane < tu) {
-      const float T = sc.col[0][lane * seg];
-      const float P = kTwo ? sc.col[1][lane * seg] : 0.f;
-      const float m0 = sc.mx[0][lane * seg];
-      const float m1 = kTwo ? sc.mx[1][lane * seg] : 0.f;
-      const bool out = !(T >= kTiny && T < __builtin_inff() && fabsf(P) < __builtin_inff());
-      const bool fix = out && m0 > 0.f && m0 < __builtin_inff() && m1 < __builtin_inff();
-      sc.shift[0][lane] = fix ? rescue_shift(m0, 0.f) : 0;
-      sc.shift[1][lane] = (fix && m1 > 0.f) ? rescue_shift(m1, 0.f) : 0;
+      int sa, sb;
+      const bool fix = unit_rescue<OP>(sc.col[0][lane * seg], sc.col[1][lane * seg],
+                                       sc.mx[0][lane * seg], sc.mx[1][lane * seg], sa, sb);
+      sc.shift[0][lane] = sa;
+      sc.shift[1][lane] = sb;
       sc.coef[3][lane] = fix ? 1.f : 0.f;            // the unit was rescued
       if (fix) sc.any_rescue = 1;
     }
@@ -240,31 +306,14 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
 
     // ---- per unit: the output coefficients
     if (wave == 0 && lane < tu) {
-      const int64_t u = u0 + lane;
       const bool scaled = sc.coef[3][lane] != 0.f;
-      const float T = sc.col[0][lane * seg];
       const float P = kTwo ? sc.col[1][lane * seg] : 0.f;
-      const int sa = sc.shift[0][lane], sb = sc.shift[1][lane];
-      if constexpr (OP == ColOp::kFwd) {
-        const float rn = sqrtf(T);
-        if (t.norm_out != nullptr) t.norm_out[u] = scaled ? ldexpf(rn, -sa) : rn;
-        const float gr = row_gain(t, u) * t.radius;
-        sc.coef[0][lane] = (rn == 0.f) ? 0.f : gr / rn;
-      } else if constexpr (OP == ColOp::kBwd) {
-        const bool zero = T == 0.f;
-        const float inv = inv_sqrt(T);
-        float dg = (t.radius * P) * inv;
-        if (scaled) dg = ldexpf(dg, -sb);
-        if (t.dgain != nullptr) t.dgain[u] = zero ? 0.f : dg;
-        sc.coef[0][lane] = zero ? 0.f : row_gain(t, u) * t.radius * inv;   // c
-        sc.coef[1][lane] = zero ? 0.f : (P * inv) * inv;                    // k
-        sc.coef[2][lane] = zero ? 1.f : 0.f;
-      } else {
-        const float inv = inv_sqrt(T);
-        sc.coef[0][lane] = t.radius * inv;                                  // c
-        sc.coef[1][lane] = (P * inv) * inv;                                 // k
-        sc.coef[2][lane] = T == 0.f ? 1.f : 0.f;                           // untouched
-      }
+      float c[3];
+      unit_coefficients<OP>(t, u0 + lane, sc.col[0][lane * seg], P, scaled, sc.shift[0][lane],
+                            sc.shift[1][lane], c);
+      sc.coef[0][lane] = c[0];
+      sc.coef[1][lane] = c[1];
+      sc.coef[2][lane] = c[2];
     }
     __syncthreads();
 
@@ -295,23 +344,16 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
           const int a = a0 + kColWaves * j;
           if (a >= A) break;
           const int64_t off = (int64_t)a * t.ld + base;
-          const float x = scaled ? ldexpf(xr[j], sa) : xr[j];
+          float o0, o1;
+          col_values<OP>(xr[j], OP == ColOp::kFwd ? 0.f : second_value<OP>(yr[j]), scaled, sa,
+                         sb, c0, c1, skip, o0, o1);
           if constexpr (OP == ColOp::kFwd) {
-            gmem_out(t.w_eff)[off] = (uint16_t)pack_bf16(x * c0, 0.f);
+            gmem_out(t.w_eff)[off] = (uint16_t)pack_bf16(o0, 0.f);
           } else if constexpr (OP == ColOp::kBwd) {
-            const float yv = second_value<OP>(yr[j]);
-            const float y = scaled ? ldexpf(yv, sb) : yv;
-            float o = c0 * __builtin_fmaf(-x, c1, y);
-            if (scaled) o = ldexpf(o, sa - sb);
-            gmem_out(t.dw)[off] = skip ? 0.f : o;
+            gmem_out(t.dw)[off] = o0;
           } else {
-            if (two) {
-              const float yv = second_value<OP>(yr[j]);
-              const float y = scaled ? ldexpf(yv, sb) : yv;
-              const float r = __builtin_fmaf(-x, c1, y);
-              gmem_out(t.v)[off] = scaled ? ldexpf(r, -sb) : r;
-            }
-            if constexpr (OP == ColOp::kAfterStep) gmem_out(t.w)[off] = x * c0;
+            if (two) gmem_out(t.v)[off] = o0;
+            if constexpr (OP == ColOp::kAfterStep) gmem_out(t.w)[off] = o1;
           }
         }
       }
