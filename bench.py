@@ -220,7 +220,7 @@ def main():
     rn_us = a.elapsed_time(b) * 1e3 / 60
     rn_bytes = rn.total_elems * 6 + rn.total_rows * 8
     ops["weight_rownorm_gain_12x4_d768"] = op(rn_us, rn_bytes, rn.total_rows)
-    ops["weight_rownorm_gain_12x4_d768"]["note"] = ("one call: one launch per row-width class, "
+    ops["weight_rownorm_gain_12x4_d768"]["note"] = ("one call: one launch per large shape class, "
                                                     "descriptor tables in the kernel arguments")
 
     # ---- a plain device copy of the same bytes as l2_rows moves (reference ceiling)
