@@ -7,7 +7,8 @@ output of the same matrix called alone (its own shape's kernel), and
 sampled rows meet the oracle's contracts.  The classes here are sized just
 under the mixing bound and together exceed one pass of the grid, so each
 workgroup runs items of one-wave rows and of four-wave rows in turn (their
-LDS combines must still alternate), with rescued rows among them.
+LDS combines must still alternate), with rescued rows among them; a class of
+two-wave rows (128-thread workgroups) runs in a launch of its own.
 """
 import numpy as np
 import pytest
@@ -35,12 +36,13 @@ def B():
 def case():
     """Three small classes of 256-thread workgroups: one-wave rows of 64 and
     of 480 values (four rows an item) and four-wave rows of 4,608 (one row an
-    item), each of ITEMS_PER_CU items per compute unit; a few rows of each
-    scaled far out of fp32's comfortable range."""
+    item), each of ITEMS_PER_CU items per compute unit, and two-wave rows of
+    2,048 (an odd count); a few rows of each scaled far out of fp32's
+    comfortable range."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n = ITEMS_PER_CU * cus
-    shapes = [(4 * n, 64), (4 * n, 480), (n, 4608)]
+    shapes = [(4 * n, 64), (4 * n, 480), (n - 1, 2048), (n, 4608)]
     c = inputs.rownorm_grad_case(shapes, 2100)
     for i, w in enumerate(c.w):
         w[5] *= np.float32(2.0 ** 100)
@@ -61,9 +63,9 @@ def test_forward_mixed_equals_single(B, case):
     announce("mixed forward", [w.shape for w in c.w])
     ws = [dev_f32(w) for w in c.w]
     gs = [dev_f32(g) for g in c.gain]
-    n_all, e_all = B.ds_weight_rownorm_gain(ws, gs, [1.0] * 3)
+    n_all, e_all = B.ds_weight_rownorm_gain(ws, gs, [1.0] * len(ws))
     torch.cuda.synchronize()
-    for i in range(3):
+    for i in range(len(c.w)):
         n1, e1 = B.ds_weight_rownorm_gain([ws[i]], [gs[i]], [1.0])
         torch.cuda.synchronize()
         assert torch.equal(n1[0], n_all[i]), f"matrix {i}: norms differ from the single call"
@@ -85,9 +87,9 @@ def test_backward_mixed_equals_single(B, case):
     ws = [dev_f32(w) for w in c.w]
     gs = [dev_f32(g) for g in c.gain]
     des = [dev_bits(d) for d in c.dwe]
-    dw_all, dg_all = B.ds_weight_rownorm_gain_backward(ws, gs, des, [1.0] * 3)
+    dw_all, dg_all = B.ds_weight_rownorm_gain_backward(ws, gs, des, [1.0] * len(ws))
     torch.cuda.synchronize()
-    for i in range(3):
+    for i in range(len(c.w)):
         dw1, dg1 = B.ds_weight_rownorm_gain_backward([ws[i]], [gs[i]], [des[i]], [1.0])
         torch.cuda.synchronize()
         assert torch.equal(dw1[0], dw_all[i]) and torch.equal(dg1[0], dg_all[i]), i
@@ -113,7 +115,7 @@ def test_rescale_mixed_equals_single(B, case):
         call = B.ds_rescale_after_step if after_step else B.ds_rescale_project
         call(ws, vs)
         torch.cuda.synchronize()
-        for i in range(3):
+        for i in range(len(c.w)):
             w1, v1 = dev_f32(c.w[i]), dev_f32(v[i])
             call([w1], [v1])
             torch.cuda.synchronize()
