@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10700          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10701          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 #define DS_MAX_ELEM_COLS 16384         /* widest fp32 weight row whose width is
                                           not a multiple of 4 */
@@ -374,8 +374,8 @@ int ds_rms_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* d
  *            be NULL with DS_GAIN_NONE.
  * dgain_total : one fp32, receives dL/dg of a scalar gain, the sum of the
  *            rows' shares (added in an order fixed by rows alone); needs
- *            DS_GAIN_SCALAR and dgain (which then holds the shares); NULL
- *            otherwise.
+ *            DS_GAIN_SCALAR and dgain (which then holds the shares; it may be
+ *            NULL for an empty matrix, whose total is 0); NULL otherwise.
  * rows, cols : as in ds_rownorm_desc.
  * dw and dgain must not overlap any input or output of the call.
  */

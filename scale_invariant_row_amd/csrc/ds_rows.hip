@@ -797,11 +797,21 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     int st = check_layout(d.rows, d.cols, d.seg, d.ld, &s, &a32, &a16, &span);
     if (st != DS_OK) return st;
     if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
-    // a total needs a scalar gain and the per-row shares it sums; no gain, no gradient
-    if (d.dgain_total != nullptr && (d.gain_mode != DS_GAIN_SCALAR || d.dgain == nullptr))
+    // a total needs a scalar gain and the per-row shares it sums (none for an
+    // empty matrix); no gain, no gradient
+    if (d.dgain_total != nullptr &&
+        (d.gain_mode != DS_GAIN_SCALAR || (d.dgain == nullptr && d.rows > 0)))
       return DS_ERR_ARG;
     if (d.gain_mode == DS_GAIN_NONE && d.dgain != nullptr) return DS_ERR_ARG;
-    if (d.rows == 0) continue;
+    if (d.rows == 0) {
+      // the sum over no rows: the total kernel writes 0 and reads nothing
+      if (d.dgain_total != nullptr) {
+        if (!aligned(d.dgain_total, 4)) return DS_ERR_ALIGN;
+        add_range(outs, d.dgain_total, 4);
+        totals.push_back({d.dgain, d.dgain_total, 0});
+      }
+      continue;
+    }
     const float* gain = d.gain_mode == DS_GAIN_NONE ? nullptr : d.gain;
     if (d.w == nullptr || d.dw_eff == nullptr || d.dw == nullptr ||
         (d.gain_mode != DS_GAIN_NONE && gain == nullptr))
@@ -835,6 +845,10 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
   int st = launch_ragged<dsr::RownormGradTask>(mats, launch_rownorm_backward_any,
                                                (hipStream_t)stream);
   if (st != DS_OK) return st;
+  if (!totals.empty()) {                          // (a call of empty matrices has no launch above)
+    int cus = 0;
+    if ((st = device_cus(&cus)) != DS_OK) return st;
+  }
   // scalar gains: sum each matrix's row shares once the shares are written
   for (size_t first = 0; first < totals.size(); first += dsr::kTotalTasks) {
     dsr::TotalArgs args{};

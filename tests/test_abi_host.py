@@ -38,7 +38,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10700
+    assert B.ds_version() == 10701
     for code in range(0, -9, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
@@ -224,6 +224,22 @@ def test_gain_mode_validation(L):
              1, None) == B.DS_ERR_ALIGN
     assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR,
                       Bp + 4096 + 60)), 1, None) == B.DS_ERR_ARG   # total over the shares
+    # an empty matrix's total (0) needs no shares, but is still checked and placed
+    assert g(_gdescs((None, None, 1.0, None, None, None, 0, 64, B.DS_GAIN_SCALAR, tot + 2)),
+             1, None) == B.DS_ERR_ALIGN
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR, tot),
+                     (None, None, 1.0, None, None, None, 0, 64, B.DS_GAIN_SCALAR, tot)),
+             2, None) == B.DS_ERR_ARG                    # two totals in one place
+
+
+@pytest.mark.skipif("not no_device()")
+def test_empty_matrix_total_is_accepted(L):
+    """rows = 0 with a scalar gain and no shares buffer passes validation and
+    stops at the device lookup for the total's launch."""
+    g = L.ds_weight_rownorm_gain_backward
+    st = g(_gdescs((None, None, 1.0, None, None, None, 0, 64, B.DS_GAIN_SCALAR, Bp + 8192)), 1,
+           None)
+    assert st == B.DS_ERR_DEVICE
 
 
 def test_column_block_validation(L):

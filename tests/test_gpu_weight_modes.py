@@ -166,6 +166,28 @@ def test_mixed_widths_ragged_equals_single(B):
         assert np.array_equal(n1[0], n_all[i]) and np.array_equal(w1[0], w_all[i]), shapes[i]
 
 
+def test_empty_matrix_scalar_gain(B):
+    """A scalar gain's gradient over an empty matrix is 0 (the sum over no
+    rows), written even though there are no shares; a neighbour with rows is
+    unaffected."""
+    import torch
+    dev = "cuda:0"
+    announce("empty matrix, scalar gain")
+    case = inputs.rownorm_grad_case([(33, 768)], 1410)
+    w0 = torch.empty(0, 768, device=dev)
+    de0 = torch.empty(0, 768, dtype=torch.bfloat16, device=dev)
+    g = torch.tensor(1.5, device=dev)
+    w1, de1 = dev_f32(case.w[0]), dev_bits(case.dwe[0])
+    g1 = dev_f32(case.gain[0][:1].copy()).reshape(())
+    dg = [torch.full((), float("nan"), device=dev), torch.full((), float("nan"), device=dev)]
+    _, dgs = B.ds_weight_rownorm_gain_backward([w0, w1], [g, g1], [de0, de1], dgain=dg)
+    torch.cuda.synchronize()
+    assert dgs[0].item() == 0.0
+    want = float(weight_rownorm_scalar_gain_backward(case.w[0], case.gain[0][:1].copy(), 1.0,
+                                                     case.dwe[0])[1])
+    assert abs(dgs[1].item() - want) <= 1e-5 * (1.0 + abs(want))
+
+
 def test_resnet50_workload(B):
     """ResNet-50's convolutions and classifier, forward and backward, sampled rows."""
     case = inputs.make("rownorm_gain_resnet50")
