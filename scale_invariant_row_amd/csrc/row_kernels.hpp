@@ -724,12 +724,15 @@ slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, 
         lerp(v, t);
       }
       uint32_t q[4];
+      if (scaled) {
+        // a branch of its own (the empty asm keeps the compiler from turning
+        // it into an ldexp and a select on every element of the common path)
+        asm volatile("" ::: "memory");
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float lo = t[2 * k], hi = t[2 * k + 1];
-        if (scaled) { lo = ldexpf(lo, sh); hi = ldexpf(hi, sh); }
-        q[k] = pack_bf16(lo * inv, hi * inv);
+        for (int k = 0; k < 8; ++k) t[k] = ldexpf(t[k], sh);
       }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[k] = pack_bf16(t[2 * k] * inv, t[2 * k + 1] * inv);
       u32x4_t w = {q[0], q[1], q[2], q[3]};
       hb.st16(w, off[v]);
     }
@@ -1245,11 +1248,21 @@ __device__ __forceinline__ void rownorm_item(const RownormTask& t, int item, con
       t.norm_out[row] = scaled ? ldexpf(rn, -sh) : rn;
     const float c = (rn == 0.f) ? 0.f : gr / rn;
     const RowBuf eb(t.w_eff + row * t.cols, (uint32_t)t.cols * 2u);
+    if (scaled) {
+      // a rescued row's values, scaled in a branch of its own: the empty asm
+      // keeps the compiler from turning it into an ldexp and a select on
+      // every element of the common path
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < NE; ++k) w[v][k] = ldexpf(w[v][k], sh);
+    }
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       float q[NE];
 #pragma unroll
-      for (int k = 0; k < NE; ++k) q[k] = (scaled ? ldexpf(w[v][k], sh) : w[v][k]) * c;
+      for (int k = 0; k < NE; ++k) q[k] = w[v][k] * c;
       store_bf16<NE>(eb, off[v] / 2, q);
     }
   }
@@ -1350,21 +1363,37 @@ __device__ __forceinline__ void rownorm_backward_item(const RownormGradTask& t, 
     if (t.dgain != nullptr && geo.g == 0 && geo.lane == 0) t.dgain[row] = zero ? 0.f : dg;
     const RowBuf ob(t.dw + row * t.cols, (uint32_t)t.cols * 4u);
     const int sh = sa - sb;
+    // three uniform cases, each a branch of its own (the empty asm keeps the
+    // compiler from merging them into selects on every element)
+    if (!scaled && !zero) {
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      float o[NE];
+      for (int v = 0; v < V; ++v) {
+        float o[NE];
 #pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        float wv = w[v][k], ev = e[v].get(k);
-        if (scaled) {
-          wv = ldexpf(wv, sa);
-          ev = ldexpf(ev, sb);
-        }
-        o[k] = c * __builtin_fmaf(-wv, kk, ev);
-        if (scaled) o[k] = ldexpf(o[k], sh);
-        if (zero) o[k] = 0.f;
+        for (int k = 0; k < NE; ++k) o[k] = c * __builtin_fmaf(-w[v][k], kk, e[v].get(k));
+        F32Vec<NE>::store(ob, off[v], o);
       }
-      F32Vec<NE>::store(ob, off[v], o);
+    } else if (zero) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float o[NE];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) o[k] = 0.f;
+        F32Vec<NE>::store(ob, off[v], o);
+      }
+    } else {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float o[NE];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+          const float wv = ldexpf(w[v][k], sa), ev = ldexpf(e[v].get(k), sb);
+          o[k] = ldexpf(c * __builtin_fmaf(-wv, kk, ev), sh);
+        }
+        F32Vec<NE>::store(ob, off[v], o);
+      }
     }
   }
 }
@@ -1475,19 +1504,35 @@ __device__ __forceinline__ void rescale_item(const RescaleTask& t, int item, con
     const float inv = inv_sqrt(T);
     const float kk = (P * inv) * inv;
     const float c = t.radius * inv;
+    // the rescued case is a branch of its own (the empty asm keeps the
+    // compiler from merging the two into selects on every element)
+    if (!scaled) {
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      float ov[NE], ow[NE];
+      for (int k = 0; k < V; ++k) {
+        float ov[NE], ow[NE];
 #pragma unroll
-      for (int j = 0; j < NE; ++j) {
-        const float wj = scaled ? ldexpf(w[k][j], sa) : w[k][j];
-        const float vj = scaled ? ldexpf(v[k][j], sb) : v[k][j];
-        const float r = __builtin_fmaf(-wj, kk, vj);
-        ov[j] = scaled ? ldexpf(r, -sb) : r;
-        ow[j] = wj * c;
+        for (int j = 0; j < NE; ++j) {
+          ov[j] = __builtin_fmaf(-w[k][j], kk, v[k][j]);
+          ow[j] = w[k][j] * c;
+        }
+        if (has_v) F32Vec<NE>::store(vb, off[k], ov);
+        if constexpr (RESCALE) F32Vec<NE>::store(wb, off[k], ow);
       }
-      if (has_v) F32Vec<NE>::store(vb, off[k], ov);
-      if constexpr (RESCALE) F32Vec<NE>::store(wb, off[k], ow);
+    } else {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        float ov[NE], ow[NE];
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+          const float wj = ldexpf(w[k][j], sa);
+          const float vj = ldexpf(v[k][j], sb);
+          ov[j] = ldexpf(__builtin_fmaf(-wj, kk, vj), -sb);
+          ow[j] = wj * c;
+        }
+        if (has_v) F32Vec<NE>::store(vb, off[k], ov);
+        if constexpr (RESCALE) F32Vec<NE>::store(wb, off[k], ow);
+      }
     }
   }
 }
