@@ -23,6 +23,8 @@
 // read twice, the second time mostly from the caches.
 #pragma once
 
+#include <type_traits>
+
 #include "row_kernels.hpp"
 
 namespace dsr {
@@ -317,9 +319,12 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
     }
     __syncthreads();
 
-    // ---- pass 2: outputs, eight stored rows in flight per wave
-    if (active) {
-      const bool scaled = sc.coef[3][uo] != 0.f;
+    // ---- pass 2: outputs, eight stored rows in flight per wave.  A tile
+    // with no rescued unit (the common case) takes a copy of the loop with
+    // the rescue's scaling compiled out, not a select on every value.
+    auto pass2 = [&](auto rescued) {
+      constexpr bool kResc = decltype(rescued)::value;
+      const bool scaled = kResc && sc.coef[3][uo] != 0.f;
       const int sa = sc.shift[0][uo], sb = sc.shift[1][uo];
       const float c0 = sc.coef[0][uo], c1 = sc.coef[1][uo];
       const bool skip = OP != ColOp::kFwd && sc.coef[2][uo] != 0.f;
@@ -356,6 +361,14 @@ __global__ void __launch_bounds__(kColThreads) colblock_kernel(const TaskArgs<ty
             if constexpr (OP == ColOp::kAfterStep) gmem_out(t.w)[off] = o1;
           }
         }
+      }
+    };
+    if (active) {
+      if (sc.any_rescue) {                          // uniform: LDS read after a barrier
+        asm volatile("" ::: "memory");
+        pass2(std::true_type{});
+      } else {
+        pass2(std::false_type{});
       }
     }
     __syncthreads();                                // LDS is reused by the next tile
