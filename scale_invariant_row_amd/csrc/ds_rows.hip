@@ -721,7 +721,8 @@ int ds_qk_rows_l2(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk
   a.nk = n_kv_heads;
   a.eps = eps;
   (void)hipGetLastError();
-  return launch_status(dsr::launch_qk_rows_l2(head_dim, a, grid_for((rows + 3) / 4, cus),
+  const int64_t units = (rows + dsr::kQkRowsPerBlock - 1) / dsr::kQkRowsPerBlock;
+  return launch_status(dsr::launch_qk_rows_l2(head_dim, a, grid_for(units, cus),
                                               (hipStream_t)stream));
 }
 

@@ -885,17 +885,21 @@ act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
 //   r_{i+HD/2} = bf16(x_{i+HD/2} cos t_i + x_i sin t_i)
 // each product and the sum rounded once in fp32 (no contraction).
 //
-// One wave per token row.  A head of HD values is spread over L = HD/4
-// lanes, four values (8 bytes) each: lane l of a head holds elements
-// 4 (l mod L/2) .. +3 of half l / (L/2), so its rotate-half partner is L/2
-// lanes away -- one permlane swap (32 for HD = 256, 16 for HD = 128) gives
-// every lane both halves, and 64/L heads go through the wave at a time.  A
-// lane's four frequencies are the same for every head of the row, so cos
-// and sin are computed once per row (the device library's sincosf, with its
-// full-range argument reduction) and reused for all q and k heads.  Heads
-// are loaded eight wave-steps at a time to keep several loads in flight.
-// The kernel is bound by load latency, not by its arithmetic: with the
-// trigonometry stubbed out it ran only ~1 us faster (of ~43).
+// Two waves per token row, two rows per workgroup.  A head of HD values is
+// spread over L = HD/4 lanes, four values (8 bytes) each: lane l of a head
+// holds elements 4 (l mod L/2) .. +3 of half l / (L/2), so its rotate-half
+// partner is L/2 lanes away -- one permlane swap (32 for HD = 256, 16 for
+// HD = 128) gives every lane both halves, and 64/L heads go through the
+// wave at a time (a wave step).  The row's q steps followed by its k steps
+// are split into two contiguous halves, one per wave; each head's arithmetic
+// is the same whichever wave runs it.  A lane's four frequencies are the
+// same for every head of the row, so each wave computes cos and sin once per
+// row (the device library's sincosf, with its full-range argument reduction)
+// and reuses them for all its heads.  Heads are loaded CH wave steps at a
+// time to keep several loads in flight.  The kernel is bound by load
+// latency, not by its arithmetic: with the trigonometry stubbed out it ran
+// only ~1 us faster (of ~43); the second wave per row took 8,192 rows of
+// 16 + 4 heads of 256 from 40.4 to 37.5 us.
 
 struct QkArgs {
   const uint16_t* q;
@@ -953,13 +957,20 @@ __device__ __forceinline__ void partner_pair(uint32_t u, uint32_t& lo, uint32_t&
   }
 }
 
+// Rows per 256-thread workgroup: two waves each.
+constexpr int kQkRowsPerBlock = 2;
+
 template <int HD>
 __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
   constexpr int L = HD / 4;             // lanes per head
   constexpr int HPW = 64 / L;           // heads per wave step
-  constexpr int CH = 8;                 // wave steps loaded at once (measured: 4 and 20 slower)
+  // wave steps loaded at once (measured with two waves per row: 6 for HD =
+  // 256 against 37.8-39.4 us at 3-5 and 7; 5 for HD = 128)
+  constexpr int CH = HD == 256 ? 6 : 5;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wave & 1;            // which half of the row's wave steps
+  const int rsub = wave >> 1;           // which row of the workgroup
   const int ll = lane % L;              // lane within its head
   const int hsub = lane / L;            // head within the wave step
   const bool upper = ll >= L / 2;       // holds the second half of the head
@@ -970,8 +981,14 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
   const float invf[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
   const RowBuf sb(a.q_scale, (uint32_t)a.nq * (uint32_t)HD * 4u);
   const int nsteps[2] = {(a.nq + HPW - 1) / HPW, (a.nk + HPW - 1) / HPW};
+  // this wave's steps: [first, last) of q's then k's, as a range in each
+  const int total = nsteps[0] + nsteps[1];
+  const int first = part * ((total + 1) / 2), last = min(total, first + (total + 1) / 2);
+  const int lo[2] = {min(first, nsteps[0]), max(0, min(first - nsteps[0], nsteps[1]))};
+  const int hi[2] = {min(last, nsteps[0]), max(0, min(last - nsteps[0], nsteps[1]))};
 
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
+  for (int64_t row = (int64_t)blockIdx.x * kQkRowsPerBlock + rsub; row < a.rows;
+       row += (int64_t)gridDim.x * kQkRowsPerBlock) {
     const float pf = (float)a.pos[row];
     float c[4], s[4];
 #pragma unroll
@@ -980,21 +997,23 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
 #pragma unroll
     for (int which = 0; which < 2; ++which) {          // q's heads, then k's
       const int nh = which == 0 ? a.nq : a.nk;
-      if (nh == 0) continue;
+      if (lo[which] >= hi[which]) continue;
       const uint16_t* src = which == 0 ? a.q + row * a.ldq : a.k + row * a.ldk;
       uint16_t* dst = which == 0 ? a.qo + row * a.ldqo : a.ko + row * a.ldko;
       const uint32_t bytes = (uint32_t)nh * (uint32_t)HD * 2u;
       const RowBuf ib(src, bytes), ob(dst, bytes);
-      for (int st0 = 0; st0 < nsteps[which]; st0 += CH) {
+      for (int st0 = lo[which]; st0 < hi[which]; st0 += CH) {
         u32x2_t x[CH];
 #pragma unroll
         for (int c4 = 0; c4 < CH; ++c4) {
-          const int h = (st0 + c4) * HPW + hsub;      // past the row: the range check reads 0
-          x[c4] = ib.ld8((h * HD + e0) * 2);
+          // only this wave's steps (the other wave loads the rest); a head
+          // index past the last head reads 0 through the range check
+          const int h = (st0 + c4) * HPW + hsub;
+          x[c4] = st0 + c4 < hi[which] ? ib.ld8((h * HD + e0) * 2) : u32x2_t{0u, 0u};
         }
 #pragma unroll
         for (int c4 = 0; c4 < CH; ++c4) {
-          if (st0 + c4 >= nsteps[which]) break;        // uniform
+          if (st0 + c4 >= hi[which]) break;            // uniform
           const int h = (st0 + c4) * HPW + hsub;
           uint32_t lo0, hi0, lo1, hi1;
           partner_pair<L>(x[c4].x, lo0, hi0);
