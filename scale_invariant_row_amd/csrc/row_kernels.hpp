@@ -805,16 +805,37 @@ template <Act A>
 __device__ __forceinline__ void act_prologue(uint32_t (&out)[4], const uint32_t (&x0)[4],
                                              const uint32_t (&x1)[4], const float* s0,
                                              const float* s1) {
+  float sig[8];
+  if constexpr (A == Act::kGate) {
+    // sigmoid(g * sg) = 1 / b, b = 1 + exp(-g sg) in [1, +inf] or NaN: the
+    // reciprocal and one fma correction, which equals the IEEE quotient for
+    // every fp32 b in [1, 2^126) (checked exhaustively on gfx950); past that
+    // the quotient is subnormal (v_rcp_f32 flushes it), +0 or NaN, so a
+    // vector holding such a b in any lane takes the IEEE division for all
+    // its values (a wave-uniform branch).
+    float b[8];
+    bool slow = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = ((j & 1) ? bf_hi(x1[j / 2]) : bf_lo(x1[j / 2])) * s0[j];   // g * sg
+      b[j] = 1.0f + exp_split(-x);
+      const float y = __builtin_amdgcn_rcpf(b[j]);
+      sig[j] = __builtin_fmaf(__builtin_fmaf(-b[j], y, 1.0f), y, y);
+      slow |= !(b[j] < 0x1p126f);
+    }
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+      asm volatile("" ::: "memory");     // a branch of its own, not a select per value
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sig[j] = 1.0f / b[j];
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     float r[2];
     if constexpr (A == Act::kGate) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float x = (h ? bf_hi(x1[k]) : bf_lo(x1[k])) * s0[2 * k + h];    // g * sg
-        const float sig = 1.0f / (1.0f + exp_split(-x));
-        r[h] = (h ? bf_hi(x0[k]) : bf_lo(x0[k])) * sig;   // o * sigmoid, rounded below
-      }
+      for (int h = 0; h < 2; ++h)
+        r[h] = (h ? bf_hi(x0[k]) : bf_lo(x0[k])) * sig[2 * k + h];   // o * sigmoid, rounded below
     } else {
       // a = bf16(g * sug) and b = bf16(u * suu), both elements of the pair at once
       const uint32_t ap = pack_bf16(bf_lo(x0[k]) * s0[2 * k], bf_hi(x0[k]) * s0[2 * k + 1]);
