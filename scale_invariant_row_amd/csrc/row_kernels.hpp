@@ -906,21 +906,22 @@ act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
 //   r_{i+HD/2} = bf16(x_{i+HD/2} cos t_i + x_i sin t_i)
 // each product and the sum rounded once in fp32 (no contraction).
 //
-// Two waves per token row, two rows per workgroup.  A head of HD values is
-// spread over L = HD/4 lanes, four values (8 bytes) each: lane l of a head
-// holds elements 4 (l mod L/2) .. +3 of half l / (L/2), so its rotate-half
-// partner is L/2 lanes away -- one permlane swap (32 for HD = 256, 16 for
-// HD = 128) gives every lane both halves, and 64/L heads go through the
+// Two waves per token row, two rows per workgroup.  A head spreads over 32
+// lanes: NV = HD/32 values each (16 bytes for HD = 256, 8 for HD = 128).
+// Lane l of a head holds elements NV (l mod 16) .. +NV-1 of half l / 16, so
+// its rotate-half partner is 16 lanes away -- one v_permlane16_swap per
+// packed dword gives every lane both halves -- and two heads go through the
 // wave at a time (a wave step).  The row's q steps followed by its k steps
 // are split into two contiguous halves, one per wave; each head's arithmetic
-// is the same whichever wave runs it.  A lane's four frequencies are the
-// same for every head of the row, so each wave computes cos and sin once per
-// row (the device library's sincosf, with its full-range argument reduction)
-// and reuses them for all its heads.  Heads are loaded CH wave steps at a
-// time to keep several loads in flight.  The kernel is bound by load
-// latency, not by its arithmetic: with the trigonometry stubbed out it ran
-// only ~1 us faster (of ~43); the second wave per row took 8,192 rows of
-// 16 + 4 heads of 256 from 40.4 to 37.5 us.
+// is the same whichever wave runs it.  A lane's NV frequencies are the same
+// for every head of the row, so each wave computes cos and sin once per row
+// (the device library's sincosf, with its full-range argument reduction) and
+// reuses them for all its heads.  Heads are loaded CH wave steps at a time to
+// keep several loads in flight.  The kernel is bound by load latency, not by
+// its arithmetic: with the trigonometry stubbed out it ran only ~1 us faster
+// (of ~43).  For 8,192 rows of 16 + 4 heads of 256, the second wave per row
+// took it from 40.4 to 37.5 us, and 16-byte lanes (half the wave steps and
+// per-head sums) from there to 34.8 us.
 
 struct QkArgs {
   const uint16_t* q;
@@ -936,46 +937,31 @@ struct QkArgs {
   float eps;
 };
 
-template <int L>
+// Sum and maximum over each 32-lane half of the wave (one head each).
 __device__ __forceinline__ float head_sum(float v) {
-  if constexpr (L == 64) {
-    return wave_sum(v);
-  } else {                      // two heads per wave: sum each 32-lane half
-    v = v + dpp_f<0xB1>(v);
-    v = v + dpp_f<0x4E>(v);
-    v = v + dpp_f<0x141>(v);
-    v = v + dpp_f<0x140>(v);
-    const f32x2_t p = swap16(v);
-    return p.x + p.y;
-  }
+  v = v + dpp_f<0xB1>(v);
+  v = v + dpp_f<0x4E>(v);
+  v = v + dpp_f<0x141>(v);
+  v = v + dpp_f<0x140>(v);
+  const f32x2_t p = swap16(v);
+  return p.x + p.y;
 }
 
-template <int L>
 __device__ __forceinline__ float head_max(float v) {
-  if constexpr (L == 64) {
-    return wave_max(v);
-  } else {
-    v = fmaxf(v, dpp_f<0xB1>(v));
-    v = fmaxf(v, dpp_f<0x4E>(v));
-    v = fmaxf(v, dpp_f<0x141>(v));
-    v = fmaxf(v, dpp_f<0x140>(v));
-    const f32x2_t p = swap16(v);
-    return fmaxf(p.x, p.y);
-  }
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const f32x2_t p = swap16(v);
+  return fmaxf(p.x, p.y);
 }
 
-// (low-half value, high-half value) of a packed dword between rotate-half partners
-template <int L>
+// (low-half value, high-half value) of a packed dword between rotate-half
+// partners, 16 lanes apart
 __device__ __forceinline__ void partner_pair(uint32_t u, uint32_t& lo, uint32_t& hi) {
-  if constexpr (L == 64) {
-    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    lo = p[0];
-    hi = p[1];
-  } else {
-    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    lo = p[0];
-    hi = p[1];
-  }
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  lo = p[0];
+  hi = p[1];
 }
 
 // Rows per 256-thread workgroup: two waves each.
@@ -983,23 +969,30 @@ constexpr int kQkRowsPerBlock = 2;
 
 template <int HD>
 __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
-  constexpr int L = HD / 4;             // lanes per head
-  constexpr int HPW = 64 / L;           // heads per wave step
-  // wave steps loaded at once (measured with two waves per row: 6 for HD =
-  // 256 against 37.8-39.4 us at 3-5 and 7; 5 for HD = 128)
-  constexpr int CH = HD == 256 ? 6 : 5;
+  constexpr int NV = HD / 32;            // values per lane
+  constexpr int L = 32;                  // lanes per head
+  constexpr int HPW = 64 / L;            // heads per wave step
+  // wave steps loaded at once (measured with two waves per row): 5 covers a
+  // wave's half of 16 + 4 heads of 256 in one chunk; at HD = 128, 3 and 4
+  // were slower
+  constexpr int CH = 5;
+  static_assert(HD == 256 || HD == 128, "head_dim 128 or 256");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int part = wave & 1;            // which half of the row's wave steps
-  const int rsub = wave >> 1;           // which row of the workgroup
-  const int ll = lane % L;              // lane within its head
-  const int hsub = lane / L;            // head within the wave step
-  const bool upper = ll >= L / 2;       // holds the second half of the head
-  const int e0 = (upper ? HD / 2 : 0) + 4 * (ll % (L / 2));    // first element of the lane
-  const int f0 = 4 * (ll % (L / 2));                           // first frequency of the lane
+  const int part = wave & 1;             // which half of the row's wave steps
+  const int rsub = wave >> 1;            // which row of the workgroup
+  const int ll = lane % L;               // lane within its head
+  const int hsub = lane / L;             // head within the wave step
+  const bool upper = ll >= L / 2;        // holds the second half of the head
+  const int e0 = (upper ? HD / 2 : 0) + NV * (ll % (L / 2));   // first element of the lane
+  const int f0 = NV * (ll % (L / 2));                          // first frequency of the lane
   const RowBuf fb(a.inv_freq, (uint32_t)(HD / 2) * 4u);
-  const f32x4_t inv4 = fb.ld16f_cached(f0 * 4);
-  const float invf[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
+  float invf[NV];
+#pragma unroll
+  for (int q4 = 0; q4 < NV / 4; ++q4) {
+    const f32x4_t v = fb.ld16f_cached((f0 + 4 * q4) * 4);
+    invf[4 * q4] = v.x; invf[4 * q4 + 1] = v.y; invf[4 * q4 + 2] = v.z; invf[4 * q4 + 3] = v.w;
+  }
   const RowBuf sb(a.q_scale, (uint32_t)a.nq * (uint32_t)HD * 4u);
   const int nsteps[2] = {(a.nq + HPW - 1) / HPW, (a.nk + HPW - 1) / HPW};
   // this wave's steps: [first, last) of q's then k's, as a range in each
@@ -1011,75 +1004,99 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
   for (int64_t row = (int64_t)blockIdx.x * kQkRowsPerBlock + rsub; row < a.rows;
        row += (int64_t)gridDim.x * kQkRowsPerBlock) {
     const float pf = (float)a.pos[row];
-    float c[4], s[4];
+    float c[NV], s[NV];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sincosf(pf * invf[j], &s[j], &c[j]);
-
+    for (int j = 0; j < NV; ++j) sincosf(pf * invf[j], &s[j], &c[j]);
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {          // q's heads, then k's
+    for (int which = 0; which < 2; ++which) {
       const int nh = which == 0 ? a.nq : a.nk;
-      if (lo[which] >= hi[which]) continue;
+      if (lo[which] >= hi[which]) continue;           // q's heads, then k's
       const uint16_t* src = which == 0 ? a.q + row * a.ldq : a.k + row * a.ldk;
       uint16_t* dst = which == 0 ? a.qo + row * a.ldqo : a.ko + row * a.ldko;
       const uint32_t bytes = (uint32_t)nh * (uint32_t)HD * 2u;
       const RowBuf ib(src, bytes), ob(dst, bytes);
       for (int st0 = lo[which]; st0 < hi[which]; st0 += CH) {
-        u32x2_t x[CH];
+        uint32_t x[CH][NV / 2];
 #pragma unroll
         for (int c4 = 0; c4 < CH; ++c4) {
           // only this wave's steps (the other wave loads the rest); a head
           // index past the last head reads 0 through the range check
           const int h = (st0 + c4) * HPW + hsub;
-          x[c4] = st0 + c4 < hi[which] ? ib.ld8((h * HD + e0) * 2) : u32x2_t{0u, 0u};
+          if constexpr (NV == 8) {
+            const u32x4_t t = st0 + c4 < hi[which] ? ib.ld16((h * HD + e0) * 2) : u32x4_t{0u, 0u, 0u, 0u};
+            x[c4][0] = t.x; x[c4][1] = t.y; x[c4][2] = t.z; x[c4][3] = t.w;
+          } else {
+            const u32x2_t t = st0 + c4 < hi[which] ? ib.ld8((h * HD + e0) * 2) : u32x2_t{0u, 0u};
+            x[c4][0] = t.x; x[c4][1] = t.y;
+          }
         }
 #pragma unroll
         for (int c4 = 0; c4 < CH; ++c4) {
           if (st0 + c4 >= hi[which]) break;            // uniform
           const int h = (st0 + c4) * HPW + hsub;
-          uint32_t lo0, hi0, lo1, hi1;
-          partner_pair<L>(x[c4].x, lo0, hi0);
-          partner_pair<L>(x[c4].y, lo1, hi1);
+          float own[NV], par[NV];
+#pragma unroll
+          for (int d = 0; d < NV / 2; ++d) {
+            uint32_t plo, phi;
+            partner_pair(x[c4][d], plo, phi);
+            const uint32_t pq = upper ? plo : phi;
+            own[2 * d] = bf_lo(x[c4][d]); own[2 * d + 1] = bf_hi(x[c4][d]);
+            par[2 * d] = bf_lo(pq); par[2 * d + 1] = bf_hi(pq);
+          }
           // own value times cos plus the partner's times +-sin: the lower half
           // is x1 c + x2 (-s), the upper x2 c + x1 s; fl(a + fl(-b s)) is
           // fl(a - fl(b s)), so negating first changes no rounding
-          const uint32_t q0 = upper ? lo0 : hi0, q1 = upper ? lo1 : hi1;
-          const float own[4] = {bf_lo(x[c4].x), bf_hi(x[c4].x), bf_lo(x[c4].y), bf_hi(x[c4].y)};
-          const float par[4] = {bf_lo(q0), bf_hi(q0), bf_lo(q1), bf_hi(q1)};
-          float rot[4];
+          float rot[NV];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) rot[j] = own[j] * c[j] + par[j] * (upper ? s[j] : -s[j]);
-          uint32_t r[2] = {pack_bf16(rot[0], rot[1]), pack_bf16(rot[2], rot[3])};
-          float rv[4] = {bf_lo(r[0]), bf_hi(r[0]), bf_lo(r[1]), bf_hi(r[1])};
+          for (int j = 0; j < NV; ++j) rot[j] = own[j] * c[j] + par[j] * (upper ? s[j] : -s[j]);
+          uint32_t r[NV / 2];
+#pragma unroll
+          for (int d = 0; d < NV / 2; ++d) r[d] = pack_bf16(rot[2 * d], rot[2 * d + 1]);
+          float rv[NV];
+#pragma unroll
+          for (int d = 0; d < NV / 2; ++d) { rv[2 * d] = bf_lo(r[d]); rv[2 * d + 1] = bf_hi(r[d]); }
           float acc = 0.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(rv[j], rv[j], acc);
-          float T = head_sum<L>(acc) + a.eps;
+          for (int j = 0; j < NV; ++j) acc = __builtin_fmaf(rv[j], rv[j], acc);
+          float T = head_sum(acc) + a.eps;
           int sh = 0;
           const bool need = T == __builtin_inff() || T < kTiny;
           if (__builtin_amdgcn_ballot_w64(need) != 0) {  // any head of this wave step
-            float m = fmaxf(fmaxf(fabsf(rv[0]), fabsf(rv[1])), fmaxf(fabsf(rv[2]), fabsf(rv[3])));
-            m = head_max<L>(m);
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) m = fmaxf(m, fabsf(rv[j]));
+            m = head_max(m);
             if (need && (m > 0.f || a.eps > 0.f) && m < __builtin_inff()) sh = rescue_shift(m, a.eps);
             float acc2 = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NV; ++j) {
               const float v = ldexpf(rv[j], sh);
               acc2 = __builtin_fmaf(v, v, acc2);
             }
-            const float T2 = head_sum<L>(acc2) + ldexpf(a.eps, 2 * sh);
+            const float T2 = head_sum(acc2) + ldexpf(a.eps, 2 * sh);
             if (sh != 0) T = T2;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) rv[j] = ldexpf(rv[j], sh);
+            for (int j = 0; j < NV; ++j) rv[j] = ldexpf(rv[j], sh);
           }
           const float inv = inv_sqrt(T);
-          uint32_t n[2] = {pack_bf16(rv[0] * inv, rv[1] * inv), pack_bf16(rv[2] * inv, rv[3] * inv)};
+          uint32_t n[NV / 2];
+#pragma unroll
+          for (int d = 0; d < NV / 2; ++d) n[d] = pack_bf16(rv[2 * d] * inv, rv[2 * d + 1] * inv);
           if (which == 0) {
-            const f32x4_t sc = sb.ld16f_cached((h * HD + e0) * 4);
-            n[0] = pack_bf16(bf_lo(n[0]) * sc.x, bf_hi(n[0]) * sc.y);
-            n[1] = pack_bf16(bf_lo(n[1]) * sc.z, bf_hi(n[1]) * sc.w);
+#pragma unroll
+            for (int q4 = 0; q4 < NV / 4; ++q4) {
+              const f32x4_t sc = sb.ld16f_cached((h * HD + e0 + 4 * q4) * 4);
+              n[2 * q4] = pack_bf16(bf_lo(n[2 * q4]) * sc.x, bf_hi(n[2 * q4]) * sc.y);
+              n[2 * q4 + 1] = pack_bf16(bf_lo(n[2 * q4 + 1]) * sc.z, bf_hi(n[2 * q4 + 1]) * sc.w);
+            }
           }
-          const u32x2_t o = {n[0], n[1]};
-          ob.st8(o, (h * HD + e0) * 2);
+          if constexpr (NV == 8) {
+            const u32x4_t o = {n[0], n[1], n[2], n[3]};
+            ob.st16(o, (h * HD + e0) * 2);
+          } else {
+            const u32x2_t o = {n[0], n[1]};
+            ob.st8(o, (h * HD + e0) * 2);
+          }
         }
       }
     }
