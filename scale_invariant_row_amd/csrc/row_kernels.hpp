@@ -972,10 +972,10 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
   constexpr int NV = HD / 32;            // values per lane
   constexpr int L = 32;                  // lanes per head
   constexpr int HPW = 64 / L;            // heads per wave step
-  // wave steps loaded at once (measured with two waves per row): 5 covers a
-  // wave's half of 16 + 4 heads of 256 in one chunk; at HD = 128, 3 and 4
-  // were slower
-  constexpr int CH = 5;
+  // wave steps loaded at once (measured with two waves per row): at HD = 256
+  // 3 (34.4 us for 16 + 4 heads, against 35.3 at 4 and 35.7 at 5); at
+  // HD = 128, 5 (3 and 4 were slower)
+  constexpr int CH = HD == 256 ? 3 : 5;
   static_assert(HD == 256 || HD == 128, "head_dim 128 or 256");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
