@@ -156,7 +156,9 @@ def _torch():
     return torch
 
 
-def _bf16_2d(t, name):
+def _bf16_2d(t, name, device: bool = True):
+    """A bf16 [rows, cols] contiguous tensor (and, unless the caller checks
+    devices itself afterwards, on a HIP device)."""
     torch = _torch()
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"{name}: expected bf16 data (bfloat16 or 16-bit int bits), got {t.dtype}")
@@ -164,7 +166,7 @@ def _bf16_2d(t, name):
         raise ValueError(f"{name}: expected a 2-D [rows, cols] tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
-    if t.device.type != "cuda":
+    if device and t.device.type != "cuda":
         raise ValueError(f"{name}: must be on a HIP device")
 
 
@@ -178,6 +180,20 @@ def _stream_of(t, stream):
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _torch_stream(t, stream):
+    """The torch stream object for ``stream`` (None: t's current stream; a raw
+    handle is wrapped without taking ownership)."""
+    torch = _torch()
+    if t is None:
+        return None
+    if stream is None:
+        return torch.cuda.current_stream(t.device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.ExternalStream(handle, device=t.device)
 
 
 def _norm_rows(name, x, r, eps, out, stream):
@@ -301,12 +317,13 @@ def ds_weight_rownorm_gain(ws: Sequence, gains: Sequence, radius: Optional[Seque
             raise ValueError(f"ws[{i}]: expected a contiguous fp32 [rows, cols] tensor")
         rows, cols, seg, ld = lay[i]
         mode = _gain_mode(g, rows, f"gains[{i}]")
-        _bf16_2d(w_eff[i], f"w_eff[{i}]")
+        _bf16_2d(w_eff[i], f"w_eff[{i}]", device=False)
         if tuple(w_eff[i].shape) != tuple(w.shape):
             raise ValueError(f"w_eff[{i}]: shape mismatch")
         if norm_out[i] is not None and (norm_out[i].dtype != torch.float32
-                                        or norm_out[i].shape != (rows,)):
-            raise ValueError(f"norm_out[{i}]: expected fp32 [rows]")
+                                        or norm_out[i].shape != (rows,)
+                                        or not norm_out[i].is_contiguous()):
+            raise ValueError(f"norm_out[{i}]: expected a contiguous fp32 [rows] tensor")
         for t in (w, g, w_eff[i], norm_out[i]):
             if t is None:
                 continue
@@ -377,30 +394,39 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
         dgain = [torch.empty(lay[i][0] if m == DS_GAIN_ROW else (), dtype=torch.float32,
                              device=w.device) if want_dgain and m != DS_GAIN_NONE else None
                  for i, (w, m) in enumerate(zip(ws, modes))]
-    shares = [torch.empty(lay[i][0], dtype=torch.float32, device=w.device)
-              if m == DS_GAIN_SCALAR and dgain[i] is not None else None
-              for i, (w, m) in enumerate(zip(ws, modes))]
-    descs = (RownormGradDesc * max(n, 1))()
     dev = None
     for i, (w, g, de) in enumerate(zip(ws, gains, dw_effs)):
         if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
             raise ValueError(f"ws[{i}]: expected a contiguous fp32 [rows, cols] tensor")
-        _bf16_2d(de, f"dw_effs[{i}]")
+        _bf16_2d(de, f"dw_effs[{i}]", device=False)
         if tuple(de.shape) != tuple(w.shape):
             raise ValueError(f"dw_effs[{i}]: shape mismatch")
         if dw[i].dtype != torch.float32 or tuple(dw[i].shape) != tuple(w.shape) \
                 or not dw[i].is_contiguous():
             raise ValueError(f"dw[{i}]: expected a contiguous fp32 tensor shaped like ws[{i}]")
-        rows, cols, seg, ld = lay[i]
-        want = (rows,) if modes[i] == DS_GAIN_ROW else ()
-        if dgain[i] is not None and (dgain[i].dtype != torch.float32 or dgain[i].shape != want):
-            raise ValueError(f"dgain[{i}]: expected fp32 of shape {want}")
-        for t in (w, g, de, dw[i], dgain[i], shares[i]):
+        want = (lay[i][0],) if modes[i] == DS_GAIN_ROW else ()
+        if dgain[i] is not None and (dgain[i].dtype != torch.float32 or dgain[i].shape != want
+                                     or not dgain[i].is_contiguous()):
+            raise ValueError(f"dgain[{i}]: expected a contiguous fp32 tensor of shape {want}")
+        for t in (w, g, de, dw[i], dgain[i]):
             if t is None:
                 continue
             if t.device.type != "cuda" or (dev is not None and t.device != dev):
                 raise ValueError("all tensors must be on one HIP device")
             dev = t.device
+    if n == 0:
+        return [], []
+    # A scalar gain's per-row shares: a temporary the kernels write and read
+    # on the launch stream.  It is allocated on that stream, so when it is
+    # dropped below, the caching allocator hands its block only to work
+    # ordered after those kernels.
+    with torch.cuda.device(dev), torch.cuda.stream(_torch_stream(ws[0], stream)):
+        shares = [torch.empty(lay[i][0], dtype=torch.float32, device=dev)
+                  if m == DS_GAIN_SCALAR and dgain[i] is not None else None
+                  for i, m in enumerate(modes)]
+    descs = (RownormGradDesc * n)()
+    for i, (w, g, de) in enumerate(zip(ws, gains, dw_effs)):
+        rows, cols, seg, ld = lay[i]
         per_row = dgain[i] if modes[i] == DS_GAIN_ROW else shares[i]
         total = dgain[i] if modes[i] == DS_GAIN_SCALAR else None
         descs[i] = RownormGradDesc(w.data_ptr(), None if g is None else g.data_ptr(),
@@ -408,8 +434,6 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
                                    None if per_row is None else per_row.data_ptr(),
                                    rows, cols, modes[i],
                                    None if total is None else total.data_ptr(), seg, ld)
-    if n == 0:
-        return [], []
     with torch.cuda.device(dev):
         st = lib().ds_weight_rownorm_gain_backward(descs, n, _stream_of(ws[0], stream))
     _check(st, "ds_weight_rownorm_gain_backward")
@@ -468,23 +492,60 @@ def ds_qk_rows_l2(q, k, positions, inv_freq, q_scale, head_dim: int, eps: float 
     ``q``/``k`` may be strided row views (a fused projection's slices); the
     number of heads is the used width / head_dim, given by ``q_scale``'s
     length for q and by k's width for k.  Returns (q_out, k_out).
+
+    Every argument is checked (dtype, shape, row count, unit column stride,
+    contiguity of the vectors, one HIP device for all) before anything is
+    launched; a bad one raises ValueError naming it.
     """
     torch = _torch()
-    nq = q_scale.shape[0] // head_dim
+    bf16 = (torch.bfloat16, torch.int16, torch.uint16)
+    head_dim = int(head_dim)
+    if head_dim <= 0:
+        raise ValueError("head_dim: must be positive")
+
+    def rows_tensor(t, name):
+        if t.dtype not in bf16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name}: expected a bf16 [rows, cols] tensor with unit column stride")
+
+    def vector(t, name, dtype, n=None):
+        if t.dtype != dtype or t.dim() != 1 or not t.is_contiguous() \
+                or (n is not None and t.shape[0] != n):
+            want = f"[{n}]" if n is not None else "[n]"
+            raise ValueError(f"{name}: expected a contiguous {dtype} {want} tensor")
+
+    rows_tensor(q, "q")
     rows = q.shape[0]
-    for t, name in ((q, "q"),) + (((k, "k"),) if k is not None else ()):
-        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or t.dim() != 2 \
-                or t.stride(1) != 1 or t.device.type != "cuda":
-            raise ValueError(f"{name}: expected a bf16 [rows, cols] HIP tensor with unit column stride")
-    nk = 0 if k is None else k.shape[1] // head_dim
-    if q.shape[1] < nq * head_dim or (k is not None and k.shape[1] % head_dim):
-        raise ValueError("q must hold n_q_heads * head_dim columns; k a whole number of heads")
-    if positions.dtype != torch.int32 or positions.shape != (rows,):
-        raise ValueError("positions: expected int32 [rows]")
-    if inv_freq.dtype != torch.float32 or inv_freq.shape != (head_dim // 2,):
-        raise ValueError("inv_freq: expected fp32 [head_dim / 2]")
-    if q_scale.dtype != torch.float32 or q_scale.dim() != 1:
-        raise ValueError("q_scale: expected fp32 [n_q_heads * head_dim]")
+    vector(q_scale, "q_scale", torch.float32)
+    if q_scale.shape[0] == 0 or q_scale.shape[0] % head_dim:
+        raise ValueError("q_scale: its length must be n_q_heads * head_dim")
+    nq = q_scale.shape[0] // head_dim
+    if q.shape[1] < nq * head_dim:
+        raise ValueError("q: must hold n_q_heads * head_dim columns")
+    nk = 0
+    if k is not None:
+        rows_tensor(k, "k")
+        if k.shape[0] != rows:
+            raise ValueError(f"k: expected {rows} rows like q, got {k.shape[0]}")
+        if k.shape[1] % head_dim:
+            raise ValueError("k: its width must be a whole number of heads")
+        nk = k.shape[1] // head_dim
+    elif k_out is not None:
+        raise ValueError("k_out: given without k")
+    vector(positions, "positions", torch.int32, rows)
+    vector(inv_freq, "inv_freq", torch.float32, head_dim // 2)
+    if q_out is not None:
+        rows_tensor(q_out, "q_out")
+        if q_out.shape[0] != rows or q_out.shape[1] < nq * head_dim:
+            raise ValueError(f"q_out: expected [{rows}, >= {nq * head_dim}]")
+    if k_out is not None:
+        rows_tensor(k_out, "k_out")
+        if k_out.shape[0] != rows or k_out.shape[1] < nk * head_dim:
+            raise ValueError(f"k_out: expected [{rows}, >= {nk * head_dim}]")
+    tensors = [("q", q), ("k", k), ("positions", positions), ("inv_freq", inv_freq),
+               ("q_scale", q_scale), ("q_out", q_out), ("k_out", k_out)]
+    for name, t in tensors:
+        if t is not None and (t.device.type != "cuda" or t.device != q.device):
+            raise ValueError(f"{name}: must be on the HIP device of q")
     if q_out is None:
         q_out = torch.empty(rows, nq * head_dim, dtype=q.dtype, device=q.device)
     if k is not None and k_out is None:

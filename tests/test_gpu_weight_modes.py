@@ -126,6 +126,33 @@ def test_scalar_gain_on_the_transformer_workload(B):
         assert abs(got - exact) <= 2e-6 * abs(exact) + 2.0 ** -16 * mag, (i, got, exact)
 
 
+def test_scalar_gain_backward_on_a_side_stream(B):
+    """On a stream other than the current one, a scalar gain's temporary row
+    shares belong to that stream: the results equal the default stream's bit
+    for bit, also when the current stream allocates and writes memory while
+    the side stream's kernels still run."""
+    import torch
+    case = inputs.make("rownorm_gain_bwd_12x4_d768")
+    announce("rownorm scalar gains on a side stream")
+    ws = [dev_f32(w) for w in case.w]
+    gs = [dev_f32(g[:1]).reshape(()) for g in case.gain]
+    des = [dev_bits(d) for d in case.dwe]
+    dw0, dg0 = B.ds_weight_rownorm_gain_backward(ws, gs, des, case.radius)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for handle in (side, side.cuda_stream):
+        side.wait_stream(torch.cuda.current_stream())
+        dw1, dg1 = B.ds_weight_rownorm_gain_backward(ws, gs, des, case.radius, stream=handle)
+        # current-stream work that would reuse a freed block at once
+        junk = [torch.full((w.shape[0],), float("nan"), device="cuda:0") for w in case.w]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        del junk
+        for i in range(len(ws)):
+            assert torch.equal(dw1[i], dw0[i]), i
+            assert torch.equal(dg1[i], dg0[i]), (i, dg1[i].item(), dg0[i].item())
+
+
 # ------------------------------------------------ widths not a multiple of 4
 
 from test_gpu_backward import check_rn, run_rn                       # noqa: E402
