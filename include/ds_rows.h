@@ -43,6 +43,10 @@
  *                         with its component along the row removed; the gain's
  *                         gradient follows by the chain rule through W_eff.
  *                         Both for a ragged batch in one call.
+ *  ds_weight_rownorm_gain_backward_noalloc
+ *                         the same gradients for callers that cannot allocate
+ *                         device memory (graph capture, serving loops): a
+ *                         scalar gain's row shares in a fixed library array.
  *
  * Numerics.  bf16 values are passed as their 16-bit patterns; every rounding
  * to bf16 is to nearest, ties to even.  Sums of squares accumulate in fp32
@@ -88,10 +92,13 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10701          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10800          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 #define DS_MAX_ELEM_COLS 16384         /* widest fp32 weight row whose width is
                                           not a multiple of 4 */
+#define DS_SCRATCH_FLOATS 1048576      /* fp32 values of the fixed device scratch
+                                          each GPU holds for the allocation-free
+                                          entry point (4 MiB) */
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
 typedef void* ds_stream_t;
@@ -112,9 +119,11 @@ enum {
   DS_ERR_LAUNCH = -6,  /* the HIP runtime reported an error for the launch,
                           the copy or the stream */
   DS_ERR_DEVICE = -7,  /* no usable HIP device */
-  DS_ERR_CAPTURE = -8  /* a ragged weight call on a capturing stream with more
+  DS_ERR_CAPTURE = -8, /* a ragged weight call on a capturing stream with more
                           than 48 matrices of one width (see
                           ds_weight_rownorm_gain) */
+  DS_ERR_SCRATCH = -9  /* an allocation-free call needs more of the library's
+                          fixed scratch than DS_SCRATCH_FLOATS */
 };
 
 /*
@@ -414,6 +423,34 @@ typedef struct ds_rownorm_grad_desc {
  */
 int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,
                                     ds_stream_t stream);
+
+/*
+ * ds_weight_rownorm_gain_backward_noalloc -- ds_weight_rownorm_gain_backward
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc.
+ *
+ * Same gradients, bit for bit, as ds_weight_rownorm_gain_backward on the same
+ * descriptors, with two differences:
+ *   - a DS_GAIN_SCALAR matrix's per-row shares are kept in a fixed device
+ *     array the library holds per GPU (DS_SCRATCH_FLOATS fp32 values, 4 MiB,
+ *     taken on the first call on a device and held until the process ends),
+ *     not in a caller buffer: its descriptor's dgain must be NULL (else
+ *     DS_ERR_ARG).  The scalar-gain matrices of one call may hold at most
+ *     DS_SCRATCH_FLOATS rows together, else DS_ERR_SCRATCH (nothing
+ *     enqueued); split larger calls;
+ *   - every launch carries its matrix table in the kernel arguments (a width
+ *     class of more than 48 matrices becomes several launches), so the call
+ *     never stages a table and never returns DS_ERR_ALLOC or DS_ERR_CAPTURE.
+ * The call allocates nothing (no hipMalloc, hipHostMalloc or hipFree) and
+ * enqueues no memset; every share is written before it is read.
+ *
+ * All calls on one GPU share that GPU's scratch array: two calls whose
+ * kernels may run at the same time on one GPU (different streams, no
+ * ordering between them) race on it and their dgain_total values are
+ * undefined.  Order such calls on one stream or with events.
+ */
+int ds_weight_rownorm_gain_backward_noalloc(const ds_rownorm_grad_desc* descs, int32_t n,
+                                            ds_stream_t stream);
 
 /*
  * One weight matrix of a rescale-method call.

@@ -29,6 +29,8 @@ DS_ERR_ALLOC = -5
 DS_ERR_LAUNCH = -6
 DS_ERR_DEVICE = -7
 DS_ERR_CAPTURE = -8
+DS_ERR_SCRATCH = -9
+DS_SCRATCH_FLOATS = 1 << 20
 
 
 class RownormDesc(ctypes.Structure):
@@ -118,9 +120,9 @@ def lib() -> ctypes.CDLL:
         for name in ("ds_l2_rows_backward", "ds_rms_rows_backward"):
             getattr(L, name).argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
             getattr(L, name).restype = ctypes.c_int
-        L.ds_weight_rownorm_gain_backward.argtypes = [ctypes.POINTER(RownormGradDesc),
-                                                      ctypes.c_int32, vp]
-        L.ds_weight_rownorm_gain_backward.restype = ctypes.c_int
+        for name in ("ds_weight_rownorm_gain_backward", "ds_weight_rownorm_gain_backward_noalloc"):
+            getattr(L, name).argtypes = [ctypes.POINTER(RownormGradDesc), ctypes.c_int32, vp]
+            getattr(L, name).restype = ctypes.c_int
         L.ds_status_string.argtypes = [ctypes.c_int]
         L.ds_status_string.restype = ctypes.c_char_p
         L.ds_version.argtypes = []
@@ -373,7 +375,8 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
                                     dw: Optional[Sequence] = None,
                                     dgain: Optional[Sequence] = None,
                                     want_dgain: bool = True, stream=None,
-                                    segs: Optional[Sequence] = None) -> Tuple[list, list]:
+                                    segs: Optional[Sequence] = None,
+                                    _noalloc: bool = False) -> Tuple[list, list]:
     """Per matrix: dL/dW (fp32) and dL/dg (fp32) from dL/dW_eff (bf16), in one call.
 
     ``gains`` and ``segs`` as for ds_weight_rownorm_gain.  Returns (dws, dgains): dL/dg is
@@ -419,10 +422,11 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
     # A scalar gain's per-row shares: a temporary the kernels write and read
     # on the launch stream.  It is allocated on that stream, so when it is
     # dropped below, the caching allocator hands its block only to work
-    # ordered after those kernels.
+    # ordered after those kernels.  (The allocation-free entry point keeps
+    # them in the library's own scratch instead.)
     with torch.cuda.device(dev), torch.cuda.stream(_torch_stream(ws[0], stream)):
         shares = [torch.empty(lay[i][0], dtype=torch.float32, device=dev)
-                  if m == DS_GAIN_SCALAR and dgain[i] is not None else None
+                  if m == DS_GAIN_SCALAR and dgain[i] is not None and not _noalloc else None
                   for i, m in enumerate(modes)]
     descs = (RownormGradDesc * n)()
     for i, (w, g, de) in enumerate(zip(ws, gains, dw_effs)):
@@ -434,10 +438,26 @@ def ds_weight_rownorm_gain_backward(ws: Sequence, gains: Sequence, dw_effs: Sequ
                                    None if per_row is None else per_row.data_ptr(),
                                    rows, cols, modes[i],
                                    None if total is None else total.data_ptr(), seg, ld)
+    name = "ds_weight_rownorm_gain_backward" + ("_noalloc" if _noalloc else "")
     with torch.cuda.device(dev):
-        st = lib().ds_weight_rownorm_gain_backward(descs, n, _stream_of(ws[0], stream))
-    _check(st, "ds_weight_rownorm_gain_backward")
+        st = getattr(lib(), name)(descs, n, _stream_of(ws[0], stream))
+    _check(st, name)
     return list(dw), list(dgain)
+
+
+def ds_weight_rownorm_gain_backward_noalloc(ws: Sequence, gains: Sequence, dw_effs: Sequence,
+                                            radius: Optional[Sequence[float]] = None,
+                                            dw: Optional[Sequence] = None,
+                                            dgain: Optional[Sequence] = None,
+                                            want_dgain: bool = True, stream=None,
+                                            segs: Optional[Sequence] = None
+                                            ) -> Tuple[list, list]:
+    """ds_weight_rownorm_gain_backward through the allocation-free entry point:
+    the library allocates nothing (a scalar gain's row shares live in its fixed
+    per-GPU scratch).  Pass ``dw`` and ``dgain`` to keep this wrapper from
+    allocating its outputs through torch."""
+    return ds_weight_rownorm_gain_backward(ws, gains, dw_effs, radius, dw, dgain, want_dgain,
+                                           stream, segs, _noalloc=True)
 
 
 def _col_vector(v, cols, like, name):

@@ -251,9 +251,14 @@ using RaggedLauncher = hipError_t (*)(Shape, const dsr::TaskArgs<Task>&, int, hi
 // larger launches share one table (tasks, then their first items as a
 // compact int32 array) staged through the ring and copied on the stream
 // first.
+//
+// With `inline_only` every launch carries its table in the kernel arguments:
+// a group of more than kInlineTasks matrices is split into launches of at
+// most that many, so the call touches no library memory (the ring is never
+// used).  A matrix's bits do not depend on the launch it lands in.
 template <class Task>
 int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLauncher<Task> launch,
-                  hipStream_t hs) {
+                  hipStream_t hs, bool inline_only = false) {
   if (mats.empty()) return DS_OK;
   std::map<int, std::vector<size_t>> classes;     // shape key -> indices into mats
   std::map<int, int64_t> class_items;
@@ -295,20 +300,24 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
       std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) {
         return mats[x].second.cols / mats[x].second.seg > mats[y].second.cols / mats[y].second.seg;
       });
-    Launch L{ls, table.size(), 0, 0};
-    int64_t items = 0;
-    for (size_t i : order) {
-      const int R = mats[i].first.rows_per_block();
-      Task t = mats[i].second;
-      t.item_begin = (int32_t)items;
-      t.shape = mats[i].first.key();
-      items += (t.rows + R - 1) / R;
-      if (items > INT32_MAX) return DS_ERR_SHAPE;
-      table.push_back(t);
-      ++L.ntasks;
+    const size_t per_launch = inline_only ? (size_t)dsr::kInlineTasks : order.size();
+    for (size_t first = 0; first < order.size(); first += per_launch) {
+      Launch L{ls, table.size(), 0, 0};
+      int64_t items = 0;
+      for (size_t k = first; k < std::min(order.size(), first + per_launch); ++k) {
+        const size_t i = order[k];
+        const int R = mats[i].first.rows_per_block();
+        Task t = mats[i].second;
+        t.item_begin = (int32_t)items;
+        t.shape = mats[i].first.key();
+        items += (t.rows + R - 1) / R;
+        if (items > INT32_MAX) return DS_ERR_SHAPE;
+        table.push_back(t);
+        ++L.ntasks;
+      }
+      L.nitems = (int)items;
+      launches.push_back(L);
     }
-    L.nitems = (int)items;
-    launches.push_back(L);
   }
 
   size_t staged_tasks = 0;
@@ -485,6 +494,7 @@ const char* ds_status_string(int status) {
     case DS_ERR_LAUNCH: return "DS_ERR_LAUNCH: the HIP runtime reported an error";
     case DS_ERR_DEVICE: return "DS_ERR_DEVICE: no usable HIP device";
     case DS_ERR_CAPTURE: return "DS_ERR_CAPTURE: a ragged weight call with more than 48 matrices of one width cannot be captured into a graph";
+    case DS_ERR_SCRATCH: return "DS_ERR_SCRATCH: the call needs more library scratch than DS_SCRATCH_FLOATS (1,048,576 scalar-gain rows)";
     default: return "unknown ds_rows status";
   }
 }
@@ -781,8 +791,42 @@ int ds_rms_rows_backward(const uint16_t* x, const uint16_t* r, const uint16_t* d
   return norm_rows_backward(dsr::launch_rms_rows_backward, x, r, dy, dx, rows, cols, eps, stream);
 }
 
-int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,
-                                    ds_stream_t stream) {
+namespace {
+
+// ------------------------------------------------------- library scratch
+//
+// The allocation-free weight gradient keeps a scalar gain's per-row shares
+// here instead of in a caller's buffer.  Each device holds its own copy of
+// the array until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory: host code uses only the address that
+// hipGetSymbolAddress returns for the current device, fetched once per device
+// and kept.  Every call on a device shares that device's array; it is
+// written (every share) before it is read, so nothing is cleared.
+
+__device__ __align__(256) float scratch[DS_SCRATCH_FLOATS];
+
+int scratch_for_current_device(float** out) {
+  static std::mutex mu;
+  static std::map<int, float*> ptrs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return DS_ERR_DEVICE;
+    it = ptrs.emplace(dev, static_cast<float*>(p)).first;
+  }
+  *out = it->second;
+  return DS_OK;
+}
+
+// The weight gradient.  `noalloc`: a scalar gain's shares go to the library
+// scratch (its descriptor's dgain must be NULL) and every launch carries its
+// table in the kernel arguments, so the call allocates nothing.
+int rownorm_backward_call(const ds_rownorm_grad_desc* descs, int32_t n, ds_stream_t stream,
+                          bool noalloc) {
   if (n < 0) return DS_ERR_ARG;
   if (n == 0) return DS_OK;
   if (descs == nullptr) return DS_ERR_NULL;
@@ -790,6 +834,9 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
   std::vector<Range> outs, ins;
   std::vector<std::pair<Shape, dsr::RownormGradTask>> mats;
   std::vector<dsr::TotalTask> totals;
+  std::vector<std::pair<size_t, int64_t>> scratch_users;   // (task in mats, offset in scratch)
+  std::vector<std::pair<size_t, int64_t>> scratch_totals;  // (entry in totals, offset)
+  int64_t scratch_used = 0;
   for (int32_t i = 0; i < n; ++i) {
     const ds_rownorm_grad_desc& d = descs[i];
     Shape s;
@@ -798,10 +845,13 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     int st = check_layout(d.rows, d.cols, d.seg, d.ld, &s, &a32, &a16, &span);
     if (st != DS_OK) return st;
     if (!std::isfinite(d.radius) || !gain_mode_ok(d.gain_mode)) return DS_ERR_ARG;
+    const bool shares_in_scratch = noalloc && d.gain_mode == DS_GAIN_SCALAR;
+    if (shares_in_scratch && d.dgain != nullptr) return DS_ERR_ARG;
     // a total needs a scalar gain and the per-row shares it sums (none for an
     // empty matrix); no gain, no gradient
     if (d.dgain_total != nullptr &&
-        (d.gain_mode != DS_GAIN_SCALAR || (d.dgain == nullptr && d.rows > 0)))
+        (d.gain_mode != DS_GAIN_SCALAR ||
+         (!shares_in_scratch && d.dgain == nullptr && d.rows > 0)))
       return DS_ERR_ARG;
     if (d.gain_mode == DS_GAIN_NONE && d.dgain != nullptr) return DS_ERR_ARG;
     if (d.rows == 0) {
@@ -827,7 +877,6 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     add_range(outs, d.dw, nel * 4);
     add_range(outs, d.dgain, (size_t)d.rows * 4);
     add_range(outs, d.dgain_total, 4);
-    if (d.dgain_total != nullptr) totals.push_back({d.dgain, d.dgain_total, d.rows});
     dsr::RownormGradTask t{};
     t.w = d.w;
     t.gain = gain;
@@ -840,11 +889,25 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     t.radius = d.radius;
     t.seg = d.seg;
     t.ld = d.ld;
+    if (shares_in_scratch && d.dgain_total != nullptr) {
+      if (d.rows > DS_SCRATCH_FLOATS - scratch_used) return DS_ERR_SCRATCH;
+      scratch_users.emplace_back(mats.size(), scratch_used);
+      scratch_totals.emplace_back(totals.size(), scratch_used);
+      scratch_used += d.rows;
+    }
+    if (d.dgain_total != nullptr) totals.push_back({d.dgain, d.dgain_total, d.rows});
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
+  if (!scratch_users.empty()) {
+    float* sp = nullptr;
+    int st = scratch_for_current_device(&sp);
+    if (st != DS_OK) return st;
+    for (auto& u : scratch_users) mats[u.first].second.dgain = sp + u.second;
+    for (auto& u : scratch_totals) totals[u.first].shares = sp + u.second;
+  }
   int st = launch_ragged<dsr::RownormGradTask>(mats, launch_rownorm_backward_any,
-                                               (hipStream_t)stream);
+                                               (hipStream_t)stream, noalloc);
   if (st != DS_OK) return st;
   if (!totals.empty()) {                          // (a call of empty matrices has no launch above)
     int cus = 0;
@@ -859,6 +922,18 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
     if (hipGetLastError() != hipSuccess) return DS_ERR_LAUNCH;
   }
   return DS_OK;
+}
+
+}  // namespace
+
+int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,
+                                    ds_stream_t stream) {
+  return rownorm_backward_call(descs, n, stream, false);
+}
+
+int ds_weight_rownorm_gain_backward_noalloc(const ds_rownorm_grad_desc* descs, int32_t n,
+                                            ds_stream_t stream) {
+  return rownorm_backward_call(descs, n, stream, true);
 }
 
 namespace {

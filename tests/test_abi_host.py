@@ -29,6 +29,7 @@ def test_exports_every_declared_function(L):
     names = B.header_functions()
     assert set(names) == {"ds_l2_rows", "ds_slerp_rows", "ds_weight_rownorm_gain",
                           "ds_l2_rows_backward", "ds_weight_rownorm_gain_backward",
+                          "ds_weight_rownorm_gain_backward_noalloc",
                           "ds_gate_l2_rows", "ds_swiglu_l2_rows", "ds_qk_rows_l2",
                           "ds_rescale_project", "ds_rescale_after_step",
                           "ds_rms_rows", "ds_rms_rows_backward",
@@ -38,8 +39,8 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10701
-    for code in range(0, -9, -1):
+    assert B.ds_version() == 10800
+    for code in range(0, -10, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s
     assert "unknown" in B.ds_status_string(42)
@@ -407,3 +408,55 @@ def test_binding_raises_on_missing_library(monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libdsrows.so")
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+# ------------------------------------------- the allocation-free weight gradient
+
+BIG = 1 << 36        # fake addresses far apart for matrices of a million rows
+
+
+def test_noalloc_validation(L):
+    g = L.ds_weight_rownorm_gain_backward_noalloc
+    tot = Bp + 8192
+    # w, gain, radius, dw_eff, dw, dgain, rows, cols, gain_mode, dgain_total
+    assert g(None, 0, None) == B.DS_OK
+    assert g(None, 1, None) == B.DS_ERR_NULL
+    # the shares live in the library's scratch: a scalar gain's dgain must be NULL
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR, tot)), 1,
+             None) == B.DS_ERR_ARG
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, Bp + 4096, 16, 64, B.DS_GAIN_SCALAR)), 1,
+             None) == B.DS_ERR_ARG
+    # the other checks are the allocating call's
+    assert g(_gdescs((A, Bp, 1.0, C, C + 65536, None, 16, 64, B.DS_GAIN_ROW, tot)), 1,
+             None) == B.DS_ERR_ARG
+    assert g(_gdescs((A, Bp, 1.0, C + 8, C + 65536, None, 16, 64)), 1, None) == B.DS_ERR_ALIGN
+
+
+def _big_scalar(i, rows):
+    base = (i + 1) * BIG
+    # w, gain, radius, dw_eff, dw, dgain, rows, cols, gain_mode, dgain_total
+    return (base, base + BIG // 2, 1.0, base + BIG // 4, base + 3 * BIG // 4, None, rows, 8,
+            B.DS_GAIN_SCALAR, base + BIG // 2 + 64)
+
+
+def test_noalloc_scratch_limit(L):
+    g = L.ds_weight_rownorm_gain_backward_noalloc
+    n = B.DS_SCRATCH_FLOATS
+    assert g(_gdescs(_big_scalar(0, n + 1)), 1, None) == B.DS_ERR_SCRATCH
+    # the limit is over the call's scalar-gain rows together
+    assert g(_gdescs(_big_scalar(0, n // 2), _big_scalar(1, n // 2 + 1)), 2,
+             None) == B.DS_ERR_SCRATCH
+    # rows with a gain per row need no scratch
+    per_row = (5 * BIG, 5 * BIG + BIG // 2, 1.0, 5 * BIG + BIG // 4, 5 * BIG + 3 * BIG // 4,
+               5 * BIG + BIG // 2 + 4 * n + 64, n, 8)
+    st = g(_gdescs(_big_scalar(0, n), per_row), 2, None)
+    assert st != B.DS_ERR_SCRATCH and st != B.DS_ERR_ARG
+    assert "DS_SCRATCH_FLOATS" in B.ds_status_string(B.DS_ERR_SCRATCH)
+
+
+@pytest.mark.skipif("not no_device()")
+def test_noalloc_valid_args_reach_device_lookup(L):
+    g = L.ds_weight_rownorm_gain_backward_noalloc
+    n = B.DS_SCRATCH_FLOATS
+    assert g(_gdescs(_big_scalar(0, n)), 1, None) == B.DS_ERR_DEVICE
+    assert g(_gdescs(_big_scalar(0, n // 2), _big_scalar(1, n // 2)), 2, None) == B.DS_ERR_DEVICE
