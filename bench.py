@@ -39,7 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
 KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
                   "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip",
                   "inst_qk.hip", "inst_rescale.hip", "inst_rms.hip", "inst_rms_bwd.hip",
-                  "colblock_kernels.hpp", "inst_colblock.hip", "ds_rows.hip"]
+                  "colblock_kernels.hpp", "inst_colblock.hip", "ds_rows.hip", "bench_stream.hip"]
 
 
 def kernel_hash() -> str:
@@ -181,6 +181,19 @@ def main():
     l2_us = batch_us(l2)
     sl_us = batch_us(slerp)
 
+    # the achievable-bandwidth reference: a plain read-2-write-1 stream with
+    # l2_rows' launch (shape, grid, buffer resources, cache hints), y = x ^ r,
+    # over the same rotating buffers (libdsbench.so, built beside the library)
+    BL = ctypes.CDLL(B.LIB_PATH.replace("libdsrows.so", "libdsbench.so"))
+    BL.dsb_stream_rows.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]
+    BL.dsb_stream_rows.restype = ctypes.c_int
+
+    def stream_ref(s):
+        return BL.dsb_stream_rows(s["x"].data_ptr(), s["r"].data_ptr(), s["y"].data_ptr(),
+                                  ROWS, COLS, sp)
+
+    st_us = batch_us(stream_ref)
+
     l2_bytes = ROWS * COLS * 2 * 3                      # x, r read; y written
     sl_bytes = ROWS * COLS * 2 * 3 + COLS * 4           # res, out read; h written; alpha once
     step_bytes = l2_bytes + sl_bytes
@@ -192,7 +205,11 @@ def main():
                 "rows_per_s": round(rows / (us * 1e-6), 1), "bytes": nbytes}
 
     ops = {"l2_rows_res_8192x4096": op(l2_us, l2_bytes, ROWS),
-           "slerp_rows_8192x4096": op(sl_us, sl_bytes, ROWS)}
+           "slerp_rows_8192x4096": op(sl_us, sl_bytes, ROWS),
+           "stream_ceiling_8192x4096": op(st_us, l2_bytes, ROWS)}
+    ops["stream_ceiling_8192x4096"]["note"] = (
+        "stream_rows_kernel: y = x ^ r with l2_rows' launch shape, grid and cache hints "
+        "(reads 2, writes 1): the rate a kernel of this shape reaches with no arithmetic")
 
     # ---- the weight op, rotating 3 copies of the 48 matrices (3 x 510 MB)
     rn = inputs.make("rownorm_gain_12x4_d768")
@@ -461,7 +478,10 @@ def main():
     roofline = {"bound": "hbm", "kernel": kname, "achieved": d["GBps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": d["frac"],
                 "traffic": traffic_for(kname),
-                "algorithmic_bytes_per_launch": d["bytes"]}
+                "algorithmic_bytes_per_launch": d["bytes"],
+                "stream_ceiling": {"kernel": "stream_rows_kernel",
+                                   "GBps": ops["stream_ceiling_8192x4096"]["GBps"],
+                                   "frac": ops["stream_ceiling_8192x4096"]["frac"]}}
 
     result = {
         "metric": "achieved HBM GB/s (% of peak) for bf16 l2_rows/slerp_rows at 8192x4096",

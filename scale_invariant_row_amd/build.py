@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libdsrows.so")
+# the benchmark's stream reference (not part of the row library's ABI)
+BENCH_LIB = os.path.join(LIBDIR, "libdsbench.so")
+BENCH_SOURCES = ["bench_stream.hip"]
 SOURCES = ["ds_rows.hip", "inst_l2.hip", "inst_slerp.hip", "inst_rownorm.hip",
            "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip", "inst_qk.hip",
            "inst_rescale.hip", "inst_rms.hip", "inst_rms_bwd.hip", "inst_colblock.hip"]
@@ -54,13 +57,14 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Build libdsrows.so and the benchmark's libdsbench.so; returns the former."""
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     cc = hipcc()
-    objs, cmds = [], []
-    for src in SOURCES:
+    objs, cmds = {}, []
+    for src in SOURCES + BENCH_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
+        objs[src] = obj
         cmds.append([cc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(_run, cmds))
@@ -69,11 +73,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             print(out)
         if rc != 0:
             raise RuntimeError(f"hipcc failed ({rc}): {' '.join(cmd)}\n{out}")
-    tmp = LIB + ".tmp"
-    rc, out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
-    if rc != 0:
-        raise RuntimeError(f"link failed ({rc}):\n{out}")
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (BENCH_LIB, BENCH_SOURCES)):
+        tmp = lib + ".tmp"
+        rc, out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-o", tmp,
+                        *[objs[s] for s in srcs]])
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}):\n{out}")
+        os.replace(tmp, lib)
     return LIB
 
 

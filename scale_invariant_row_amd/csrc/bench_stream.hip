@@ -1,0 +1,78 @@
+// A plain read-2-write-1 stream over bf16 rows: the benchmark's reference
+// for the bandwidth a kernel of l2_rows' launch shape can reach on this GPU.
+// It has the same shape policy, grid, row-to-wave mapping, buffer resources
+// and cache hints as l2_rows_kernel.  Where l2_rows normalises, it does one
+// bitwise op per dword (y = x ^ r), so what remains is the memory traffic.
+//
+// Built into its own library (libdsbench.so) for bench.py; it is not part of
+// the row library or its C ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "launch.hpp"
+#include "row_kernels.hpp"
+
+namespace dsr {
+
+template <int G, int V>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+stream_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int nvec) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  int off[V];
+  geo.offsets(off, 16);
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
+    const int64_t row = base + geo.rr;
+    if (G == 1 && row >= rows) break;
+    Bf16Row<V> a, b;
+    a.load(RowBuf(x + row * nvec, row_bytes), off);
+    b.load(RowBuf(r + row * nvec, row_bytes), off);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a.p[v][k] ^= b.p[v][k];
+    a.store(RowBuf(y + row * nvec, row_bytes), off);
+  }
+}
+
+template <int G, int V>
+static hipError_t run(const void* x, const void* r, void* y, int64_t rows, int nvec, int grid,
+                      hipStream_t stream) {
+  stream_rows_kernel<G, V><<<grid, Geo<G>::THREADS, 0, stream>>>(
+      (const u32x4_t*)x, (const u32x4_t*)r, (u32x4_t*)y, rows, nvec);
+  return hipGetLastError();
+}
+
+}  // namespace dsr
+
+// y = x ^ r over [rows, cols] bf16 rows (cols a multiple of 8, up to 8,192),
+// with the launch l2_rows would use.  Returns 0, or -1 for an unsupported
+// width, -2 for a runtime error.
+extern "C" int dsb_stream_rows(const void* x, const void* r, void* y, int64_t rows,
+                               int64_t cols, void* stream) {
+  using namespace dsr;
+  if (rows < 0 || cols < 8 || cols > 8192 || cols % 8 != 0) return -1;
+  if (rows == 0) return 0;
+  const int nvec = (int)(cols / 8);
+  const Shape s = pick_bf16_shape(nvec);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -2;
+  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * 64));
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  switch (s.G * 100 + s.V) {
+    case 101: e = run<1, 1>(x, r, y, rows, nvec, grid, hs); break;
+    case 102: e = run<1, 2>(x, r, y, rows, nvec, grid, hs); break;
+    case 202: e = run<2, 2>(x, r, y, rows, nvec, grid, hs); break;
+    case 402: e = run<4, 2>(x, r, y, rows, nvec, grid, hs); break;
+    case 403: e = run<4, 3>(x, r, y, rows, nvec, grid, hs); break;
+    case 404: e = run<4, 4>(x, r, y, rows, nvec, grid, hs); break;
+    default: return -1;
+  }
+  return e == hipSuccess ? 0 : -2;
+}
