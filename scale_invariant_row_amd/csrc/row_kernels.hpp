@@ -913,13 +913,14 @@ act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
 // packed dword gives every lane both halves -- and two heads go through the
 // wave at a time (a wave step).  The row's q steps followed by its k steps
 // are split into two contiguous halves, one per wave; each head's arithmetic
-// is the same whichever wave runs it.  A lane's NV frequencies are the same
-// for every head of the row, so each wave computes cos and sin once per row
-// (the device library's sincosf, with its full-range argument reduction) and
-// reuses them for all its heads.  Heads are loaded CH wave steps at a time to
-// keep several loads in flight.  The kernel is bound by load latency, not by
-// its arithmetic: with the trigonometry stubbed out it ran only ~1 us faster
-// (of ~43).  For 8,192 rows of 16 + 4 heads of 256, the second wave per row
+// is the same whichever wave runs it.  A row has HD/2 distinct angles, the
+// same for every head: the row's two waves evaluate them once between them,
+// one per lane (the device library's sincosf, with its full-range argument
+// reduction, of the fp32 product pos * inv), and put them in LDS; after a
+// barrier every lane reads its NV cosines and sines (a lane would otherwise
+// evaluate NV of them itself, and every angle is needed by 8 lanes of the
+// row).  Heads are loaded CH wave steps at a time to keep several loads in
+// flight.  For 8,192 rows of 16 + 4 heads of 256, the second wave per row
 // took it from 40.4 to 37.5 us, and 16-byte lanes (half the wave steps and
 // per-head sums) from there to 34.8 us.
 
@@ -986,13 +987,15 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
   const bool upper = ll >= L / 2;        // holds the second half of the head
   const int e0 = (upper ? HD / 2 : 0) + NV * (ll % (L / 2));   // first element of the lane
   const int f0 = NV * (ll % (L / 2));                          // first frequency of the lane
-  const RowBuf fb(a.inv_freq, (uint32_t)(HD / 2) * 4u);
-  float invf[NV];
-#pragma unroll
-  for (int q4 = 0; q4 < NV / 4; ++q4) {
-    const f32x4_t v = fb.ld16f_cached((f0 + 4 * q4) * 4);
-    invf[4 * q4] = v.x; invf[4 * q4 + 1] = v.y; invf[4 * q4 + 2] = v.z; invf[4 * q4 + 3] = v.w;
-  }
+  // the angle this lane evaluates for its row: frequency part * NF/2 + lane
+  constexpr int NF = HD / 2;
+  const int fi = part * (NF / 2) + lane;
+  const bool evaluates = lane < NF / 2;
+  const float invf = evaluates ? a.inv_freq[fi] : 0.f;
+  // per row of the workgroup: cos then sin of its NF angles; two buffers,
+  // alternated per row, so one barrier per row orders the writes and reads
+  __shared__ __attribute__((aligned(16))) float trig[2][kQkRowsPerBlock][2][NF];
+  int buf = 0;
   const RowBuf sb(a.q_scale, (uint32_t)a.nq * (uint32_t)HD * 4u);
   const int nsteps[2] = {(a.nq + HPW - 1) / HPW, (a.nk + HPW - 1) / HPW};
   // this wave's steps: [first, last) of q's then k's, as a range in each
@@ -1001,12 +1004,30 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
   const int lo[2] = {min(first, nsteps[0]), max(0, min(first - nsteps[0], nsteps[1]))};
   const int hi[2] = {min(last, nsteps[0]), max(0, min(last - nsteps[0], nsteps[1]))};
 
-  for (int64_t row = (int64_t)blockIdx.x * kQkRowsPerBlock + rsub; row < a.rows;
-       row += (int64_t)gridDim.x * kQkRowsPerBlock) {
-    const float pf = (float)a.pos[row];
+  // every wave runs every iteration (the barrier is workgroup-wide); a wave
+  // whose row is past the end only takes part in the barrier
+  for (int64_t base = (int64_t)blockIdx.x * kQkRowsPerBlock; base < a.rows;
+       base += (int64_t)gridDim.x * kQkRowsPerBlock) {
+    const int64_t row = base + rsub;
+    const bool valid = row < a.rows;
+    float(&cs)[2][NF] = trig[buf][rsub];
+    buf ^= 1;
+    if (valid && evaluates) {
+      float sv, cv;
+      sincosf((float)a.pos[row] * invf, &sv, &cv);
+      cs[0][fi] = cv;
+      cs[1][fi] = sv;
+    }
+    __syncthreads();
+    if (!valid) continue;
     float c[NV], s[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) sincosf(pf * invf[j], &s[j], &c[j]);
+    for (int q4 = 0; q4 < NV / 4; ++q4) {
+      const f32x4_t cv = *reinterpret_cast<const f32x4_t*>(&cs[0][f0 + 4 * q4]);
+      const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(&cs[1][f0 + 4 * q4]);
+      c[4 * q4] = cv.x; c[4 * q4 + 1] = cv.y; c[4 * q4 + 2] = cv.z; c[4 * q4 + 3] = cv.w;
+      s[4 * q4] = sv.x; s[4 * q4 + 1] = sv.y; s[4 * q4 + 2] = sv.z; s[4 * q4 + 3] = sv.w;
+    }
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       const int nh = which == 0 ? a.nq : a.nk;
