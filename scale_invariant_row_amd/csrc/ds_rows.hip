@@ -628,7 +628,7 @@ int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, co
   const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
   (void)hipGetLastError();
   return launch_status(dsr::launch_swiglu_l2_rows(s, g, u, sug, suu, y, rows, (int)(cols / 8),
-                                                  eps, grid_for(units, cus),
+                                                  eps, grid_for(units, cus), cus,
                                                   (hipStream_t)stream));
 }
 

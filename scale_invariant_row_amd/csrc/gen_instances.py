@@ -297,11 +297,38 @@ hipError_t launch_gate_l2_rows(Shape s, const void* o, const void* g, const floa
   }
 }
 
+// SwiGLU: with at least kSiluTableRows rows per resident workgroup, a grid of
+// the resident workgroups (each filling the silu table once, then looping
+// over its rows); otherwise one workgroup per row group and the formula.
+// The two give the same bits.
+template <int G, int V>
+static hipError_t run_swiglu(const void* g, const void* u, const float* sug, const float* suu,
+                             void* y, int64_t rows, int nvec, float eps, int grid, int cus,
+                             hipStream_t stream) {
+  constexpr int T = Geo<G>::THREADS;
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, swiglu_table_l2_rows_kernel<G, V>, T, 0) != hipSuccess)
+      n = 0;
+    return n;
+  }();
+  const int64_t units = (rows + Geo<G>::R - 1) / Geo<G>::R;
+  const int64_t resident = (int64_t)cus * per_cu;
+  if (per_cu > 0 && units >= (int64_t)kSiluTableRows * resident) {
+    swiglu_table_l2_rows_kernel<G, V><<<(int)resident, T, 0, stream>>>(
+        (const u32x4_t*)g, (const u32x4_t*)u, (const f32x4_t*)sug, (const f32x4_t*)suu,
+        (u32x4_t*)y, rows, nvec, eps);
+    return hipGetLastError();
+  }
+  return run<G, V, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);
+}
+
 hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const float* sug,
                                  const float* suu, void* y, int64_t rows, int nvec, float eps,
-                                 int grid, hipStream_t stream) {
+                                 int grid, int cus, hipStream_t stream) {
   switch (s.G * 100 + s.V) {
-''' + cases(actsh, "return run<{G}, {V}, Act::kSwiglu>(g, u, sug, suu, y, rows, nvec, eps, grid, stream);") + '''
+''' + cases(actsh, "return run_swiglu<{G}, {V}>(g, u, sug, suu, y, rows, nvec, eps, grid, cus, stream);") + '''
     default: return hipErrorInvalidValue;
   }
 }

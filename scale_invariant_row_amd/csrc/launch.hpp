@@ -132,7 +132,7 @@ hipError_t launch_gate_l2_rows(Shape s, const void* o, const void* g, const floa
                                int64_t rows, int nvec, float eps, int grid, hipStream_t stream);
 hipError_t launch_swiglu_l2_rows(Shape s, const void* g, const void* u, const float* sug,
                                  const float* suu, void* y, int64_t rows, int nvec, float eps,
-                                 int grid, hipStream_t stream);
+                                 int grid, int cus, hipStream_t stream);
 hipError_t launch_rescale_project(Shape s, const TaskArgs<RescaleTask>& args, int grid,
                                   hipStream_t stream);
 hipError_t launch_rescale_after_step(Shape s, const TaskArgs<RescaleTask>& args, int grid,

@@ -775,6 +775,24 @@ __device__ __forceinline__ float exp_split(float x) {
   return __builtin_isfinite(r) ? r : e0;
 }
 
+// silu(a) = a / (1 + exp(-a)) in fp32 with IEEE division.
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + exp_split(-a)); }
+
+// The SwiGLU silu table.  SwiGLU's silu input a = bf16(g * sug) is a bf16
+// value, so silu(a) can come from a table instead of the exp, the add and
+// the division.  A workgroup that loops over many rows fills one table in
+// LDS and reuses it: silu(a) for the 8,192 bf16 values whose exponent field
+// lies in [kSiluE0, kSiluE0 + 31] (magnitudes 2^-25 up to 2^7, both signs),
+// entry (sign << 12) | ((bits & 0x7fff) - (kSiluE0 << 7)).  Each entry is
+// computed by silu_f32, the code of the formula path, so a lookup returns
+// the bits the formula does.  Any other a (zero, tiny, huge, infinite, NaN)
+// takes the formula.
+constexpr uint32_t kSiluE0 = 102;
+constexpr uint32_t kSiluBase = kSiluE0 << 7;
+constexpr int kSiluEntries = 8192;
+// rows a resident workgroup must have to fill a table (measured)
+constexpr int kSiluTableRows = 2;
+
 // The fp32 column scales of this lane's columns: NV vectors of 8 values per
 // 16-byte row vector; held in VGPRs when the shape is narrow, else re-read
 // (from L2) next to each row.
@@ -801,10 +819,10 @@ struct ColScales {
 
 // One row vector's 8 outputs of the prologue, packed: x0 and x1 hold the two
 // input rows' packed values (o, g for the gate; g, u for SwiGLU).
-template <Act A>
+template <Act A, bool TABLE = false>
 __device__ __forceinline__ void act_prologue(uint32_t (&out)[4], const uint32_t (&x0)[4],
                                              const uint32_t (&x1)[4], const float* s0,
-                                             const float* s1) {
+                                             const float* s1, const float* tab = nullptr) {
   float sig[8];
   if constexpr (A == Act::kGate) {
     // sigmoid(g * sg) = 1 / b, b = 1 + exp(-g sg) in [1, +inf] or NaN: the
@@ -829,52 +847,84 @@ __device__ __forceinline__ void act_prologue(uint32_t (&out)[4], const uint32_t 
       for (int j = 0; j < 8; ++j) sig[j] = 1.0f / b[j];
     }
   }
+  if constexpr (A == Act::kGate) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float r[2];
-    if constexpr (A == Act::kGate) {
+    for (int k = 0; k < 4; ++k) {
+      float r[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         r[h] = (h ? bf_hi(x0[k]) : bf_lo(x0[k])) * sig[2 * k + h];   // o * sigmoid, rounded below
-    } else {
-      // a = bf16(g * sug) and b = bf16(u * suu), both elements of the pair at once
+      out[k] = pack_bf16(r[0], r[1]);
+    }
+  } else {
+    // a = bf16(g * sug) and b = bf16(u * suu), both elements of a pair at once
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
       const uint32_t ap = pack_bf16(bf_lo(x0[k]) * s0[2 * k], bf_hi(x0[k]) * s0[2 * k + 1]);
       const uint32_t bp = pack_bf16(bf_lo(x1[k]) * s1[2 * k], bf_hi(x1[k]) * s1[2 * k + 1]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float a = h ? bf_hi(ap) : bf_lo(ap);
-        const float b = h ? bf_hi(bp) : bf_lo(bp);
-        const float silu = a / (1.0f + exp_split(-a));
-        r[h] = silu * b;                                  // rounded below
+      float sl, sh;
+      const uint32_t ilo = (ap & 0x7fffu) - kSiluBase, ihi = ((ap >> 16) & 0x7fffu) - kSiluBase;
+      // a value outside the table sends the wave's pair to the formula (a
+      // wave-uniform branch)
+      if (!TABLE || __builtin_amdgcn_ballot_w64((ilo >= 4096u) | (ihi >= 4096u)) != 0) {
+        sl = silu_f32(bf_lo(ap));
+        sh = silu_f32(bf_hi(ap));
+      } else {
+        sl = tab[ilo | ((ap >> 3) & 0x1000u)];
+        sh = tab[ihi | ((ap >> 19) & 0x1000u)];
       }
+      out[k] = pack_bf16(sl * bf_lo(bp), sh * bf_hi(bp));   // silu(a) b, rounded
     }
-    out[k] = pack_bf16(r[0], r[1]);
   }
 }
 
-template <int G, int V, Act A>
-__global__ void __launch_bounds__(Geo<G>::THREADS)
-act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
-                   const f32x4_t* sc1, u32x4_t* y, int64_t rows, int nvec, float eps) {
+// TABLE (SwiGLU only): fill the silu table first; the launcher then runs a
+// grid of resident workgroups, each looping over several rows.
+template <int G, int V, Act A, bool TABLE>
+__device__ __forceinline__ void act_rows(const u32x4_t* in0, const u32x4_t* in1,
+                                         const f32x4_t* sc0, const f32x4_t* sc1, u32x4_t* y,
+                                         int64_t rows, int nvec, float eps) {
+  static_assert(!TABLE || A == Act::kSwiglu, "the table holds silu");
   constexpr int R = Geo<G>::R;
   constexpr int NS = (A == Act::kGate) ? 1 : 2;
   const Geo<G> geo;
   __shared__ GroupScratch<G> gs;
-  int slot = 0;
+  __shared__ float tab[TABLE ? kSiluEntries : 1];
   int off[V];
   geo.offsets(off, 16);
   const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  Bf16Row<V> t, q;
+  bool loaded = false;
+  int64_t base = (int64_t)blockIdx.x * R;
+  if constexpr (TABLE) {
+    // the first row's loads go out before the table is filled, so the fill
+    // runs while they are in flight
+    const int64_t row = base + geo.rr;
+    if (row < rows) {
+      t.load(RowBuf(in0 + row * nvec, row_bytes), off);
+      q.load(RowBuf(in1 + row * nvec, row_bytes), off);
+      loaded = true;
+    }
+    for (int i = (int)threadIdx.x; i < kSiluEntries; i += Geo<G>::THREADS) {
+      const uint32_t bits = ((uint32_t)(i >> 12) << 15) | (kSiluBase + (uint32_t)(i & 4095));
+      tab[i] = silu_f32(__uint_as_float(bits << 16));
+    }
+    __syncthreads();
+  }
+  int slot = 0;
   const RowBuf sb0(sc0, row_bytes * 2u);                        // cols fp32 = 2 x row bytes
   const RowBuf sb1(NS == 2 ? sc1 : sc0, row_bytes * 2u);
   ColScales<V, NS> cs;
   cs.init(sb0, sb1, off);
 
-  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
+  for (; base < rows; base += (int64_t)gridDim.x * R) {
     const int64_t row = base + geo.rr;
     if (G == 1 && row >= rows) break;
-    Bf16Row<V> t, q;
-    t.load(RowBuf(in0 + row * nvec, row_bytes), off);
-    q.load(RowBuf(in1 + row * nvec, row_bytes), off);
+    if (!loaded) {
+      t.load(RowBuf(in0 + row * nvec, row_bytes), off);
+      q.load(RowBuf(in1 + row * nvec, row_bytes), off);
+    }
+    loaded = false;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       float tmp[NS][8];
@@ -886,7 +936,7 @@ act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
       const float* s0 = ColScales<V, NS>::kHeld ? cs.c[ColScales<V, NS>::kHeld ? v : 0][0] : tmp[0];
       const float* s1 = ColScales<V, NS>::kHeld ? cs.c[ColScales<V, NS>::kHeld ? v : 0][NS - 1]
                                                 : tmp[NS - 1];
-      act_prologue<A>(t.p[v], t.p[v], q.p[v], s0, s1);
+      act_prologue<A, TABLE>(t.p[v], t.p[v], q.p[v], s0, s1, tab);
     }
     float S[1] = {wave_sum(t.sumsq())};
     t.fence();
@@ -894,6 +944,21 @@ act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
     l2_in_place<G, V>(t, S[0], eps, gs, slot, geo);
     t.store(RowBuf(y + row * nvec, row_bytes), off);
   }
+}
+
+template <int G, int V, Act A>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+act_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
+                   const f32x4_t* sc1, u32x4_t* y, int64_t rows, int nvec, float eps) {
+  act_rows<G, V, A, false>(in0, in1, sc0, sc1, y, rows, nvec, eps);
+}
+
+// SwiGLU through the silu table (the launcher runs the resident workgroups).
+template <int G, int V>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+swiglu_table_l2_rows_kernel(const u32x4_t* in0, const u32x4_t* in1, const f32x4_t* sc0,
+                            const f32x4_t* sc1, u32x4_t* y, int64_t rows, int nvec, float eps) {
+  act_rows<G, V, Act::kSwiglu, true>(in0, in1, sc0, sc1, y, rows, nvec, eps);
 }
 
 // ----------------------------------------------------------------- q/k rows

@@ -192,3 +192,37 @@ def test_nonfinite(B):
     gv, wv = bf16_value(got), bf16_value(want)
     assert np.array_equal(np.isnan(gv), np.isnan(wv))
     assert np.array_equal(gv[2:], wv[2:]) or contract_bf16(got[2:], want[2:]).all()
+
+
+def test_swiglu_silu_table_equals_formula(B):
+    """Enough rows for the silu table (a grid of resident workgroups, each
+    filling the table once) give the bits of the formula path (the same rows
+    in calls of 37), also on vectors holding values outside the table: zero,
+    tiny, huge and infinite gate inputs, and NaN."""
+    import torch
+    rows, cols = 16384, 1024
+    c = inputs.swiglu_case(rows, cols, 1650)
+    g = c.a.copy()
+    rng = np.random.default_rng(1651)
+    planted = rng.choice(rows, 64, replace=False)
+    for i, r in enumerate(planted):
+        j = rng.integers(0, cols, 4)
+        g[r, j[0]] = 0x0000 if i % 2 else 0x8000                  # +-0
+        g[r, j[1]] = bf16_rne(np.array([2.0 ** -40 * (1 + i)]))[0]   # below the table
+        g[r, j[2]] = bf16_rne(np.array([(-1) ** i * 3.0e3]))[0]      # above it
+        g[r, j[3]] = [0x7F80, 0xFF80, 0x7FC0, 0x4300][i % 4]          # +-inf, NaN, 128
+    announce("swiglu silu table vs formula", rows, cols)
+    gd, ud, s0, s1 = dev_bits(g), dev_bits(c.b), dev_f32(c.s0), dev_f32(c.s1)
+    full = B.ds_swiglu_l2_rows(gd, ud, s0, s1, 1e-6)
+    pieces = [B.ds_swiglu_l2_rows(gd[a:a + 37], ud[a:a + 37], s0, s1, 1e-6)
+              for a in range(0, rows, 37)]
+    torch.cuda.synchronize()
+    got = host_bits(full)
+    assert np.array_equal(got, np.concatenate([host_bits(p) for p in pieces]))
+    check_rows = np.sort(np.concatenate([planted, sample_rows(rows, 40, 1652)]))
+    finite = np.isfinite(bf16_value(g[check_rows])).all(axis=1)
+    check_swiglu(got[check_rows[finite]], g[check_rows[finite]], c.b[check_rows[finite]],
+                 c.s0, c.s1, 1e-6, "swiglu table rows", min_unique=0.9)
+    want = swiglu_l2_rows(g[check_rows[~finite]], c.b[check_rows[~finite]], c.s0, c.s1, 1e-6)
+    gv, wv = bf16_value(got[check_rows[~finite]]), bf16_value(want)
+    assert np.array_equal(np.isnan(gv), np.isnan(wv))
