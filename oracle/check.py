@@ -652,7 +652,14 @@ def admissible_rownorm_backward(got_dw, got_dg, w, g, rho, dweff_bits,
 # its admissible bf16 values run from bf16(lo) to bf16(hi), and the output
 # is checked over every such choice as slerp's is over a and b.
 
-EXPF_ULPS = 2.0     # the kernels' exp measured within 1.22 ulp over 23M arguments on gfx950
+# EXPF_ULPS: the error the page's check allows for exp is "expf's ulps"
+# (TensorFold PR #1260, the activation-row commit): the fp32 expf of the
+# CUDA toolchain those kernels were built with, whose published maximum error
+# is 2 units in the last place over its full range (the CUDA C++ Programming
+# Guide's table of single-precision mathematical functions).  The bound is
+# the page's, not a measurement of the kernels checked here (gfx950's exp
+# measured within 1.22 ulp, inside it).
+EXPF_ULPS = 2.0
 F32_MAX = float(np.finfo(np.float32).max)
 
 
@@ -774,6 +781,10 @@ def admissible_act_rows(got_bits, c_lo, c_hi, exact_bits=None, finite_rows=None,
 # one fp32 product rounded to bf16 -- a monotone map of the normalized value,
 # so the admissible q outputs are the images of the admissible n range.
 
+# COSF_ULPS: "cosf's ulps on the fp32 angle pos * inv" (TensorFold PR
+# #1260, the q/k commit): the published maximum error of CUDA's fp32 cosf and
+# sinf (and sincosf), 2 units in the last place over the full range (the same
+# table).  gfx950's device library sincosf measured within 1.57 ulp, inside it.
 COSF_ULPS = 2.0
 
 

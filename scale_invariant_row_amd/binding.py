@@ -17,7 +17,9 @@ import re
 from typing import List, Optional, Sequence, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "_lib", "libdsrows.so")
+# DS_ROWS_LIB may name another build of the same library (the tests'
+# AddressSanitizer build of the host code); there is no fallback either way
+LIB_PATH = os.environ.get("DS_ROWS_LIB") or os.path.join(PKG, "_lib", "libdsrows.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "ds_rows.h")
 
 DS_OK = 0

@@ -36,7 +36,7 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wextra", "-Wno-unused-parameter",
+    "-Wall", "-Wextra", "-Wno-unused-parameter", "-Werror",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 

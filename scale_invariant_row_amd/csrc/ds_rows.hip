@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -143,7 +144,23 @@ Ring* ring_for_current_device() {
   return r;
 }
 
-int grow(Slot& s, size_t bytes) {
+// Failure injection for the tests of the staging path.  DS_ROWS_TEST_FAIL
+// names one step to fail as if the runtime had refused it: "alloc" (the
+// slot's buffers), "copy" (the table's upload) or "launch" (the first
+// kernel launch after the upload).  Read only when a call stages a table.
+enum class Fail { kNone, kAlloc, kCopy, kLaunch };
+
+Fail injected_failure() {
+  const char* f = std::getenv("DS_ROWS_TEST_FAIL");
+  if (f == nullptr) return Fail::kNone;
+  if (std::strcmp(f, "alloc") == 0) return Fail::kAlloc;
+  if (std::strcmp(f, "copy") == 0) return Fail::kCopy;
+  if (std::strcmp(f, "launch") == 0) return Fail::kLaunch;
+  return Fail::kNone;
+}
+
+int grow(Slot& s, size_t bytes, Fail fail) {
+  if (fail == Fail::kAlloc) return DS_ERR_ALLOC;
   if (s.ev == nullptr && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
     s.ev = nullptr;
     return DS_ERR_ALLOC;
@@ -165,7 +182,7 @@ int grow(Slot& s, size_t bytes) {
   return DS_OK;
 }
 
-int acquire(Ring& r, size_t bytes, int* out) {
+int acquire(Ring& r, size_t bytes, int* out, Fail fail) {
   std::lock_guard<std::mutex> lock(r.mu);
   int pick = -1;
   for (int t = 0; t < kSlots && pick < 0; ++t) {
@@ -187,7 +204,7 @@ int acquire(Ring& r, size_t bytes, int* out) {
     if (hipEventSynchronize(r.slot[pick].ev) != hipSuccess) return DS_ERR_LAUNCH;
     r.slot[pick].pending = false;
   }
-  int st = grow(r.slot[pick], bytes);
+  int st = grow(r.slot[pick], bytes, fail);
   if (st != DS_OK) return st;
   r.slot[pick].busy = true;
   r.next = (pick + 1) % kSlots;
@@ -335,13 +352,14 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
   int slot = -1;
   const Task* dev_tasks = nullptr;
   const int32_t* dev_begins = nullptr;
+  const Fail fail = staged_tasks > 0 ? injected_failure() : Fail::kNone;
   (void)hipGetLastError();
   if (staged_tasks > 0) {
     ring = ring_for_current_device();
     if (ring == nullptr) return DS_ERR_DEVICE;
     const size_t task_bytes = staged_tasks * sizeof(Task);
     const size_t bytes = task_bytes + staged_tasks * sizeof(int32_t);
-    if ((st = acquire(*ring, bytes, &slot)) != DS_OK) return st;
+    if ((st = acquire(*ring, bytes, &slot, fail)) != DS_OK) return st;
     Slot& sl = ring->slot[slot];
     auto* host_tasks = static_cast<Task*>(sl.host);
     auto* host_begins = reinterpret_cast<int32_t*>(static_cast<char*>(sl.host) + task_bytes);
@@ -353,7 +371,8 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
         host_begins[k] = table[L.first + i].item_begin;
       }
     }
-    if (hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
+    if (fail == Fail::kCopy ||
+        hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess) {
       release(*ring, slot, false, hs);        // nothing enqueued: refund the slot
       return DS_ERR_LAUNCH;
     }
@@ -379,7 +398,7 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
       args.begins = dev_begins + staged_at;
       staged_at += (size_t)L.ntasks;
     }
-    if (launch(L.s, args, grid_for(L.nitems, cus), hs) != hipSuccess) {
+    if (fail == Fail::kLaunch || launch(L.s, args, grid_for(L.nitems, cus), hs) != hipSuccess) {
       result = DS_ERR_LAUNCH;
       break;
     }

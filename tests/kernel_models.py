@@ -154,13 +154,15 @@ def rownorm_backward_model(w, g, rho, dwe_bits, acc="f32", proj="w"):
 
 # ------------------------------------------------------------ activation rows
 
-def _l2_of_f32_rows(t32, eps):
-    inv = inv_norm(lane_sum_sq(t32), eps)
-    return bf16_rne((t32 * inv[:, None]).astype(np.float64))
+def _l2_of_f32_rows(t32, eps, acc="f32"):
+    with np.errstate(all="ignore"):
+        inv = inv_norm(lane_sum_sq(t32, acc), eps)
+        return bf16_rne((t32 * inv[:, None]).astype(np.float64))
 
 
-def gate_model(o_bits, g_bits, sg, eps=1e-6, round_t=True):
-    """fp32 steps of the gate row; the control leaves the gated row unrounded."""
+def gate_model(o_bits, g_bits, sg, eps=1e-6, round_t=True, acc="f32"):
+    """fp32 steps of the gate row; the control leaves the gated row unrounded
+    (or, with acc="f16", sums its squares in fp16)."""
     o = bf16_value(o_bits).astype(np.float32)
     g = bf16_value(g_bits).astype(np.float32)
     with np.errstate(all="ignore"):
@@ -169,11 +171,13 @@ def gate_model(o_bits, g_bits, sg, eps=1e-6, round_t=True):
         t = o * sig
     if round_t:
         t = bf16_of_f32(t)
-    return _l2_of_f32_rows(t.astype(np.float32), eps)
+    return _l2_of_f32_rows(t.astype(np.float32), eps, acc)
 
 
-def swiglu_model(g_bits, u_bits, sug, suu, eps=1e-6, round_a=True, round_b=True, round_p=True):
-    """fp32 steps of the SwiGLU row; each control leaves one rounding point out."""
+def swiglu_model(g_bits, u_bits, sug, suu, eps=1e-6, round_a=True, round_b=True, round_p=True,
+                 acc="f32"):
+    """fp32 steps of the SwiGLU row; each control leaves one rounding point out
+    (or, with acc="f16", sums the squares in fp16)."""
     g = bf16_value(g_bits).astype(np.float32)
     u = bf16_value(u_bits).astype(np.float32)
     with np.errstate(all="ignore"):
@@ -187,15 +191,15 @@ def swiglu_model(g_bits, u_bits, sug, suu, eps=1e-6, round_a=True, round_b=True,
         p = silu * b
     if round_p:
         p = bf16_of_f32(p)
-    return _l2_of_f32_rows(p.astype(np.float32), eps)
+    return _l2_of_f32_rows(p.astype(np.float32), eps, acc)
 
 
 # ------------------------------------------------------------------ q/k rows
 
 def qk_model(q_bits, k_bits, positions, inv_freq, q_scale, hd, eps=1e-6,
-             round_r=True, round_n=True):
+             round_r=True, round_n=True, acc="f32"):
     """fp32 steps of qk_rows_l2; the controls leave the rotated head or the
-    normalized head unrounded."""
+    normalized head unrounded, or (acc="f16") sum each head's squares in fp16."""
     th = (np.asarray(positions).astype(np.float32)[:, None]
           * np.asarray(inv_freq, np.float32)[None, :]).astype(np.float32)
     c, s = np.cos(th)[:, None, :], np.sin(th)[:, None, :]
@@ -208,8 +212,9 @@ def qk_model(q_bits, k_bits, positions, inv_freq, q_scale, hd, eps=1e-6,
         rot = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1).astype(np.float32)
         r = bf16_of_f32(rot) if round_r else rot
         r2 = r.reshape(-1, hd)
-        inv = inv_norm(lane_sum_sq(r2), eps)
-        n = (r2 * inv[:, None]).astype(np.float32)
+        with np.errstate(all="ignore"):
+            inv = inv_norm(lane_sum_sq(r2, acc), eps)
+            n = (r2 * inv[:, None]).astype(np.float32)
         if round_n:
             n = bf16_of_f32(n)
         return n.reshape(rows, width)

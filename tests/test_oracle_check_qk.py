@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import kernel_models as km
-from oracle.bf16 import bf16_rne
+from oracle.bf16 import bf16_rne, bf16_value
 from oracle.check import admissible_qk_rows, contract_bf16
 from oracle.rows import qk_rows_l2
 
@@ -51,3 +51,22 @@ def test_integer_heads_at_position_zero_are_exact():
     qo, _ = km.qk_model(q, None, pos, inv, sc, hd)
     rq, _, uq, _ = admissible_qk_rows(qo, None, q, None, pos, inv, sc, hd, depth=0)
     assert rq.ok, str(rq)
+
+
+def test_integer_heads_fp16_sum_control_fails():
+    """The pages' gate 4 for q/k: integer heads with no rotation (position 0)
+    overflow an fp16 sum to a zero output, which fails the strict check."""
+    rng = np.random.default_rng(333)
+    hd = 256
+    q = bf16_rne(rng.integers(-64, 65, (6, 4 * hd)).astype(float))
+    k = bf16_rne(rng.integers(-64, 65, (6, hd)).astype(float))
+    pos = np.zeros(6, np.int64)
+    inv = (10000.0 ** (-np.arange(0, hd, 2) / hd)).astype(np.float32)
+    sc = rng.uniform(0.5, 2.0, 4 * hd).astype(np.float32)
+    qo, ko = km.qk_model(q, k, pos, inv, sc, hd)
+    rq, rk, _, _ = admissible_qk_rows(qo, ko, q, k, pos, inv, sc, hd, depth=0)
+    assert rq.ok and rk.ok, (str(rq), str(rk))
+    qo16, ko16 = km.qk_model(q, k, pos, inv, sc, hd, acc="f16")
+    assert not bf16_value(qo16).any() and not bf16_value(ko16).any()
+    rq, rk, _, _ = admissible_qk_rows(qo16, ko16, q, k, pos, inv, sc, hd)
+    assert rq.outside > 0.9 * qo16.size and rk.outside > 0.9 * ko16.size, (str(rq), str(rk))
