@@ -23,7 +23,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -36,24 +35,11 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 ROWS, COLS = 8192, 4096
 EPS = 1e-6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_row_kernels.txt")
-KERNEL_SOURCES = ["row_kernels.hpp", "launch.hpp", "inst_l2.hip", "inst_slerp.hip",
-                  "inst_rownorm.hip", "inst_l2_bwd.hip", "inst_rownorm_bwd.hip", "inst_act.hip",
-                  "inst_qk.hip", "inst_rescale.hip", "inst_rms.hip", "inst_rms_bwd.hip",
-                  "colblock_kernels.hpp", "inst_colblock.hip", "ds_rows.hip", "bench_stream.hip"]
-
-
-def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "scale_invariant_row_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_for(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, each calibrated on a copy of known size), or
-    None when it is missing or was taken from different kernel sources."""
+    (FETCH_SIZE + WRITE_SIZE, each calibrated on a copy of known size; written
+    by scale_invariant_row_amd.rocprof_summary), or None when it is missing or
+    was taken from different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             lines = f.read().splitlines()
@@ -66,7 +52,8 @@ def traffic_for(kernel: str):
             khash = parts[1]
         if len(parts) == 3 and parts[0] == "traffic" and parts[1] == kernel:
             found = int(parts[2])
-    return found if khash == kernel_hash() else None
+    from scale_invariant_row_amd.rocprof_summary import kernel_sources_hash
+    return found if khash == kernel_sources_hash() else None
 
 
 def cpu_baseline(l2c, slc, rows: int):
