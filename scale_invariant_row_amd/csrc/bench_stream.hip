@@ -4,8 +4,9 @@
 // and cache hints as l2_rows_kernel.  Where l2_rows normalises, it does one
 // bitwise op per dword (y = x ^ r), so what remains is the memory traffic.
 //
-// Built into its own library (libdsbench.so) for bench.py; it is not part of
-// the row library or its C ABI.
+// Built into its own library (libdsbench.so) for bench.py and the tests (it
+// also holds a check kernel the tests run); it is not part of the row library
+// or its C ABI.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -75,4 +76,43 @@ extern "C" int dsb_stream_rows(const void* x, const void* r, void* y, int64_t ro
     default: return -1;
   }
   return e == hipSuccess ? 0 : -2;
+}
+
+// ---------------------------------------------------------------- test kernel
+//
+// The gate's fast reciprocal against IEEE division over a range of fp32 bit
+// patterns [first, first + count): counts the values where the two differ
+// and keeps the smallest such pattern.  The test suite runs it over every b
+// in [1, 2^126) and beyond.  `out` holds two uint32: the count (cleared by
+// the caller) and the smallest differing pattern (set to ~0 by the caller).
+namespace dsr {
+__global__ void __launch_bounds__(256)
+recip_check_kernel(uint32_t first, uint32_t count, uint32_t* out) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256u;
+  uint32_t bad = 0, lowest = 0xffffffffu;
+  // a 64-bit index: i + stride never wraps, so every lane's loop ends
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < count; i += stride) {
+    const uint32_t bits = first + (uint32_t)i;
+    const float b = __uint_as_float(bits);
+    const float fast = recip_fast(b);
+    const float ieee = 1.0f / b;
+    if (__float_as_uint(fast) != __float_as_uint(ieee)) {
+      ++bad;
+      lowest = min(lowest, bits);
+    }
+  }
+  if (bad) {
+    atomicAdd(&out[0], bad);
+    atomicMin(&out[1], lowest);
+  }
+}
+}  // namespace dsr
+
+// Runs the check over [first, first + count) (count > 0, first + count <=
+// 2^32) on `stream`; out: device memory as above.  Returns 0, or -2 for a
+// runtime error.
+extern "C" int dsb_recip_check(uint32_t first, uint32_t count, uint32_t* out, void* stream) {
+  if (count == 0 || (uint64_t)first + count > (1ull << 32)) return -1;
+  dsr::recip_check_kernel<<<4096, 256, 0, (hipStream_t)stream>>>(first, count, out);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
 }

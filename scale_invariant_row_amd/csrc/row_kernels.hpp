@@ -775,6 +775,16 @@ __device__ __forceinline__ float exp_split(float x) {
   return __builtin_isfinite(r) ? r : e0;
 }
 
+// 1 / b for b in [1, 2^126): gfx950's v_rcp_f32 estimate y and one fma
+// correction, y + y (1 - b y).  Over every fp32 b in [1, 2^126) this equals
+// the IEEE quotient (checked exhaustively on the GPU by the tests); from
+// 2^126 up the quotient is subnormal, which v_rcp_f32 flushes, so callers
+// take the IEEE division there.
+__device__ __forceinline__ float recip_fast(float b) {
+  const float y = __builtin_amdgcn_rcpf(b);
+  return __builtin_fmaf(__builtin_fmaf(-b, y, 1.0f), y, y);
+}
+
 // silu(a) = a / (1 + exp(-a)) in fp32 with IEEE division.
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + exp_split(-a)); }
 
@@ -837,8 +847,7 @@ __device__ __forceinline__ void act_prologue(uint32_t (&out)[4], const uint32_t 
     for (int j = 0; j < 8; ++j) {
       const float x = ((j & 1) ? bf_hi(x1[j / 2]) : bf_lo(x1[j / 2])) * s0[j];   // g * sg
       b[j] = 1.0f + exp_split(-x);
-      const float y = __builtin_amdgcn_rcpf(b[j]);
-      sig[j] = __builtin_fmaf(__builtin_fmaf(-b[j], y, 1.0f), y, y);
+      sig[j] = recip_fast(b[j]);
       slow |= !(b[j] < 0x1p126f);
     }
     if (__builtin_amdgcn_ballot_w64(slow) != 0) {
