@@ -231,3 +231,29 @@ def rownorm_backward_job(got_dw, got_dg, w, g, rho, dwe, depth, base):
 def chunks(rows: int, chunk: int = CHUNK_ROWS):
     """(start, stop) row ranges covering [0, rows)."""
     return [(a, min(rows, a + chunk)) for a in range(0, rows, chunk)]
+
+
+def rescale_job(got_w, got_v, w, v, rho, after_step, depth, base):
+    """The rescale method's rows base..: v (the projected gradient or momentum)
+    against the gradient contract, w (after a step) within 2e-6, and both
+    inside the strict set."""
+    from oracle.check import admissible_rescale, contract_grad, contract_rel, rescale_terms
+    from oracle.rows import rescale_after_step, rescale_project
+    if after_step:
+        ws, ms = rescale_after_step([w], [v], [rho])
+        okw = contract_rel(got_w, ws[0])
+    else:
+        ms = rescale_project([w], [v])
+        okw = got_w == w
+    terms = rescale_terms(w.astype(np.float64), v.astype(np.float64))
+    okv = contract_grad(got_v, ms[0], terms, "f32")
+    rw, rv = admissible_rescale(got_w, got_v, w, v, rho, after_step, depth=depth)
+    bad = np.flatnonzero(~(okv & okw))
+    return {
+        "n": int(got_v.size),
+        "beyond": int(bad.size),
+        "outside": int(rv.outside + rv.loose + (rw.outside + rw.loose if after_step else 0)),
+        "two": 0,
+        "wide": int(rv.wide),
+        "first_bad": [int(base * w.shape[1] + b) for b in bad[:10]] + list(rv.first_bad[:10]),
+    }

@@ -228,3 +228,134 @@ def test_rownorm_backward_12x4_d768(B):
     assert counts["n"] == case.total_elems and counts["dg"] == case.total_rows
     assert counts["dg_beyond"] == 0
     assert_clean(case.name, counts)
+
+
+# ---------------------------------------------------- the other workloads
+
+
+def test_rms_rows_16384x768(B):
+    g = inputs.make("rms_rows_bwd_16384x768")        # its x: the forward's input
+    c = inputs.L2Case("rms_rows_16384x768", g.x, None, g.eps)
+    l2_workload(B, c, c.name, None, mean=True)
+
+
+def _weights_forward(B, name, case, depth_of=None):
+    import torch
+    t0 = time.perf_counter()
+    announce("full-size weights", name, len(case.w))
+    norms, weffs = B.ds_weight_rownorm_gain([dev_f32(w) for w in case.w],
+                                            [dev_f32(g) for g in case.gain], case.radius)
+    torch.cuda.synchronize()
+    got_n = [n.cpu().numpy() for n in norms]
+    got_w = [host_bits(w) for w in weffs]
+    jobs = []
+    for i, (w, g) in enumerate(zip(case.w, case.gain)):
+        depth = depth_for(w.shape[1])
+        for a, b in J.chunks(w.shape[0]):
+            jobs.append((got_n[i][a:b], got_w[i][a:b], w[a:b], g[a:b], case.radius[i], depth, a))
+    counts = report(name, J.merge(J.run_pool(J.rownorm_job, jobs)), t0)
+    assert counts["n"] == case.total_elems and counts["norms"] == case.total_rows
+    assert counts["norms_beyond"] == 0
+    assert_clean(name, counts)
+
+
+def _weights_backward(B, name, case):
+    import torch
+    t0 = time.perf_counter()
+    announce("full-size weight gradient", name, len(case.w))
+    dws, dgs = B.ds_weight_rownorm_gain_backward([dev_f32(w) for w in case.w],
+                                                 [dev_f32(g) for g in case.gain],
+                                                 [dev_bits(d) for d in case.dwe], case.radius)
+    torch.cuda.synchronize()
+    dws = [d.cpu().numpy() for d in dws]
+    dgs = [d.cpu().numpy() for d in dgs]
+    jobs = []
+    for i, (w, g, de) in enumerate(zip(case.w, case.gain, case.dwe)):
+        depth = depth_for(w.shape[1])
+        for a, b in J.chunks(w.shape[0]):
+            jobs.append((dws[i][a:b], dgs[i][a:b], w[a:b], g[a:b], case.radius[i], de[a:b],
+                         depth, a))
+    counts = report(name, J.merge(J.run_pool(J.rownorm_backward_job, jobs)), t0)
+    assert counts["n"] == case.total_elems and counts["dg"] == case.total_rows
+    assert counts["dg_beyond"] == 0
+    assert_clean(name, counts)
+
+
+@pytest.mark.parametrize("name", ["rownorm_gain_resnet50", "rownorm_gain_embedding_50304x768"])
+def test_weights_forward(B, name):
+    _weights_forward(B, name, inputs.make(name))
+
+
+def test_weights_11008x4096(B):
+    case = inputs.make("rownorm_gain_bwd_11008x4096")
+    _weights_forward(B, "rownorm_gain_11008x4096", case)
+    _weights_backward(B, case.name, case)
+
+
+def test_weights_backward_resnet50(B):
+    _weights_backward(B, "rownorm_gain_bwd_resnet50", inputs.make("rownorm_gain_bwd_resnet50"))
+
+
+def test_gpt2_conv1d_column_blocks(B):
+    """GPT-2's 48 Conv1D weights stored [in, out]: every unit (a stored column)
+    gathered into a row, forward and gradient, at the column-block kernel's
+    sum-tree depth."""
+    import torch
+    from oracle.rows import column_block_rows
+    from test_gpu_colblock import depth_col
+    c = inputs.make("rownorm_gain_gpt2_conv1d")
+    t0 = time.perf_counter()
+    announce("full-size column blocks", c.name, len(c.w))
+    segs = [1] * len(c.w)
+    norms, weffs = B.ds_weight_rownorm_gain([dev_f32(w) for w in c.w],
+                                            [dev_f32(g) for g in c.gain], [1.0] * len(c.w),
+                                            segs=segs)
+    dws, dgs = B.ds_weight_rownorm_gain_backward([dev_f32(w) for w in c.w],
+                                                 [dev_f32(g) for g in c.gain],
+                                                 [dev_bits(d) for d in c.dwe], [1.0] * len(c.w),
+                                                 segs=segs)
+    torch.cuda.synchronize()
+    rows = lambda a: column_block_rows(a, a.shape[1], 1)
+    fwd, bwd = [], []
+    for i, (w, g, de) in enumerate(zip(c.w, c.gain, c.dwe)):
+        wr, er = rows(w), rows(host_bits(weffs[i]))
+        dwr, der = rows(dws[i].cpu().numpy()), rows(de)
+        n, dg = norms[i].cpu().numpy(), dgs[i].cpu().numpy()
+        depth = depth_col(w.shape[0], 1)
+        for a, b in J.chunks(wr.shape[0]):
+            fwd.append((n[a:b], er[a:b], wr[a:b], g[a:b], 1.0, depth, a))
+            bwd.append((dwr[a:b], dg[a:b], wr[a:b], g[a:b], 1.0, der[a:b], depth, a))
+    cf = report(c.name, J.merge(J.run_pool(J.rownorm_job, fwd)), t0)
+    cb = report(c.name + "_bwd", J.merge(J.run_pool(J.rownorm_backward_job, bwd)), t0)
+    el = sum(w.size for w in c.w)
+    assert cf["n"] == el and cb["n"] == el
+    assert cf["norms_beyond"] == 0 and cb["dg_beyond"] == 0
+    assert_clean(c.name, cf)
+    assert_clean(c.name + " gradient", cb)
+
+
+@pytest.mark.parametrize("after_step", [False, True])
+def test_rescale_12x4_d768(B, after_step):
+    import torch
+    case = inputs.make("rescale_12x4_d768")
+    name = case.name + ("_after_step" if after_step else "_project")
+    t0 = time.perf_counter()
+    announce("full-size rescale", name)
+    ws = [dev_f32(w) for w in case.w]
+    vs = [dev_f32(v) for v in case.v]
+    if after_step:
+        B.ds_rescale_after_step(ws, vs, case.radius)
+    else:
+        B.ds_rescale_project(ws, vs)
+    torch.cuda.synchronize()
+    gw = [w.cpu().numpy() for w in ws]
+    gv = [v.cpu().numpy() for v in vs]
+    jobs = []
+    for i, (w, v) in enumerate(zip(case.w, case.v)):
+        depth = depth_for(w.shape[1])
+        for a, b in J.chunks(w.shape[0]):
+            jobs.append((gw[i][a:b], gv[i][a:b], w[a:b], v[a:b], case.radius[i], after_step,
+                         depth, a))
+    counts = report(name, J.merge(J.run_pool(J.rescale_job, jobs)), t0)
+    assert counts["n"] == sum(w.size for w in case.w)
+    assert_clean(name, counts)
