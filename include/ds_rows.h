@@ -92,7 +92,7 @@
 extern "C" {
 #endif
 
-#define DS_ROWS_VERSION 10800          /* major * 10000 + minor * 100 + patch */
+#define DS_ROWS_VERSION 10900          /* major * 10000 + minor * 100 + patch */
 #define DS_MAX_COLS 65536              /* widest row any entry point accepts */
 #define DS_MAX_ELEM_COLS 16384         /* widest fp32 weight row whose width is
                                           not a multiple of 4 */
@@ -299,7 +299,11 @@ enum {
  *            cols = (in / groups) * seg.  Needs 1 <= seg <= 64, cols a
  *            multiple of seg, ld >= rows * seg; w_eff (and every other
  *            per-element buffer of the call) has the same layout; fp32
- *            buffers 4-byte aligned, bf16 ones 2-byte aligned.
+ *            buffers 4-byte aligned, bf16 ones 2-byte aligned.  A seg = 1
+ *            block whose rows and ld are multiples of 4, with 16-byte-aligned
+ *            fp32 buffers (8-byte bf16), reads W from memory once when
+ *            cols <= 768 (the single-pass tile); other blocks read it twice.
+ *            Results meet the same contract either way.
  */
 typedef struct ds_rownorm_desc {
   const float* w;

@@ -407,27 +407,31 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
   return result;
 }
 
-// The weight launchers: row kernels, or the column-block kernel for a
-// column-block shape class.
+// The weight launchers: row kernels, or a column-block kernel (single-pass
+// or two-pass) for a column-block shape class.
 hipError_t launch_rownorm_any(Shape s, const dsr::TaskArgs<dsr::RownormTask>& a, int grid,
                               hipStream_t hs) {
+  if (s.col1 > 0) return dsr::launch_colblock1_rownorm(a, grid, hs);
   return s.units > 0 ? dsr::launch_colblock_rownorm(a, grid, hs) : dsr::launch_rownorm(s, a, grid, hs);
 }
 
 hipError_t launch_rownorm_backward_any(Shape s, const dsr::TaskArgs<dsr::RownormGradTask>& a,
                                        int grid, hipStream_t hs) {
+  if (s.col1 > 0) return dsr::launch_colblock1_rownorm_backward(a, grid, hs);
   return s.units > 0 ? dsr::launch_colblock_rownorm_backward(a, grid, hs)
                      : dsr::launch_rownorm_backward(s, a, grid, hs);
 }
 
 hipError_t launch_project_any(Shape s, const dsr::TaskArgs<dsr::RescaleTask>& a, int grid,
                               hipStream_t hs) {
+  if (s.col1 > 0) return dsr::launch_colblock1_rescale(false, a, grid, hs);
   return s.units > 0 ? dsr::launch_colblock_rescale(false, a, grid, hs)
                      : dsr::launch_rescale_project(s, a, grid, hs);
 }
 
 hipError_t launch_after_step_any(Shape s, const dsr::TaskArgs<dsr::RescaleTask>& a, int grid,
                                  hipStream_t hs) {
+  if (s.col1 > 0) return dsr::launch_colblock1_rescale(true, a, grid, hs);
   return s.units > 0 ? dsr::launch_colblock_rescale(true, a, grid, hs)
                      : dsr::launch_rescale_after_step(s, a, grid, hs);
 }
@@ -468,6 +472,20 @@ int check_layout(int64_t rows, int64_t cols, int32_t seg, int64_t ld, Shape* s,
   *a32 = 4;
   *a16 = 2;
   return DS_OK;
+}
+
+// A column block that the seg-1 kernel takes: seg 1, a unit count and ld
+// that are multiples of 4, and 16-byte-aligned fp32 buffers (8 for bf16; the
+// caller checks them into `vec_aligned`).  Its tiles are single-pass (4 lanes
+// units) when col1_single admits the matrix, else two-pass (64 units).
+// Others keep the two-pass kernel's shape `s`.
+Shape single_pass(Shape s, int K, int lanes, int64_t rows, int64_t cols, int32_t seg, int64_t ld,
+                  bool vec_aligned) {
+  if (s.units == 0 || seg != 1 || rows % 4 != 0 || ld % 4 != 0 || !vec_aligned) return s;
+  Shape c{};
+  c.units = dsr::col1_single(cols, ld, K, lanes) ? 4 * lanes : 64;
+  c.col1 = K * 100 + lanes;
+  return c;
 }
 
 bool gain_mode_ok(int32_t m) {
@@ -794,6 +812,8 @@ int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t 
     t.radius = d.radius;
     t.seg = d.seg;
     t.ld = d.ld;
+    s = single_pass(s, dsr::kCol1KFwd, dsr::kCol1LanesFwd, d.rows, d.cols, d.seg, d.ld,
+                    aligned(d.w, 16) && aligned(d.w_eff, 8));
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
@@ -915,6 +935,8 @@ int rownorm_backward_call(const ds_rownorm_grad_desc* descs, int32_t n, ds_strea
       scratch_used += d.rows;
     }
     if (d.dgain_total != nullptr) totals.push_back({d.dgain, d.dgain_total, d.rows});
+    s = single_pass(s, dsr::kCol1KBwd, dsr::kCol1LanesBwd, d.rows, d.cols, d.seg, d.ld,
+                    aligned(d.w, 16) && aligned(d.dw_eff, 8) && aligned(d.dw, 16));
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;
@@ -987,6 +1009,8 @@ int rescale_call(const ds_rescale_desc* descs, int32_t n, bool after_step, ds_st
     t.radius = d.radius;
     t.seg = d.seg;
     t.ld = d.ld;
+    s = single_pass(s, dsr::kCol1KRescale, dsr::kCol1LanesRescale, d.rows, d.cols, d.seg, d.ld,
+                    aligned(d.w, 16) && aligned(d.v, 16));
     mats.emplace_back(s, t);
   }
   if (!outputs_disjoint(outs, ins)) return DS_ERR_ARG;

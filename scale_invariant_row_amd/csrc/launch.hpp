@@ -17,19 +17,25 @@ struct RescaleTask;
 // (the fp32 weight kernels: 4 for 16-byte vectors, 1 for single elements;
 // every other kernel uses 16-byte vectors).
 // A column-block weight (its rows spread over the stored rows) instead runs
-// one 1024-thread workgroup per tile of `units` adjacent rows.  A launch
-// with `mixed` > 0 runs the ragged weight kernels' mixed-shape kernel of
-// that workgroup size: each task carries its own row shape.
+// one 1024-thread workgroup per tile of `units` adjacent rows; `col1` > 0
+// (K * 100 + LANES) picks the seg-1 kernel whose tiles are single-pass where
+// the matrix fits and two-pass elsewhere (its tile width varies with the
+// matrix, so its launches group by col1 alone).  A launch with `mixed` > 0
+// runs the ragged weight kernels' mixed-shape kernel of that workgroup size:
+// each task carries its own row shape.
 struct Shape {
   int G = 0;
   int V = 0;
   int NE = 4;
   int units = 0;
+  int col1 = 0;
   int mixed = 0;
   int rows_per_block() const { return units > 0 ? units : (G == 1 ? 4 : 1); }
   int threads() const { return mixed > 0 ? mixed : units > 0 ? 1024 : 64 * G * rows_per_block(); }
   bool ok() const { return G > 0 || units > 0; }
-  int key() const { return units > 0 ? 1000000 + units : NE * 10000 + G * 100 + V; }
+  int key() const {
+    return col1 > 0 ? 2000000 + col1 : units > 0 ? 1000000 + units : NE * 10000 + G * 100 + V;
+  }
 };
 
 // Mixed-shape launches of the ragged weight calls (measured on MI355X): the
@@ -48,6 +54,35 @@ inline Shape colblock_shape(int64_t seg) {
   Shape s{};
   if (seg >= 1 && seg <= kMaxSeg) s.units = (int)(64 / seg);
   return s;
+}
+
+// Single-pass column blocks (seg 1): a tile of 4 LANES adjacent units, each
+// lane holding K 16-byte vectors of W (and of the second input), so the
+// workgroup holds 1024 K / LANES stored rows.  Per op: the forward and the
+// gradient 64-unit tiles (K = 12: W takes 48 VGPRs, the gradient's bf16
+// dW_eff 24 more), so every stream moves whole 128-byte lines; the rescale
+// calls 32-unit tiles (fp32 only, K = 6).  Each holds the 768 stored rows of
+// GPT-2's attention and MLP-input weights.  A taller matrix (GPT-2's
+// 3,072-row MLP projection) runs the two-pass tile in the same launch: tiles
+// narrower than a line to fit its rows lost more to partial-line traffic
+// than the second read costs.  Host and kernel share this rule.
+#ifndef DSR_COL1_K_FWD
+#define DSR_COL1_K_FWD 12
+#endif
+#ifndef DSR_COL1_K_BWD
+#define DSR_COL1_K_BWD 12
+#endif
+#ifndef DSR_COL1_LANES_BWD
+#define DSR_COL1_LANES_BWD 16
+#endif
+constexpr int kCol1KFwd = DSR_COL1_K_FWD, kCol1LanesFwd = 16;
+constexpr int kCol1KBwd = DSR_COL1_K_BWD, kCol1LanesBwd = DSR_COL1_LANES_BWD;
+constexpr int kCol1KRescale = 6, kCol1LanesRescale = 8;
+// Whether a matrix of A stored rows, ld elements apart, takes the single-pass
+// tile: A within the capacity, and 32-bit buffer offsets over every stored
+// row a tile addresses.
+__host__ __device__ constexpr inline bool col1_single(int64_t A, int64_t ld, int K, int lanes) {
+  return A <= (int64_t)1024 * K / lanes && (int64_t)1024 * K / lanes * ld * 4 + 256 <= 0x7fffffff;
 }
 
 // Shape policy, measured on MI355X (the gradients use the same rules as
@@ -149,5 +184,11 @@ hipError_t launch_colblock_rownorm_backward(const TaskArgs<RownormGradTask>& arg
                                             hipStream_t stream);
 hipError_t launch_colblock_rescale(bool after_step, const TaskArgs<RescaleTask>& args, int grid,
                                    hipStream_t stream);
+hipError_t launch_colblock1_rownorm(const TaskArgs<RownormTask>& args, int grid,
+                                    hipStream_t stream);
+hipError_t launch_colblock1_rownorm_backward(const TaskArgs<RownormGradTask>& args, int grid,
+                                             hipStream_t stream);
+hipError_t launch_colblock1_rescale(bool after_step, const TaskArgs<RescaleTask>& args, int grid,
+                                    hipStream_t stream);
 
 }  // namespace dsr

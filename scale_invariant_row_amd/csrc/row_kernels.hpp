@@ -89,6 +89,19 @@ struct RowBuf {
   __device__ __forceinline__ u32x2_t ld8(int off) const {
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolLd);
   }
+  // with a wave-uniform byte offset `soff` added in the scalar offset field
+  __device__ __forceinline__ f32x4_t ld16f(int off, int soff) const {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kCpolLd));
+  }
+  __device__ __forceinline__ u32x2_t ld8(int off, int soff) const {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kCpolLd);
+  }
+  __device__ __forceinline__ void st16(u32x4_t v, int off, int soff) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, kCpolSt);
+  }
+  __device__ __forceinline__ void st8(u32x2_t v, int off, int soff) const {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, soff, kCpolSt);
+  }
   __device__ __forceinline__ void st16(u32x4_t v, int off) const {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSt);
   }

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert B.ds_version() == 10800
+    assert B.ds_version() == 10900
     for code in range(0, -10, -1):
         s = B.ds_status_string(code)
         assert s.startswith("DS_"), s

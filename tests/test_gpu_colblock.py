@@ -31,11 +31,48 @@ def B():
     return binding
 
 
-def depth_col(stored_rows, seg):
-    """Additions along any path of the column-block sum tree: a chain of
-    ceil(A / 128) terms, the eight chains and sixteen waves pairwise, a unit's
-    seg columns pairwise (plus one for the chain's first addition)."""
-    return -(-stored_rows // 128) + 1 + 3 + 4 + (math.ceil(math.log2(seg)) if seg > 1 else 0)
+# The seg-1 kernel's single-pass tiles, per op (the library's rule): vectors
+# per lane K and lanes per stored row.
+SINGLE_PASS = {"fwd": (12, 16), "bwd": (12, 16), "rescale": (6, 8)}
+
+
+def single_pass_lanes(A, units, seg, op, ld=None, aligned=True):
+    """Lanes per stored row of the single-pass column-block tile for this
+    layout, or 0 when a two-pass tile runs: seg 1, units and ld multiples of
+    4, 16-byte-aligned buffers, A within the tile's 1024 K / lanes stored rows
+    and 32-bit offsets over them."""
+    ld = units * seg if ld is None else ld
+    if seg != 1 or units % 4 or ld % 4 or not aligned:
+        return 0
+    k, lanes = SINGLE_PASS[op]
+    cap = 1024 * k // lanes
+    if A > cap or cap * ld * 4 + 256 > 2 ** 31 - 1:
+        return 0
+    return lanes
+
+
+def tree_adds(n):
+    """Additions along the deepest path of the single-pass kernel's per-lane
+    tree over n values (pairs: a product and an fma; then pairwise)."""
+    if n <= 1:
+        return 0
+    if n == 2:
+        return 1
+    return 1 + max(tree_adds(n // 2), tree_adds(n - n // 2))
+
+
+def depth_col(stored_rows, seg, op=None, units=None, ld=None):
+    """Additions along any path of the column-block sum tree.  Two-pass
+    kernel: a chain of ceil(A / 128) terms, the eight chains and sixteen waves
+    pairwise, a unit's seg columns pairwise (plus one for the chain's first
+    addition).  Single-pass kernel (when `op` and `units` say it runs): the
+    lane's K values pairwise, the 64 / lanes row slots and the sixteen waves
+    pairwise."""
+    two_pass = -(-stored_rows // 128) + 1 + 3 + 4 + (math.ceil(math.log2(seg)) if seg > 1 else 0)
+    lanes = single_pass_lanes(stored_rows, units, seg, op, ld) if op and units else 0
+    if not lanes:
+        return two_pass
+    return tree_adds(SINGLE_PASS[op][0]) + int(math.log2(64 // lanes)) + 4
 
 
 def rows_of(stored, seg):
@@ -52,7 +89,7 @@ def check_forward(norm, weff_bits, w, g, rho, seg, label, sample=None):
     ok = contract_bf16(got_e[idx], e_ref[0], zero_sign=False)
     assert ok.all(), f"{label}: W_eff beyond 1 ulp at {np.argwhere(~ok)[:4]}"
     rn, rw = admissible_rownorm(norm[idx], got_e[idx], rows[idx], g[idx], rho,
-                                depth=depth_col(w.shape[0], seg))
+                                depth=depth_col(w.shape[0], seg, "fwd", units))
     assert rn.ok and rw.ok, f"{label}: {rn} / {rw}"
 
 
@@ -66,7 +103,7 @@ def check_backward(dw, dg, w, g, rho, de, seg, label, sample=None):
     assert contract_grad(drows[idx], want_dw[0], tw, "f32").all(), f"{label}: dW"
     assert contract_grad(dg[idx], want_dg[0], tg, "f32").all(), f"{label}: dg"
     rw, rg = admissible_rownorm_backward(drows[idx], dg[idx], rows[idx], g[idx], rho, derows[idx],
-                                         depth=depth_col(w.shape[0], seg))
+                                         depth=depth_col(w.shape[0], seg, "bwd", units))
     assert rw.ok and rg.ok, f"{label}: {rw} / {rg}"
 
 
@@ -113,7 +150,8 @@ def test_shapes(B, A, units, seg):
     terms = rescale_terms(rows.astype(np.float64), vrows.astype(np.float64))
     assert contract_grad(got_v, want_v, terms, "f32").all(), "project"
     assert np.array_equal(wd.cpu().numpy(), w)
-    _, rv = admissible_rescale(rows, got_v, rows, vrows, 1.0, False, depth=depth_col(A, seg))
+    depth = depth_col(A, seg, "rescale", units)
+    _, rv = admissible_rescale(rows, got_v, rows, vrows, 1.0, False, depth=depth)
     assert rv.ok, f"project: {rv}"
     wd, vd = dev_f32(w), dev_f32(v)
     B.ds_rescale_after_step([wd], [vd], [3.0], segs=[seg])
@@ -122,7 +160,7 @@ def test_shapes(B, A, units, seg):
     got_w, got_v = rows_of(wd.cpu().numpy(), seg), rows_of(vd.cpu().numpy(), seg)
     assert contract_rel(got_w, ws_ref[0]).all(), "after step: w"
     assert contract_grad(got_v, vs_ref[0], terms, "f32").all(), "after step: v"
-    rw, rv = admissible_rescale(got_w, got_v, rows, vrows, 3.0, True, depth=depth_col(A, seg))
+    rw, rv = admissible_rescale(got_w, got_v, rows, vrows, 3.0, True, depth=depth)
     assert rw.ok and rv.ok, f"after step: {rw} / {rv}"
 
 
@@ -143,7 +181,8 @@ def test_after_step_without_momentum(B, A, units, seg):
     want, _ = rescale_after_step([rows], [None], [1.5])
     assert contract_rel(got, want[0]).all(), "after step: w"
     assert np.array_equal(got[1], rows[1]), "zero unit"
-    rw, _ = admissible_rescale(got, None, rows, None, 1.5, True, depth=depth_col(A, seg))
+    rw, _ = admissible_rescale(got, None, rows, None, 1.5, True,
+                               depth=depth_col(A, seg, "rescale", units))
     assert rw.ok, f"after step: {rw}"
 
 

@@ -298,8 +298,8 @@ def test_weights_backward_resnet50(B):
 
 def test_gpt2_conv1d_column_blocks(B):
     """GPT-2's 48 Conv1D weights stored [in, out]: every unit (a stored column)
-    gathered into a row, forward and gradient, at the column-block kernel's
-    sum-tree depth."""
+    gathered into a row, forward and gradient, at the sum-tree depth of the
+    column-block kernel that runs (single-pass for these layouts)."""
     import torch
     from oracle.rows import column_block_rows
     from test_gpu_colblock import depth_col
@@ -321,10 +321,11 @@ def test_gpt2_conv1d_column_blocks(B):
         wr, er = rows(w), rows(host_bits(weffs[i]))
         dwr, der = rows(dws[i].cpu().numpy()), rows(de)
         n, dg = norms[i].cpu().numpy(), dgs[i].cpu().numpy()
-        depth = depth_col(w.shape[0], 1)
+        depth_f = depth_col(w.shape[0], 1, "fwd", w.shape[1])
+        depth_b = depth_col(w.shape[0], 1, "bwd", w.shape[1])
         for a, b in J.chunks(wr.shape[0]):
-            fwd.append((n[a:b], er[a:b], wr[a:b], g[a:b], 1.0, depth, a))
-            bwd.append((dwr[a:b], dg[a:b], wr[a:b], g[a:b], 1.0, der[a:b], depth, a))
+            fwd.append((n[a:b], er[a:b], wr[a:b], g[a:b], 1.0, depth_f, a))
+            bwd.append((dwr[a:b], dg[a:b], wr[a:b], g[a:b], 1.0, der[a:b], depth_b, a))
     cf = report(c.name, J.merge(J.run_pool(J.rownorm_job, fwd)), t0)
     cb = report(c.name + "_bwd", J.merge(J.run_pool(J.rownorm_backward_job, bwd)), t0)
     el = sum(w.size for w in c.w)
