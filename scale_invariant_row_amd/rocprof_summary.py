@@ -197,10 +197,15 @@ def bench_launches() -> Dict[Tuple[str, Optional[int]], Tuple[str, int, int, int
     conv = inputs.gpt2_conv1d()
     el = sum(a * b for a, b in conv)
     units = sum(b for _, b in conv)
-    t[("colblock_kernel<(ColOp)0>", None)] = ("W rownorm, GPT-2 Conv1D (column blocks)",
-                                              el * 4 + units * 4, el * 2 + units * 4, el)
-    t[("colblock_kernel<(ColOp)1>", None)] = ("W gradient, GPT-2 Conv1D (column blocks)",
-                                              el * 6 + units * 4, el * 4 + units * 4, el)
+    # (the seg-1 kernel: single-pass tiles for the 768-row weights, two-pass
+    # tiles for the 3,072-row MLP projections, one launch per op)
+    fwd_w = ("W rownorm, GPT-2 Conv1D (column blocks)", el * 4 + units * 4, el * 2 + units * 4, el)
+    bwd_w = ("W gradient, GPT-2 Conv1D (column blocks)", el * 6 + units * 4, el * 4 + units * 4,
+             el)
+    t[("colblock1_kernel<(ColOp)0, 12, 16>", None)] = fwd_w
+    t[("colblock1_kernel<(ColOp)1, 12, 16>", None)] = bwd_w
+    t[("colblock_kernel<(ColOp)0>", None)] = fwd_w
+    t[("colblock_kernel<(ColOp)1>", None)] = bwd_w
     return t
 
 
