@@ -163,6 +163,8 @@ CASES = [
     (64, 200, 200),     # short; a tile of 8 units last
     (769, 16, 16),      # one stored row past the capacity: two-pass tiles
     (3072, 36, 44),     # GPT-2's MLP projection height: two-pass tiles; gap of 8
+    (2000, 72, 72),     # two-pass, a stored-row count that is not a multiple of 128
+    (3073, 8, 8),       # one stored row past 3,072
 ]
 
 
