@@ -24,9 +24,9 @@ stream_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows,
   int off[V];
   geo.offsets(off, 16);
   const uint32_t row_bytes = (uint32_t)nvec * 16u;
-  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
-    const int64_t row = base + geo.rr;
-    if (G == 1 && row >= rows) break;
+  {
+    const int64_t row = (int64_t)blockIdx.x * R + geo.rr;   // one row group per workgroup
+    if (G == 1 && row >= rows) return;
     Bf16Row<V> a, b;
     a.load(RowBuf(x + row * nvec, row_bytes), off);
     b.load(RowBuf(r + row * nvec, row_bytes), off);
@@ -62,20 +62,30 @@ extern "C" int dsb_stream_rows(const void* x, const void* r, void* y, int64_t ro
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return -2;
-  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * 64));
+  // as the row library launches l2_rows: one row group per workgroup, in
+  // launches of at most 64 row groups per compute unit
+  const int rpg = s.rows_per_block();
+  const int64_t piece = (int64_t)cus * 64 * rpg;
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e;
-  switch (s.G * 100 + s.V) {
-    case 101: e = run<1, 1>(x, r, y, rows, nvec, grid, hs); break;
-    case 102: e = run<1, 2>(x, r, y, rows, nvec, grid, hs); break;
-    case 202: e = run<2, 2>(x, r, y, rows, nvec, grid, hs); break;
-    case 402: e = run<4, 2>(x, r, y, rows, nvec, grid, hs); break;
-    case 403: e = run<4, 3>(x, r, y, rows, nvec, grid, hs); break;
-    case 404: e = run<4, 4>(x, r, y, rows, nvec, grid, hs); break;
-    default: return -1;
+  for (int64_t r0 = 0; r0 < rows; r0 += piece) {
+    const int64_t n = std::min<int64_t>(piece, rows - r0);
+    const int grid = (int)((n + rpg - 1) / rpg);
+    const char* xp = (const char*)x + r0 * cols * 2;
+    const char* rp = (const char*)r + r0 * cols * 2;
+    char* yp = (char*)y + r0 * cols * 2;
+    hipError_t e;
+    switch (s.G * 100 + s.V) {
+      case 101: e = run<1, 1>(xp, rp, yp, n, nvec, grid, hs); break;
+      case 102: e = run<1, 2>(xp, rp, yp, n, nvec, grid, hs); break;
+      case 202: e = run<2, 2>(xp, rp, yp, n, nvec, grid, hs); break;
+      case 402: e = run<4, 2>(xp, rp, yp, n, nvec, grid, hs); break;
+      case 403: e = run<4, 3>(xp, rp, yp, n, nvec, grid, hs); break;
+      case 404: e = run<4, 4>(xp, rp, yp, n, nvec, grid, hs); break;
+      default: return -1;
+    }
+    if (e != hipSuccess) return -2;
   }
-  return e == hipSuccess ? 0 : -2;
+  return 0;
 }
 
 // ---------------------------------------------------------------- test kernel

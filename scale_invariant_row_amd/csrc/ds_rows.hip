@@ -109,6 +109,19 @@ int grid_for(int64_t units, int cus) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DS_OK : DS_ERR_LAUNCH; }
 
+// For kernels that take one row group per workgroup, with no grid-stride
+// loop: launch(r0, n) over rows [r0, r0 + n), in pieces of at most the grid
+// cap of row groups (rows_per_group rows each).
+template <class F>
+hipError_t launch_in_pieces(int64_t rows, int rows_per_group, int cus, F&& launch) {
+  const int64_t piece = (int64_t)grid_for(INT64_MAX, cus) * rows_per_group;
+  for (int64_t r0 = 0; r0 < rows; r0 += piece) {
+    const hipError_t e = launch(r0, std::min<int64_t>(piece, rows - r0));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // ----------------------------------------------------- descriptor staging
 //
 // A ring of pinned host + device buffers per device.  A slot is filled on the
@@ -557,10 +570,13 @@ int norm_rows(ForwardLaunch launch, const uint16_t* x, const uint16_t* r, uint16
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
-  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  const int rpg = s.rows_per_block();
   (void)hipGetLastError();   // start from a clean error state
-  return launch_status(launch(s, x, r, y, rows, (int)(cols / 8), eps, grid_for(units, cus),
-                              (hipStream_t)stream));
+  return launch_status(launch_in_pieces(rows, rpg, cus, [&](int64_t r0, int64_t n) {
+    const int64_t at = r0 * cols;
+    return launch(s, x + at, r != nullptr ? r + at : nullptr, y + at, n, (int)(cols / 8), eps,
+                  (int)((n + rpg - 1) / rpg), (hipStream_t)stream);
+  }));
 }
 
 using BackwardLaunch = hipError_t (*)(Shape, const void*, const void*, const void*, void*,
@@ -575,10 +591,13 @@ int norm_rows_backward(BackwardLaunch launch, const uint16_t* x, const uint16_t*
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
-  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  const int rpg = s.rows_per_block();
   (void)hipGetLastError();
-  return launch_status(launch(s, x, r, dy, dx, rows, (int)(cols / 8), eps, grid_for(units, cus),
-                              (hipStream_t)stream));
+  return launch_status(launch_in_pieces(rows, rpg, cus, [&](int64_t r0, int64_t n) {
+    const int64_t at = r0 * cols;
+    return launch(s, x + at, r != nullptr ? r + at : nullptr, dy + at, dx + at, n,
+                  (int)(cols / 8), eps, (int)((n + rpg - 1) / rpg), (hipStream_t)stream);
+  }));
 }
 
 }  // namespace
@@ -610,10 +629,13 @@ int ds_slerp_rows(const uint16_t* res, const uint16_t* out, const float* alpha, 
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
-  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  const int rpg = s.rows_per_block();
   (void)hipGetLastError();
-  return launch_status(dsr::launch_slerp_rows(s, res, out, alpha, h, rows, (int)(cols / 8), eps,
-                                              grid_for(units, cus), (hipStream_t)stream));
+  return launch_status(launch_in_pieces(rows, rpg, cus, [&](int64_t r0, int64_t n) {
+    const int64_t at = r0 * cols;
+    return dsr::launch_slerp_rows(s, res + at, out + at, alpha, h + at, n, (int)(cols / 8), eps,
+                                  (int)((n + rpg - 1) / rpg), (hipStream_t)stream);
+  }));
 }
 
 namespace {
@@ -648,10 +670,13 @@ int ds_gate_l2_rows(const uint16_t* o, const uint16_t* g, const float* sg, uint1
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
-  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  const int rpg = s.rows_per_block();
   (void)hipGetLastError();
-  return launch_status(dsr::launch_gate_l2_rows(s, o, g, sg, y, rows, (int)(cols / 8), eps,
-                                                grid_for(units, cus), (hipStream_t)stream));
+  return launch_status(launch_in_pieces(rows, rpg, cus, [&](int64_t r0, int64_t n) {
+    const int64_t at = r0 * cols;
+    return dsr::launch_gate_l2_rows(s, o + at, g + at, sg, y + at, n, (int)(cols / 8), eps,
+                                    (int)((n + rpg - 1) / rpg), (hipStream_t)stream);
+  }));
 }
 
 int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, const float* suu,
@@ -662,11 +687,14 @@ int ds_swiglu_l2_rows(const uint16_t* g, const uint16_t* u, const float* sug, co
   if (!s.ok()) return DS_ERR_SHAPE;
   int cus = 0;
   if ((st = device_cus(&cus)) != DS_OK) return st;
-  const int64_t units = (rows + s.rows_per_block() - 1) / s.rows_per_block();
+  const int rpg = s.rows_per_block();
   (void)hipGetLastError();
-  return launch_status(dsr::launch_swiglu_l2_rows(s, g, u, sug, suu, y, rows, (int)(cols / 8),
-                                                  eps, grid_for(units, cus), cus,
-                                                  (hipStream_t)stream));
+  return launch_status(launch_in_pieces(rows, rpg, cus, [&](int64_t r0, int64_t n) {
+    const int64_t at = r0 * cols;
+    return dsr::launch_swiglu_l2_rows(s, g + at, u + at, sug, suu, y + at, n, (int)(cols / 8),
+                                      eps, (int)((n + rpg - 1) / rpg), cus,
+                                      (hipStream_t)stream);
+  }));
 }
 
 namespace {
@@ -768,9 +796,17 @@ int ds_qk_rows_l2(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk
   a.nk = n_kv_heads;
   a.eps = eps;
   (void)hipGetLastError();
-  const int64_t units = (rows + dsr::kQkRowsPerBlock - 1) / dsr::kQkRowsPerBlock;
-  return launch_status(dsr::launch_qk_rows_l2(head_dim, a, grid_for(units, cus),
-                                              (hipStream_t)stream));
+  const int rpg = dsr::kQkRowsPerBlock;
+  return launch_status(launch_in_pieces(rows, rpg, cus, [&](int64_t r0, int64_t n) {
+    dsr::QkArgs p = a;
+    p.q = q != nullptr ? q + r0 * ldq : nullptr;
+    p.k = k != nullptr ? k + r0 * ldk : nullptr;
+    p.pos = positions + r0;
+    p.qo = q_out != nullptr ? q_out + r0 * ldq_out : nullptr;
+    p.ko = k_out != nullptr ? k_out + r0 * ldk_out : nullptr;
+    p.rows = n;
+    return dsr::launch_qk_rows_l2(head_dim, p, (int)((n + rpg - 1) / rpg), (hipStream_t)stream);
+  }));
 }
 
 int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n, ds_stream_t stream) {

@@ -467,9 +467,9 @@ l2_rows_kernel(const u32x4_t* x, const u32x4_t* r, u32x4_t* y, int64_t rows, int
   geo.offsets(off, 16);
   const uint32_t row_bytes = (uint32_t)nvec * 16u;
 
-  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
-    const int64_t row = base + geo.rr;
-    if (G == 1 && row >= rows) break;             // waves of a G == 1 group are independent
+  {
+    const int64_t row = (int64_t)blockIdx.x * R + geo.rr;   // one row group per workgroup
+    if (G == 1 && row >= rows) return;            // waves of a G == 1 group are independent
     Bf16Row<V> s;
     s.load(RowBuf(x + row * nvec, row_bytes), off);
     if constexpr (RES) {
@@ -514,9 +514,9 @@ l2_rows_backward_kernel(const u32x4_t* x, const u32x4_t* r, const u32x4_t* dy, u
   const uint32_t row_bytes = (uint32_t)nvec * 16u;
   const float n = (float)(8 * nvec);
 
-  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
-    const int64_t row = base + geo.rr;
-    if (G == 1 && row >= rows) break;
+  {
+    const int64_t row = (int64_t)blockIdx.x * R + geo.rr;   // one row group per workgroup
+    if (G == 1 && row >= rows) return;
     Bf16Row<V> s, d;
     s.load(RowBuf(x + row * nvec, row_bytes), off);
     if constexpr (RES) {
@@ -592,7 +592,7 @@ template <int V>
 struct AbsAlpha {
   static constexpr bool kHeld = V <= 4;
   float a[kHeld ? V : 1][8];
-  __device__ __forceinline__ void load_into(float (&dst)[8], const RowBuf& b, int off) const {
+  static __device__ __forceinline__ void load_into(float (&dst)[8], const RowBuf& b, int off) {
     const f32x4_t a0 = b.ld16f_cached(2 * off);
     const f32x4_t a1 = b.ld16f_cached(2 * off + 16);
     dst[0] = fabsf(a0.x); dst[1] = fabsf(a0.y); dst[2] = fabsf(a0.z); dst[3] = fabsf(a0.w);
@@ -606,6 +606,296 @@ struct AbsAlpha {
   }
 };
 
+// One row with the rescues inline, the row and its u held in registers
+// (u recomputed for V > 4): the kernel's path for wide shapes.
+template <int G, int V>
+__device__ __forceinline__ void slerp_row_full(const u32x4_t* res, const u32x4_t* out,
+                                               const RowBuf& abuf, const AbsAlpha<V>& al,
+                                               u32x4_t* h, int64_t row, int nvec, float eps,
+                                               GroupScratch<G>& gs, int& slot, const Geo<G>& geo,
+                                               const int (&off)[V]) {
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  Bf16Row<V> a, b;
+  a.load(RowBuf(res + row * nvec, row_bytes), off);
+  b.load(RowBuf(out + row * nvec, row_bytes), off);
+  float S[2] = {wave_sum(a.sumsq()), wave_sum(b.sumsq())};
+  a.fence();
+  b.fence();
+  group_sum<G, 2>(S, gs.next(slot), geo.g, geo.lane);
+  l2_in_place<G, V>(a, S[0], eps, gs, slot, geo);   // a = bf16(l2(res))
+  l2_in_place<G, V>(b, S[1], eps, gs, slot, geo);   // b = bf16(l2(out))
+
+  // u = a + |alpha| * (b - a), three rounded fp32 steps.  Narrow shapes keep
+  // u in VGPRs; wide ones (V > 4) recompute it, bit for bit, when storing.
+  constexpr bool kKeepU = V <= 4;
+  float u[kKeepU ? V : 1][8];
+  // Wide shapes unpack a and b and re-load alpha (an L2 hit) in each pass:
+  // the fences and the empty asm with a memory clobber stop the compiler
+  // from keeping the first pass's unpacked values and alpha alive instead,
+  // which would spill.  None of them emits an instruction.
+  auto reload_point = [&]() {
+    if constexpr (!kKeepU) {
+      a.fence();
+      b.fence();
+      asm volatile("" ::: "memory");
+    }
+  };
+  auto lerp = [&](int v, float (&uv)[8]) {
+    float tmp[8];
+    if constexpr (!kKeepU) asm volatile("" ::: "memory");   // one vector's alpha at a time
+    if constexpr (!AbsAlpha<V>::kHeld) al.load_into(tmp, abuf, off[v]);
+    const float* alv = AbsAlpha<V>::kHeld ? al.a[AbsAlpha<V>::kHeld ? v : 0] : tmp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float alo = bf_lo(a.p[v][k]), ahi = bf_hi(a.p[v][k]);
+      const float blo = bf_lo(b.p[v][k]), bhi = bf_hi(b.p[v][k]);
+      const float dlo = blo - alo, dhi = bhi - ahi;
+      const float tlo = alv[2 * k] * dlo, thi = alv[2 * k + 1] * dhi;
+      uv[2 * k] = alo + tlo;
+      uv[2 * k + 1] = ahi + thi;
+    }
+  };
+  float a0 = 0.f, a1 = 0.f;
+  float m = 0.f;
+  reload_point();
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float t[8];
+    lerp(v, t);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a0 = __builtin_fmaf(t[2 * k], t[2 * k], a0);
+      a1 = __builtin_fmaf(t[2 * k + 1], t[2 * k + 1], a1);
+    }
+    if constexpr (kKeepU) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) u[v][k] = t[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(t[k]));
+    }
+  }
+  float Su[1] = {wave_sum(a0 + a1)};
+  group_sum<G, 1>(Su, gs.next(slot), geo.g, geo.lane);
+
+  float T = Su[0] + eps;
+  bool scaled = false;
+  int sh = 0;
+  if (T == __builtin_inff() || T < kTiny) {          // uniform over the group
+    if constexpr (kKeepU) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(u[v][k]));
+    }
+    m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
+    if ((m > 0.f || eps > 0.f) && m < __builtin_inff()) {
+      sh = rescue_shift(m, eps);
+      float c0 = 0.f, c1 = 0.f;
+      reload_point();
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float t[8];
+        if constexpr (kKeepU) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) t[k] = u[v][k];
+        } else {
+          lerp(v, t);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = ldexpf(t[2 * k], sh), hi = ldexpf(t[2 * k + 1], sh);
+          c0 = __builtin_fmaf(lo, lo, c0);
+          c1 = __builtin_fmaf(hi, hi, c1);
+        }
+      }
+      float tt[1] = {wave_sum(c0 + c1)};
+      group_sum<G, 1>(tt, gs.next(slot), geo.g, geo.lane);
+      T = tt[0] + ldexpf(eps, 2 * sh);
+      scaled = true;
+    }
+  }
+  const float inv = inv_sqrt(T);
+  const RowBuf hb(h + row * nvec, row_bytes);
+  reload_point();
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float t[8];
+    if constexpr (kKeepU) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = u[v][k];
+    } else {
+      lerp(v, t);
+    }
+    uint32_t q[4];
+    if (scaled) {
+      // a branch of its own (the empty asm keeps the compiler from turning
+      // it into an ldexp and a select on every element of the common path)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = ldexpf(t[k], sh);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = pack_bf16(t[2 * k] * inv, t[2 * k + 1] * inv);
+    u32x4_t w = {q[0], q[1], q[2], q[3]};
+    hb.st16(w, off[v]);
+  }
+}
+
+// Whether a sum handed to inv_sqrt needs no rescue (the row kernels' range).
+__device__ __forceinline__ bool plain_sum(float T) {
+  return !(T == __builtin_inff() || T < kTiny);
+}
+
+// One row with a sum out of range, from memory: the same arithmetic as
+// slerp_row_full, in the same order, one 16-byte vector at a time (each pass
+// reads the row again), so it needs few registers beside the common path.
+// S: the row's sums of squares of res and out, already combined.
+template <int G, int V>
+__device__ __forceinline__ void slerp_row_rescue(const u32x4_t* res, const u32x4_t* out,
+                                                 const RowBuf& abuf, u32x4_t* h, int64_t row,
+                                                 int nvec, float eps, const float (&S)[2],
+                                                 GroupScratch<G>& gs, int& slot,
+                                                 const Geo<G>& geo, const int (&off)[V]) {
+  const uint32_t row_bytes = (uint32_t)nvec * 16u;
+  const RowBuf rb[2] = {RowBuf(res + row * nvec, row_bytes), RowBuf(out + row * nvec, row_bytes)};
+  // l2_in_place's scaling of each input: p <- bf16(p inv) or bf16((p 2^sh) inv)
+  float inv[2];
+  bool sc[2];
+  int sh[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float T = S[i] + eps;
+    sc[i] = false;
+    sh[i] = 0;
+    if (!plain_sum(T)) {
+      u16x2_t mx = {0, 0};
+#pragma unroll 1
+      for (int v = 0; v < V; ++v) {
+        const u32x4_t p = rb[i].ld16(off[v]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, p[k] & 0x7fff7fffu));
+      }
+      const float m = group_max<G>(wave_max(__uint_as_float((uint32_t)(mx.x > mx.y ? mx.x : mx.y) << 16)),
+                                   gs.next(slot), geo.g, geo.lane);
+      if ((m > 0.f || eps > 0.f) && m < __builtin_inff()) {
+        sh[i] = rescue_shift(m, eps);
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll 1
+        for (int v = 0; v < V; ++v) {
+          const u32x4_t p = rb[i].ld16(off[v]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float lo = ldexpf(bf_lo(p[k]), sh[i]), hi = ldexpf(bf_hi(p[k]), sh[i]);
+            a0 = __builtin_fmaf(lo, lo, a0);
+            a1 = __builtin_fmaf(hi, hi, a1);
+          }
+        }
+        float t[1] = {wave_sum(a0 + a1)};
+        group_sum<G, 1>(t, gs.next(slot), geo.g, geo.lane);
+        T = t[0] + ldexpf(eps, 2 * sh[i]);
+        sc[i] = true;
+      }
+    }
+    inv[i] = inv_sqrt(T);
+  }
+  // u for vector v: a and b rounded as above, then the lerp's three steps
+  auto u_of = [&](int v, float (&uv)[8]) {
+    float al[8];
+    AbsAlpha<V>::load_into(al, abuf, off[v]);
+    uint32_t q[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4_t p = rb[i].ld16(off[v]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = sc[i] ? ldexpf(bf_lo(p[k]), sh[i]) : bf_lo(p[k]);
+        const float hi = sc[i] ? ldexpf(bf_hi(p[k]), sh[i]) : bf_hi(p[k]);
+        q[i][k] = pack_bf16(lo * inv[i], hi * inv[i]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float alo = bf_lo(q[0][k]), ahi = bf_hi(q[0][k]);
+      const float blo = bf_lo(q[1][k]), bhi = bf_hi(q[1][k]);
+      const float dlo = blo - alo, dhi = bhi - ahi;
+      const float tlo = al[2 * k] * dlo, thi = al[2 * k + 1] * dhi;
+      uv[2 * k] = alo + tlo;
+      uv[2 * k + 1] = ahi + thi;
+    }
+  };
+  float a0 = 0.f, a1 = 0.f, m = 0.f;
+#pragma unroll 1
+  for (int v = 0; v < V; ++v) {
+    float t[8];
+    u_of(v, t);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a0 = __builtin_fmaf(t[2 * k], t[2 * k], a0);
+      a1 = __builtin_fmaf(t[2 * k + 1], t[2 * k + 1], a1);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(t[k]));
+  }
+  float Su[1] = {wave_sum(a0 + a1)};
+  group_sum<G, 1>(Su, gs.next(slot), geo.g, geo.lane);
+  float T = Su[0] + eps;
+  bool scaled = false;
+  int shu = 0;
+  if (!plain_sum(T)) {                                 // uniform over the group
+    m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
+    if ((m > 0.f || eps > 0.f) && m < __builtin_inff()) {
+      shu = rescue_shift(m, eps);
+      float c0 = 0.f, c1 = 0.f;
+#pragma unroll 1
+      for (int v = 0; v < V; ++v) {
+        float t[8];
+        u_of(v, t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = ldexpf(t[2 * k], shu), hi = ldexpf(t[2 * k + 1], shu);
+          c0 = __builtin_fmaf(lo, lo, c0);
+          c1 = __builtin_fmaf(hi, hi, c1);
+        }
+      }
+      float tt[1] = {wave_sum(c0 + c1)};
+      group_sum<G, 1>(tt, gs.next(slot), geo.g, geo.lane);
+      T = tt[0] + ldexpf(eps, 2 * shu);
+      scaled = true;
+    }
+  }
+  const float invu = inv_sqrt(T);
+  const RowBuf hb(h + row * nvec, row_bytes);
+  // every wave has read all of its vectors before the first barrier above,
+  // so writing h over res or out (in place) reads nothing it wrote
+#pragma unroll 1
+  for (int v = 0; v < V; ++v) {
+    float t[8];
+    u_of(v, t);
+    if (scaled) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = ldexpf(t[k], shu);
+    }
+    u32x4_t w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = pack_bf16(t[2 * k] * invu, t[2 * k + 1] * invu);
+    hb.st16(w, off[v]);
+  }
+}
+
+// The kernel.  The launcher gives every row group its own workgroup (a call
+// with more row groups than one launch should hold runs as several
+// launches).  Shapes up to V = 4 run a row straight through, with no rescue
+// branch in the way of the schedule: a and b are loaded, then |alpha|; only a
+// row whose sum falls outside the range (S + eps overflowing or below 2^-96,
+// rare) is done again by slerp_row_rescue, from memory, before anything of it
+// is stored.  Wider shapes take slerp_row_full.  V < 4 runs its one row with
+// no loop; V >= 4 keeps a grid-stride loop (which runs once).  Measured on
+// MI355X against the previous kernel (slerp_row_full in a grid-stride loop):
+//   8,192 x 4,096 (4, 2): 34.4 -> 33.9 us; with the loop, 34.6;
+//   8,192 x 7,168 (4, 4): 58.4-59.0 -> 59.2 us; without the loop, 59.6-59.8;
+//   4,096 x 16,384 (8, 4): 69.9 -> 68.3 us; without the loop, 69.0.
 template <int G, int V>
 __global__ void __launch_bounds__(Geo<G>::THREADS)
 slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, u32x4_t* h,
@@ -619,136 +909,69 @@ slerp_rows_kernel(const u32x4_t* res, const u32x4_t* out, const f32x4_t* alpha, 
   const uint32_t row_bytes = (uint32_t)nvec * 16u;
   const RowBuf abuf(alpha, row_bytes * 2u);        // alpha: cols fp32 = 2 x row_bytes
   AbsAlpha<V> al;
-  al.init(abuf, off);
+  if constexpr (V > 4) al.init(abuf, off);
 
-  for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
-    const int64_t row = base + geo.rr;
-    if (G == 1 && row >= rows) break;
-    Bf16Row<V> a, b;
-    a.load(RowBuf(res + row * nvec, row_bytes), off);
-    b.load(RowBuf(out + row * nvec, row_bytes), off);
-    float S[2] = {wave_sum(a.sumsq()), wave_sum(b.sumsq())};
-    a.fence();
-    b.fence();
-    group_sum<G, 2>(S, gs.next(slot), geo.g, geo.lane);
-    l2_in_place<G, V>(a, S[0], eps, gs, slot, geo);   // a = bf16(l2(res))
-    l2_in_place<G, V>(b, S[1], eps, gs, slot, geo);   // b = bf16(l2(out))
-
-    // u = a + |alpha| * (b - a), three rounded fp32 steps.  Narrow shapes keep
-    // u in VGPRs; wide ones (V > 4) recompute it, bit for bit, when storing.
-    constexpr bool kKeepU = V <= 4;
-    float u[kKeepU ? V : 1][8];
-    // Wide shapes unpack a and b and re-load alpha (an L2 hit) in each pass:
-    // the fences and the empty asm with a memory clobber stop the compiler
-    // from keeping the first pass's unpacked values and alpha alive instead,
-    // which would spill.  None of them emits an instruction.
-    auto reload_point = [&]() {
-      if constexpr (!kKeepU) {
-        a.fence();
-        b.fence();
-        asm volatile("" ::: "memory");
-      }
-    };
-    auto lerp = [&](int v, float (&uv)[8]) {
-      float tmp[8];
-      if constexpr (!kKeepU) asm volatile("" ::: "memory");   // one vector's alpha at a time
-      if constexpr (!AbsAlpha<V>::kHeld) al.load_into(tmp, abuf, off[v]);
-      const float* alv = AbsAlpha<V>::kHeld ? al.a[AbsAlpha<V>::kHeld ? v : 0] : tmp;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float alo = bf_lo(a.p[v][k]), ahi = bf_hi(a.p[v][k]);
-        const float blo = bf_lo(b.p[v][k]), bhi = bf_hi(b.p[v][k]);
-        const float dlo = blo - alo, dhi = bhi - ahi;
-        const float tlo = alv[2 * k] * dlo, thi = alv[2 * k + 1] * dhi;
-        uv[2 * k] = alo + tlo;
-        uv[2 * k + 1] = ahi + thi;
-      }
-    };
-    float a0 = 0.f, a1 = 0.f;
-    float m = 0.f;
-    reload_point();
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      float t[8];
-      lerp(v, t);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        a0 = __builtin_fmaf(t[2 * k], t[2 * k], a0);
-        a1 = __builtin_fmaf(t[2 * k + 1], t[2 * k + 1], a1);
-      }
-      if constexpr (kKeepU) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) u[v][k] = t[k];
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(t[k]));
-      }
-    }
-    float Su[1] = {wave_sum(a0 + a1)};
-    group_sum<G, 1>(Su, gs.next(slot), geo.g, geo.lane);
-
-    float T = Su[0] + eps;
-    bool scaled = false;
-    int sh = 0;
-    if (T == __builtin_inff() || T < kTiny) {          // uniform over the group
-      if constexpr (kKeepU) {
+  auto do_row = [&](int64_t row) {
+    if constexpr (V > 4) {
+      slerp_row_full<G, V>(res, out, abuf, al, h, row, nvec, eps, gs, slot, geo, off);
+    } else {
+      Bf16Row<V> a, b;
+      a.load(RowBuf(res + row * nvec, row_bytes), off);
+      b.load(RowBuf(out + row * nvec, row_bytes), off);
+      al.init(abuf, off);
+      float S[2] = {wave_sum(a.sumsq()), wave_sum(b.sumsq())};
+      a.fence();
+      b.fence();
+      group_sum<G, 2>(S, gs.next(slot), geo.g, geo.lane);
+      bool done = false;
+      if (plain_sum(S[0] + eps) && plain_sum(S[1] + eps)) {    // uniform over the group
+        a.scale(inv_sqrt(S[0] + eps), false, 0);                 // a = bf16(l2(res))
+        b.scale(inv_sqrt(S[1] + eps), false, 0);                 // b = bf16(l2(out))
+        // u = a + |alpha| (b - a), three rounded fp32 steps
+        float u[V][8];
+        float c0 = 0.f, c1 = 0.f;
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
-          for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(u[v][k]));
-      }
-      m = group_max<G>(wave_max(m), gs.next(slot), geo.g, geo.lane);
-      if ((m > 0.f || eps > 0.f) && m < __builtin_inff()) {
-        sh = rescue_shift(m, eps);
-        float c0 = 0.f, c1 = 0.f;
-        reload_point();
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          float t[8];
-          if constexpr (kKeepU) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) t[k] = u[v][k];
-          } else {
-            lerp(v, t);
-          }
-#pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const float lo = ldexpf(t[2 * k], sh), hi = ldexpf(t[2 * k + 1], sh);
-            c0 = __builtin_fmaf(lo, lo, c0);
-            c1 = __builtin_fmaf(hi, hi, c1);
+            const float alo = bf_lo(a.p[v][k]), ahi = bf_hi(a.p[v][k]);
+            const float blo = bf_lo(b.p[v][k]), bhi = bf_hi(b.p[v][k]);
+            const float dlo = blo - alo, dhi = bhi - ahi;
+            const float tlo = al.a[v][2 * k] * dlo, thi = al.a[v][2 * k + 1] * dhi;
+            u[v][2 * k] = alo + tlo;
+            u[v][2 * k + 1] = ahi + thi;
+            c0 = __builtin_fmaf(u[v][2 * k], u[v][2 * k], c0);
+            c1 = __builtin_fmaf(u[v][2 * k + 1], u[v][2 * k + 1], c1);
           }
+        float Su[1] = {wave_sum(c0 + c1)};
+        group_sum<G, 1>(Su, gs.next(slot), geo.g, geo.lane);
+        if (plain_sum(Su[0] + eps)) {                            // uniform over the group
+          const float inv = inv_sqrt(Su[0] + eps);
+          const RowBuf hb(h + row * nvec, row_bytes);
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            u32x4_t w;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = pack_bf16(u[v][2 * k] * inv, u[v][2 * k + 1] * inv);
+            hb.st16(w, off[v]);
+          }
+          done = true;
         }
-        float tt[1] = {wave_sum(c0 + c1)};
-        group_sum<G, 1>(tt, gs.next(slot), geo.g, geo.lane);
-        T = tt[0] + ldexpf(eps, 2 * sh);
-        scaled = true;
       }
+      if (__builtin_expect(!done, 0))
+        slerp_row_rescue<G, V>(res, out, abuf, h, row, nvec, eps, S, gs, slot, geo, off);
     }
-    const float inv = inv_sqrt(T);
-    const RowBuf hb(h + row * nvec, row_bytes);
-    reload_point();
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      float t[8];
-      if constexpr (kKeepU) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) t[k] = u[v][k];
-      } else {
-        lerp(v, t);
-      }
-      uint32_t q[4];
-      if (scaled) {
-        // a branch of its own (the empty asm keeps the compiler from turning
-        // it into an ldexp and a select on every element of the common path)
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int k = 0; k < 8; ++k) t[k] = ldexpf(t[k], sh);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) q[k] = pack_bf16(t[2 * k] * inv, t[2 * k + 1] * inv);
-      u32x4_t w = {q[0], q[1], q[2], q[3]};
-      hb.st16(w, off[v]);
+  };
+  if constexpr (V >= 4) {
+    for (int64_t base = (int64_t)blockIdx.x * R; base < rows; base += (int64_t)gridDim.x * R) {
+      const int64_t row = base + geo.rr;
+      if (G == 1 && row >= rows) break;
+      do_row(row);
     }
+  } else {
+    const int64_t row = (int64_t)blockIdx.x * R + geo.rr;
+    if (G == 1 && row >= rows) return;            // waves of a G == 1 group are independent
+    do_row(row);
   }
 }
 
@@ -1091,10 +1314,11 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
   const int lo[2] = {min(first, nsteps[0]), max(0, min(first - nsteps[0], nsteps[1]))};
   const int hi[2] = {min(last, nsteps[0]), max(0, min(last - nsteps[0], nsteps[1]))};
 
-  // every wave runs every iteration (the barrier is workgroup-wide); a wave
-  // whose row is past the end only takes part in the barrier
-  for (int64_t base = (int64_t)blockIdx.x * kQkRowsPerBlock; base < a.rows;
-       base += (int64_t)gridDim.x * kQkRowsPerBlock) {
+  // one row group per workgroup (no loop); every wave takes part in the
+  // barrier (it is workgroup-wide), and a wave whose row is past the end
+  // leaves after it
+  {
+    const int64_t base = (int64_t)blockIdx.x * kQkRowsPerBlock;
     const int64_t row = base + rsub;
     const bool valid = row < a.rows;
     float(&cs)[2][NF] = trig[buf][rsub];
@@ -1106,7 +1330,7 @@ __global__ void __launch_bounds__(256) qk_rows_l2_kernel(const QkArgs a) {
       cs[1][fi] = sv;
     }
     __syncthreads();
-    if (!valid) continue;
+    if (!valid) return;
     float c[NV], s[NV];
 #pragma unroll
     for (int q4 = 0; q4 < NV / 4; ++q4) {

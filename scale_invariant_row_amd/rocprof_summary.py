@@ -139,10 +139,14 @@ def bench_launches() -> Dict[Tuple[str, Optional[int]], Tuple[str, int, int, int
 
     def rows_launch(kernel, rows, cols, per_block, threads, rd_per_elt, wr_per_elt, extra_rd,
                     label):
+        # one row group per workgroup, a call split into launches of at most
+        # 64 row groups per compute unit (equal pieces for these workloads)
         units = -(-rows // per_block)
+        pieces = -(-units // (64 * CUS))
         grid = min(units, 64 * CUS) * threads
-        n = rows * cols
-        t[(kernel, grid)] = (label, n * rd_per_elt + extra_rd, n * wr_per_elt, n)
+        n = rows * cols // pieces
+        t[(kernel, grid)] = (label if pieces == 1 else f"{label} (one of {pieces} launches)",
+                             n * rd_per_elt + extra_rd, n * wr_per_elt, n)
 
     rows_launch("l2_rows_kernel<4, 2, true, false>", 8192, 4096, 1, 256, 4, 2, 0,
                 "l2_rows + residual 8192x4096")

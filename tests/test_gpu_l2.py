@@ -117,6 +117,13 @@ def test_workload_stress_32768x8192(B):
     got = host_bits(y)[ints[:100]]
     rep = admissible_l2_rows(got, c.x[ints[:100]], c.r[ints[:100]], c.eps, depth=0)
     assert rep.ok, str(rep)
+    # the call runs as two launches (64 one-row workgroups per compute unit
+    # each): rows across the seam, alone, give the same bits
+    piece = torch.cuda.get_device_properties(0).multi_processor_count * 64
+    a, b = piece - 500, piece + 500
+    ys = B.ds_l2_rows(xd[a:b].contiguous(), rd[a:b].contiguous(), c.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(ys.view(torch.int16), y[a:b].view(torch.int16))
     # the same workload without the residual
     y0 = B.ds_l2_rows(xd, None, c.eps)
     torch.cuda.synchronize()

@@ -73,6 +73,27 @@ def test_workloads(B, name):
     assert torch.equal(hs.view(torch.int16), h[a:b].view(torch.int16))
 
 
+def test_more_rows_than_one_launch(B):
+    """A call with more row groups than one launch takes (64 per compute unit)
+    runs as several launches: rows on both sides of the seam meet the oracle,
+    and any run of rows alone gives the same bits as inside the whole call."""
+    import torch
+    cols = 4096                                   # one row per workgroup at this width
+    piece = torch.cuda.get_device_properties(0).multi_processor_count * 64
+    rows = piece + 116
+    c = inputs.slerp_case(rows, cols, 7171)
+    announce("slerp_rows over several launches", rows, cols)
+    rd, od, ad = dev_bits(c.res), dev_bits(c.out), dev_f32(c.alpha)
+    h = B.ds_slerp_rows(rd, od, ad, c.eps)
+    torch.cuda.synchronize()
+    idx = np.unique(np.r_[0, piece - 3:piece + 3, rows - 2:rows, sample_rows(rows, 60, 17)])
+    full_check(host_bits(h)[idx], c.res[idx], c.out[idx], c.alpha, c.eps, "several launches")
+    a, b = piece - 100, rows
+    hs = B.ds_slerp_rows(rd[a:b].contiguous(), od[a:b].contiguous(), ad, c.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(hs.view(torch.int16), h[a:b].view(torch.int16))
+
+
 def test_alpha_special_cases(B):
     """alpha = 0 (h = l2(a)), alpha = 1 (h = l2(b)), res == out (h = l2(a))."""
     c = inputs.slerp_case(40, 4096, 701)
