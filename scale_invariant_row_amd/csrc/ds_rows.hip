@@ -100,11 +100,25 @@ int device_cus(int* cus) {
   return DS_OK;
 }
 
-// Workgroups for `units` row groups: one per group up to a cap well above
-// what the chip holds at once; past it the kernels loop (grid-stride).
+// Workgroups for `units` row groups (or items): one each, up to 64 per
+// compute unit in a launch, well above what the chip holds at once.  Past
+// that the ragged kernels loop (grid-stride) and the row kernels run as
+// several launches (launch_in_pieces).  A cap of 2^20 workgroups measured
+// the same (GPT-2's 768-wide linears, 18,432 items: 89.6-89.9 against
+// 89.8-90.3 us forward).  DS_ROWS_TEST_MAX_GROUPS lowers the cap: a test
+// hook that runs the several-launch and grid-stride paths at small sizes.
+int64_t max_launch_groups(int cus) {
+  const int64_t cap = (int64_t)cus * 64;
+  const char* e = std::getenv("DS_ROWS_TEST_MAX_GROUPS");
+  if (e != nullptr) {
+    const long long v = std::atoll(e);
+    if (v >= 1 && v < cap) return v;
+  }
+  return cap;
+}
+
 int grid_for(int64_t units, int cus) {
-  int64_t cap = (int64_t)cus * 64;
-  return (int)std::max<int64_t>(1, std::min(units, cap));
+  return (int)std::max<int64_t>(1, std::min(units, max_launch_groups(cus)));
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DS_OK : DS_ERR_LAUNCH; }
@@ -114,7 +128,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? DS_OK : DS_ERR_LAUNCH
 // cap of row groups (rows_per_group rows each).
 template <class F>
 hipError_t launch_in_pieces(int64_t rows, int rows_per_group, int cus, F&& launch) {
-  const int64_t piece = (int64_t)grid_for(INT64_MAX, cus) * rows_per_group;
+  const int64_t piece = max_launch_groups(cus) * rows_per_group;
   for (int64_t r0 = 0; r0 < rows; r0 += piece) {
     const hipError_t e = launch(r0, std::min<int64_t>(piece, rows - r0));
     if (e != hipSuccess) return e;

@@ -41,7 +41,8 @@ from typing import Dict, List, Optional, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 HBM_PEAK_GBPS = 8000.0
-CUS = 256                        # MI355X compute units (the launch grids bench.py makes)
+CUS = 256                        # MI355X compute units
+MAX_LAUNCH_GROUPS = 64 * CUS     # workgroups per launch, at most (the library's grid cap)
 XCDS = 8                         # accelerator complex dies: GRBM counters are summed over them
 COPY_BYTES = 8192 * 4096 * 3     # bench.py's torch copy: one 100,663,296-byte buffer
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -120,7 +121,7 @@ def _ragged(mats, op: str, gi, lim) -> List[Tuple[str, int, int, int, int]]:
             G, V, NE = next(iter(cls))
             extra = {"fwd": "", "bwd": "", "project": ", false", "after": ", true"}[op]
             kname = f"{base}_kernel<{G}, {V}, {NE}{extra}>"
-        grid = min(items, 64 * CUS) * threads
+        grid = min(items, MAX_LAUNCH_GROUPS) * threads
         rd = wr = el = 0
         for ms, _, _ in cls.values():
             for rows, cols, re_, we, rr, wr_ in ms:
@@ -140,10 +141,10 @@ def bench_launches() -> Dict[Tuple[str, Optional[int]], Tuple[str, int, int, int
     def rows_launch(kernel, rows, cols, per_block, threads, rd_per_elt, wr_per_elt, extra_rd,
                     label):
         # one row group per workgroup, a call split into launches of at most
-        # 64 row groups per compute unit (equal pieces for these workloads)
+        # MAX_LAUNCH_GROUPS row groups (equal pieces for these workloads)
         units = -(-rows // per_block)
-        pieces = -(-units // (64 * CUS))
-        grid = min(units, 64 * CUS) * threads
+        pieces = -(-units // MAX_LAUNCH_GROUPS)
+        grid = min(units, MAX_LAUNCH_GROUPS) * threads
         n = rows * cols // pieces
         t[(kernel, grid)] = (label if pieces == 1 else f"{label} (one of {pieces} launches)",
                              n * rd_per_elt + extra_rd, n * wr_per_elt, n)

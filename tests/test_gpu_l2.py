@@ -117,18 +117,35 @@ def test_workload_stress_32768x8192(B):
     got = host_bits(y)[ints[:100]]
     rep = admissible_l2_rows(got, c.x[ints[:100]], c.r[ints[:100]], c.eps, depth=0)
     assert rep.ok, str(rep)
-    # the call runs as two launches (64 one-row workgroups per compute unit
-    # each): rows across the seam, alone, give the same bits
-    piece = torch.cuda.get_device_properties(0).multi_processor_count * 64
-    a, b = piece - 500, piece + 500
-    ys = B.ds_l2_rows(xd[a:b].contiguous(), rd[a:b].contiguous(), c.eps)
-    torch.cuda.synchronize()
-    assert torch.equal(ys.view(torch.int16), y[a:b].view(torch.int16))
     # the same workload without the residual
     y0 = B.ds_l2_rows(xd, None, c.eps)
     torch.cuda.synchronize()
     idx = sample_rows(c.rows, 200, 8, must)
     full_check(host_bits(y0)[idx], c.x[idx], None, c.eps, c.name + " r=NULL")
+
+
+def test_more_rows_than_one_launch(B, monkeypatch):
+    """l2_rows, rms_rows and their gradients over several launches
+    (DS_ROWS_TEST_MAX_GROUPS lowers the cap of 64 workgroups per compute
+    unit): the bits equal one launch's, at one row per workgroup and at
+    four."""
+    import torch
+    for rows, cols, cap in ((301, 4096, "64"), (301, 768, "10")):
+        c = inputs.l2_case(rows, cols, 631 + cols, residual=True)
+        announce("l2/rms rows in pieces", rows, cols, cap)
+        xd, rd = dev_bits(c.x), dev_bits(c.r)
+        dy = dev_bits(inputs.l2_case(rows, cols, 632 + cols).x)
+        calls = (lambda: B.ds_l2_rows(xd, rd, c.eps), lambda: B.ds_rms_rows(xd, rd, c.eps),
+                 lambda: B.ds_l2_rows_backward(xd, rd, dy, c.eps),
+                 lambda: B.ds_rms_rows_backward(xd, rd, dy, c.eps))
+        one = [f() for f in calls]
+        monkeypatch.setenv("DS_ROWS_TEST_MAX_GROUPS", cap)
+        pieces = [f() for f in calls]
+        monkeypatch.delenv("DS_ROWS_TEST_MAX_GROUPS")
+        torch.cuda.synchronize()
+        for a, b in zip(one, pieces):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (rows, cols)
+        full_check(host_bits(pieces[0]), c.x, c.r, c.eps, f"pieces {rows}x{cols}")
 
 
 def test_zero_rows_enqueue_nothing(B):

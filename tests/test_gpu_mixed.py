@@ -5,11 +5,15 @@ kernel picks each task's row body by its shape key.  A matrix's bits must
 not depend on that: every output of a mixed call equals, bit for bit, the
 output of the same matrix called alone (its own shape's kernel), and
 sampled rows meet the oracle's contracts.  The classes here are sized just
-under the mixing bound and together exceed one pass of the grid, so each
-workgroup runs items of one-wave rows and of four-wave rows in turn (their
-LDS combines must still alternate), with rescued rows among them; a class of
-two-wave rows (128-thread workgroups) runs in a launch of its own.
+under the mixing bound and together exceed one pass of the grid (64
+workgroups per compute unit, the library's cap, held here through
+DS_ROWS_TEST_MAX_GROUPS whatever the environment says), so each workgroup
+runs items of one-wave rows and of four-wave rows in turn (their LDS combines
+must still alternate), with rescued rows among them; a class of two-wave rows
+(128-thread workgroups) runs in a launch of its own.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -23,6 +27,20 @@ from scale_invariant_row_amd import inputs
 pytestmark = pytest.mark.gpu
 
 ITEMS_PER_CU = 31          # just under the library's mixing bound of 32 per CU
+
+
+@pytest.fixture(scope="module", autouse=True)
+def grid_of_64_per_cu():
+    """Every launch of this module on a grid of at most 64 workgroups per CU."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    old = os.environ.get("DS_ROWS_TEST_MAX_GROUPS")
+    os.environ["DS_ROWS_TEST_MAX_GROUPS"] = str(64 * cus)
+    yield
+    if old is None:
+        del os.environ["DS_ROWS_TEST_MAX_GROUPS"]
+    else:
+        os.environ["DS_ROWS_TEST_MAX_GROUPS"] = old
 
 
 @pytest.fixture(scope="module")

@@ -83,37 +83,32 @@ def test_workload(B):
     check(gq, gk, c, rows, c.name)
 
 
-def test_more_rows_than_one_launch(B):
-    """A call with more row groups than one launch takes (64 per compute unit,
-    two rows each) runs as several launches; strided views and in-place
-    outputs move with each piece: rows on both sides of a seam meet the
-    oracle, and rows alone give the bits they have inside the whole call."""
+def test_more_rows_than_one_launch(B, monkeypatch):
+    """A call with more row groups than one launch takes runs as several
+    launches (DS_ROWS_TEST_MAX_GROUPS lowers the cap of 64 workgroups per
+    compute unit): strided views and in-place outputs move with each piece,
+    the bits equal one launch's, and rows on both sides of each seam meet
+    the oracle."""
     import torch
-    piece = torch.cuda.get_device_properties(0).multi_processor_count * 64 * 2
-    rows = 2 * piece + 9
-    c = inputs.qk_case(rows, 1, 1, 128, 1703)
-    announce("qk_rows_l2 over several launches", rows)
+    rows = 333                                          # pieces of 2 x 50 rows
+    c = inputs.qk_case(rows, 3, 2, 128, 1703)
+    announce("qk_rows_l2 in pieces", rows)
     want_q, want_k = run(B, c)
     d = torch.device("cuda:0")
-    fused = torch.zeros(rows, 384, dtype=torch.int16, device=d)       # q | k | v
-    fused[:, :128] = torch.from_numpy(c.q.view(np.int16)).to(d)
-    fused[:, 128:256] = torch.from_numpy(c.k.view(np.int16)).to(d)
+    fused = torch.zeros(rows, 6 * 128 + 64, dtype=torch.int16, device=d)     # q | k | v
+    fused[:, :384] = torch.from_numpy(c.q.view(np.int16)).to(d)
+    fused[:, 384:640] = torch.from_numpy(c.k.view(np.int16)).to(d)
     fused = fused.view(torch.bfloat16)
     _, _, pos, inv, sc = _dev(c)
-    qv, kv = fused[:, :128], fused[:, 128:256]
+    qv, kv = fused[:, :384], fused[:, 384:640]
+    monkeypatch.setenv("DS_ROWS_TEST_MAX_GROUPS", "50")
     B.ds_qk_rows_l2(qv, kv, pos, inv, sc, 128, q_out=qv, k_out=kv)
     torch.cuda.synchronize()
+    monkeypatch.delenv("DS_ROWS_TEST_MAX_GROUPS")
     assert np.array_equal(host_bits(qv.contiguous()), want_q)
     assert np.array_equal(host_bits(kv.contiguous()), want_k)
-    assert not fused[:, 256:].view(torch.int16).any()
-    seams = np.r_[0, piece - 2:piece + 2, 2 * piece - 2:2 * piece + 2, rows - 3:rows]
-    check(want_q, want_k, c, np.unique(np.r_[seams, sample_rows(rows, 40, 1704)]), "several launches")
-    a = piece - 5
-    q, k, _, _, _ = _dev(c)
-    part_q, part_k = B.ds_qk_rows_l2(q[a:], k[a:], pos[a:], inv, sc, 128)
-    torch.cuda.synchronize()
-    assert np.array_equal(host_bits(part_q), want_q[a:])
-    assert np.array_equal(host_bits(part_k), want_k[a:])
+    assert not fused[:, 640:].view(torch.int16).any()
+    check(want_q, want_k, c, np.arange(rows), "pieces")
 
 
 def test_strided_views_and_in_place(B):

@@ -76,6 +76,43 @@ def test_ragged_equals_single(B):
         assert np.array_equal(w_r[len(case.w) - 1 - i], w_all[i])
 
 
+def test_grid_stride_equals_one_item_each(B, monkeypatch):
+    """With the per-launch cap of 64 workgroups per compute unit lowered
+    (the DS_ROWS_TEST_MAX_GROUPS hook) the ragged kernels' grid-stride loops run
+    several items per workgroup: forward, gradient and both rescale calls
+    give the bits of one item per workgroup, over every launch kind (a large
+    class of its own, mixed small classes, single-element rows, column
+    blocks)."""
+    import torch
+    shapes = [(900, 768), (37, 3072), (33, 44), (64, 147), (300, 4096)]
+    c = inputs.rownorm_grad_case(shapes, 811)
+    cb = inputs.colblock_grad_case([(96, 320), (12, 90)], 1, 812)
+    announce("weights on a grid of 7 workgroups against one item each")
+
+    def calls():
+        ws = [dev_f32(w) for w in c.w] + [dev_f32(w) for w in cb.w]
+        gs = [dev_f32(g) for g in c.gain] + [dev_f32(g) for g in cb.gain]
+        des = [torch.from_numpy(np.ascontiguousarray(d).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+               for d in c.dwe + cb.dwe]
+        segs = [None] * len(c.w) + [1] * len(cb.w)
+        n, e = B.ds_weight_rownorm_gain(ws, gs, None, segs=segs)
+        dw, dg = B.ds_weight_rownorm_gain_backward(ws, gs, des, segs=segs)
+        vs = [0.01 * torch.ones_like(w) for w in ws]
+        B.ds_rescale_project(ws, vs, segs=segs)
+        B.ds_rescale_after_step(ws, vs, segs=segs)
+        torch.cuda.synchronize()
+        return [t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+                for t in n + e + dw + dg + vs + ws]
+
+    one = calls()
+    monkeypatch.setenv("DS_ROWS_TEST_MAX_GROUPS", "7")
+    loop = calls()
+    monkeypatch.delenv("DS_ROWS_TEST_MAX_GROUPS")
+    assert len(one) == len(loop)
+    for i, (a, b) in enumerate(zip(one, loop)):
+        assert torch.equal(a, b), i
+
+
 def test_step0_identity_and_radius(B):
     """g = ||W_i|| (the gain init that keeps the output) gives W_eff = bf16(W)."""
     case = inputs.rownorm_case([(256, 768)], 811)

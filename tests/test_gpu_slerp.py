@@ -73,25 +73,28 @@ def test_workloads(B, name):
     assert torch.equal(hs.view(torch.int16), h[a:b].view(torch.int16))
 
 
-def test_more_rows_than_one_launch(B):
-    """A call with more row groups than one launch takes (64 per compute unit)
-    runs as several launches: rows on both sides of the seam meet the oracle,
-    and any run of rows alone gives the same bits as inside the whole call."""
+def test_more_rows_than_one_launch(B, monkeypatch):
+    """A call with more row groups than one launch takes runs as several
+    launches (DS_ROWS_TEST_MAX_GROUPS lowers the cap of 64 workgroups per
+    compute unit so small calls take that path): the bits equal one
+    launch's, and rows on both sides of each seam meet the oracle."""
     import torch
-    cols = 4096                                   # one row per workgroup at this width
-    piece = torch.cuda.get_device_properties(0).multi_processor_count * 64
-    rows = piece + 116
-    c = inputs.slerp_case(rows, cols, 7171)
-    announce("slerp_rows over several launches", rows, cols)
+    c = inputs.slerp_case(300, 4096, 7171)              # one row per workgroup
     rd, od, ad = dev_bits(c.res), dev_bits(c.out), dev_f32(c.alpha)
-    h = B.ds_slerp_rows(rd, od, ad, c.eps)
+    announce("slerp_rows in one launch and in pieces of 64 rows", 300, 4096)
+    one = B.ds_slerp_rows(rd, od, ad, c.eps)
+    monkeypatch.setenv("DS_ROWS_TEST_MAX_GROUPS", "64")
+    pieces = B.ds_slerp_rows(rd, od, ad, c.eps)
+    small = inputs.slerp_case(301, 1024, 7172)         # four rows per workgroup
+    one_s = B.ds_slerp_rows(dev_bits(small.res), dev_bits(small.out), dev_f32(small.alpha), small.eps)
+    monkeypatch.delenv("DS_ROWS_TEST_MAX_GROUPS")
+    one_s2 = B.ds_slerp_rows(dev_bits(small.res), dev_bits(small.out), dev_f32(small.alpha), small.eps)
     torch.cuda.synchronize()
-    idx = np.unique(np.r_[0, piece - 3:piece + 3, rows - 2:rows, sample_rows(rows, 60, 17)])
-    full_check(host_bits(h)[idx], c.res[idx], c.out[idx], c.alpha, c.eps, "several launches")
-    a, b = piece - 100, rows
-    hs = B.ds_slerp_rows(rd[a:b].contiguous(), od[a:b].contiguous(), ad, c.eps)
-    torch.cuda.synchronize()
-    assert torch.equal(hs.view(torch.int16), h[a:b].view(torch.int16))
+    assert torch.equal(one.view(torch.int16), pieces.view(torch.int16))
+    assert torch.equal(one_s.view(torch.int16), one_s2.view(torch.int16))
+    idx = np.r_[0, 62:66, 126:130, 254:258, 298:300]
+    full_check(host_bits(pieces)[idx], c.res[idx], c.out[idx], c.alpha, c.eps, "pieces")
+    full_check(host_bits(one_s), small.res, small.out, small.alpha, small.eps, "pieces, 1024")
 
 
 def test_alpha_special_cases(B):
