@@ -14,8 +14,10 @@ reported beside them.
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (each input
 read once, each output written once) over its time, in GB/s.  The K steps are
 timed with events at the two ends of the region only; each kernel's average
-duration (``ops``, ``roofline``) comes from K back-to-back launches of that
-kernel between two events on the launch stream.
+duration (``ops``, ``roofline``) comes from max(K, 200) back-to-back launches
+of that kernel between two events on the launch stream.  The two step
+kernels are timed alone first, then come the W warmup steps and the K timed
+steps, then the other lines.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu]
 """
@@ -126,15 +128,39 @@ def main():
         return L.ds_slerp_rows(s["res"].data_ptr(), s["out"].data_ptr(), alpha.data_ptr(),
                                s["h"].data_ptr(), ROWS, COLS, eps, sp)
 
-    for i in range(args.warmup):
-        s = sets[i % len(sets)]
-        assert l2(s) == 0 and slerp(s) == 0
-    torch.cuda.synchronize()
-
     K = args.steps
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
+
+    # per-kernel duration: NK back-to-back launches of one kernel between two
+    # events on the launch stream (an event between every pair of launches
+    # would add its own ~2 us to each).  At least 200 launches whatever K is,
+    # so that a short run's per-kernel averages are not a handful of launches.
+    NK = max(K, 200)
+
+    def batch_us(fn):
+        for i in range(3):             # untimed: the first launch of a kernel loads its code
+            if fn(sets[i % len(sets)]):
+                raise RuntimeError("launch failed")
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(NK):
+            if fn(sets[i % len(sets)]):
+                raise RuntimeError("launch failed")
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / NK
+
+    # the two kernels alone first, then the W warmup steps and the K timed steps
+    l2_us = batch_us(l2)
+    sl_us = batch_us(slerp)
+
+    for i in range(args.warmup):
+        s = sets[i % len(sets)]
+        assert l2(s) == 0 and slerp(s) == 0
+    torch.cuda.synchronize()
 
     # timed region: exactly K steps, events at its two ends only
     t_start, t_end = ev(), ev()
@@ -150,26 +176,6 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
-
-    # per-kernel duration: K back-to-back launches of one kernel between two
-    # events on the launch stream (an event between every pair of launches
-    # would add its own ~2 us to each)
-    def batch_us(fn):
-        for i in range(3):             # untimed: the first launch of a kernel loads its code
-            if fn(sets[i % len(sets)]):
-                raise RuntimeError("launch failed")
-        a, b = ev(), ev()
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(K):
-            if fn(sets[i % len(sets)]):
-                raise RuntimeError("launch failed")
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / K
-
-    l2_us = batch_us(l2)
-    sl_us = batch_us(slerp)
 
     # the achievable-bandwidth reference: a plain read-2-write-1 stream with
     # l2_rows' launch (shape, grid, buffer resources, cache hints), y = x ^ r,
