@@ -103,11 +103,10 @@ def threads_of(G):
 
 # Workgroup sizes with a mixed-shape kernel (launch.hpp's kMaxMixedThreads):
 # at 1,024 threads the union of the bodies no longer fits the registers.
+# Each item builds its geometry with Geo::per_item, so a mixed kernel needs
+# the registers of its largest shape, not of all its shapes' lane offsets
+# at once.
 MIXED_THREADS = (128, 256, 512)
-# Waves per SIMD the 256-thread mixed kernels are compiled for (a register
-# cap of 128): measured faster than the compiler's own choice for the
-# gradient (ResNet-50's weights, 54.3 against 58.1 us).
-MIXED_WAVES_256 = 4
 
 
 def mixed(name, item, args, task, lists, rescale=False):
@@ -128,13 +127,12 @@ def mixed(name, item, args, task, lists, rescale=False):
         shapes = by_threads[T]
         decl = "\n".join(f"  __shared__ GroupScratch<{G}> gs{G};"
                          for G in sorted({G for _, G, _ in shapes}))
-        waves = f", {MIXED_WAVES_256}" if T == 256 else ""
         body = "\n".join(
             f"      case {ne * 10000 + G * 100 + V}: "
-            f"{item}<{G}, {V}, {ne}{extra}>(t, item, Geo<{G}>(), gs{G}, slot); break;"
+            f"{item}<{G}, {V}, {ne}{extra}>(t, item, Geo<{G}>::per_item(), gs{G}, slot); break;"
             for ne, G, V in shapes)
         out.append(f"""
-{tmpl}__global__ void __launch_bounds__({T}{waves}) {name}_mixed_{T}(const {args} args) {{
+{tmpl}__global__ void __launch_bounds__({T}) {name}_mixed_{T}(const {args} args) {{
 {decl}
   int slot = 0;
   for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {{

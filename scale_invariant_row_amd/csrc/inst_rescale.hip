@@ -20,38 +20,38 @@ __global__ void __launch_bounds__(128) rescale_mixed_128(const RescaleArgs args)
   for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
     const RescaleTask t = task_of(args, item, (int)(threadIdx.x & 63));
     switch (t.shape) {
-      case 40204: rescale_item<2, 4, 4, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
-      case 40205: rescale_item<2, 5, 4, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
-      case 40206: rescale_item<2, 6, 4, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
-      case 10216: rescale_item<2, 16, 1, RESCALE>(t, item, Geo<2>(), gs2, slot); break;
+      case 40204: rescale_item<2, 4, 4, RESCALE>(t, item, Geo<2>::per_item(), gs2, slot); break;
+      case 40205: rescale_item<2, 5, 4, RESCALE>(t, item, Geo<2>::per_item(), gs2, slot); break;
+      case 40206: rescale_item<2, 6, 4, RESCALE>(t, item, Geo<2>::per_item(), gs2, slot); break;
+      case 10216: rescale_item<2, 16, 1, RESCALE>(t, item, Geo<2>::per_item(), gs2, slot); break;
       default: break;
     }
   }
 }
 
 template <bool RESCALE>
-__global__ void __launch_bounds__(256, 4) rescale_mixed_256(const RescaleArgs args) {
+__global__ void __launch_bounds__(256) rescale_mixed_256(const RescaleArgs args) {
   __shared__ GroupScratch<1> gs1;
   __shared__ GroupScratch<4> gs4;
   int slot = 0;
   for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
     const RescaleTask t = task_of(args, item, (int)(threadIdx.x & 63));
     switch (t.shape) {
-      case 40101: rescale_item<1, 1, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 40102: rescale_item<1, 2, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 40103: rescale_item<1, 3, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 40104: rescale_item<1, 4, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 40105: rescale_item<1, 5, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 40106: rescale_item<1, 6, 4, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 40404: rescale_item<4, 4, 4, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
-      case 40405: rescale_item<4, 5, 4, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
-      case 40406: rescale_item<4, 6, 4, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
-      case 10101: rescale_item<1, 1, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 10102: rescale_item<1, 2, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 10104: rescale_item<1, 4, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 10108: rescale_item<1, 8, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 10116: rescale_item<1, 16, 1, RESCALE>(t, item, Geo<1>(), gs1, slot); break;
-      case 10416: rescale_item<4, 16, 1, RESCALE>(t, item, Geo<4>(), gs4, slot); break;
+      case 40101: rescale_item<1, 1, 4, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40102: rescale_item<1, 2, 4, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40103: rescale_item<1, 3, 4, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40104: rescale_item<1, 4, 4, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40105: rescale_item<1, 5, 4, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40106: rescale_item<1, 6, 4, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40404: rescale_item<4, 4, 4, RESCALE>(t, item, Geo<4>::per_item(), gs4, slot); break;
+      case 40405: rescale_item<4, 5, 4, RESCALE>(t, item, Geo<4>::per_item(), gs4, slot); break;
+      case 40406: rescale_item<4, 6, 4, RESCALE>(t, item, Geo<4>::per_item(), gs4, slot); break;
+      case 10101: rescale_item<1, 1, 1, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10102: rescale_item<1, 2, 1, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10104: rescale_item<1, 4, 1, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10108: rescale_item<1, 8, 1, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10116: rescale_item<1, 16, 1, RESCALE>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10416: rescale_item<4, 16, 1, RESCALE>(t, item, Geo<4>::per_item(), gs4, slot); break;
       default: break;
     }
   }
@@ -64,10 +64,10 @@ __global__ void __launch_bounds__(512) rescale_mixed_512(const RescaleArgs args)
   for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
     const RescaleTask t = task_of(args, item, (int)(threadIdx.x & 63));
     switch (t.shape) {
-      case 40804: rescale_item<8, 4, 4, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
-      case 40805: rescale_item<8, 5, 4, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
-      case 40806: rescale_item<8, 6, 4, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
-      case 10816: rescale_item<8, 16, 1, RESCALE>(t, item, Geo<8>(), gs8, slot); break;
+      case 40804: rescale_item<8, 4, 4, RESCALE>(t, item, Geo<8>::per_item(), gs8, slot); break;
+      case 40805: rescale_item<8, 5, 4, RESCALE>(t, item, Geo<8>::per_item(), gs8, slot); break;
+      case 40806: rescale_item<8, 6, 4, RESCALE>(t, item, Geo<8>::per_item(), gs8, slot); break;
+      case 10816: rescale_item<8, 16, 1, RESCALE>(t, item, Geo<8>::per_item(), gs8, slot); break;
       default: break;
     }
   }

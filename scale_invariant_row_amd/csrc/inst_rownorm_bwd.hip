@@ -19,37 +19,37 @@ __global__ void __launch_bounds__(128) rownorm_backward_mixed_128(const RownormG
   for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
     const RownormGradTask t = task_of(args, item, (int)(threadIdx.x & 63));
     switch (t.shape) {
-      case 40204: rownorm_backward_item<2, 4, 4>(t, item, Geo<2>(), gs2, slot); break;
-      case 40205: rownorm_backward_item<2, 5, 4>(t, item, Geo<2>(), gs2, slot); break;
-      case 40206: rownorm_backward_item<2, 6, 4>(t, item, Geo<2>(), gs2, slot); break;
-      case 10216: rownorm_backward_item<2, 16, 1>(t, item, Geo<2>(), gs2, slot); break;
+      case 40204: rownorm_backward_item<2, 4, 4>(t, item, Geo<2>::per_item(), gs2, slot); break;
+      case 40205: rownorm_backward_item<2, 5, 4>(t, item, Geo<2>::per_item(), gs2, slot); break;
+      case 40206: rownorm_backward_item<2, 6, 4>(t, item, Geo<2>::per_item(), gs2, slot); break;
+      case 10216: rownorm_backward_item<2, 16, 1>(t, item, Geo<2>::per_item(), gs2, slot); break;
       default: break;
     }
   }
 }
 
-__global__ void __launch_bounds__(256, 4) rownorm_backward_mixed_256(const RownormGradArgs args) {
+__global__ void __launch_bounds__(256) rownorm_backward_mixed_256(const RownormGradArgs args) {
   __shared__ GroupScratch<1> gs1;
   __shared__ GroupScratch<4> gs4;
   int slot = 0;
   for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
     const RownormGradTask t = task_of(args, item, (int)(threadIdx.x & 63));
     switch (t.shape) {
-      case 40101: rownorm_backward_item<1, 1, 4>(t, item, Geo<1>(), gs1, slot); break;
-      case 40102: rownorm_backward_item<1, 2, 4>(t, item, Geo<1>(), gs1, slot); break;
-      case 40103: rownorm_backward_item<1, 3, 4>(t, item, Geo<1>(), gs1, slot); break;
-      case 40104: rownorm_backward_item<1, 4, 4>(t, item, Geo<1>(), gs1, slot); break;
-      case 40105: rownorm_backward_item<1, 5, 4>(t, item, Geo<1>(), gs1, slot); break;
-      case 40106: rownorm_backward_item<1, 6, 4>(t, item, Geo<1>(), gs1, slot); break;
-      case 40404: rownorm_backward_item<4, 4, 4>(t, item, Geo<4>(), gs4, slot); break;
-      case 40405: rownorm_backward_item<4, 5, 4>(t, item, Geo<4>(), gs4, slot); break;
-      case 40406: rownorm_backward_item<4, 6, 4>(t, item, Geo<4>(), gs4, slot); break;
-      case 10101: rownorm_backward_item<1, 1, 1>(t, item, Geo<1>(), gs1, slot); break;
-      case 10102: rownorm_backward_item<1, 2, 1>(t, item, Geo<1>(), gs1, slot); break;
-      case 10104: rownorm_backward_item<1, 4, 1>(t, item, Geo<1>(), gs1, slot); break;
-      case 10108: rownorm_backward_item<1, 8, 1>(t, item, Geo<1>(), gs1, slot); break;
-      case 10116: rownorm_backward_item<1, 16, 1>(t, item, Geo<1>(), gs1, slot); break;
-      case 10416: rownorm_backward_item<4, 16, 1>(t, item, Geo<4>(), gs4, slot); break;
+      case 40101: rownorm_backward_item<1, 1, 4>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40102: rownorm_backward_item<1, 2, 4>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40103: rownorm_backward_item<1, 3, 4>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40104: rownorm_backward_item<1, 4, 4>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40105: rownorm_backward_item<1, 5, 4>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40106: rownorm_backward_item<1, 6, 4>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 40404: rownorm_backward_item<4, 4, 4>(t, item, Geo<4>::per_item(), gs4, slot); break;
+      case 40405: rownorm_backward_item<4, 5, 4>(t, item, Geo<4>::per_item(), gs4, slot); break;
+      case 40406: rownorm_backward_item<4, 6, 4>(t, item, Geo<4>::per_item(), gs4, slot); break;
+      case 10101: rownorm_backward_item<1, 1, 1>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10102: rownorm_backward_item<1, 2, 1>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10104: rownorm_backward_item<1, 4, 1>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10108: rownorm_backward_item<1, 8, 1>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10116: rownorm_backward_item<1, 16, 1>(t, item, Geo<1>::per_item(), gs1, slot); break;
+      case 10416: rownorm_backward_item<4, 16, 1>(t, item, Geo<4>::per_item(), gs4, slot); break;
       default: break;
     }
   }
@@ -61,10 +61,10 @@ __global__ void __launch_bounds__(512) rownorm_backward_mixed_512(const RownormG
   for (int item = blockIdx.x; item < args.nitems; item += gridDim.x) {
     const RownormGradTask t = task_of(args, item, (int)(threadIdx.x & 63));
     switch (t.shape) {
-      case 40804: rownorm_backward_item<8, 4, 4>(t, item, Geo<8>(), gs8, slot); break;
-      case 40805: rownorm_backward_item<8, 5, 4>(t, item, Geo<8>(), gs8, slot); break;
-      case 40806: rownorm_backward_item<8, 6, 4>(t, item, Geo<8>(), gs8, slot); break;
-      case 10816: rownorm_backward_item<8, 16, 1>(t, item, Geo<8>(), gs8, slot); break;
+      case 40804: rownorm_backward_item<8, 4, 4>(t, item, Geo<8>::per_item(), gs8, slot); break;
+      case 40805: rownorm_backward_item<8, 5, 4>(t, item, Geo<8>::per_item(), gs8, slot); break;
+      case 40806: rownorm_backward_item<8, 6, 4>(t, item, Geo<8>::per_item(), gs8, slot); break;
+      case 10816: rownorm_backward_item<8, 16, 1>(t, item, Geo<8>::per_item(), gs8, slot); break;
       default: break;
     }
   }

@@ -261,6 +261,17 @@ struct Geo {
     g = (G == 1) ? 0 : wave;
     rr = (G == 1) ? wave : 0;
   }
+  // A Geo made inside a loop whose lane index the compiler cannot compute
+  // once, ahead of the loop.  The mixed-shape kernels make one per item: with
+  // the lane hoisted, every shape's lane offsets were computed before the
+  // item loop and stayed live across it (the 256-thread fp32 rownorm kernel
+  // rose to 96 VGPRs, five waves per SIMD, against 60 for its largest shape
+  // alone); per item, only the running shape's offsets exist.
+  static __device__ __forceinline__ Geo per_item() {
+    Geo q;
+    asm volatile("" : "+v"(q.lane));
+    return q;
+  }
   __device__ __forceinline__ int vec_index(int v) const { return (v * G + g) * 64 + lane; }
   template <int V>
   __device__ __forceinline__ void offsets(int (&off)[V], int vbytes) const {
