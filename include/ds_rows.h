@@ -119,9 +119,9 @@ enum {
   DS_ERR_LAUNCH = -6,  /* the HIP runtime reported an error for the launch,
                           the copy or the stream */
   DS_ERR_DEVICE = -7,  /* no usable HIP device */
-  DS_ERR_CAPTURE = -8, /* a ragged weight call on a capturing stream with more
-                          than 48 matrices of one width (see
-                          ds_weight_rownorm_gain) */
+  DS_ERR_CAPTURE = -8, /* reserved: no call returns it (a ragged weight call
+                          on a capturing stream splits its launches instead;
+                          see ds_weight_rownorm_gain) */
   DS_ERR_SCRATCH = -9  /* an allocation-free call needs more of the library's
                           fixed scratch than DS_SCRATCH_FLOATS */
 };
@@ -330,12 +330,14 @@ typedef struct ds_rownorm_desc {
  * stream : the hipStream_t to launch on.
  *
  * Matrices are grouped by row width; a group of at most 48 matrices travels
- * inside the kernel arguments (no copy, no allocation; such calls may be
- * captured into a HIP graph).  A larger group's descriptors are staged in a
- * device table through a library-owned pinned buffer, kept until the stream
- * has consumed it (an event recorded behind the launches); a slot whose copy
- * fails is returned at once.  DS_ERR_ALLOC if that buffer cannot be made;
- * DS_ERR_CAPTURE if it would be needed while the stream is capturing.
+ * inside the kernel arguments (no copy, no allocation).  A larger group's
+ * descriptors are staged in a device table through a library-owned pinned
+ * buffer, kept until the stream has consumed it (an event recorded behind the
+ * launches); a slot whose copy fails is returned at once.  DS_ERR_ALLOC if
+ * that buffer cannot be made.  On a stream being captured into a HIP graph
+ * nothing is staged: a larger group becomes several launches of at most 48
+ * matrices, each carrying its table in the kernel arguments, so any call may
+ * be captured (its outputs are the same, bit for bit).
  */
 int ds_weight_rownorm_gain(const ds_rownorm_desc* descs, int32_t n,
                            ds_stream_t stream);
@@ -423,7 +425,7 @@ typedef struct ds_rownorm_grad_desc {
  *
  * descs, n, stream : as for ds_weight_rownorm_gain, including the grouping by
  *                    row width, the 48-matrix inline limit, the staged table
- *                    and DS_ERR_CAPTURE.
+ *                    and the split launches under graph capture.
  */
 int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n,
                                     ds_stream_t stream);
@@ -444,7 +446,7 @@ int ds_weight_rownorm_gain_backward(const ds_rownorm_grad_desc* descs, int32_t n
  *     enqueued); split larger calls;
  *   - every launch carries its matrix table in the kernel arguments (a width
  *     class of more than 48 matrices becomes several launches), so the call
- *     never stages a table and never returns DS_ERR_ALLOC or DS_ERR_CAPTURE.
+ *     never stages a table and never returns DS_ERR_ALLOC.
  * The call allocates nothing (no hipMalloc, hipHostMalloc or hipFree) and
  * enqueues no memset; every share is written before it is read.
  *
@@ -488,7 +490,7 @@ typedef struct ds_rescale_desc {
  *
  * A zero row of w leaves v's row unchanged.  descs, n, stream: as for
  * ds_weight_rownorm_gain (grouping by width, the 48-matrix inline limit,
- * the staged table, DS_ERR_CAPTURE).
+ * the staged table, the split launches under graph capture).
  */
 int ds_rescale_project(const ds_rescale_desc* descs, int32_t n, ds_stream_t stream);
 

@@ -299,7 +299,9 @@ using RaggedLauncher = hipError_t (*)(Shape, const dsr::TaskArgs<Task>&, int, hi
 // With `inline_only` every launch carries its table in the kernel arguments:
 // a group of more than kInlineTasks matrices is split into launches of at
 // most that many, so the call touches no library memory (the ring is never
-// used).  A matrix's bits do not depend on the launch it lands in.
+// used).  A matrix's bits do not depend on the launch it lands in.  A call
+// that would stage a table on a stream being captured into a graph is
+// planned this way instead.
 template <class Task>
 int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLauncher<Task> launch,
                   hipStream_t hs, bool inline_only = false) {
@@ -369,11 +371,13 @@ int launch_ragged(const std::vector<std::pair<Shape, Task>>& mats, RaggedLaunche
     if (L.ntasks > dsr::kInlineTasks) staged_tasks += (size_t)L.ntasks;
 
   if (staged_tasks > 0) {
-    // a staged table is copied from a reusable host slot: a graph replay
-    // would copy whatever that slot holds by then
+    // A staged table is copied from a reusable host slot: a graph replay
+    // would copy whatever that slot holds by then.  On a capturing stream
+    // the call is planned again with every table in the kernel arguments
+    // (more launches, the same bits); nothing has been enqueued yet.
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return DS_ERR_LAUNCH;
-    if (cap != hipStreamCaptureStatusNone) return DS_ERR_CAPTURE;
+    if (cap != hipStreamCaptureStatusNone) return launch_ragged(mats, launch, hs, true);
   }
   Ring* ring = nullptr;
   int slot = -1;
@@ -557,7 +561,7 @@ const char* ds_status_string(int status) {
     case DS_ERR_ALLOC: return "DS_ERR_ALLOC: could not allocate the descriptor staging buffer";
     case DS_ERR_LAUNCH: return "DS_ERR_LAUNCH: the HIP runtime reported an error";
     case DS_ERR_DEVICE: return "DS_ERR_DEVICE: no usable HIP device";
-    case DS_ERR_CAPTURE: return "DS_ERR_CAPTURE: a ragged weight call with more than 48 matrices of one width cannot be captured into a graph";
+    case DS_ERR_CAPTURE: return "DS_ERR_CAPTURE: reserved (a ragged call on a capturing stream now splits its launches instead)";
     case DS_ERR_SCRATCH: return "DS_ERR_SCRATCH: the call needs more library scratch than DS_SCRATCH_FLOATS (1,048,576 scalar-gain rows)";
     default: return "unknown ds_rows status";
   }

@@ -2,8 +2,10 @@
 
 Between replays the test writes new inputs eagerly and synchronises, then
 compares each replay's outputs bit for bit with the same library calls made
-eagerly on the same inputs.  A ragged weight call that would need the staged
-descriptor table (more than 48 matrices of one width) refuses to be captured.
+eagerly on the same inputs.  A ragged weight call that would stage its
+descriptor table (more than 48 matrices of one width) splits into launches
+that carry their tables in the kernel arguments when its stream is being
+captured; captured, its replays match eager calls too.
 """
 import numpy as np
 import pytest
@@ -81,23 +83,67 @@ def test_graph_replays_match_eager(B):
                 f"replay {rep}: rownorm {i}"
 
 
-def test_staged_ragged_call_refuses_capture(B):
+@pytest.mark.parametrize("shapes", [
+    [(8, 256)] * 50,                                               # one class of 50
+    # four small classes: three share a 256-thread mixed launch of 75 matrices
+    [(3 + i % 7, (256, 768, 147, 3072)[i % 4]) for i in range(100)],
+])
+def test_staged_ragged_calls_capture(B, shapes):
+    """Ragged calls whose eager form stages a table (forward, gradient and the
+    two rescale calls), captured into one graph and replayed three times."""
     import torch
     dev = "cuda:0"
-    case = inputs.rownorm_case([(8, 256)] * 50, 902)
+    case = inputs.rownorm_grad_case(shapes, 902)
+    v0 = inputs.rescale_case(shapes, 903).v
     ws = [torch.from_numpy(m).to(dev) for m in case.w]
-    gs = [torch.from_numpy(v).to(dev) for v in case.gain]
+    gs = [torch.from_numpy(g).to(dev) for g in case.gain]
+    des = [torch.from_numpy(d.view(np.int16)).to(dev).view(torch.bfloat16) for d in case.dwe]
+    w2 = [m.clone() for m in ws]                       # the rescale calls' own rows
+    vs = [torch.from_numpy(v).to(dev) for v in v0]
     ns = [torch.empty(m.shape[0], device=dev) for m in ws]
     es = [torch.empty(m.shape, dtype=torch.bfloat16, device=dev) for m in ws]
-    B.ds_weight_rownorm_gain(ws, gs, norm_out=ns, w_eff=es)     # eager: fine
+    dws = [torch.empty_like(m) for m in ws]
+    dgs = [torch.empty(m.shape[0], device=dev) for m in ws]
+
+    def step():
+        B.ds_weight_rownorm_gain(ws, gs, norm_out=ns, w_eff=es)
+        B.ds_weight_rownorm_gain_backward(ws, gs, des, dw=dws, dgain=dgs)
+        B.ds_rescale_project(ws, vs)
+        B.ds_rescale_after_step(w2, vs)
+
+    announce("graph capture of staged ragged calls:", len(shapes), "matrices")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                         # eager, staged
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    announce("graph capture refusal: 50 matrices of one width")
     graph = torch.cuda.CUDAGraph()
-    with pytest.raises(RuntimeError, match="DS_ERR_CAPTURE"):
-        with torch.cuda.graph(graph):
-            B.ds_weight_rownorm_gain(ws, gs, norm_out=ns, w_eff=es)
-    torch.cuda.synchronize()
-    # the library and the device still work
-    n2, e2 = B.ds_weight_rownorm_gain(ws, gs)
-    torch.cuda.synchronize()
-    assert all(torch.equal(a, b) for a, b in zip(ns, n2))
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        gen = torch.Generator(device=dev).manual_seed(200 + rep)
+        for m, m2 in zip(ws, w2):
+            m.copy_(0.02 * torch.randn(m.shape, device=dev, generator=gen))
+            m2.copy_(m)
+        for v in vs:
+            v.copy_(1e-3 * torch.randn(v.shape, device=dev, generator=gen))
+        w_in = [m.clone() for m in ws]
+        v_in = [v.clone() for v in vs]
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ne, ee = B.ds_weight_rownorm_gain(w_in, gs)
+        dwe, dge = B.ds_weight_rownorm_gain_backward(w_in, gs, des)
+        ve = [v.clone() for v in v_in]
+        B.ds_rescale_project(w_in, ve)
+        w2e = [m.clone() for m in w_in]
+        B.ds_rescale_after_step(w2e, ve)
+        torch.cuda.synchronize()
+        for i in range(len(ws)):
+            assert torch.equal(ns[i], ne[i]) and torch.equal(_bits(es[i]), _bits(ee[i])), \
+                f"replay {rep}: forward {i}"
+            assert torch.equal(dws[i], dwe[i]) and torch.equal(dgs[i], dge[i]), \
+                f"replay {rep}: gradient {i}"
+            assert torch.equal(vs[i], ve[i]) and torch.equal(w2[i], w2e[i]), \
+                f"replay {rep}: rescale {i}"
