@@ -401,12 +401,50 @@ def main():
     del rs_sets
     torch.cuda.empty_cache()
 
+    # the weight op's own stream reference: fp32 rows read, bf16 written, with
+    # the launch the weight op gives rows of that width (libdsbench.so), over
+    # each set's matrix in turn
+    BL.dsb_stream_f32_rows.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]
+    BL.dsb_stream_f32_rows.restype = ctypes.c_int
+
+    def f32_stream_us(sets, n):
+        def one(s):
+            w, e = s[3][0][0], s[3][4]           # the set's weight and its bf16 output
+            return BL.dsb_stream_f32_rows(w.data_ptr(), e.data_ptr(), w.shape[0], w.shape[1], sp)
+        for i in range(4):
+            assert one(sets[i % len(sets)]) == 0
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for i in range(n):
+            one(sets[i % len(sets)])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
     big = [(11008, 4096)]
     wsets = weight_sets(big, 4)
     f_us = ragged_us(wsets, 0, 40)
     b_us = ragged_us(wsets, 1, 40)
+    fs_us = f32_stream_us(wsets, 40)
     del wsets
     torch.cuda.empty_cache()
+    # the 48 linears' 768-wide rows (qkv, o, up: 73,728 of them) as one matrix
+    tall = [(73728, 768)]
+    wsets = weight_sets(tall, 3)
+    t_us = ragged_us(wsets, 0, 40)
+    ts_us = f32_stream_us(wsets, 40)
+    del wsets
+    torch.cuda.empty_cache()
+    n_tall = 73728 * 768
+    f32_note = ("stream_f32_rows_kernel: fp32 rows read, bf16 written, with the weight op's launch "
+                "for the width (shape, grid, buffer resources, cache hints): the weight op's "
+                "traffic with no arithmetic")
+    ops["weight_rownorm_gain_73728x768"] = op(t_us, n_tall * 6 + 73728 * 8, 73728)
+    ops["stream_f32_ceiling_73728x768"] = op(ts_us, n_tall * 6, 73728)
+    ops["stream_f32_ceiling_73728x768"]["note"] = f32_note
+    ops["stream_f32_ceiling_11008x4096"] = op(fs_us, 11008 * 4096 * 6, 11008)
+    ops["stream_f32_ceiling_11008x4096"]["note"] = f32_note
     n_big = 11008 * 4096
     ops["weight_rownorm_gain_11008x4096"] = op(f_us, n_big * 6 + 11008 * 8, 11008)
     ops["weight_rownorm_gain_bwd_11008x4096"] = op(b_us, n_big * 10 + 11008 * 8, 11008)

@@ -88,6 +88,83 @@ extern "C" int dsb_stream_rows(const void* x, const void* r, void* y, int64_t ro
   return 0;
 }
 
+// ------------------------------------------------- fp32 in, bf16 out (weights)
+//
+// The weight op's traffic without its arithmetic: fp32 rows read, each value
+// rounded to bf16 and written, with the launch the weight rows of this width
+// get (pick_rownorm_shape, items of R rows, one workgroup per item up to 64
+// per compute unit, the rest grid-stride), the same buffer resources and
+// cache hints.  The reference rate for the fp32 weight kernels, whose other
+// traffic (gains and lengths, 8 bytes a row) is negligible.
+namespace dsr {
+
+template <int G, int V>
+__global__ void __launch_bounds__(Geo<G>::THREADS)
+stream_f32_rows_kernel(const float* x, uint16_t* y, int64_t rows, int cols, int64_t items) {
+  constexpr int R = Geo<G>::R;
+  const Geo<G> geo;
+  int off[V];
+  geo.offsets(off, 16);
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t row = item * R + geo.rr;
+    if (G == 1 && row >= rows) break;       // a wave's rows only grow
+    const RowBuf xb(x + row * cols, (uint32_t)cols * 4u);
+    const RowBuf yb(y + row * cols, (uint32_t)cols * 2u);
+    f32x4_t w[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) w[v] = xb.ld16f(off[v]);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      yb.st8(u32x2_t{pack_bf16(w[v].x, w[v].y), pack_bf16(w[v].z, w[v].w)}, off[v] / 2);
+  }
+}
+
+template <int G, int V>
+static hipError_t run_f32(const float* x, uint16_t* y, int64_t rows, int cols, int64_t items,
+                          int grid, hipStream_t stream) {
+  stream_f32_rows_kernel<G, V><<<grid, Geo<G>::THREADS, 0, stream>>>(x, y, rows, cols, items);
+  return hipGetLastError();
+}
+
+}  // namespace dsr
+
+// y = bf16(x) over [rows, cols] fp32 rows (cols a multiple of 4 whose weight
+// shape is one of the cases below), with the launch the weight op uses for
+// that width.  Returns 0, -1 for an unsupported width, -2 for a runtime error.
+extern "C" int dsb_stream_f32_rows(const float* x, uint16_t* y, int64_t rows, int64_t cols,
+                                   void* stream) {
+  using namespace dsr;
+  if (rows < 0 || cols < 4 || cols % 4 != 0 || cols > 65536) return -1;
+  if (rows == 0) return 0;
+  const Shape s = pick_rownorm_shape(cols / 4);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -2;
+  const int rpg = s.rows_per_block();
+  const int64_t items = (rows + rpg - 1) / rpg;
+  const int grid = (int)std::min<int64_t>(items, (int64_t)cus * 64);
+  const int c = (int)cols;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  switch (s.G * 100 + s.V) {
+    case 101: e = run_f32<1, 1>(x, y, rows, c, items, grid, hs); break;
+    case 102: e = run_f32<1, 2>(x, y, rows, c, items, grid, hs); break;
+    case 103: e = run_f32<1, 3>(x, y, rows, c, items, grid, hs); break;
+    case 104: e = run_f32<1, 4>(x, y, rows, c, items, grid, hs); break;
+    case 105: e = run_f32<1, 5>(x, y, rows, c, items, grid, hs); break;
+    case 106: e = run_f32<1, 6>(x, y, rows, c, items, grid, hs); break;
+    case 204: e = run_f32<2, 4>(x, y, rows, c, items, grid, hs); break;
+    case 205: e = run_f32<2, 5>(x, y, rows, c, items, grid, hs); break;
+    case 206: e = run_f32<2, 6>(x, y, rows, c, items, grid, hs); break;
+    case 404: e = run_f32<4, 4>(x, y, rows, c, items, grid, hs); break;
+    case 405: e = run_f32<4, 5>(x, y, rows, c, items, grid, hs); break;
+    case 406: e = run_f32<4, 6>(x, y, rows, c, items, grid, hs); break;
+    default: return -1;
+  }
+  return e == hipSuccess ? 0 : -2;
+}
+
 // ---------------------------------------------------------------- test kernel
 //
 // The gate's fast reciprocal against IEEE division over a range of fp32 bit
