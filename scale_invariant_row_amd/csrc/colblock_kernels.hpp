@@ -775,21 +775,6 @@ struct Col1Tile {
 };
 
 
-// A value known to be uniform, moved word by word into scalar registers.  A
-// task read from the staged table (a vector load: stores precede it in the
-// item loop) would otherwise stay in VGPRs, 20 of them, beside the tile.
-template <class T>
-__device__ __forceinline__ T scalarize(const T& v) {
-  static_assert(sizeof(T) % 4 == 0, "whole words");
-  struct Words {
-    uint32_t w[sizeof(T) / 4];
-  };
-  Words a = __builtin_bit_cast(Words, v);
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) a.w[i] = __builtin_amdgcn_readfirstlane(a.w[i]);
-  return __builtin_bit_cast(T, a);
-}
-
 // The seg-1 column-block kernel: single-pass tiles of 4 LPR units for the
 // matrices col1_single admits, two-pass tiles (col2_tile) for the others, in
 // one launch (tasks tallest first, so the long two-pass tiles start early).

@@ -1584,11 +1584,37 @@ __device__ __forceinline__ int owning_task(const TaskArgs<Task>& a, int item, in
   return count - 1;
 }
 
-// The task owning `item` (its index is uniform over the workgroup).
+// A value known to be uniform, moved word by word into scalar registers.
+template <class T>
+__device__ __forceinline__ T scalarize(const T& v) {
+  static_assert(sizeof(T) % 4 == 0, "whole words");
+  struct Words {
+    uint32_t w[sizeof(T) / 4];
+  };
+  Words a = __builtin_bit_cast(Words, v);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) a.w[i] = __builtin_amdgcn_readfirstlane(a.w[i]);
+  return __builtin_bit_cast(T, a);
+}
+
+// The task owning `item`, in scalar registers.  The owner comes from the
+// ballot search (none for a launch of one task); a task in the kernel
+// arguments is then read with scalar loads, one in a staged table with a
+// vector load whose words are moved to scalar registers.  Either way every
+// address the row's buffer resources are made from is uniform and in scalar
+// registers: a task left in VGPRs makes the compiler wrap each buffer load
+// and store of the row in a readfirstlane loop.  (A scan of the kernel
+// arguments' item starts on the scalar unit instead of the ballot was
+// measured slower: the compiler kept all 47 starts in SGPRs across the item
+// loop, spilling, and a 768-wide item's rows are short.)
 template <class Task>
 __device__ __forceinline__ Task task_of(const TaskArgs<Task>& a, int item, int lane) {
+  if (a.tasks == nullptr) {
+    const int lo = a.ntasks == 1 ? 0 : __builtin_amdgcn_readfirstlane(owning_task(a, item, lane));
+    return a.inline_tasks[lo];
+  }
   const int lo = __builtin_amdgcn_readfirstlane(owning_task(a, item, lane));
-  return a.tasks != nullptr ? a.tasks[lo] : a.inline_tasks[lo];
+  return scalarize(a.tasks[lo]);
 }
 
 // One item (R rows) of a task.  Shared by the one-shape kernel below and the
