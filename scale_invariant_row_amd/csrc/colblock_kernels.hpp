@@ -50,17 +50,6 @@ struct ColTaskOf<ColOp::kFwd> { using T = RownormTask; };
 template <>
 struct ColTaskOf<ColOp::kBwd> { using T = RownormGradTask; };
 
-// Global-memory view of a task pointer: plain loads through it compile to
-// global (not flat) accesses, counted only against the vector-memory counter.
-template <class T>
-__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
-  return (const __attribute__((address_space(1))) T*)p;
-}
-template <class T>
-__device__ __forceinline__ __attribute__((address_space(1))) T* gmem_out(T* p) {
-  return (__attribute__((address_space(1))) T*)p;
-}
-
 // The second input of a unit's sums: dL/dW_eff (bf16), the gradient or
 // momentum v (fp32, may be absent after a step), or none (forward).  It is
 // loaded as raw bits and converted once every load of a batch is in flight;
@@ -141,7 +130,7 @@ __device__ __forceinline__ void unit_coefficients(const Task& t, int64_t u, floa
   c[0] = c[1] = c[2] = 0.f;
   if constexpr (OP == ColOp::kFwd) {
     const float rn = sqrtf(T);
-    if (t.norm_out != nullptr) t.norm_out[u] = scaled ? ldexpf(rn, -sa) : rn;
+    if (t.norm_out != nullptr) gmem_out(t.norm_out)[u] = scaled ? ldexpf(rn, -sa) : rn;
     const float gr = row_gain(t, u) * t.radius;
     c[0] = (rn == 0.f) ? 0.f : gr / rn;
   } else if constexpr (OP == ColOp::kBwd) {
@@ -149,7 +138,7 @@ __device__ __forceinline__ void unit_coefficients(const Task& t, int64_t u, floa
     const float inv = inv_sqrt(T);
     float dg = (t.radius * P) * inv;
     if (scaled) dg = ldexpf(dg, -sb);
-    if (t.dgain != nullptr) t.dgain[u] = zero ? 0.f : dg;
+    if (t.dgain != nullptr) gmem_out(t.dgain)[u] = zero ? 0.f : dg;
     c[0] = zero ? 0.f : row_gain(t, u) * t.radius * inv;   // c
     c[1] = zero ? 0.f : (P * inv) * inv;                    // k
     c[2] = zero ? 1.f : 0.f;
@@ -807,7 +796,7 @@ colblock1_kernel(const TaskArgs<typename ColTaskOf<OP>::T> args) {
   // (tasks run tallest first, so task 0 tells) they would push the two-pass
   // tiles' first-pass lines out of L2 before their second pass: there the
   // reads are non-temporal.
-  const Task t0 = scalarize(args.tasks != nullptr ? args.tasks[0] : args.inline_tasks[0]);
+  const Task t0 = task_of(args, 0, lane);
   const bool cached = col1_single(t0.cols, t0.ld, K, LPR);
   int buf = 0;
   for (int item = first; item < nitems; item += G) {

@@ -1543,10 +1543,24 @@ struct RownormGradTask {
   int64_t ld;
 };
 
+// Global-memory view of a task pointer: plain loads and stores through it
+// compile to global (not flat) accesses, counted only against the
+// vector-memory counter.  A flat access also counts against the counter the
+// scalar loads wait on, so a row's last flat store would hold up the next
+// item's task load.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem_out(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // The gain of a row: its own, the matrix's one value, or 1 with no gain.
 template <class Task>
 __device__ __forceinline__ float row_gain(const Task& t, int64_t row) {
-  return t.gain != nullptr ? t.gain[row * t.gain_stride] : 1.f;
+  return t.gain != nullptr ? gmem(t.gain)[row * t.gain_stride] : 1.f;
 }
 
 // The tasks of one launch.  Up to kInlineTasks of them travel inside the
@@ -1671,7 +1685,7 @@ __device__ __forceinline__ void rownorm_item(const RownormTask& t, int item, con
     }
     const float rn = sqrtf(T);                       // length (of the scaled row)
     if (t.norm_out != nullptr && geo.g == 0 && geo.lane == 0)
-      t.norm_out[row] = scaled ? ldexpf(rn, -sh) : rn;
+      gmem_out(t.norm_out)[row] = scaled ? ldexpf(rn, -sh) : rn;
     const float c = (rn == 0.f) ? 0.f : gr / rn;
     const RowBuf eb(t.w_eff + row * t.cols, (uint32_t)t.cols * 2u);
     if (scaled) {
@@ -1786,7 +1800,7 @@ __device__ __forceinline__ void rownorm_backward_item(const RownormGradTask& t, 
     if (scaled) dg = ldexpf(dg, -sb);
     const float kk = zero ? 0.f : (P * inv) * inv;
     const float c = zero ? 0.f : gr * inv;
-    if (t.dgain != nullptr && geo.g == 0 && geo.lane == 0) t.dgain[row] = zero ? 0.f : dg;
+    if (t.dgain != nullptr && geo.g == 0 && geo.lane == 0) gmem_out(t.dgain)[row] = zero ? 0.f : dg;
     const RowBuf ob(t.dw + row * t.cols, (uint32_t)t.cols * 4u);
     const int sh = sa - sb;
     // three uniform cases, each a branch of its own (the empty asm keeps the
