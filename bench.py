@@ -9,7 +9,11 @@ Inputs are resident in HBM before timing starts; the steps rotate over
 several buffer sets whose total is well above the 256 MB last-level cache, so
 every launch streams from HBM.  The weight op (ds_weight_rownorm_gain over a
 12-layer transformer's 48 linears) is timed after the headline steps and
-reported beside them.
+reported beside them.  Two plain stream kernels (libdsbench.so, built beside
+the library) give the reference rates: y = x ^ r over bf16 rows with l2_rows'
+launch (the ``stream_ceiling`` of the roofline), and y = bf16(x) over fp32
+rows with the weight op's launch for the width (the ``stream_f32_ceiling``
+lines).
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (each input
 read once, each output written once) over its time, in GB/s.  The K steps are
